@@ -1,0 +1,194 @@
+/*
+ * CPU oracle for the fused PPO-family policy losses.
+ *
+ * TEST INFRASTRUCTURE ONLY.  The test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library; the product path (the
+ * HIP kernels behind include/rl_post_loss.h) never does, and shares no code
+ * with it.
+ *
+ * Plain C99, every quantity in double, the tokens visited one by one in
+ * row-major order.  The log-prob planes arrive already widened (exactly) from
+ * their storage dtype to double.  Nothing is blocked, fused or reordered
+ * beyond what the formulas state.
+ *
+ * Source: the model card "Geometric-AI Kernels" (Hugging Face page of
+ * Geometric-AI/geometric-ai-kernels):
+ *   - section "BNPO Loss": ratio, clipped, per_token and kl formulas, and the
+ *     global token-mean  loss = sum((per_token + beta*kl)*mask) / max(sum(mask), 1);
+ *   - section "GRPO Loss": per-response normalisation
+ *     loss = mean_r( sum_t((per_token + beta*kl)*mask) / max(sum_t(mask), 1) );
+ *   - section "Reverse KL": global token mean with an unclamped 1/sum(mask).
+ *
+ * Readings of points the card leaves open (each is also listed with its
+ * reason in the design notes):
+ *   - per_token = -A * min(ratio, clip(ratio, 1-eps, 1+eps_high)) literally;
+ *     when ratio equals its clipped value the unclipped branch is taken, so
+ *     d per_token / d lp = -A*ratio unless clipping lowered ratio to 1+eps_high.
+ *   - masked slots are selected out: they add nothing, their gradient is +0 and
+ *     their log-probs are never read.  Any nonzero mask byte means "valid".
+ *   - GRPO averages over all bs rows; a fully masked row adds 0 and still counts.
+ *   - Reverse-KL on per-token log-probs is the card's per-token KL estimator
+ *     exp(x) - x - 1 with x = teacher - student, averaged over valid tokens
+ *     with the unclamped 1/N, so an all-masked batch gives 0/0 = NaN loss and
+ *     a +0 gradient.
+ *
+ * Parity pins for every function here live in tests/test_oracle.py.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#define RLPL_ORACLE_VERSION 1
+
+int rlpl_oracle_version(void) { return RLPL_ORACLE_VERSION; }
+
+/* PPO-clipped ratio term of one token ("BNPO Loss": ratio, clipped, per_token).
+ * Returns per_token; *slope receives d per_token / d lp (d ratio / d lp = ratio). */
+static double clipped_ratio_term(double lp, double old, double adv, double lo, double hi,
+                                 double *slope)
+{
+    double ratio = exp(lp - old);
+    double clipped = ratio;
+    if (clipped < lo) clipped = lo;
+    if (clipped > hi) clipped = hi;
+    double chosen, dchosen;
+    if (ratio <= clipped) {
+        chosen = ratio;          /* min picks the unclipped ratio (ties included) */
+        dchosen = ratio;
+    } else {
+        chosen = clipped;        /* only when clipping lowered ratio to hi, a constant */
+        dchosen = 0.0;
+    }
+    *slope = -adv * dchosen;
+    return -adv * chosen;
+}
+
+/* k3 KL estimator of one token ("BNPO Loss": kl), x = ref - lp.
+ * Returns kl; *slope receives d kl / d lp = -(exp(x) - 1). */
+static double k3_kl(double lp, double ref, double *slope)
+{
+    double x = ref - lp;
+    double e = exp(x);
+    *slope = -(e - 1.0);
+    return e - x - 1.0;
+}
+
+/* Per-token loss contribution (per_token + beta*kl) and its derivative in lp. */
+static double token_term(const double *lp, const double *old, const double *ref,
+                         double adv, int64_t i, double beta, double lo, double hi,
+                         double *slope)
+{
+    double dpol;
+    double term = clipped_ratio_term(lp[i], old[i], adv, lo, hi, &dpol);
+    double dkl = 0.0;
+    if (beta != 0.0) {
+        double kl = k3_kl(lp[i], ref[i], &dkl);
+        term += beta * kl;
+    }
+    *slope = dpol + beta * dkl;
+    return term;
+}
+
+/*
+ * BNPO: loss = sum((per_token + beta*kl) * mask) / max(sum(mask), 1).
+ * grad[i] = d loss / d lp[i]  (mask[i] != 0), +0 otherwise.  grad may be NULL
+ * (loss only).  ref may be NULL when beta == 0.  *n_valid = sum(mask != 0).
+ * Returns 0, or -1 on a NULL required pointer / bad shape.
+ */
+int rlpl_oracle_bnpo(int64_t bs, int64_t seq_len, const double *lp, const double *old,
+                     const double *ref, const double *adv, const uint8_t *mask,
+                     double beta, double eps, double eps_high,
+                     double *loss, double *grad, int64_t *n_valid)
+{
+    if (bs < 0 || seq_len < 0 || !lp || !old || !adv || !mask || !loss || !n_valid) return -1;
+    if (beta != 0.0 && !ref) return -1;
+    const double lo = 1.0 - eps, hi = 1.0 + eps_high;
+    int64_t n = 0;
+    double sum = 0.0, slope;
+    for (int64_t r = 0; r < bs; ++r)
+        for (int64_t t = 0; t < seq_len; ++t) {
+            int64_t i = r * seq_len + t;
+            if (mask[i] == 0) continue;
+            ++n;
+            sum += token_term(lp, old, ref, adv[r], i, beta, lo, hi, &slope);
+        }
+    double denom = (double)n;
+    if (denom < 1.0) denom = 1.0;   /* max(mask.sum(), 1) */
+    *loss = sum / denom;
+    *n_valid = n;
+    if (grad)
+        for (int64_t r = 0; r < bs; ++r)
+            for (int64_t t = 0; t < seq_len; ++t) {
+                int64_t i = r * seq_len + t;
+                if (mask[i] == 0) { grad[i] = 0.0; continue; }
+                token_term(lp, old, ref, adv[r], i, beta, lo, hi, &slope);
+                grad[i] = slope / denom;
+            }
+    return 0;
+}
+
+/*
+ * GRPO: loss = (1/bs) * sum_r [ sum_t((per_token + beta*kl) * mask) / max(sum_t(mask), 1) ].
+ * grad[i] = d loss / d lp[i].  n_valid has bs entries (per-row counts).
+ */
+int rlpl_oracle_grpo(int64_t bs, int64_t seq_len, const double *lp, const double *old,
+                     const double *ref, const double *adv, const uint8_t *mask,
+                     double beta, double eps, double eps_high,
+                     double *loss, double *grad, int64_t *n_valid)
+{
+    if (bs < 0 || seq_len < 0 || !lp || !old || !adv || !mask || !loss || !n_valid) return -1;
+    if (beta != 0.0 && !ref) return -1;
+    const double lo = 1.0 - eps, hi = 1.0 + eps_high;
+    double total = 0.0, slope;
+    for (int64_t r = 0; r < bs; ++r) {
+        int64_t n = 0;
+        double row_sum = 0.0;
+        for (int64_t t = 0; t < seq_len; ++t) {
+            int64_t i = r * seq_len + t;
+            if (mask[i] == 0) continue;
+            ++n;
+            row_sum += token_term(lp, old, ref, adv[r], i, beta, lo, hi, &slope);
+        }
+        double denom = (double)n;
+        if (denom < 1.0) denom = 1.0;   /* max(mask.sum(-1), 1) */
+        total += row_sum / denom;
+        n_valid[r] = n;
+        if (grad)
+            for (int64_t t = 0; t < seq_len; ++t) {
+                int64_t i = r * seq_len + t;
+                if (mask[i] == 0) { grad[i] = 0.0; continue; }
+                token_term(lp, old, ref, adv[r], i, beta, lo, hi, &slope);
+                grad[i] = slope / (denom * (double)bs);
+            }
+    }
+    *loss = bs > 0 ? total / (double)bs : 0.0;   /* mean over the bs rows */
+    return 0;
+}
+
+/*
+ * Reverse-KL on per-token log-probs: x = teacher - student,
+ * loss = sum(mask * (exp(x) - x - 1)) / sum(mask)  (unclamped: 0/0 = NaN when
+ * every token is masked), grad[i] = (1 - exp(x)) / sum(mask) on valid tokens,
+ * +0 elsewhere.
+ */
+int rlpl_oracle_rkl(int64_t bs, int64_t seq_len, const double *student, const double *teacher,
+                    const uint8_t *mask, double *loss, double *grad, int64_t *n_valid)
+{
+    if (bs < 0 || seq_len < 0 || !student || !teacher || !mask || !loss || !n_valid) return -1;
+    int64_t n = 0;
+    double sum = 0.0, slope;
+    for (int64_t i = 0; i < bs * seq_len; ++i) {
+        if (mask[i] == 0) continue;
+        ++n;
+        sum += k3_kl(student[i], teacher[i], &slope);
+    }
+    *loss = sum / (double)n;   /* not clamped: 0/0 is NaN when no token is valid */
+    *n_valid = n;
+    if (grad)
+        for (int64_t i = 0; i < bs * seq_len; ++i) {
+            if (mask[i] == 0) { grad[i] = 0.0; continue; }
+            k3_kl(student[i], teacher[i], &slope);
+            grad[i] = slope / (double)n;
+        }
+    return 0;
+}

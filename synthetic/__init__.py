@@ -1,0 +1,150 @@
+"""Seeded synthetic inputs for the fused PPO-family policy losses.
+
+This module only draws random numbers and lays them out. It holds none of the
+loss arithmetic, so both the CPU oracle and the HIP path can take their inputs
+from it without sharing any part of the method.
+
+Shapes and value distributions follow the workloads the loss kernels are run
+on (model card "Geometric-AI Kernels", sections "BNPO Loss", "GRPO Loss" and
+"Reverse KL": per-token log-prob planes of shape (bs, seq_len) in
+fp32/fp16/bf16, per-row advantages of shape (bs,), a bool or int8 completion
+mask of shape (bs, seq_len)):
+
+* policy log-probs = -|N(0,1)|, rounded to the plane dtype;
+* old-policy log-probs = policy + N(0, 0.05), rounded;
+* reference log-probs  = policy + N(0, 0.1), rounded;
+* advantages = N(0, 1) per row, rounded to the plane dtype;
+* completion mask = a prefix of integer length U[lo, hi] (both ends
+  inclusive) per row; optionally a fixed number of rows fully masked;
+* reverse-KL: student = -|N(0,1)|, teacher = student + N(0, 0.3).
+
+All draws come from ``numpy.random.default_rng(seed)`` (PCG64) in float64, in
+the fixed order listed in ``policy_inputs`` / ``rkl_inputs``.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field, replace
+from typing import Optional
+
+import numpy as np
+import torch
+
+DTYPES = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}
+MASK_DTYPES = {"bool": torch.bool, "int8": torch.int8}
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One loss invocation: which loss, its shape, dtypes, parameters and mask recipe."""
+    name: str
+    op: str                 # "bnpo", "bnpo_fwd", "grpo", "rkl"
+    dtype: str              # plane dtype: fp32 / fp16 / bf16
+    mask_dtype: str         # bool / int8
+    bs: int
+    seq_len: int
+    len_lo: int             # prefix length drawn from U[len_lo, len_hi]
+    len_hi: int
+    beta: float = 0.0
+    epsilon: float = 0.2
+    epsilon_high: float = 0.28
+    masked_rows: int = 0    # rows forced fully masked (drawn without replacement)
+    seed: int = 0
+
+    def with_(self, **kw) -> "Workload":
+        return replace(self, **kw)
+
+    @property
+    def slots(self) -> int:
+        return self.bs * self.seq_len
+
+
+# The five workloads the path is specified on.  Where a parameter is not given
+# for a workload, the value of the neighbouring workloads is used (eps=0.2,
+# eps_high=0.28; int8 masks for the BNPO/GRPO planes, bool for reverse-KL; seed 0).
+WORKLOADS = {
+    "bnpo_fp32_4x64": Workload("bnpo_fp32_4x64", "bnpo", "fp32", "bool", 4, 64, 1, 64,
+                               beta=0.04, epsilon=0.2, epsilon_high=0.28),
+    "bnpo_bf16_16x1024": Workload("bnpo_bf16_16x1024", "bnpo", "bf16", "int8", 16, 1024, 1, 1024,
+                                  beta=0.04, epsilon=0.2, epsilon_high=0.28),
+    "bnpo_bf16_64x4096": Workload("bnpo_bf16_64x4096", "bnpo", "bf16", "int8", 64, 4096, 256, 4096,
+                                  beta=0.04, epsilon=0.2, epsilon_high=0.28),
+    "grpo_fp16_128x2048": Workload("grpo_fp16_128x2048", "grpo", "fp16", "int8", 128, 2048, 1, 2048,
+                                   beta=0.04, epsilon=0.2, epsilon_high=0.2,
+                                   masked_rows=round(0.05 * 128)),
+    "rkl_bf16_256x8192": Workload("rkl_bf16_256x8192", "rkl", "bf16", "bool", 256, 8192, 1024, 8192),
+}
+
+
+def _round(x: np.ndarray, dtype: str) -> torch.Tensor:
+    """Round a float64 array to the plane dtype (torch CPU conversion, round-to-nearest-even)."""
+    return torch.from_numpy(np.ascontiguousarray(x)).to(DTYPES[dtype])
+
+
+def _prefix_mask(lengths: np.ndarray, seq_len: int, mask_dtype: str) -> torch.Tensor:
+    m = np.arange(seq_len, dtype=np.int64)[None, :] < lengths[:, None]
+    return torch.from_numpy(m).to(MASK_DTYPES[mask_dtype])
+
+
+def _lengths(rng: np.random.Generator, w: Workload) -> np.ndarray:
+    lengths = rng.integers(w.len_lo, w.len_hi + 1, size=w.bs)
+    if w.masked_rows:
+        rows = rng.choice(w.bs, size=w.masked_rows, replace=False)
+        lengths[rows] = 0
+    return lengths
+
+
+def policy_inputs(w: Workload) -> dict:
+    """Inputs of the BNPO/GRPO losses, as CPU tensors.
+
+    Draw order: z1 (bs,T) -> policy; z2 (bs,T) -> old; z3 (bs,T) -> ref;
+    z4 (bs,) -> advantages; prefix lengths; the fully-masked rows.
+    """
+    rng = np.random.default_rng(w.seed)
+    shape = (w.bs, w.seq_len)
+    policy = _round(-np.abs(rng.standard_normal(shape)), w.dtype)
+    pol64 = policy.to(torch.float64).numpy()
+    old = _round(pol64 + 0.05 * rng.standard_normal(shape), w.dtype)
+    ref = _round(pol64 + 0.1 * rng.standard_normal(shape), w.dtype)
+    adv = _round(rng.standard_normal(w.bs), w.dtype)
+    lengths = _lengths(rng, w)
+    mask = _prefix_mask(lengths, w.seq_len, w.mask_dtype)
+    return {"policy": policy, "old": old, "ref": ref, "advantages": adv, "mask": mask,
+            "lengths": lengths}
+
+
+def rkl_inputs(w: Workload) -> dict:
+    """Inputs of the per-token reverse-KL loss, as CPU tensors.
+
+    Draw order: z1 (bs,T) -> student; z2 (bs,T) -> teacher; prefix lengths.
+    """
+    rng = np.random.default_rng(w.seed)
+    shape = (w.bs, w.seq_len)
+    student = _round(-np.abs(rng.standard_normal(shape)), w.dtype)
+    teacher = _round(student.to(torch.float64).numpy() + 0.3 * rng.standard_normal(shape), w.dtype)
+    lengths = _lengths(rng, w)
+    mask = _prefix_mask(lengths, w.seq_len, w.mask_dtype)
+    return {"student": student, "teacher": teacher, "mask": mask, "lengths": lengths}
+
+
+def inputs(w: Workload) -> dict:
+    return rkl_inputs(w) if w.op == "rkl" else policy_inputs(w)
+
+
+def device_policy_inputs(w: Workload, device: str) -> dict:
+    """Large-size inputs drawn directly on the device with torch's seeded generator.
+
+    Same distributions as ``policy_inputs`` (not the same values); used where
+    host-side float64 generation would be too slow (size sweeps).
+    """
+    g = torch.Generator(device=device)
+    g.manual_seed(w.seed)
+    shape = (w.bs, w.seq_len)
+    dt = DTYPES[w.dtype]
+    policy = (-torch.randn(shape, generator=g, device=device, dtype=torch.float32).abs()).to(dt)
+    pf = policy.float()
+    old = (pf + 0.05 * torch.randn(shape, generator=g, device=device)).to(dt)
+    ref = (pf + 0.1 * torch.randn(shape, generator=g, device=device)).to(dt)
+    adv = torch.randn(w.bs, generator=g, device=device).to(dt)
+    lengths = torch.randint(w.len_lo, w.len_hi + 1, (w.bs,), generator=g, device=device)
+    mask = (torch.arange(w.seq_len, device=device)[None, :] < lengths[:, None]).to(MASK_DTYPES[w.mask_dtype])
+    return {"policy": policy, "old": old, "ref": ref, "advantages": adv, "mask": mask}
