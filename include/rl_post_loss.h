@@ -1,0 +1,187 @@
+/*
+ * rl_post_loss: fused forward+backward PPO-family policy losses on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * One call = one kernel launch on the caller's stream that returns the scalar
+ * loss and, for the fused forward+backward entry points, the gradient of the
+ * loss with respect to the policy (student) log-probs, with no host
+ * synchronisation.  The operations are defined on the model card
+ * "Geometric-AI Kernels" (Hugging Face, Geometric-AI/geometric-ai-kernels),
+ * sections "BNPO Loss", "GRPO Loss" and "Reverse KL".
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers are device pointers (hipMalloc'd or torch CUDA-tensor storage)
+ * unless stated otherwise.  The caller allocates and owns every buffer; the
+ * library never allocates or frees device memory.
+ *
+ * Layouts: log-prob planes and the mask are dense row-major (bs, seq_len) with
+ * no strides; `advantages` is dense (bs,).  The planes, the mask and grad_out
+ * must be 16-byte aligned (every kernel streams them with 128-bit accesses);
+ * advantages needs only element alignment, loss_out and n_valid_out 4-byte
+ * alignment.
+ *
+ * dtype (RLPL_F32 / RLPL_F16 / RLPL_BF16) applies to the log-prob planes, the
+ * advantages and grad_out.  mask_dtype (RLPL_MASK_BOOL / RLPL_MASK_INT8) is one
+ * byte per slot; any nonzero byte marks a valid (completion) token.  Masked
+ * slots contribute nothing, get a +0 gradient and their log-probs are never
+ * read.  All arithmetic is float32 in registers; the loss is always written as
+ * one float32 (device memory); grad_out is written in `dtype`, rounded to
+ * nearest even, for every slot (masked slots included).
+ *
+ * Workspace: `workspace` is device memory of at least
+ * rlpl_workspace_bytes(bs, seq_len, op) bytes, 256-byte aligned, zero-filled
+ * once by the caller before its first use.  Every call leaves it in the state
+ * the next call needs, so it is re-used as is.  Only one call may be in flight
+ * per workspace (calls on one stream are serialised and may share one).
+ *
+ * Errors: arguments are validated on the host before anything is enqueued; a
+ * rejected call enqueues nothing and returns a nonzero rlpl_status.  A failed
+ * launch returns RLPL_ERR_LAUNCH.  RLPL_OK means the launch was enqueued; the
+ * call does not synchronise, so device faults surface at the caller's next
+ * synchronisation.  Results of an enqueued call are valid once the stream has
+ * reached it.  Inputs must be finite (masked slots excepted).
+ *
+ * The functions are thread-safe; the first call on a device queries and caches
+ * that device's compute-unit count and kernel occupancies.
+ */
+#ifndef RL_POST_LOSS_H
+#define RL_POST_LOSS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* The HIP stream handle, as hip_runtime_api.h declares it. */
+typedef struct ihipStream_t* hipStream_t;
+
+enum rlpl_dtype { RLPL_F32 = 0, RLPL_F16 = 1, RLPL_BF16 = 2 };
+enum rlpl_mask_dtype { RLPL_MASK_BOOL = 0, RLPL_MASK_INT8 = 1 };
+
+/* Operation selector for rlpl_workspace_bytes. */
+enum rlpl_op {
+    RLPL_OP_BNPO = 0, RLPL_OP_BNPO_FWD = 1, RLPL_OP_GRPO = 2, RLPL_OP_GRPO_FWD = 3,
+    RLPL_OP_RKL = 4, RLPL_OP_RKL_FWD = 5
+};
+
+enum rlpl_status {
+    RLPL_OK = 0,
+    RLPL_ERR_NULL = 1,       /* a required pointer is NULL                                 */
+    RLPL_ERR_SHAPE = 2,      /* bs < 1, seq_len < 1, or bs*seq_len >= 2^31                  */
+    RLPL_ERR_ALIGN = 3,      /* a plane, mask or grad pointer is not 16-byte aligned, or     */
+                             /* advantages / loss / counts / workspace misaligned            */
+    RLPL_ERR_DTYPE = 4,      /* unknown dtype or mask_dtype                                  */
+    RLPL_ERR_PARAM = 5,      /* non-finite beta/epsilon/epsilon_high, or 1-eps > 1+eps_high  */
+    RLPL_ERR_WORKSPACE = 6,  /* workspace NULL or smaller than rlpl_workspace_bytes          */
+    RLPL_ERR_DEVICE = 7,     /* no current HIP device, or it is not gfx950-capable           */
+    RLPL_ERR_LAUNCH = 8      /* the kernel launch failed                                     */
+};
+
+/*
+ * BNPO, fused forward + backward (model card, "BNPO Loss").
+ *
+ *   ratio     = exp(policy_lp - old_lp)
+ *   clipped   = clip(ratio, 1 - epsilon, 1 + epsilon_high)
+ *   per_token = -advantages[row] * min(ratio, clipped)
+ *   kl        = exp(ref_lp - policy_lp) - (ref_lp - policy_lp) - 1
+ *   loss      = sum((per_token + beta * kl) * mask) / max(sum(mask), 1)
+ *
+ * The global valid-token count sum(mask) is formed on the GPU in the same
+ * launch (no host round trip).  grad_out[i] = d loss / d policy_lp[i]; where
+ * ratio equals its clipped value the unclipped branch is taken, so the
+ * policy part of the gradient is -A*ratio/N unless clipping lowered ratio to
+ * 1+epsilon_high (then 0).  With beta == 0.0f the KL term is compiled out and
+ * ref_lp is never read (it may be NULL).
+ *
+ * policy_lp, old_lp, ref_lp : (bs, seq_len) `dtype`, 16-byte aligned
+ * advantages                : (bs,) `dtype`
+ * mask                      : (bs, seq_len) bytes, 16-byte aligned
+ * loss_out                  : 1 float (written)
+ * grad_out                  : (bs, seq_len) `dtype`, 16-byte aligned (written, every slot)
+ * n_valid_out               : 1 uint32 = sum(mask != 0) (written), or NULL
+ */
+int bnpo_loss(const void* policy_lp, const void* old_lp, const void* ref_lp,
+              const void* advantages, const void* mask, int64_t bs, int64_t seq_len,
+              int dtype, int mask_dtype, float beta, float epsilon, float epsilon_high,
+              float* loss_out, void* grad_out, uint32_t* n_valid_out,
+              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* BNPO, forward only: the same loss as bnpo_loss (bit-identical for the same
+ * inputs on the same device), no gradient buffer. */
+int bnpo_loss_fwd(const void* policy_lp, const void* old_lp, const void* ref_lp,
+                  const void* advantages, const void* mask, int64_t bs, int64_t seq_len,
+                  int dtype, int mask_dtype, float beta, float epsilon, float epsilon_high,
+                  float* loss_out, uint32_t* n_valid_out,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * GRPO, fused forward + backward (model card, "GRPO Loss"): the per-token
+ * terms of bnpo_loss, normalised per response and averaged over the batch:
+ *
+ *   loss = (1/bs) * sum_r [ sum_t((per_token + beta*kl) * mask) / max(sum_t(mask), 1) ]
+ *
+ * All bs rows count in the mean; a fully masked row adds 0.  Each row's count
+ * is reduced inside the workgroups that touch the row (no cross-workgroup
+ * exchange before the gradient is scaled).  n_valid_out, if not NULL, receives
+ * bs uint32 per-row counts.  Arguments as for bnpo_loss.
+ */
+int grpo_loss(const void* policy_lp, const void* old_lp, const void* ref_lp,
+              const void* advantages, const void* mask, int64_t bs, int64_t seq_len,
+              int dtype, int mask_dtype, float beta, float epsilon, float epsilon_high,
+              float* loss_out, void* grad_out, uint32_t* n_valid_out,
+              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* GRPO, forward only: the same loss as grpo_loss (bit-identical), no gradient. */
+int grpo_loss_fwd(const void* policy_lp, const void* old_lp, const void* ref_lp,
+                  const void* advantages, const void* mask, int64_t bs, int64_t seq_len,
+                  int dtype, int mask_dtype, float beta, float epsilon, float epsilon_high,
+                  float* loss_out, uint32_t* n_valid_out,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Reverse KL(student || teacher) self-distillation on per-token log-probs
+ * (model card, "Reverse KL": global token mean with the unclamped
+ * inv_n_valid = 1/sum(mask), gradient scaled by mask[r]*inv_n_valid), using
+ * the card's per-token KL estimator with x = teacher_lp - student_lp:
+ *
+ *   loss = sum(mask * (exp(x) - x - 1)) / sum(mask)
+ *   grad_out[i] = mask[i] ? (1 - exp(x_i)) / sum(mask) : +0
+ *
+ * A batch with no valid token gives loss = NaN (0/0, as on the card) and an
+ * all +0 gradient; it is not an error.  student_lp, teacher_lp: (bs, seq_len)
+ * `dtype`, 16-byte aligned; the rest as for bnpo_loss.
+ */
+int reverse_kl(const void* student_lp, const void* teacher_lp, const void* mask,
+               int64_t bs, int64_t seq_len, int dtype, int mask_dtype,
+               float* loss_out, void* grad_out, uint32_t* n_valid_out,
+               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Reverse KL, forward only: the same loss as reverse_kl (bit-identical), no gradient. */
+int reverse_kl_fwd(const void* student_lp, const void* teacher_lp, const void* mask,
+                   int64_t bs, int64_t seq_len, int dtype, int mask_dtype,
+                   float* loss_out, uint32_t* n_valid_out,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace an `op` call on a (bs, seq_len) problem needs (0 for a bad op). */
+size_t rlpl_workspace_bytes(int64_t bs, int64_t seq_len, int op);
+
+/* Sticky error bits the kernels left in a workspace (host pointer `flags_out`
+ * receives them; synchronises `stream`).  Bit 0: a cross-workgroup wait gave
+ * up after its time limit, so that call's results are not valid and the
+ * workspace must be zero-filled again before its next use. */
+int rlpl_workspace_flags(const void* workspace, uint32_t* flags_out, hipStream_t stream);
+
+/* Human-readable name of an rlpl_status value (static string). */
+const char* rlpl_status_string(int status);
+
+/* ABI version of this library. */
+int rlpl_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RL_POST_LOSS_H */

@@ -1,0 +1,243 @@
+"""Fused forward+backward PPO-family policy losses on MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``librl_post_loss.so`` (declared in
+``include/rl_post_loss.h``).  It only marshals arguments: it checks and
+flattens tensors, allocates the outputs and the per-stream workspace with
+torch, and passes raw device pointers plus the current HIP stream.  Every step
+of the loss runs in the library's HIP kernels; there is no fallback.  If the
+library is missing it is built from ``csrc/`` with hipcc; if that fails, or no
+gfx950 GPU is current, the calls raise.
+
+Entry points (model card "Geometric-AI Kernels": sections "BNPO Loss",
+"GRPO Loss", "Reverse KL"; the same names as the C ABI):
+
+* ``bnpo_loss(lp, old, ref, advantages, mask, epsilon=, epsilon_high=, beta=)`` -> (loss, grad)
+* ``bnpo_loss_fwd(...)`` -> loss
+* ``grpo_loss(...)`` -> (loss, grad);  ``grpo_loss_fwd(...)`` -> loss
+* ``reverse_kl(student_lp, teacher_lp, mask)`` -> (loss, grad);  ``reverse_kl_fwd(...)`` -> loss
+
+``loss`` is a 0-d float32 tensor on the device; ``grad`` has the dtype and
+shape of the policy/student log-probs.  Pass ``return_n_valid=True`` to also
+get the valid-token count(s) as an int32 tensor (one entry, or bs for GRPO).
+``workspace=`` takes a caller-owned zero-initialised uint8 tensor of
+``rlpl_workspace_bytes`` bytes; by default one workspace per (device, stream)
+is created on first use and reused.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch  # loaded first so the library binds to torch's HIP runtime
+
+from . import build as _build
+
+__all__ = ["bnpo_loss", "bnpo_loss_fwd", "grpo_loss", "grpo_loss_fwd", "reverse_kl",
+           "reverse_kl_fwd", "library", "library_path", "RlplError", "STATUS", "workspace_for"]
+
+STATUS = {0: "RLPL_OK", 1: "RLPL_ERR_NULL", 2: "RLPL_ERR_SHAPE", 3: "RLPL_ERR_ALIGN",
+          4: "RLPL_ERR_DTYPE", 5: "RLPL_ERR_PARAM", 6: "RLPL_ERR_WORKSPACE", 7: "RLPL_ERR_DEVICE",
+          8: "RLPL_ERR_LAUNCH"}
+DTYPE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+MASK_DTYPE = {torch.bool: 0, torch.int8: 1, torch.uint8: 1}
+OP = {"bnpo": 0, "bnpo_fwd": 1, "grpo": 2, "grpo_fwd": 3, "rkl": 4, "rkl_fwd": 5}
+
+
+class RlplError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        msg = library().rlpl_status_string(status).decode()
+        super().__init__(f"{fn}: {msg}")
+
+
+_lib = None
+_lock = threading.Lock()
+_workspaces: dict = {}
+
+
+def library_path() -> str:
+    return _build.LIB
+
+
+def _declare(lib):
+    vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+    sz = ctypes.c_size_t
+    policy = [vp, vp, vp, vp, vp, i64, i64, i32, i32, f32, f32, f32, vp, vp, vp, vp, sz, vp]
+    policy_fwd = [vp, vp, vp, vp, vp, i64, i64, i32, i32, f32, f32, f32, vp, vp, vp, sz, vp]
+    rkl = [vp, vp, vp, i64, i64, i32, i32, vp, vp, vp, vp, sz, vp]
+    rkl_fwd = [vp, vp, vp, i64, i64, i32, i32, vp, vp, vp, sz, vp]
+    for name, args in (("bnpo_loss", policy), ("grpo_loss", policy), ("bnpo_loss_fwd", policy_fwd),
+                       ("grpo_loss_fwd", policy_fwd), ("reverse_kl", rkl), ("reverse_kl_fwd", rkl_fwd)):
+        f = getattr(lib, name)
+        f.argtypes, f.restype = args, ctypes.c_int
+    lib.rlpl_workspace_bytes.argtypes, lib.rlpl_workspace_bytes.restype = [i64, i64, i32], sz
+    lib.rlpl_workspace_flags.argtypes = [vp, ctypes.POINTER(ctypes.c_uint32), vp]
+    lib.rlpl_workspace_flags.restype = ctypes.c_int
+    lib.rlpl_status_string.argtypes, lib.rlpl_status_string.restype = [i32], ctypes.c_char_p
+    lib.rlpl_version.argtypes, lib.rlpl_version.restype = [], ctypes.c_int
+    return lib
+
+
+def library():
+    """The loaded C library (built from csrc/ first if it is not there)."""
+    global _lib
+    if _lib is None:
+        with _lock:
+            if _lib is None:
+                if not os.path.exists(_build.LIB):
+                    _build.build()
+                _lib = _declare(ctypes.CDLL(_build.LIB))
+    return _lib
+
+
+def workspace_for(device: torch.device, stream_ptr: int, op: str = "bnpo") -> torch.Tensor:
+    """The zero-initialised workspace used for calls on (device, stream); reused across calls."""
+    key = (device.index, stream_ptr)
+    ws = _workspaces.get(key)
+    if ws is None:
+        nbytes = library().rlpl_workspace_bytes(1, 1, OP[op])
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def _aligned(t: torch.Tensor) -> torch.Tensor:
+    t = t.contiguous()
+    return t if t.data_ptr() % 16 == 0 else t.clone()
+
+
+def _plane(t: torch.Tensor, name: str, shape, dtype=None) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dim() != 2 or (shape is not None and tuple(t.shape) != tuple(shape)):
+        raise ValueError(f"{name} must have shape (bs, seq_len){'' if shape is None else ' = ' + str(tuple(shape))}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must have dtype {dtype}, got {t.dtype}")
+    return _aligned(t)
+
+
+def _mask(m: torch.Tensor, shape) -> torch.Tensor:
+    if m.dtype not in MASK_DTYPE:
+        raise TypeError("completions_mask must be bool, int8 or uint8")
+    return _plane(m, "completions_mask", shape)
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise RlplError(fn, status)
+
+
+def _workspace(dev, stream, op, workspace):
+    if workspace is None:
+        return workspace_for(dev, stream, op)
+    if workspace.device != dev or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor on the inputs' device")
+    return workspace
+
+
+def _policy(op: str, fused: bool, policy_logprobs, old_policy_logprobs, ref_logprobs, advantages,
+            completions_mask, epsilon, epsilon_high, beta, return_n_valid, workspace):
+    lp = policy_logprobs.detach()
+    if lp.dtype not in DTYPE:
+        raise TypeError("log-probs must be float32, float16 or bfloat16")
+    lp = _plane(lp, "policy_logprobs", None)
+    bs, T = lp.shape
+    old = _plane(old_policy_logprobs.detach(), "old_policy_logprobs", lp.shape, lp.dtype)
+    beta = float(beta)
+    ref = None
+    if ref_logprobs is not None:
+        ref = _plane(ref_logprobs.detach(), "ref_logprobs", lp.shape, lp.dtype)
+    adv = advantages.detach().contiguous()
+    if adv.dtype != lp.dtype or tuple(adv.shape) != (bs,) or not adv.is_cuda:
+        raise ValueError(f"advantages must be a ({bs},) CUDA tensor of dtype {lp.dtype}")
+    mask = _mask(completions_mask.detach(), lp.shape)
+    eps_high = epsilon if epsilon_high is None else epsilon_high
+    dev = lp.device
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    ws = _workspace(dev, stream, op, workspace)
+    loss = torch.empty((), dtype=torch.float32, device=dev)
+    grad = torch.empty_like(lp) if fused else None
+    n = torch.empty(bs if op.startswith("grpo") else 1, dtype=torch.int32, device=dev) \
+        if return_n_valid else None
+    lib = library()
+    name = f"{op}_loss" + ("" if fused else "_fwd")
+    args = [lp.data_ptr(), old.data_ptr(), None if ref is None else ref.data_ptr(), adv.data_ptr(),
+            mask.data_ptr(), bs, T, DTYPE[lp.dtype], MASK_DTYPE[mask.dtype], beta, float(epsilon),
+            float(eps_high), loss.data_ptr()]
+    if fused:
+        args.append(grad.data_ptr())
+    args += [None if n is None else n.data_ptr(), ws.data_ptr(), ws.numel(), stream]
+    _check(name, getattr(lib, name)(*args))
+    out = (loss, grad) if fused else (loss,)
+    if return_n_valid:
+        out = out + (n,)
+    return out if len(out) > 1 else out[0]
+
+
+def bnpo_loss(policy_logprobs, old_policy_logprobs, ref_logprobs, advantages, completions_mask, *,
+              epsilon=0.2, epsilon_high=None, beta=0.0, return_n_valid=False, workspace=None):
+    """BNPO fused forward+backward: (loss, d loss / d policy_logprobs) from one launch."""
+    return _policy("bnpo", True, policy_logprobs, old_policy_logprobs, ref_logprobs, advantages,
+                   completions_mask, epsilon, epsilon_high, beta, return_n_valid, workspace)
+
+
+def bnpo_loss_fwd(policy_logprobs, old_policy_logprobs, ref_logprobs, advantages, completions_mask,
+                  *, epsilon=0.2, epsilon_high=None, beta=0.0, return_n_valid=False, workspace=None):
+    """BNPO forward only: the scalar loss, no gradient buffer."""
+    return _policy("bnpo", False, policy_logprobs, old_policy_logprobs, ref_logprobs, advantages,
+                   completions_mask, epsilon, epsilon_high, beta, return_n_valid, workspace)
+
+
+def grpo_loss(policy_logprobs, old_policy_logprobs, ref_logprobs, advantages, completions_mask, *,
+              epsilon=0.2, epsilon_high=None, beta=0.0, return_n_valid=False, workspace=None):
+    """GRPO (per-response normalised) fused forward+backward: (loss, grad)."""
+    return _policy("grpo", True, policy_logprobs, old_policy_logprobs, ref_logprobs, advantages,
+                   completions_mask, epsilon, epsilon_high, beta, return_n_valid, workspace)
+
+
+def grpo_loss_fwd(policy_logprobs, old_policy_logprobs, ref_logprobs, advantages, completions_mask,
+                  *, epsilon=0.2, epsilon_high=None, beta=0.0, return_n_valid=False, workspace=None):
+    """GRPO forward only: the scalar loss."""
+    return _policy("grpo", False, policy_logprobs, old_policy_logprobs, ref_logprobs, advantages,
+                   completions_mask, epsilon, epsilon_high, beta, return_n_valid, workspace)
+
+
+def _rkl(fused: bool, student_logprobs, teacher_logprobs, completions_mask, return_n_valid, workspace):
+    s = student_logprobs.detach()
+    if s.dtype not in DTYPE:
+        raise TypeError("log-probs must be float32, float16 or bfloat16")
+    s = _plane(s, "student_logprobs", None)
+    bs, T = s.shape
+    t = _plane(teacher_logprobs.detach(), "teacher_logprobs", s.shape, s.dtype)
+    mask = _mask(completions_mask.detach(), s.shape)
+    dev = s.device
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    ws = _workspace(dev, stream, "rkl", workspace)
+    loss = torch.empty((), dtype=torch.float32, device=dev)
+    grad = torch.empty_like(s) if fused else None
+    n = torch.empty(1, dtype=torch.int32, device=dev) if return_n_valid else None
+    lib = library()
+    args = [s.data_ptr(), t.data_ptr(), mask.data_ptr(), bs, T, DTYPE[s.dtype], MASK_DTYPE[mask.dtype],
+            loss.data_ptr()]
+    if fused:
+        args.append(grad.data_ptr())
+    args += [None if n is None else n.data_ptr(), ws.data_ptr(), ws.numel(), stream]
+    name = "reverse_kl" if fused else "reverse_kl_fwd"
+    _check(name, getattr(lib, name)(*args))
+    out = (loss, grad) if fused else (loss,)
+    if return_n_valid:
+        out = out + (n,)
+    return out if len(out) > 1 else out[0]
+
+
+def reverse_kl(student_logprobs, teacher_logprobs, completions_mask, *, return_n_valid=False,
+               workspace=None):
+    """Per-token reverse KL(student || teacher), fused forward+backward: (loss, d loss / d student)."""
+    return _rkl(True, student_logprobs, teacher_logprobs, completions_mask, return_n_valid, workspace)
+
+
+def reverse_kl_fwd(student_logprobs, teacher_logprobs, completions_mask, *, return_n_valid=False,
+                   workspace=None):
+    """Per-token reverse KL, forward only: the scalar loss."""
+    return _rkl(False, student_logprobs, teacher_logprobs, completions_mask, return_n_valid, workspace)

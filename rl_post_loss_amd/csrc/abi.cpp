@@ -1,0 +1,278 @@
+// C ABI of the fused policy-loss library (declared in include/rl_post_loss.h).
+//
+// Each entry point validates its arguments on the host (no HIP call before
+// they pass), then picks the kernel instantiation <dtype, mode, KL on/off,
+// gradient on/off>, sizes the persistent grid from the per-device
+// occupancy cache and enqueues exactly one launch on the caller's stream.
+// Nothing here allocates device memory or synchronises the stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+
+#include "loss_kernels.h"
+#include "rl_post_loss.h"
+
+namespace {
+
+using rlpl::Args;
+using rlpl::kModeBNPO;
+using rlpl::kModeGRPO;
+using rlpl::kModeRKL;
+
+constexpr int kAbiVersion = 1;
+constexpr int kMaxDevices = 64;
+
+// Per-device launch facts, filled once per device (thread-safe) and then read-only.
+struct DeviceInfo {
+    int status = RLPL_ERR_DEVICE;
+    int grid_cap[3][3] = {};     // [dtype][mode]: co-resident workgroups of the family
+};
+DeviceInfo g_info[kMaxDevices];
+std::once_flag g_once[kMaxDevices];
+
+void init_device(int dev, DeviceInfo& info) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return;
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return;
+    if (cus <= 0) return;
+    for (int dt = 0; dt < 3; ++dt)
+        for (int mode = 0; mode < 3; ++mode) {
+            // The whole family shares one grid size so that its forward-only and
+            // fwd+bwd kernels reduce over identical partitions (identical losses),
+            // and that size never exceeds what is co-resident on the device, which
+            // the fwd+bwd count exchange relies on.
+            int occ = 1 << 30;
+            for (int kl = 0; kl < 2; ++kl)
+                for (int wg = 0; wg < 2; ++wg) {
+                    const void* k = rlpl::pick_kernel(dt, mode, kl != 0 || mode == kModeRKL, wg != 0);
+                    int nb = 0;
+                    if (!k || hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k, rlpl::kThreads, 0) !=
+                                  hipSuccess || nb < 1)
+                        return;
+                    if (nb < occ) occ = nb;
+                }
+            long cap = long(occ) * cus;
+            if (cap > rlpl::kMaxGrid) cap = rlpl::kMaxGrid;
+            info.grid_cap[dt][mode] = int(cap);
+        }
+    info.status = RLPL_OK;
+}
+
+int current_device(const DeviceInfo** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return RLPL_ERR_DEVICE;
+    std::call_once(g_once[dev], [dev] { init_device(dev, g_info[dev]); });
+    *out = &g_info[dev];
+    return g_info[dev].status;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+size_t elem_bytes(int dtype) { return dtype == RLPL_F32 ? 4 : 2; }
+
+// Shape, dtype and the pointers every operation shares.
+int check_common(const void* mask, int64_t bs, int64_t seq_len, int dtype, int mask_dtype,
+                 const float* loss_out, const uint32_t* n_valid_out, const void* workspace,
+                 size_t workspace_bytes) {
+    if (!mask || !loss_out) return RLPL_ERR_NULL;
+    if (bs < 1 || seq_len < 1 || bs > (int64_t(1) << 31) / seq_len ||
+        bs * seq_len >= (int64_t(1) << 31))
+        return RLPL_ERR_SHAPE;
+    if (dtype != RLPL_F32 && dtype != RLPL_F16 && dtype != RLPL_BF16) return RLPL_ERR_DTYPE;
+    if (mask_dtype != RLPL_MASK_BOOL && mask_dtype != RLPL_MASK_INT8) return RLPL_ERR_DTYPE;
+    if (!aligned(mask, 16) || !aligned(loss_out, 4) || (n_valid_out && !aligned(n_valid_out, 4)))
+        return RLPL_ERR_ALIGN;
+    if (!workspace || workspace_bytes < rlpl::kWorkspaceBytes) return RLPL_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return RLPL_ERR_ALIGN;
+    return RLPL_OK;
+}
+
+// A plain launch: the grid is capped at the co-resident capacity, so every
+// workgroup of an exchange kernel is resident together on an otherwise idle
+// device (and, with other work present, becomes resident as that work drains;
+// the exchange wait is also bounded in time).  A cooperative launch would
+// guarantee the same but costs ~16 us of extra dispatch latency per call here.
+int launch(const void* kernel, const Args& a, int64_t grid, hipStream_t stream) {
+    void* params[] = {const_cast<Args*>(&a)};
+    const hipError_t e =
+        hipLaunchKernel(kernel, dim3(unsigned(grid)), dim3(rlpl::kThreads), params, 0, stream);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();   // clear the sticky launch error
+        return RLPL_ERR_LAUNCH;
+    }
+    return RLPL_OK;
+}
+
+// Shared tail of every entry point: grid sizing and the launch.
+int run(int mode, bool write_grad, bool has_kl, Args& a, int dtype, hipStream_t stream) {
+    const DeviceInfo* info = nullptr;
+    const int st = current_device(&info);
+    if (st != RLPL_OK) return st;
+    const void* kernel = rlpl::pick_kernel(dtype, mode, has_kl, write_grad);
+    if (!kernel) return RLPL_ERR_DTYPE;
+    a.tiles = (a.slots + rlpl::kTile - 1) / rlpl::kTile;
+    const int64_t cap = info->grid_cap[dtype][mode];
+    const int64_t grid = a.tiles < cap ? a.tiles : cap;
+    return launch(kernel, a, grid, stream);
+}
+
+int policy_loss(int mode, bool write_grad, const void* policy_lp, const void* old_lp,
+                const void* ref_lp, const void* advantages, const void* mask, int64_t bs,
+                int64_t seq_len, int dtype, int mask_dtype, float beta, float epsilon,
+                float epsilon_high, float* loss_out, void* grad_out, uint32_t* n_valid_out,
+                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    int st = check_common(mask, bs, seq_len, dtype, mask_dtype, loss_out, n_valid_out, workspace,
+                          workspace_bytes);
+    if (st != RLPL_OK) return st;
+    const bool has_kl = beta != 0.0f;
+    if (!policy_lp || !old_lp || !advantages || (has_kl && !ref_lp) || (write_grad && !grad_out))
+        return RLPL_ERR_NULL;
+    if (!aligned(policy_lp, 16) || !aligned(old_lp, 16) || (has_kl && !aligned(ref_lp, 16)) ||
+        (write_grad && !aligned(grad_out, 16)) || !aligned(advantages, elem_bytes(dtype)))
+        return RLPL_ERR_ALIGN;
+    if (!std::isfinite(beta) || !std::isfinite(epsilon) || !std::isfinite(epsilon_high))
+        return RLPL_ERR_PARAM;
+    const float lo = 1.0f - epsilon, hi = 1.0f + epsilon_high;
+    if (!(lo <= hi)) return RLPL_ERR_PARAM;
+
+    Args a{};
+    a.lp = policy_lp;
+    a.old = old_lp;
+    a.ref = has_kl ? ref_lp : nullptr;
+    a.adv = advantages;
+    a.mask = static_cast<const uint8_t*>(mask);
+    a.grad = write_grad ? grad_out : nullptr;
+    a.loss = loss_out;
+    a.n_out = n_valid_out;
+    a.ws = static_cast<rlpl::Workspace*>(workspace);
+    a.slots = bs * seq_len;
+    a.seq_len = int32_t(seq_len);
+    a.bs = int32_t(bs);
+    a.beta = beta;
+    a.lo = lo;
+    a.hi = hi;
+    return run(mode, write_grad, has_kl, a, dtype, stream);
+}
+
+int rkl_loss(bool write_grad, const void* student_lp, const void* teacher_lp, const void* mask,
+             int64_t bs, int64_t seq_len, int dtype, int mask_dtype, float* loss_out,
+             void* grad_out, uint32_t* n_valid_out, void* workspace, size_t workspace_bytes,
+             hipStream_t stream) {
+    int st = check_common(mask, bs, seq_len, dtype, mask_dtype, loss_out, n_valid_out, workspace,
+                          workspace_bytes);
+    if (st != RLPL_OK) return st;
+    if (!student_lp || !teacher_lp || (write_grad && !grad_out)) return RLPL_ERR_NULL;
+    if (!aligned(student_lp, 16) || !aligned(teacher_lp, 16) || (write_grad && !aligned(grad_out, 16)))
+        return RLPL_ERR_ALIGN;
+    Args a{};
+    a.lp = student_lp;
+    a.ref = teacher_lp;
+    a.mask = static_cast<const uint8_t*>(mask);
+    a.grad = write_grad ? grad_out : nullptr;
+    a.loss = loss_out;
+    a.n_out = n_valid_out;
+    a.ws = static_cast<rlpl::Workspace*>(workspace);
+    a.slots = bs * seq_len;
+    a.seq_len = int32_t(seq_len);
+    a.bs = int32_t(bs);
+    a.beta = 1.0f;
+    return run(kModeRKL, write_grad, true, a, dtype, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int bnpo_loss(const void* policy_lp, const void* old_lp, const void* ref_lp, const void* advantages,
+              const void* mask, int64_t bs, int64_t seq_len, int dtype, int mask_dtype, float beta,
+              float epsilon, float epsilon_high, float* loss_out, void* grad_out,
+              uint32_t* n_valid_out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return policy_loss(kModeBNPO, true, policy_lp, old_lp, ref_lp, advantages, mask, bs, seq_len,
+                       dtype, mask_dtype, beta, epsilon, epsilon_high, loss_out, grad_out,
+                       n_valid_out, workspace, workspace_bytes, stream);
+}
+
+int bnpo_loss_fwd(const void* policy_lp, const void* old_lp, const void* ref_lp,
+                  const void* advantages, const void* mask, int64_t bs, int64_t seq_len, int dtype,
+                  int mask_dtype, float beta, float epsilon, float epsilon_high, float* loss_out,
+                  uint32_t* n_valid_out, void* workspace, size_t workspace_bytes,
+                  hipStream_t stream) {
+    return policy_loss(kModeBNPO, false, policy_lp, old_lp, ref_lp, advantages, mask, bs, seq_len,
+                       dtype, mask_dtype, beta, epsilon, epsilon_high, loss_out, nullptr,
+                       n_valid_out, workspace, workspace_bytes, stream);
+}
+
+int grpo_loss(const void* policy_lp, const void* old_lp, const void* ref_lp, const void* advantages,
+              const void* mask, int64_t bs, int64_t seq_len, int dtype, int mask_dtype, float beta,
+              float epsilon, float epsilon_high, float* loss_out, void* grad_out,
+              uint32_t* n_valid_out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return policy_loss(kModeGRPO, true, policy_lp, old_lp, ref_lp, advantages, mask, bs, seq_len,
+                       dtype, mask_dtype, beta, epsilon, epsilon_high, loss_out, grad_out,
+                       n_valid_out, workspace, workspace_bytes, stream);
+}
+
+int grpo_loss_fwd(const void* policy_lp, const void* old_lp, const void* ref_lp,
+                  const void* advantages, const void* mask, int64_t bs, int64_t seq_len, int dtype,
+                  int mask_dtype, float beta, float epsilon, float epsilon_high, float* loss_out,
+                  uint32_t* n_valid_out, void* workspace, size_t workspace_bytes,
+                  hipStream_t stream) {
+    return policy_loss(kModeGRPO, false, policy_lp, old_lp, ref_lp, advantages, mask, bs, seq_len,
+                       dtype, mask_dtype, beta, epsilon, epsilon_high, loss_out, nullptr,
+                       n_valid_out, workspace, workspace_bytes, stream);
+}
+
+int reverse_kl(const void* student_lp, const void* teacher_lp, const void* mask, int64_t bs,
+               int64_t seq_len, int dtype, int mask_dtype, float* loss_out, void* grad_out,
+               uint32_t* n_valid_out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return rkl_loss(true, student_lp, teacher_lp, mask, bs, seq_len, dtype, mask_dtype, loss_out,
+                    grad_out, n_valid_out, workspace, workspace_bytes, stream);
+}
+
+int reverse_kl_fwd(const void* student_lp, const void* teacher_lp, const void* mask, int64_t bs,
+                   int64_t seq_len, int dtype, int mask_dtype, float* loss_out,
+                   uint32_t* n_valid_out, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream) {
+    return rkl_loss(false, student_lp, teacher_lp, mask, bs, seq_len, dtype, mask_dtype, loss_out,
+                    nullptr, n_valid_out, workspace, workspace_bytes, stream);
+}
+
+size_t rlpl_workspace_bytes(int64_t bs, int64_t seq_len, int op) {
+    (void)bs;
+    (void)seq_len;
+    if (op < RLPL_OP_BNPO || op > RLPL_OP_RKL_FWD) return 0;
+    return rlpl::kWorkspaceBytes;
+}
+
+int rlpl_workspace_flags(const void* workspace, uint32_t* flags_out, hipStream_t stream) {
+    if (!workspace || !flags_out) return RLPL_ERR_NULL;
+    if (!aligned(workspace, 256)) return RLPL_ERR_ALIGN;
+    const auto* src = static_cast<const unsigned char*>(workspace) + rlpl::kFlagsOffset;
+    if (hipMemcpyAsync(flags_out, src, sizeof(uint32_t), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+        return RLPL_ERR_LAUNCH;
+    return RLPL_OK;
+}
+
+const char* rlpl_status_string(int status) {
+    switch (status) {
+    case RLPL_OK: return "RLPL_OK";
+    case RLPL_ERR_NULL: return "RLPL_ERR_NULL: a required pointer is NULL";
+    case RLPL_ERR_SHAPE: return "RLPL_ERR_SHAPE: need bs >= 1, seq_len >= 1, bs*seq_len < 2^31";
+    case RLPL_ERR_ALIGN: return "RLPL_ERR_ALIGN: a pointer breaks the alignment contract";
+    case RLPL_ERR_DTYPE: return "RLPL_ERR_DTYPE: unknown dtype or mask dtype";
+    case RLPL_ERR_PARAM: return "RLPL_ERR_PARAM: non-finite parameter or 1-epsilon > 1+epsilon_high";
+    case RLPL_ERR_WORKSPACE: return "RLPL_ERR_WORKSPACE: workspace missing or too small";
+    case RLPL_ERR_DEVICE: return "RLPL_ERR_DEVICE: no usable gfx950 device is current";
+    case RLPL_ERR_LAUNCH: return "RLPL_ERR_LAUNCH: the kernel launch failed";
+    }
+    return "unknown rlpl status";
+}
+
+int rlpl_version(void) { return kAbiVersion; }
+
+}  // extern "C"

@@ -1,0 +1,100 @@
+"""Comparison of the HIP path with the oracle at the stated tolerances.
+
+* fp32 planes: loss relative error <= 1e-5, gradient absolute error <= 1e-6.
+* fp16 / bf16 planes: loss relative error <= 1e-3, gradient within 2 ulp of
+  the output dtype (ulp taken at the oracle's value).
+* valid-token counts: bit-exact.
+
+Tokens whose ratio lies within 1e-5 (relative) of 1 + epsilon_high sit on the
+clip kink: fp32 and double may take different branches there, and either
+branch's gradient is accepted (the loss is continuous, so it is unaffected).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+import oracle
+
+MANT = {torch.float32: 23, torch.float16: 10, torch.bfloat16: 7}
+MIN_NORMAL_EXP = {torch.float32: -126, torch.float16: -14, torch.bfloat16: -126}
+
+
+def ulp(x: np.ndarray, dtype) -> np.ndarray:
+    """Spacing of `dtype` at |x| (subnormal spacing below the normal range)."""
+    ax = np.abs(np.asarray(x, dtype=np.float64))
+    _, e = np.frexp(ax)                       # ax = m * 2^e, m in [0.5, 1)
+    e = np.maximum(e - 1, MIN_NORMAL_EXP[dtype])
+    return np.ldexp(1.0, e - MANT[dtype])
+
+
+def f32(v: float) -> float:
+    """The float32 value the GPU receives for a scalar parameter."""
+    return float(np.float32(v))
+
+
+def kink_tokens(policy, old, mask, epsilon_high) -> np.ndarray:
+    lp, od = oracle.to_f64(policy), oracle.to_f64(old)
+    hi = 1.0 + f32(epsilon_high)
+    ratio = np.exp(lp - od)
+    return (np.abs(ratio - hi) <= 1e-5 * hi) & (oracle.to_mask_u8(mask) != 0)
+
+
+def kink_alternative(grad_ref, policy, old, advantages, mask, epsilon_high, scale):
+    """Oracle gradient with the other clip branch taken at every token (used only at kinks)."""
+    lp, od = oracle.to_f64(policy), oracle.to_f64(old)
+    a = oracle.to_f64(advantages)[:, None]
+    hi = 1.0 + f32(epsilon_high)
+    ratio = np.exp(lp - od)
+    unclipped = ratio <= hi
+    g_pol = -a * ratio * scale
+    return np.where(unclipped, grad_ref - g_pol, grad_ref + g_pol)
+
+
+def check_loss(got: float, want: float, dtype, what=""):
+    tol = 1e-5 if dtype == torch.float32 else 1e-3
+    if math.isnan(want):
+        assert math.isnan(got), f"{what}: loss {got}, oracle NaN"
+        return 0.0
+    if want == 0.0:
+        assert got == 0.0, f"{what}: loss {got}, oracle 0"
+        return 0.0
+    rel = abs(got - want) / abs(want)
+    assert rel <= tol, f"{what}: loss {got!r} vs oracle {want!r}: rel err {rel:.3e} > {tol}"
+    return rel
+
+
+def grad_errors(got: np.ndarray, want: np.ndarray, dtype, alt: np.ndarray | None = None,
+                kinks: np.ndarray | None = None):
+    """Per-element error and allowance; at kink tokens the closer branch is used."""
+    err = np.abs(got - want)
+    if alt is not None and kinks is not None and kinks.any():
+        err = np.where(kinks, np.minimum(err, np.abs(got - alt)), err)
+    if dtype == torch.float32:
+        allow = np.full_like(want, 1e-6)
+    else:
+        allow = 2.0 * ulp(want, dtype)
+    return err, allow
+
+
+def check_grad(got_t: torch.Tensor, want: np.ndarray, dtype, what="", alt=None, kinks=None):
+    got = got_t.detach().cpu().to(torch.float64).numpy()
+    assert got.shape == want.shape
+    err, allow = grad_errors(got, want, dtype, alt, kinks)
+    bad = err > allow
+    if bad.any():
+        i = np.unravel_index(np.argmax(err / allow), err.shape)
+        raise AssertionError(
+            f"{what}: {int(bad.sum())} of {bad.size} gradient elements out of tolerance; worst at "
+            f"{i}: got {got[i]!r} oracle {want[i]!r} (allowed {allow[i]:.3e})")
+    # masked slots must be exactly +0
+    return float(np.max(err / allow)) if err.size else 0.0
+
+
+def check_masked_zero(grad_t: torch.Tensor, mask_t: torch.Tensor, what=""):
+    g = grad_t.detach().cpu().to(torch.float32)
+    m = mask_t.detach().cpu() != 0
+    z = g[~m]
+    assert torch.all(z == 0) and not torch.any(torch.signbit(z)), f"{what}: masked slots not +0"

@@ -1,0 +1,188 @@
+"""The C ABI on the host: exported symbols, constants and argument validation.
+
+Validation is pure host code that runs before any HIP call, so every status
+below is checked without a GPU.  Pointers here are fake integers: the calls
+must reject them before touching the device (the one call that passes
+validation is only made when no GPU is present).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import rl_post_loss_amd as rl
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "rl_post_loss.h")
+
+A = 0x7F0000001000          # a fake 16-byte-aligned "device" address
+WS = 0x7F0000100000         # fake 256-byte-aligned workspace
+
+
+def header_text():
+    src = open(HEADER).read()
+    return re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+
+
+def declared_functions():
+    return re.findall(r"^\s*(?:int|size_t|const char\*)\s+(\w+)\s*\(", header_text(), flags=re.M)
+
+
+def header_enum(name):
+    body = re.search(r"enum\s+%s\s*\{(.*?)\}" % name, header_text(), flags=re.S).group(1)
+    return {k: int(v) for k, v in re.findall(r"(\w+)\s*=\s*(\d+)", body)}
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return rl.library()
+
+
+def test_library_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert set(names) >= {"bnpo_loss", "bnpo_loss_fwd", "grpo_loss", "grpo_loss_fwd", "reverse_kl",
+                          "reverse_kl_fwd", "rlpl_workspace_bytes", "rlpl_workspace_flags",
+                          "rlpl_status_string", "rlpl_version"}
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.rlpl_version() == 1
+
+
+def test_header_constants_match_binding():
+    st = header_enum("rlpl_status")
+    assert {v: k for k, v in st.items()} == rl.STATUS
+    dt = header_enum("rlpl_dtype")
+    assert dt == {"RLPL_F32": rl.DTYPE[torch.float32], "RLPL_F16": rl.DTYPE[torch.float16],
+                  "RLPL_BF16": rl.DTYPE[torch.bfloat16]}
+    md = header_enum("rlpl_mask_dtype")
+    assert md == {"RLPL_MASK_BOOL": rl.MASK_DTYPE[torch.bool], "RLPL_MASK_INT8": rl.MASK_DTYPE[torch.int8]}
+    ops = header_enum("rlpl_op")
+    assert ops == {"RLPL_OP_" + k.upper(): v for k, v in rl.OP.items()}
+
+
+def test_status_strings(lib):
+    seen = set()
+    for code, name in rl.STATUS.items():
+        s = lib.rlpl_status_string(code).decode()
+        assert s.startswith(name)
+        seen.add(s)
+    assert len(seen) == len(rl.STATUS)
+    assert "unknown" in lib.rlpl_status_string(99).decode()
+
+
+def test_workspace_bytes(lib):
+    for op in range(6):
+        n = lib.rlpl_workspace_bytes(64, 4096, op)
+        assert n >= 256 + 4 * 1024 and n % 256 == 0
+    assert lib.rlpl_workspace_bytes(64, 4096, 6) == 0
+    assert lib.rlpl_workspace_bytes(64, 4096, -1) == 0
+
+
+def _bnpo_args(**over):
+    a = dict(lp=A, old=A + 0x100000, ref=A + 0x200000, adv=A + 0x300000, mask=A + 0x400000,
+             bs=4, T=64, dtype=2, mask_dtype=1, beta=0.04, eps=0.2, eps_high=0.28,
+             loss=A + 0x500000, grad=A + 0x600000, n=A + 0x700000, ws=WS, ws_bytes=1 << 20,
+             stream=None)
+    a.update(over)
+    return a
+
+
+def call_bnpo(lib, fused=True, **over):
+    a = _bnpo_args(**over)
+    args = [a["lp"], a["old"], a["ref"], a["adv"], a["mask"], a["bs"], a["T"], a["dtype"],
+            a["mask_dtype"], a["beta"], a["eps"], a["eps_high"], a["loss"]]
+    if fused:
+        args.append(a["grad"])
+    args += [a["n"], a["ws"], a["ws_bytes"], a["stream"]]
+    return (lib.bnpo_loss if fused else lib.bnpo_loss_fwd)(*args)
+
+
+def call_rkl(lib, fused=True, **over):
+    a = _bnpo_args(**over)
+    args = [a["lp"], a["ref"], a["mask"], a["bs"], a["T"], a["dtype"], a["mask_dtype"], a["loss"]]
+    if fused:
+        args.append(a["grad"])
+    args += [a["n"], a["ws"], a["ws_bytes"], a["stream"]]
+    return (lib.reverse_kl if fused else lib.reverse_kl_fwd)(*args)
+
+
+CASES = [
+    ("RLPL_ERR_NULL", dict(lp=None)),
+    ("RLPL_ERR_NULL", dict(old=None)),
+    ("RLPL_ERR_NULL", dict(adv=None)),
+    ("RLPL_ERR_NULL", dict(mask=None)),
+    ("RLPL_ERR_NULL", dict(loss=None)),
+    ("RLPL_ERR_NULL", dict(ref=None)),                 # beta != 0 needs ref
+    ("RLPL_ERR_SHAPE", dict(bs=0)),
+    ("RLPL_ERR_SHAPE", dict(T=0)),
+    ("RLPL_ERR_SHAPE", dict(bs=-3)),
+    ("RLPL_ERR_SHAPE", dict(bs=1 << 16, T=1 << 15)),   # exactly 2^31 slots
+    ("RLPL_ERR_SHAPE", dict(bs=1 << 40, T=1 << 40)),   # overflow guard
+    ("RLPL_ERR_DTYPE", dict(dtype=3)),
+    ("RLPL_ERR_DTYPE", dict(dtype=-1)),
+    ("RLPL_ERR_DTYPE", dict(mask_dtype=2)),
+    ("RLPL_ERR_ALIGN", dict(lp=A + 2)),
+    ("RLPL_ERR_ALIGN", dict(old=A + 8)),
+    ("RLPL_ERR_ALIGN", dict(ref=A + 4)),
+    ("RLPL_ERR_ALIGN", dict(mask=A + 0x400000 + 1)),
+    ("RLPL_ERR_ALIGN", dict(adv=A + 0x300000 + 1)),
+    ("RLPL_ERR_ALIGN", dict(loss=A + 0x500000 + 2)),
+    ("RLPL_ERR_ALIGN", dict(n=A + 0x700000 + 1)),
+    ("RLPL_ERR_ALIGN", dict(ws=WS + 64)),
+    ("RLPL_ERR_PARAM", dict(beta=float("nan"))),
+    ("RLPL_ERR_PARAM", dict(beta=float("inf"))),
+    ("RLPL_ERR_PARAM", dict(eps=float("nan"))),
+    ("RLPL_ERR_PARAM", dict(eps_high=float("-inf"))),
+    ("RLPL_ERR_PARAM", dict(eps=-0.5, eps_high=-0.6)),  # 1-eps > 1+eps_high
+    ("RLPL_ERR_WORKSPACE", dict(ws=None)),
+    ("RLPL_ERR_WORKSPACE", dict(ws_bytes=1024)),
+]
+
+
+@pytest.mark.parametrize("want,over", CASES, ids=[f"{w}-{list(o)[0]}" for w, o in CASES])
+def test_bnpo_validation(lib, want, over):
+    assert rl.STATUS[call_bnpo(lib, **over)] == want
+    if "grad" not in over:
+        assert rl.STATUS[call_bnpo(lib, fused=False, **over)] == want
+
+
+def test_fused_needs_grad_and_grad_alignment(lib):
+    assert rl.STATUS[call_bnpo(lib, grad=None)] == "RLPL_ERR_NULL"
+    assert rl.STATUS[call_bnpo(lib, grad=A + 0x600000 + 2)] == "RLPL_ERR_ALIGN"
+    for fn in (lib.grpo_loss,):
+        a = _bnpo_args(grad=None)
+        assert rl.STATUS[fn(a["lp"], a["old"], a["ref"], a["adv"], a["mask"], 4, 64, 2, 1, 0.04,
+                            0.2, 0.28, a["loss"], None, None, WS, 1 << 20, None)] == "RLPL_ERR_NULL"
+
+
+def test_rkl_validation(lib):
+    assert rl.STATUS[call_rkl(lib, lp=None)] == "RLPL_ERR_NULL"
+    assert rl.STATUS[call_rkl(lib, ref=None)] == "RLPL_ERR_NULL"
+    assert rl.STATUS[call_rkl(lib, grad=None)] == "RLPL_ERR_NULL"
+    assert rl.STATUS[call_rkl(lib, lp=A + 2)] == "RLPL_ERR_ALIGN"
+    assert rl.STATUS[call_rkl(lib, T=0)] == "RLPL_ERR_SHAPE"
+    assert rl.STATUS[call_rkl(lib, dtype=7)] == "RLPL_ERR_DTYPE"
+    assert rl.STATUS[call_rkl(lib, ws_bytes=0)] == "RLPL_ERR_WORKSPACE"
+
+
+def test_workspace_flags_validation(lib):
+    flags = ctypes.c_uint32(0)
+    assert rl.STATUS[lib.rlpl_workspace_flags(None, ctypes.byref(flags), None)] == "RLPL_ERR_NULL"
+    assert rl.STATUS[lib.rlpl_workspace_flags(WS + 4, ctypes.byref(flags), None)] == "RLPL_ERR_ALIGN"
+
+
+def test_beta_zero_allows_missing_ref_without_a_device(lib):
+    # Passes validation (beta == 0 compiles the KL term out, ref may be NULL) and then
+    # stops at the device check: only meaningful, and only safe, on a host with no GPU.
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present: a call that passes validation would launch")
+    assert rl.STATUS[call_bnpo(lib, beta=0.0, ref=None)] == "RLPL_ERR_DEVICE"
+    assert rl.STATUS[call_rkl(lib)] == "RLPL_ERR_DEVICE"
+
+
+def test_binding_rejects_cpu_tensors():
+    x = torch.zeros(2, 16)
+    with pytest.raises(TypeError):
+        rl.bnpo_loss(x, x, x, torch.zeros(2), torch.ones(2, 16, dtype=torch.bool), beta=0.04)

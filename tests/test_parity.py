@@ -1,0 +1,293 @@
+"""Parity of the HIP kernels (through the C ABI binding) with the CPU oracle.
+
+Every workload runs at its full size (the oracle finishes each in well under a
+second), element by element, at the tolerances in parity.py.  Edge cases
+cover empty and ragged inputs, tails shorter than a lane, seq_len not a
+multiple of 16, one-slot rows, odd int8 mask bytes, grids where every
+workgroup owns several tiles, and rows longer than a tile.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import rl_post_loss_amd as rl
+import synthetic
+from parity import (check_grad, check_loss, check_masked_zero, f32, kink_alternative, kink_tokens)
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+TORCH_DT = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}
+
+
+def dev(x):
+    return {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+
+
+def gpu_policy(op, fused, g, beta, eps, eps_high, ref=True):
+    fn = {("bnpo", True): rl.bnpo_loss, ("bnpo", False): rl.bnpo_loss_fwd,
+          ("grpo", True): rl.grpo_loss, ("grpo", False): rl.grpo_loss_fwd}[(op, fused)]
+    out = fn(g["policy"], g["old"], g["ref"] if ref else None, g["advantages"], g["mask"],
+             epsilon=eps, epsilon_high=eps_high, beta=beta, return_n_valid=True)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_policy(op, x, beta, eps, eps_high):
+    fn = oracle.bnpo if op == "bnpo" else oracle.grpo
+    return fn(x["policy"], x["old"], x["ref"], x["advantages"], x["mask"], f32(beta), f32(eps),
+              f32(eps_high))
+
+
+def assert_policy_parity(op, x, beta, eps, eps_high, what, fused=True):
+    g = dev(x)
+    ref = oracle_policy(op, x, beta, eps, eps_high)
+    out = gpu_policy(op, fused, g, beta, eps, eps_high, ref=beta != 0.0)
+    loss, n = (out[0], out[-1])
+    dt = x["policy"].dtype
+    check_loss(float(loss.cpu()), ref.loss, dt, what)
+    if op == "bnpo":
+        assert int(n.cpu()[0]) == ref.n_valid, what
+    else:
+        np.testing.assert_array_equal(n.cpu().numpy().astype(np.int64), ref.n_valid, err_msg=what)
+    if fused:
+        grad = out[1]
+        assert grad.dtype == dt and grad.shape == x["policy"].shape
+        if op == "bnpo":
+            scale = 1.0 / max(ref.n_valid, 1)
+        else:
+            scale = (1.0 / (np.maximum(ref.n_valid, 1) * x["policy"].shape[0]))[:, None]
+        kinks = kink_tokens(x["policy"], x["old"], x["mask"], eps_high)
+        alt = kink_alternative(ref.grad, x["policy"], x["old"], x["advantages"], x["mask"],
+                               eps_high, scale)
+        check_grad(grad, ref.grad, dt, what, alt, kinks)
+        check_masked_zero(grad, x["mask"], what)
+    return out
+
+
+def assert_rkl_parity(x, what, fused=True):
+    g = dev(x)
+    ref = oracle.rkl(x["student"], x["teacher"], x["mask"])
+    fn = rl.reverse_kl if fused else rl.reverse_kl_fwd
+    out = fn(g["student"], g["teacher"], g["mask"], return_n_valid=True)
+    torch.cuda.synchronize()
+    dt = x["student"].dtype
+    check_loss(float(out[0].cpu()), ref.loss, dt, what)
+    assert int(out[-1].cpu()[0]) == ref.n_valid, what
+    if fused:
+        check_grad(out[1], ref.grad, dt, what)
+        check_masked_zero(out[1], x["mask"], what)
+    return out
+
+
+# --------------------------------------------------------------------------- the five workloads
+
+@pytest.mark.parametrize("name", ["bnpo_fp32_4x64", "bnpo_bf16_16x1024", "bnpo_bf16_64x4096",
+                                  "grpo_fp16_128x2048"])
+def test_workload_parity(name):
+    w = synthetic.WORKLOADS[name]
+    x = synthetic.inputs(w)
+    print(f"[parity] {name} beta={w.beta}", flush=True)
+    assert_policy_parity(w.op, x, w.beta, w.epsilon, w.epsilon_high, name)
+    assert_policy_parity(w.op, x, w.beta, w.epsilon, w.epsilon_high, name + " fwd", fused=False)
+
+
+def test_bnpo_64x4096_beta0_kl_compiled_out():
+    w = synthetic.WORKLOADS["bnpo_bf16_64x4096"].with_(beta=0.0)
+    x = synthetic.inputs(w)
+    assert_policy_parity("bnpo", x, 0.0, w.epsilon, w.epsilon_high, "beta0")
+    assert_policy_parity("bnpo", x, 0.0, w.epsilon, w.epsilon_high, "beta0 fwd", fused=False)
+
+
+def test_rkl_workload_parity():
+    w = synthetic.WORKLOADS["rkl_bf16_256x8192"]
+    x = synthetic.inputs(w)
+    print("[parity] rkl_bf16_256x8192", flush=True)
+    assert_rkl_parity(x, "rkl")
+    assert_rkl_parity(x, "rkl fwd", fused=False)
+
+
+# --------------------------------------------------------------------------- exactness properties
+
+@pytest.mark.parametrize("op", ["bnpo", "grpo", "rkl"])
+def test_forward_only_loss_equals_fused_loss_bitwise(op):
+    if op == "rkl":
+        x = dev(synthetic.inputs(synthetic.WORKLOADS["rkl_bf16_256x8192"]))
+        a = rl.reverse_kl(x["student"], x["teacher"], x["mask"])[0]
+        b = rl.reverse_kl_fwd(x["student"], x["teacher"], x["mask"])
+    else:
+        w = synthetic.WORKLOADS["bnpo_bf16_64x4096" if op == "bnpo" else "grpo_fp16_128x2048"]
+        x = dev(synthetic.inputs(w))
+        kw = dict(epsilon=w.epsilon, epsilon_high=w.epsilon_high, beta=w.beta)
+        fused, fwd = (rl.bnpo_loss, rl.bnpo_loss_fwd) if op == "bnpo" else (rl.grpo_loss, rl.grpo_loss_fwd)
+        a = fused(x["policy"], x["old"], x["ref"], x["advantages"], x["mask"], **kw)[0]
+        b = fwd(x["policy"], x["old"], x["ref"], x["advantages"], x["mask"], **kw)
+    assert a.cpu().view(torch.int32).item() == b.cpu().view(torch.int32).item()
+
+
+def test_repeated_calls_are_bitwise_identical_and_rearm_the_workspace():
+    w = synthetic.WORKLOADS["bnpo_bf16_64x4096"]
+    x = dev(synthetic.inputs(w))
+    kw = dict(epsilon=w.epsilon, epsilon_high=w.epsilon_high, beta=w.beta)
+    l0, g0 = rl.bnpo_loss(x["policy"], x["old"], x["ref"], x["advantages"], x["mask"], **kw)
+    for _ in range(50):
+        l1, g1 = rl.bnpo_loss(x["policy"], x["old"], x["ref"], x["advantages"], x["mask"], **kw)
+        assert torch.equal(l1.view(torch.int32), l0.view(torch.int32))
+        assert torch.equal(g1.view(torch.int16), g0.view(torch.int16))
+    torch.cuda.synchronize()
+    ws = rl.workspace_for(DEV, torch.cuda.current_stream(DEV).cuda_stream, "bnpo")
+    head = ws[:1280].cpu()
+    gen = int(head[0:4].view(torch.int32)[0]) & 0xFFFFFFFF
+    w64 = head.view(torch.int64).numpy()
+    arrive, release, depart = int(w64[32]), int(w64[64]) & (2**64 - 1), int(w64[96])
+    assert arrive == 0 and depart == 0                 # count exchange and tickets re-armed
+    assert (release >> 32) == gen                      # last exchange's tag = its generation + 1
+    assert int(head[1024:1028].view(torch.int32)[0]) == 0   # no timeout flag
+    import ctypes
+    flags = ctypes.c_uint32(7)
+    assert rl.library().rlpl_workspace_flags(ws.data_ptr(), ctypes.byref(flags),
+                                             torch.cuda.current_stream(DEV).cuda_stream) == 0
+    assert flags.value == 0
+
+
+def test_lower_clip_bound_has_no_effect():
+    w = synthetic.WORKLOADS["bnpo_bf16_16x1024"]
+    x = dev(synthetic.inputs(w))
+    base = rl.bnpo_loss(x["policy"], x["old"], x["ref"], x["advantages"], x["mask"],
+                        epsilon=0.2, epsilon_high=0.28, beta=0.04)
+    for eps in (0.0, 0.5, 0.9):
+        o = rl.bnpo_loss(x["policy"], x["old"], x["ref"], x["advantages"], x["mask"],
+                         epsilon=eps, epsilon_high=0.28, beta=0.04)
+        assert torch.equal(o[0], base[0]) and torch.equal(o[1], base[1])
+
+
+# --------------------------------------------------------------------------- edge cases
+
+def _custom(op, dtype, bs, T, mask_kind="prefix", seed=5, mask_dtype="int8", lo=0, hi=None):
+    w = synthetic.Workload("edge", op, dtype, mask_dtype, bs, T, lo, T if hi is None else hi, seed=seed)
+    x = synthetic.inputs(w)
+    rng = np.random.default_rng(seed + 100)
+    if mask_kind == "random":
+        m = rng.random((bs, T)) < 0.6
+        x["mask"] = torch.from_numpy(m).to(synthetic.MASK_DTYPES[mask_dtype])
+    elif mask_kind == "none":
+        x["mask"] = torch.zeros(bs, T, dtype=synthetic.MASK_DTYPES[mask_dtype])
+    elif mask_kind == "odd_bytes":
+        v = rng.integers(-128, 128, size=(bs, T)).astype(np.int8)
+        v[rng.random((bs, T)) < 0.4] = 0
+        x["mask"] = torch.from_numpy(v)
+    return x
+
+
+SHAPES = [(1, 1), (1, 5), (3, 37), (2, 17), (5, 3), (7, 1), (4, 1000), (2, 4097), (1, 4096),
+          (3, 16), (9, 4095)]
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16", "fp16"])
+@pytest.mark.parametrize("bs,T", SHAPES)
+def test_edge_shapes_bnpo_grpo(dtype, bs, T):
+    x = _custom("bnpo", dtype, bs, T, "random", seed=bs * 131 + T)
+    what = f"{dtype} {bs}x{T}"
+    assert_policy_parity("bnpo", x, 0.04, 0.2, 0.28, "bnpo " + what)
+    assert_policy_parity("grpo", x, 0.04, 0.2, 0.28, "grpo " + what)
+    assert_policy_parity("bnpo", x, 0.0, 0.2, 0.28, "bnpo beta0 " + what)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16", "fp16"])
+@pytest.mark.parametrize("bs,T", [(1, 1), (3, 37), (4, 1000), (2, 4097)])
+def test_edge_shapes_rkl(dtype, bs, T):
+    w = synthetic.Workload("edge", "rkl", dtype, "bool", bs, T, 1, T, seed=bs + T)
+    x = synthetic.inputs(w)
+    assert_rkl_parity(x, f"rkl {dtype} {bs}x{T}")
+
+
+@pytest.mark.parametrize("op", ["bnpo", "grpo"])
+def test_all_masked_policy(op):
+    x = _custom(op, "bf16", 4, 300, "none")
+    out = assert_policy_parity(op, x, 0.04, 0.2, 0.28, f"{op} all masked")
+    assert float(out[0].cpu()) == 0.0
+    assert torch.all(out[1] == 0)
+
+
+def test_all_masked_rkl_gives_nan_loss_and_zero_grad():
+    w = synthetic.Workload("edge", "rkl", "bf16", "bool", 3, 100, 1, 100)
+    x = synthetic.inputs(w)
+    x["mask"] = torch.zeros(3, 100, dtype=torch.bool)
+    out = assert_rkl_parity(x, "rkl all masked")
+    assert math.isnan(float(out[0].cpu()))
+    assert torch.all(out[1] == 0)
+
+
+def test_single_valid_token():
+    x = _custom("bnpo", "fp32", 3, 50, "none")
+    x["mask"][1, 17] = 1
+    assert_policy_parity("bnpo", x, 0.04, 0.2, 0.28, "single token bnpo")
+    assert_policy_parity("grpo", x, 0.04, 0.2, 0.28, "single token grpo")
+
+
+def test_int8_mask_nonzero_bytes_are_valid():
+    x = _custom("bnpo", "bf16", 6, 333, "odd_bytes")
+    assert_policy_parity("bnpo", x, 0.04, 0.2, 0.28, "odd bytes bnpo")
+    assert_policy_parity("grpo", x, 0.04, 0.2, 0.28, "odd bytes grpo")
+
+
+def test_bool_and_int8_masks_agree():
+    x = _custom("bnpo", "bf16", 8, 512, "random", mask_dtype="bool")
+    a = dev(x)
+    o1 = rl.bnpo_loss(a["policy"], a["old"], a["ref"], a["advantages"], a["mask"], beta=0.04)
+    o2 = rl.bnpo_loss(a["policy"], a["old"], a["ref"], a["advantages"], a["mask"].to(torch.int8), beta=0.04)
+    assert torch.equal(o1[0], o2[0]) and torch.equal(o1[1], o2[1])
+
+
+def test_multi_tile_grid_bnpo_and_rkl():
+    # 8M slots: more tiles than co-resident workgroups, so each workgroup counts
+    # several masks before the exchange and then streams its tiles.
+    x = _custom("bnpo", "bf16", 1024, 8192, "prefix", lo=0)
+    print("[parity] multi-tile bnpo 1024x8192", flush=True)
+    assert_policy_parity("bnpo", x, 0.04, 0.2, 0.28, "multi-tile bnpo")
+    assert_policy_parity("bnpo", x, 0.04, 0.2, 0.28, "multi-tile bnpo fwd", fused=False)
+    w = synthetic.Workload("edge", "rkl", "bf16", "bool", 1024, 8192, 1, 8192)
+    assert_rkl_parity(synthetic.inputs(w), "multi-tile rkl")
+
+
+def test_grpo_rows_longer_than_a_tile():
+    x = _custom("grpo", "fp16", 6, 50000, "prefix", lo=0)
+    assert_policy_parity("grpo", x, 0.04, 0.2, 0.2, "grpo long rows")
+
+
+def test_grpo_one_slot_rows():
+    x = _custom("grpo", "bf16", 9000, 1, "random")
+    assert_policy_parity("grpo", x, 0.04, 0.2, 0.28, "grpo T=1")
+
+
+def _all_ops(x_bnpo, x_rkl, ws):
+    kw = dict(epsilon=0.2, epsilon_high=0.28, beta=0.04, workspace=ws)
+    b = x_bnpo
+    out = []
+    out += list(rl.bnpo_loss(b["policy"], b["old"], b["ref"], b["advantages"], b["mask"], **kw))
+    out += [rl.bnpo_loss_fwd(b["policy"], b["old"], b["ref"], b["advantages"], b["mask"], **kw)]
+    out += list(rl.grpo_loss(b["policy"], b["old"], b["ref"], b["advantages"], b["mask"], **kw))
+    out += [rl.grpo_loss_fwd(b["policy"], b["old"], b["ref"], b["advantages"], b["mask"], **kw)]
+    out += list(rl.reverse_kl(x_rkl["student"], x_rkl["teacher"], x_rkl["mask"], workspace=ws))
+    out += [rl.reverse_kl_fwd(x_rkl["student"], x_rkl["teacher"], x_rkl["mask"], workspace=ws)]
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("start_gen", [0, 1, 2**31, 2**32 - 2])
+def test_fresh_workspace_first_calls_and_generation_wraparound(start_gen):
+    # Every op's first use of a zero-filled workspace, and launches across the 32-bit
+    # generation wrap, give bit-identical results to calls on a long-used workspace.
+    xb = dev(synthetic.inputs(synthetic.WORKLOADS["bnpo_bf16_64x4096"]))
+    xr = dev(synthetic.inputs(synthetic.Workload("w", "rkl", "bf16", "bool", 64, 4096, 1, 4096)))
+    ref = _all_ops(xb, xr, None)
+    nbytes = rl.library().rlpl_workspace_bytes(64, 4096, 0)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
+    ws[0:4].view(torch.int32)[0] = start_gen - 2**32 if start_gen >= 2**31 else start_gen
+    for _ in range(3):
+        got = _all_ops(xb, xr, ws)
+        for a, b in zip(got, ref):
+            assert torch.equal(a, b)
+    assert int(ws[1024:1028].cpu().view(torch.int32)[0]) == 0
