@@ -1,21 +1,29 @@
 #!/usr/bin/env python3
 """Throughput of the fused PPO-family policy loss on one MI355X.
 
-One step = one fused forward+backward BNPO call (bs=64, seq_len=4096, bf16
-log-probs, int8 prefix mask with lengths U[256, 4096], beta=0.04, eps=0.2,
-eps_high=0.28): the whole hot path (stream-in, per-token policy and KL terms,
-local reduction, on-GPU global count, 1/N scaling, gradient store, loss
-finalise) in one launch through the C ABI.
+Default step = one fused forward+backward BNPO call (bs=64, seq_len=4096,
+bf16 log-probs, int8 prefix mask with lengths U[256, 4096], beta=0.04,
+eps=0.2, eps_high=0.28): the whole hot path (stream-in, per-token policy and
+KL terms, local reduction, on-GPU global count, 1/N scaling, gradient store,
+loss finalise) in one launch through the C ABI.
 
 Inputs are generated once, copied into rotating sets totalling >= 1 GiB (so
 each step reads from HBM rather than the 256 MB last-level cache) and are
 resident before timing starts.  W warmup steps, then exactly K timed steps
-between two stream synchronisations.  HIP events are recorded
-on the stream it runs on at both ends of the timed region: their span / K is
-the per-launch kernel duration used for the roofline (back-to-back launches
-keep the GPU busy, so this agrees with rocprofv3's kernel durations).
+between two stream synchronisations.  HIP events recorded on the launch
+stream at both ends of the timed region give the per-launch kernel duration
+(span / K) used for the roofline: back-to-back launches keep the GPU busy, so
+this agrees with rocprofv3's kernel durations.
 
-Prints one JSON line (see the keys below).  --gpus above 1 is not supported.
+Options for context measurements (never the headline line's workload):
+  --op bnpo|bnpo_fwd|grpo|grpo_fwd|rkl|rkl_fwd   another entry point
+  --bs / --seq-len                               another size (inputs drawn on
+                                                 the device above 2^24 slots)
+  --copy-mib M                                   a plain device copy of M MiB
+                                                 (streaming ceiling; also the
+                                                 reference for traffic counters)
+
+Prints one JSON line.  --gpus above 1 is not supported.
 """
 from __future__ import annotations
 
@@ -31,18 +39,63 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0   # MI355X HBM3E peak
+METRIC = "tokens/s and achieved HBM GB/s (% of peak) for fused loss fwd+bwd"
 
 
 def algorithmic_bytes(op: str, slots: int, valid: int, bs: int, elem: int, has_kl: bool, fused: bool) -> int:
     """Bytes the method must move: the mask and (fused) the dense gradient for every slot;
     the input planes only for valid tokens; the advantages and the 4-byte loss."""
-    planes = 2 if op == "rkl" else (3 if has_kl else 2)
+    planes = 2 if op.startswith("rkl") else (3 if has_kl else 2)
     b = slots * 1 + valid * planes * elem + 4
     if fused:
         b += slots * elem
-    if op != "rkl":
+    if not op.startswith("rkl"):
         b += bs * elem
     return b
+
+
+def timed(fn, calls, K, W, stream, torch):
+    """W warmup calls, then K timed back-to-back calls; returns (ms per step wall, ms per launch GPU)."""
+    n = len(calls)
+    for i in range(W):
+        rc = fn(*calls[i % n])
+        if rc != 0:
+            raise RuntimeError(f"{getattr(fn, '__name__', 'call')} returned status {rc}")
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    bad = 0
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(K):
+        bad |= fn(*calls[(W + i) % n])
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    if bad:
+        raise RuntimeError("a timed call returned an error status")
+    return (t1 - t0) * 1e3 / K, ev0.elapsed_time(ev1) / K
+
+
+def copy_ceiling(args, torch):
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    nbytes = int(args.copy_mib * (1 << 20)) // 16 * 16
+    nsets = max(2, math.ceil((1 << 30) / (2 * nbytes)))
+    pairs = [(torch.empty(nbytes, dtype=torch.uint8, device=dev),
+              torch.empty(nbytes, dtype=torch.uint8, device=dev)) for _ in range(nsets)]
+    calls = [(d, s) for s, d in pairs]
+
+    def fn(d, s):
+        d.copy_(s)
+        return 0
+    ms_wall, ms_gpu = timed(fn, calls, args.steps, args.warmup, stream, torch)
+    gbs = 2 * nbytes / (ms_gpu * 1e-3) / 1e9
+    print(json.dumps({"metric": "plain device copy (read + write)", "bytes_read": nbytes,
+                      "bytes_written": nbytes, "us_per_launch": round(ms_gpu * 1e3, 3),
+                      "GBs": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
+                      "steps": args.steps, "rotating_sets": nsets}), flush=True)
+    return 0
 
 
 def main() -> int:
@@ -51,9 +104,14 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="bnpo_bf16_64x4096")
+    ap.add_argument("--op", default=None, choices=["bnpo", "bnpo_fwd", "grpo", "grpo_fwd", "rkl", "rkl_fwd"])
+    ap.add_argument("--bs", type=int, default=None)
+    ap.add_argument("--seq-len", type=int, default=None)
+    ap.add_argument("--beta", type=float, default=None)
     ap.add_argument("--rotate-gib", type=float, default=1.0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=float, default=None)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported: this build measures one GPU only "
@@ -63,99 +121,97 @@ def main() -> int:
     import numpy as np
     import torch
 
+    if args.copy_mib is not None:
+        return copy_ceiling(args, torch)
+
     import rl_post_loss_amd as rl
     import synthetic
 
     w = synthetic.WORKLOADS[args.workload]
-    if w.op not in ("bnpo", "grpo", "rkl"):
-        raise SystemExit(f"unknown op {w.op}")
+    headline = args.op is None and args.bs is None and args.seq_len is None and args.beta is None
+    op = args.op or w.op
+    if args.bs or args.seq_len:
+        w = w.with_(bs=args.bs or w.bs, seq_len=args.seq_len or w.seq_len,
+                    len_lo=min(w.len_lo, args.seq_len or w.seq_len), len_hi=args.seq_len or w.len_hi,
+                    name=f"{w.name}@{args.bs or w.bs}x{args.seq_len or w.seq_len}")
+    if args.beta is not None:
+        w = w.with_(beta=args.beta)
+    fused = not op.endswith("_fwd")
+    is_rkl = op.startswith("rkl")
+    if is_rkl and not w.op == "rkl":
+        w = w.with_(op="rkl")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
     sptr = stream.cuda_stream
     lib = rl.library()
 
-    x = synthetic.inputs(w)
-    mask_cpu = x["mask"]
-    valid = int(torch.count_nonzero(mask_cpu))
-    planes = ["student", "teacher"] if w.op == "rkl" else (["policy", "old", "ref"] if w.beta != 0
-                                                            else ["policy", "old"])
+    on_device = w.slots > (1 << 24)
+    if on_device:
+        d = synthetic.device_policy_inputs(w, "cuda:0")
+        x = {"student": d["policy"], "teacher": d["ref"], "mask": d["mask"]} if is_rkl else d
+    else:
+        x = synthetic.inputs(w)
+    valid = int(torch.count_nonzero(x["mask"]))
+    planes = ["student", "teacher"] if is_rkl else (["policy", "old", "ref"] if w.beta != 0 else ["policy", "old"])
     dt = x[planes[0]].dtype
     elem = x[planes[0]].element_size()
-    base = {k: x[k].to(dev) for k in planes + ["mask"] + ([] if w.op == "rkl" else ["advantages"])}
-    set_bytes = sum(t.numel() * t.element_size() for t in base.values()) + w.slots * elem
-    nsets = max(2, math.ceil(args.rotate_gib * (1 << 30) / set_bytes))
+    base = {k: x[k].to(dev) for k in planes + ["mask"] + ([] if is_rkl else ["advantages"])}
+    set_bytes = sum(t.numel() * t.element_size() for t in base.values()) + (w.slots * elem if fused else 0)
+    nsets = max(1, math.ceil(args.rotate_gib * (1 << 30) / set_bytes)) if set_bytes < (1 << 29) else 1
+    if nsets == 1 and not on_device:
+        nsets = 2
     ws = rl.workspace_for(dev, sptr, w.op)
+    name = {"bnpo": "bnpo_loss", "bnpo_fwd": "bnpo_loss_fwd", "grpo": "grpo_loss",
+            "grpo_fwd": "grpo_loss_fwd", "rkl": "reverse_kl", "rkl_fwd": "reverse_kl_fwd"}[op]
+    fn = getattr(lib, name)
     sets, calls = [], []
-    fn = {"bnpo": lib.bnpo_loss, "grpo": lib.grpo_loss, "rkl": lib.reverse_kl}[w.op]
-    for _ in range(nsets):
-        s = {k: v.clone() for k, v in base.items()}
-        s["grad"] = torch.empty(w.bs, w.seq_len, dtype=dt, device=dev)
+    for i in range(nsets):
+        s = base if i == 0 else {k: v.clone() for k, v in base.items()}
+        s = dict(s)
+        s["grad"] = torch.empty(w.bs, w.seq_len, dtype=dt, device=dev) if fused else None
         s["loss"] = torch.empty((), dtype=torch.float32, device=dev)
         s["n"] = torch.empty(w.bs, dtype=torch.int32, device=dev)
         sets.append(s)
-        if w.op == "rkl":
-            a = (s["student"].data_ptr(), s["teacher"].data_ptr(), s["mask"].data_ptr(), w.bs,
-                 w.seq_len, rl.DTYPE[dt], rl.MASK_DTYPE[s["mask"].dtype], s["loss"].data_ptr(),
-                 s["grad"].data_ptr(), s["n"].data_ptr(), ws.data_ptr(), ws.numel(), sptr)
+        g = [s["grad"].data_ptr()] if fused else []
+        if is_rkl:
+            a = [s["student"].data_ptr(), s["teacher"].data_ptr(), s["mask"].data_ptr(), w.bs,
+                 w.seq_len, rl.DTYPE[dt], rl.MASK_DTYPE[s["mask"].dtype], s["loss"].data_ptr()]
         else:
-            a = (s["policy"].data_ptr(), s["old"].data_ptr(),
-                 s["ref"].data_ptr() if "ref" in s else None, s["advantages"].data_ptr(),
-                 s["mask"].data_ptr(), w.bs, w.seq_len, rl.DTYPE[dt], rl.MASK_DTYPE[s["mask"].dtype],
-                 w.beta, w.epsilon, w.epsilon_high, s["loss"].data_ptr(), s["grad"].data_ptr(),
-                 s["n"].data_ptr(), ws.data_ptr(), ws.numel(), sptr)
-        calls.append(a)
+            a = [s["policy"].data_ptr(), s["old"].data_ptr(), s["ref"].data_ptr() if "ref" in s else None,
+                 s["advantages"].data_ptr(), s["mask"].data_ptr(), w.bs, w.seq_len, rl.DTYPE[dt],
+                 rl.MASK_DTYPE[s["mask"].dtype], w.beta, w.epsilon, w.epsilon_high, s["loss"].data_ptr()]
+        calls.append(tuple(a + g + [s["n"].data_ptr(), ws.data_ptr(), ws.numel(), sptr]))
     torch.cuda.synchronize()
 
     K, W = args.steps, args.warmup
-    for i in range(W):
-        rc = fn(*calls[i % nsets])
-        if rc != 0:
-            raise rl.RlplError(fn.__name__, rc)
-    torch.cuda.synchronize()
-
-    # Timed region: K back-to-back launches between two stream synchronisations, with
-    # HIP events recorded on the launch stream at both ends of it.
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    bad = 0
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for i in range(K):
-        bad |= fn(*calls[(W + i) % nsets])
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    if bad:
-        raise RuntimeError("a timed call returned an error status")
-    k_mean = ev0.elapsed_time(ev1) / K          # ms per launch on the GPU timeline
-    ms_per_step = (t1 - t0) * 1e3 / K
+    ms_per_step, ms_gpu = timed(fn, calls, K, W, stream, torch)
     tokens_per_s = w.slots / (ms_per_step * 1e-3)
 
-    # Check one timed result against the oracle-free invariants the kernel must keep.
-    n0 = int(sets[(W + K - 1) % nsets]["n"][0].cpu()) if w.op != "grpo" else None
-    if n0 is not None and n0 != valid:
-        raise RuntimeError(f"valid count {n0} != {valid}")
+    if not op.startswith("grpo"):
+        n0 = int(sets[(W + K - 1) % nsets]["n"][0].cpu())
+        if n0 != valid:
+            raise RuntimeError(f"valid count {n0} != {valid}")
 
-    alg = algorithmic_bytes(w.op, w.slots, valid, w.bs, elem, w.op == "rkl" or w.beta != 0, True)
-    achieved = alg / (k_mean * 1e-3) / 1e9
+    alg = algorithmic_bytes(op, w.slots, valid, w.bs, elem, is_rkl or w.beta != 0, fused)
+    achieved = alg / (ms_gpu * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 5), "traffic": None}
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if headline and not args.no_cpu_baseline:
         import oracle
         xs = {k: oracle.to_f64(v) for k, v in x.items() if k in planes or k == "advantages"}
-        m8 = oracle.to_mask_u8(mask_cpu)
+        m8 = oracle.to_mask_u8(x["mask"])
         f32 = lambda v: float(np.float32(v))
         runs, tc0 = 0, time.perf_counter()
         while True:
-            if w.op == "rkl":
+            if is_rkl:
                 oracle.rkl(xs["student"], xs["teacher"], m8)
             else:
-                fo = oracle.bnpo if w.op == "bnpo" else oracle.grpo
+                fo = oracle.bnpo if op.startswith("bnpo") else oracle.grpo
                 fo(xs["policy"], xs["old"], xs.get("ref"), xs["advantages"], m8, f32(w.beta),
-                   f32(w.epsilon), f32(w.epsilon_high))
+                   f32(w.epsilon), f32(w.epsilon_high), grad=fused)
             runs += 1
             if time.perf_counter() - tc0 >= args.cpu_seconds:
                 break
@@ -165,7 +221,7 @@ def main() -> int:
                          f"{tc * 1e3:.1f} ms each"}
 
     out = {
-        "metric": "tokens/s and achieved HBM GB/s (% of peak) for fused loss fwd+bwd",
+        "metric": METRIC,
         "value": round(tokens_per_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -177,15 +233,19 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": {torch.bfloat16: "bf16", torch.float16: "fp16", torch.float32: "fp32"}[dt],
         "data": "synthetic",
-        "config": {"workload": w.name, "op": w.op + " fwd+bwd", "bs": w.bs, "seq_len": w.seq_len,
-                   "beta": w.beta, "epsilon": w.epsilon, "epsilon_high": w.epsilon_high,
+        "config": {"workload": w.name, "op": op.replace("_fwd", " fwd-only") + ("" if op.endswith("_fwd") else " fwd+bwd"),
+                   "bs": w.bs, "seq_len": w.seq_len, "beta": 1.0 if is_rkl else w.beta,
+                   "epsilon": w.epsilon, "epsilon_high": w.epsilon_high,
                    "mask": f"{w.mask_dtype} prefix U[{w.len_lo},{w.len_hi}]", "valid_tokens": valid,
+                   "inputs": "device-generated" if on_device else "host-generated",
                    "rotating_sets": nsets, "parallelism": "single GPU"},
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "kernel_us_per_launch": round(k_mean * 1e3, 3),
+        "kernel_us_per_launch": round(ms_gpu * 1e3, 3),
         "algorithmic_bytes_per_launch": alg,
     }
+    if not headline:
+        out["context_only"] = True
     print(json.dumps(out), flush=True)
     return 0
 

@@ -14,6 +14,7 @@
 
 #include "loss_kernels.h"
 #include "rl_post_loss.h"
+#include "row_divisor.h"
 
 namespace {
 
@@ -28,7 +29,8 @@ constexpr int kMaxDevices = 64;
 // Per-device launch facts, filled once per device (thread-safe) and then read-only.
 struct DeviceInfo {
     int status = RLPL_ERR_DEVICE;
-    int grid_cap[3][3] = {};     // [dtype][mode]: co-resident workgroups of the family
+    int cus = 0;
+    int grid_cap[3][3][2] = {};  // [dtype][mode][vec small/large]: co-resident workgroups
 };
 DeviceInfo g_info[kMaxDevices];
 std::once_flag g_once[kMaxDevices];
@@ -40,26 +42,29 @@ void init_device(int dev, DeviceInfo& info) {
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return;
     if (cus <= 0) return;
+    info.cus = cus;
     for (int dt = 0; dt < 3; ++dt)
-        for (int mode = 0; mode < 3; ++mode) {
-            // The whole family shares one grid size so that its forward-only and
-            // fwd+bwd kernels reduce over identical partitions (identical losses),
-            // and that size never exceeds what is co-resident on the device, which
-            // the fwd+bwd count exchange relies on.
-            int occ = 1 << 30;
-            for (int kl = 0; kl < 2; ++kl)
-                for (int wg = 0; wg < 2; ++wg) {
-                    const void* k = rlpl::pick_kernel(dt, mode, kl != 0 || mode == kModeRKL, wg != 0);
-                    int nb = 0;
-                    if (!k || hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k, rlpl::kThreads, 0) !=
-                                  hipSuccess || nb < 1)
-                        return;
-                    if (nb < occ) occ = nb;
-                }
-            long cap = long(occ) * cus;
-            if (cap > rlpl::kMaxGrid) cap = rlpl::kMaxGrid;
-            info.grid_cap[dt][mode] = int(cap);
-        }
+        for (int mode = 0; mode < 3; ++mode)
+            for (int v = 0; v < 2; ++v) {
+                // The whole family shares one grid size so that its forward-only and
+                // fwd+bwd kernels reduce over identical partitions (identical losses),
+                // and that size never exceeds what is co-resident on the device, which
+                // the fwd+bwd count exchange relies on.
+                int occ = 1 << 30;
+                for (int kl = 0; kl < 2; ++kl)
+                    for (int wg = 0; wg < 2; ++wg) {
+                        const void* k = rlpl::pick_kernel(dt, mode, kl != 0 || mode == kModeRKL, wg != 0,
+                                                          v ? rlpl::kVecLarge : rlpl::kVecSmall);
+                        int nb = 0;
+                        if (!k || hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k, rlpl::kThreads, 0) !=
+                                      hipSuccess || nb < 1)
+                            return;
+                        if (nb < occ) occ = nb;
+                    }
+                long cap = long(occ) * cus;
+                if (cap > rlpl::kMaxGrid) cap = rlpl::kMaxGrid;
+                info.grid_cap[dt][mode][v] = int(cap);
+            }
     info.status = RLPL_OK;
 }
 
@@ -108,16 +113,22 @@ int launch(const void* kernel, const Args& a, int64_t grid, hipStream_t stream) 
     return RLPL_OK;
 }
 
-// Shared tail of every entry point: grid sizing and the launch.
+// Shared tail of every entry point: lane width, grid sizing and the launch.
 int run(int mode, bool write_grad, bool has_kl, Args& a, int dtype, hipStream_t stream) {
     const DeviceInfo* info = nullptr;
     const int st = current_device(&info);
     if (st != RLPL_OK) return st;
-    const void* kernel = rlpl::pick_kernel(dtype, mode, has_kl, write_grad);
+    // Small problems take the narrow lane so that every compute unit gets a tile.
+    const int64_t large_tile = int64_t(rlpl::kThreads) * rlpl::kVecLarge;
+    const bool small = a.slots < int64_t(info->cus) * rlpl::kSmallTilesPerCu * large_tile;
+    const int vec = small ? rlpl::kVecSmall : rlpl::kVecLarge;
+    const void* kernel = rlpl::pick_kernel(dtype, mode, has_kl, write_grad, vec);
     if (!kernel) return RLPL_ERR_DTYPE;
-    a.tiles = (a.slots + rlpl::kTile - 1) / rlpl::kTile;
-    const int64_t cap = info->grid_cap[dtype][mode];
-    const int64_t grid = a.tiles < cap ? a.tiles : cap;
+    const int64_t tile = int64_t(rlpl::kThreads) * vec;
+    a.tiles = uint32_t((a.slots + tile - 1) / tile);
+    if (!rlpl::row_divisor(uint32_t(a.seq_len), &a.row_magic, &a.row_shift)) return RLPL_ERR_SHAPE;
+    const int64_t cap = info->grid_cap[dtype][mode][small ? 0 : 1];
+    const int64_t grid = int64_t(a.tiles) < cap ? int64_t(a.tiles) : cap;
     return launch(kernel, a, grid, stream);
 }
 

@@ -7,40 +7,55 @@
 
 namespace rlpl {
 
-constexpr int kVec = 16;                    // consecutive slots per lane (one 128-bit mask load)
 constexpr int kThreads = 256;               // lanes per workgroup (4 wave64)
 constexpr int kWaves = kThreads / 64;
-constexpr int kTile = kVec * kThreads;      // slots per workgroup tile
-constexpr int kMaxGrid = 8192;              // upper bound on the persistent grid
+// Consecutive slots per lane: kVecLarge (one 128-bit mask load per lane) for
+// large problems, kVecSmall (so that a small problem spreads over every
+// compute unit) when there would be fewer than kSmallTilesPerCu large tiles
+// per compute unit.  A tile is kThreads * VEC slots.
+constexpr int kVecLarge = 16;
+constexpr int kVecSmall = 4;
+#ifndef RLPL_SMALL_TILES_PER_CU
+#define RLPL_SMALL_TILES_PER_CU 1
+#endif
+constexpr int kSmallTilesPerCu = RLPL_SMALL_TILES_PER_CU;
+constexpr int kMaxGrid = 4096;              // upper bound on the persistent grid (gfx950: <= 256 CUs x 8)
 constexpr uint64_t kWaitLimitTicks = 100000000ull;   // ~1 s of the 100 MHz wall clock
 constexpr uint32_t kWaitLimitPolls = 1u << 24;        // second bound on the same wait
 constexpr uint32_t kFlagWaitTimeout = 1u;
+// Pause between two polls of a word another workgroup will publish, in units
+// of 64 clocks (s_sleep); spaces out the polling of a whole grid.
+#ifndef RLPL_POLL_SLEEP
+#define RLPL_POLL_SLEEP 1
+#endif
+constexpr int kPollSleep = RLPL_POLL_SLEEP;
 
 enum { kModeBNPO = 0, kModeGRPO = 1, kModeRKL = 2 };
 enum { kF32 = 0, kF16 = 1, kBF16 = 2 };
 
-// Device workspace.  Zero-filled once by the caller.  Each protocol word sits
-// on its own 256-byte line so that polling one never contends with atomics on
-// another.  Every launch leaves `arrive` and `depart` at zero and advances
-// `generation` by one, ready for the next call.
-struct Workspace {
-    uint32_t generation;       // launch counter: read by every workgroup at its start and
-    uint32_t pad0[63];         // advanced by the launch's final ticket holder
-    uint64_t arrive;           // count exchange: [63:32 workgroups arrived | 31:0 their count]
-    uint64_t pad1[31];
-    uint64_t release;          // [63:32 tag (generation + 1) of the exchange | 31:0 total count]
-    uint64_t pad2[31];
-    uint64_t depart;           // finish tickets: [63:32 workgroups done | 31:0 their count]
-    uint64_t pad3[31];
-    uint32_t flags;            // sticky error bits (kFlagWaitTimeout)
-    uint32_t pad4[63];
-    uint64_t partial[kMaxGrid];   // per-workgroup partial loss: [63:32 tag (generation + 1) | 31:0 float]
+// One workgroup's published words: [63:32 tag (generation + 1) | 31:0 value].
+// One slot per 256-byte line: stores from many workgroups to a shared line
+// become visible to the other compute units markedly later than stores to
+// lines of their own.
+struct alignas(256) Slot {
+    uint64_t count;            // valid-token count of the workgroup's tiles
+    uint64_t partial;          // float bits of the workgroup's partial loss
 };
-static_assert(offsetof(Workspace, arrive) == 256, "protocol words on separate lines");
-static_assert(offsetof(Workspace, release) == 512, "protocol words on separate lines");
-static_assert(offsetof(Workspace, depart) == 768, "protocol words on separate lines");
-static_assert(offsetof(Workspace, flags) == 1024, "protocol words on separate lines");
-static_assert(offsetof(Workspace, partial) == 1280, "workspace header");
+
+// Device workspace.  Zero-filled once by the caller; every launch advances
+// `generation` by one and leaves nothing else that the next launch depends on.
+struct Workspace {
+    uint32_t generation;       // launch counter: read by every workgroup at its start,
+    uint32_t pad0[63];         // advanced by workgroup 0 at the end of the launch
+    uint32_t flags;            // sticky error bits (kFlagWaitTimeout)
+    uint32_t pad1[63];
+    uint64_t release;          // [63:32 tag | 31:0 global count], published by workgroup 0
+    uint64_t pad2[31];
+    Slot slot[kMaxGrid];
+};
+static_assert(offsetof(Workspace, flags) == 256, "header words on separate lines");
+static_assert(offsetof(Workspace, release) == 512, "header words on separate lines");
+static_assert(offsetof(Workspace, slot) == 768, "workspace header");
 constexpr size_t kWorkspaceBytes = sizeof(Workspace);
 constexpr size_t kFlagsOffset = offsetof(Workspace, flags);
 
@@ -56,15 +71,17 @@ struct Args {
     uint32_t* n_out;       // valid count(s) or NULL
     Workspace* ws;
     int64_t slots;         // bs * seq_len  (< 2^31)
-    int64_t tiles;         // ceil(slots / kTile)
+    uint32_t tiles;        // ceil(slots / (kThreads * VEC))
     int32_t seq_len;
     int32_t bs;
+    uint32_t row_magic;    // s / seq_len == (s * row_magic) >> row_shift for every s < 2^31
+    uint32_t row_shift;
     float beta;
     float lo;              // 1 - epsilon
     float hi;              // 1 + epsilon_high
 };
 
-// The kernel instantiation for (dtype, mode, KL on/off, gradient on/off), or NULL.
-const void* pick_kernel(int dtype, int mode, bool has_kl, bool write_grad);
+// The kernel instantiation for (dtype, mode, KL on/off, gradient on/off, VEC), or NULL.
+const void* pick_kernel(int dtype, int mode, bool has_kl, bool write_grad, int vec);
 
 }  // namespace rlpl

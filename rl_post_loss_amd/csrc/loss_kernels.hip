@@ -11,33 +11,40 @@
 // Design (one launch per call; the path is elementwise + reductions and
 // HBM-bound, so there is no MFMA here):
 //  * The (bs, seq_len) planes are treated as one flat run of `slots`.  A tile
-//    is kThreads lanes x kVec consecutive slots; each lane moves its 16 mask
-//    bytes with one 128-bit load and its 16 log-probs per plane with two
-//    (16-bit dtypes) or four (fp32) 128-bit loads.  When streaming several
-//    tiles per workgroup, plane loads are skipped for lanes whose 16 mask
-//    bytes are all zero.
+//    is kThreads lanes x VEC consecutive slots.  Each lane moves its VEC mask
+//    bytes and its VEC log-probs per plane with 32/64/128-bit loads.  VEC is
+//    16 for large problems and 4 for small ones, so that a small problem
+//    still spreads over every compute unit.
 //  * A persistent grid of G <= (co-resident workgroups) takes tiles
-//    wg, wg+G, wg+2G, ...  Per-token math is fp32 in registers.
+//    wg, wg+G, wg+2G, ...  Per-token math is fp32 in registers and
+//    branch-free: every slot of a lane is computed and masked slots are
+//    selected away (their values never reach a result).
 //  * Reductions: per-lane sums -> wavefront shuffle tree -> LDS across the
-//    4 waves -> one partial per workgroup in the workspace.  The last
-//    workgroup to finish (ticket from an agent-scope atomic) sums the G
-//    partials in workgroup order, so the loss is deterministic and identical
-//    between the fwd+bwd and forward-only kernels.
+//    4 waves -> one partial per workgroup in the workspace.  The partial that
+//    finishes last sums the G partials in workgroup order, so the loss is
+//    deterministic and identical between the fwd+bwd and forward-only kernels.
 //  * BNPO / RKL fwd+bwd need the global valid count N before any gradient is
-//    scaled: each workgroup adds (1<<32 | its count) to one 64-bit word; the
-//    last arrival publishes N (with a generation number) in another word the
-//    others poll.  All cross-workgroup traffic is agent-scope relaxed atomics
-//    and device-coherent loads/stores, never an L2-wide writeback/invalidate.
-//    The grid never exceeds the co-resident capacity; the wait is bounded in
-//    time anyway and sets a sticky flag if it ever gives up.  When a
-//    workgroup owns a single tile, its plane loads are issued with its mask
-//    load, stay in flight while it waits, and the tile never leaves
-//    registers; with more tiles it counts its masks first and streams after.
+//    scaled: each workgroup publishes its count in a slot of its own;
+//    workgroup 0 gathers them and publishes N on a release line that the
+//    others read once their own tile is computed.  All cross-workgroup
+//    traffic is device-coherent loads/stores of generation-tagged words: no
+//    read-modify-write atomics, never an L2-wide writeback or invalidate.
+//    The grid never exceeds the co-resident capacity; every wait is bounded
+//    in time anyway and sets a sticky flag if it ever gives up.
+//    When a workgroup owns a single tile, its plane loads are issued with its
+//    mask load, its count is published as soon as the mask has arrived, and
+//    the tile never leaves registers; with more tiles it counts its masks
+//    first (eight loads in flight) and streams after.
 //  * GRPO needs only each row's own count: a workgroup counts the mask of
 //    every row its tile touches into LDS (no cross-workgroup exchange before
 //    the gradient is scaled), as the card's one-block-per-row design does.
+//  * When streaming several tiles per workgroup, plane loads wait for the
+//    mask and are skipped for lanes whose mask bytes are all zero, and the
+//    next tile's mask is fetched while the current tile is computed.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "loss_kernels.h"
 
@@ -45,107 +52,145 @@ namespace rlpl {
 
 // ----------------------------------------------------------------------------- element types
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
 template <typename T> struct Elem;
 template <> struct Elem<float> {
-    static __device__ __forceinline__ float to_f32(uint32_t bits) { return __uint_as_float(bits); }
-    static __device__ __forceinline__ uint32_t from_f32(float v) { return __float_as_uint(v); }
+    static __device__ __forceinline__ float get(const uint32_t* w, int k) { return __uint_as_float(w[k]); }
 };
 template <> struct Elem<_Float16> {
-    static __device__ __forceinline__ float to_f32(uint32_t bits) {
-        return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+    static __device__ __forceinline__ float get(const uint32_t* w, int k) {
+        return (float)__builtin_bit_cast(_Float16, uint16_t(w[k >> 1] >> (16 * (k & 1))));
     }
-    static __device__ __forceinline__ uint32_t from_f32(float v) {   // round to nearest even
-        return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v);
+    // two floats -> two fp16 (round to nearest even, subnormals kept) in one dword
+    static __device__ __forceinline__ uint32_t pack(float a, float b) {
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
     }
 };
 template <> struct Elem<__bf16> {
-    static __device__ __forceinline__ float to_f32(uint32_t bits) { return __uint_as_float(bits << 16); }
-    static __device__ __forceinline__ uint32_t from_f32(float v) {   // round to nearest even
-        return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v);
+    static __device__ __forceinline__ float get(const uint32_t* w, int k) {
+        return __uint_as_float((k & 1) ? (w[k >> 1] & 0xFFFF0000u) : (w[k >> 1] << 16));
+    }
+    // two floats -> two bf16 (round to nearest even) in one dword
+    static __device__ __forceinline__ uint32_t pack(float a, float b) {
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
     }
 };
 
-// 16 consecutive elements of one plane held in registers as raw 128-bit words.
-template <typename T>
-struct Vec16 {
-    static constexpr int kWords = kVec * (int)sizeof(T) / 4;
-    static constexpr int kQuads = kWords / 4;
-    uint32_t w[kWords];
+// ----------------------------------------------------------------------------- lane registers
 
-    __device__ __forceinline__ void load(const T* __restrict__ base, int64_t s, int64_t slots) {
-        if (s + kVec <= slots) {
-            const uint4* p = reinterpret_cast<const uint4*>(base + s);
-#pragma unroll
-            for (int q = 0; q < kQuads; ++q) {
-                uint4 v = p[q];
-                w[4 * q + 0] = v.x; w[4 * q + 1] = v.y; w[4 * q + 2] = v.z; w[4 * q + 3] = v.w;
-            }
+// N dwords moved with the widest aligned accesses (N * 4 bytes aligned to min(N * 4, 16)).
+template <int N>
+struct Dwords {
+    uint32_t w[N];
+    __device__ __forceinline__ void load(const void* p) {
+        if constexpr (N == 1) {
+            w[0] = *static_cast<const uint32_t*>(p);
+        } else if constexpr (N == 2) {
+            const uint2 v = *static_cast<const uint2*>(p);
+            w[0] = v.x; w[1] = v.y;
         } else {
-            const uint16_t* p16 = reinterpret_cast<const uint16_t*>(base);
-            const uint32_t* p32 = reinterpret_cast<const uint32_t*>(base);
 #pragma unroll
-            for (int i = 0; i < kWords; ++i) w[i] = 0;
-#pragma unroll
-            for (int k = 0; k < kVec; ++k) {
-                if (s + k < slots) {
-                    if constexpr (sizeof(T) == 4) w[k] = p32[s + k];
-                    else w[k >> 1] |= (uint32_t)p16[s + k] << (16 * (k & 1));
-                }
+            for (int q = 0; q < N / 4; ++q) {
+                const uint4 v = static_cast<const uint4*>(p)[q];
+                w[4 * q] = v.x; w[4 * q + 1] = v.y; w[4 * q + 2] = v.z; w[4 * q + 3] = v.w;
             }
         }
     }
-    __device__ __forceinline__ float get(int k) const {
-        if constexpr (sizeof(T) == 4) return Elem<T>::to_f32(w[k]);
-        else return Elem<T>::to_f32((w[k >> 1] >> (16 * (k & 1))) & 0xFFFFu);
-    }
-    __device__ __forceinline__ void set(int k, float v) {
-        if constexpr (sizeof(T) == 4) w[k] = Elem<T>::from_f32(v);
-        else if ((k & 1) == 0) w[k >> 1] = Elem<T>::from_f32(v);
-        else w[k >> 1] |= Elem<T>::from_f32(v) << 16;
-    }
-    __device__ __forceinline__ void store(T* __restrict__ base, int64_t s, int64_t slots) const {
-        if (s + kVec <= slots) {
-            uint4* p = reinterpret_cast<uint4*>(base + s);
-#pragma unroll
-            for (int q = 0; q < kQuads; ++q)
-                p[q] = make_uint4(w[4 * q + 0], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
+    __device__ __forceinline__ void store(void* p) const {
+        if constexpr (N == 1) {
+            *static_cast<uint32_t*>(p) = w[0];
+        } else if constexpr (N == 2) {
+            *static_cast<uint2*>(p) = make_uint2(w[0], w[1]);
         } else {
-            uint16_t* p16 = reinterpret_cast<uint16_t*>(base);
-            uint32_t* p32 = reinterpret_cast<uint32_t*>(base);
 #pragma unroll
-            for (int k = 0; k < kVec; ++k) {
-                if (s + k < slots) {
-                    if constexpr (sizeof(T) == 4) p32[s + k] = w[k];
-                    else p16[s + k] = (uint16_t)(w[k >> 1] >> (16 * (k & 1)));
-                }
-            }
+            for (int q = 0; q < N / 4; ++q)
+                static_cast<uint4*>(p)[q] = make_uint4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
         }
     }
 };
 
-// 16 mask bytes of one lane.
-struct Mask16 {
-    uint32_t w[4];
-    __device__ __forceinline__ void load(const uint8_t* __restrict__ mask, int64_t s, int64_t slots) {
-        if (s + kVec <= slots) {
-            uint4 v = *reinterpret_cast<const uint4*>(mask + s);
-            w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+// VEC consecutive elements of one plane.  A lane that runs past `slots` (only
+// in the last tile) moves its in-range elements one by one and zero-fills.
+template <typename T, int VEC>
+struct Plane {
+    static constexpr int kWords = VEC * int(sizeof(T)) / 4;
+    Dwords<kWords> d;
+
+    __device__ __forceinline__ void load(const T* __restrict__ base, uint32_t s, uint32_t slots) {
+        if (s + VEC <= slots) {
+            d.load(base + s);
         } else {
-            w[0] = w[1] = w[2] = w[3] = 0;
 #pragma unroll
-            for (int k = 0; k < kVec; ++k)
-                if (s + k < slots) w[k >> 2] |= (uint32_t)mask[s + k] << (8 * (k & 3));
+            for (int i = 0; i < kWords; ++i) d.w[i] = 0;
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) {
+                if (s + k < slots) {
+                    if constexpr (sizeof(T) == 4) d.w[k] = reinterpret_cast<const uint32_t*>(base)[s + k];
+                    else d.w[k >> 1] |= uint32_t(reinterpret_cast<const uint16_t*>(base)[s + k]) << (16 * (k & 1));
+                }
+            }
         }
     }
-    __device__ __forceinline__ bool any() const { return (w[0] | w[1] | w[2] | w[3]) != 0; }
-    __device__ __forceinline__ bool valid(int k) const { return ((w[k >> 2] >> (8 * (k & 3))) & 0xFFu) != 0; }
+    __device__ __forceinline__ float get(int k) const { return Elem<T>::get(d.w, k); }
+};
+
+// A lane's gradient values, converted to T and stored.
+template <typename T, int VEC>
+__device__ __forceinline__ void store_values(T* __restrict__ base, uint32_t s, uint32_t slots,
+                                             const float (&v)[VEC]) {
+    Dwords<VEC * int(sizeof(T)) / 4> out;
+    if constexpr (sizeof(T) == 4) {
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) out.w[k] = __float_as_uint(v[k]);
+    } else {
+#pragma unroll
+        for (int k = 0; k < VEC; k += 2) out.w[k >> 1] = Elem<T>::pack(v[k], v[k + 1]);
+    }
+    if (s + VEC <= slots) {
+        out.store(base + s);
+    } else {
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) {
+            if (s + k < slots) {
+                if constexpr (sizeof(T) == 4) reinterpret_cast<uint32_t*>(base)[s + k] = out.w[k];
+                else reinterpret_cast<uint16_t*>(base)[s + k] = uint16_t(out.w[k >> 1] >> (16 * (k & 1)));
+            }
+        }
+    }
+}
+
+// VEC mask bytes of one lane.
+template <int VEC>
+struct Mask {
+    Dwords<VEC / 4> d;
+    __device__ __forceinline__ void load(const uint8_t* __restrict__ mask, uint32_t s, uint32_t slots) {
+        if (s + VEC <= slots) {
+            d.load(mask + s);
+        } else {
+#pragma unroll
+            for (int i = 0; i < VEC / 4; ++i) d.w[i] = 0;
+#pragma unroll
+            for (int k = 0; k < VEC; ++k)
+                if (s + k < slots) d.w[k >> 2] |= uint32_t(mask[s + k]) << (8 * (k & 3));
+        }
+    }
+    __device__ __forceinline__ bool any() const {
+        uint32_t o = 0;
+#pragma unroll
+        for (int i = 0; i < VEC / 4; ++i) o |= d.w[i];
+        return o != 0;
+    }
+    __device__ __forceinline__ bool valid(int k) const { return ((d.w[k >> 2] >> (8 * (k & 3))) & 0xFFu) != 0; }
     // Number of nonzero bytes: for each byte, (b & 0x7F) + 0x7F sets bit 7 iff the low 7 bits
     // are nonzero; OR-ing b itself covers bit 7.
     __device__ __forceinline__ uint32_t count() const {
         uint32_t n = 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            uint32_t x = ((w[i] & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | w[i];
+        for (int i = 0; i < VEC / 4; ++i) {
+            const uint32_t x = ((d.w[i] & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | d.w[i];
             n += __builtin_popcount(x & 0x80808080u);
         }
         return n;
@@ -168,15 +213,15 @@ __device__ __forceinline__ void token_terms(float lp, float old, float ref, floa
         g = -em1;                                 // d/dstudent = 1 - exp(x)
     } else {
         const float ratio = fast_exp(lp - old);
-        const float clipped = fminf(fmaxf(ratio, lo), hi);
+        const float clipped = __builtin_amdgcn_fmed3f(ratio, lo, hi);   // clip, lo <= hi
         const float chosen = fminf(ratio, clipped);
         c = -A * chosen;
         g = (ratio <= clipped) ? -A * ratio : 0.0f;   // ties take the unclipped branch
         if constexpr (HAS_KL) {
             const float x = ref - lp;
             const float em1 = fast_exp(x) - 1.0f;
-            c += beta * (em1 - x);
-            g -= beta * em1;
+            c = fmaf(beta, em1 - x, c);
+            g = fmaf(-beta, em1, g);
         }
     }
 }
@@ -210,14 +255,18 @@ __device__ __forceinline__ V block_sum(V v, V* red) {
 
 // ----------------------------------------------------------------------------- workspace protocol
 //
-// Everything one workgroup tells another travels inside an agent-scope atomic
-// word (or a device-coherent store followed by a wait for its completion), so
-// no L2-wide writeback or invalidate (what an agent-scope release/acquire
-// costs on this chip, per workgroup and per poll) is ever issued.
+// Cross-workgroup traffic uses no read-modify-write atomics at all (on this
+// chip device-scope atomics to one line serialise at several ns each, which a
+// grid of a thousand workgroups turns into microseconds).  Instead every
+// workgroup owns one slot of the workspace and publishes two tagged 64-bit
+// words there: its valid-token count and its partial loss.  A tag is the
+// launch generation + 1, so a reader can tell this launch's words from older
+// ones.  A workgroup that needs the global count reads every slot's count
+// word (all-gather by polling); workgroup 0 reads every partial word in slot
+// order, writes the loss and advances the generation for the next launch.
+// All accesses are agent-scope relaxed atomic loads/stores (device-coherent,
+// never an L2-wide writeback or invalidate).
 
-__device__ __forceinline__ uint64_t atomic_add_relaxed(uint64_t* p, uint64_t v) {
-    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 __device__ __forceinline__ uint64_t load_relaxed(const uint64_t* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -229,28 +278,29 @@ __device__ __forceinline__ void store_relaxed(V* p, V v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Makes `v` depend on `dep` as far as the compiler knows (no instruction is
-// emitted): an atomic whose operand is laundered this way is issued only after
-// `dep` has been loaded.
-__device__ __forceinline__ uint64_t after(uint64_t v, uint32_t dep) {
-    asm volatile("" : "+v"(v) : "v"(dep));
-    return v;
-}
-
 // Tags published by the launch of generation `gen`.  A zero-filled workspace
 // holds tag 0 everywhere, which is the tag of no launch's first use; a slot
-// left from an older launch carries an older tag.
+// left from an older launch carries an older tag (32-bit, so a stale tag
+// could only match after 2^32 launches on one workspace).
 __device__ __forceinline__ uint32_t tag_of(uint32_t gen) { return gen + 1u; }
+__device__ __forceinline__ uint64_t tagged(uint32_t tag, uint32_t value) {
+    return (uint64_t(tag) << 32) | value;
+}
 
-// Polls a tagged partial until it carries `tag` (bounded like every wait).
-__device__ uint64_t wait_tagged(Workspace* ws, const uint64_t* slot, uint32_t tag) {
-    uint64_t v = load_relaxed(slot);
+// Polls a tagged word until it carries `tag`.  Bounded: the grid never exceeds
+// the co-resident capacity, so every workgroup publishes within microseconds;
+// the wait gives up after ~1 s of the 100 MHz clock (or kWaitLimitPolls polls,
+// should that clock not advance) and leaves a sticky flag.
+__device__ uint64_t wait_tagged(Workspace* ws, const uint64_t* word, uint32_t tag) {
+    uint64_t v = load_relaxed(word);
     if (uint32_t(v >> 32) == tag) return v;
+    // The clock is read once per 64 polls: reading it is itself a slow scalar
+    // memory access that would otherwise sit between consecutive polls.
     const uint64_t t0 = wall_clock64();
     uint32_t polls = 0;
-    while (uint32_t((v = load_relaxed(slot)) >> 32) != tag) {
-        __builtin_amdgcn_s_sleep(1);
-        if (wall_clock64() - t0 > kWaitLimitTicks || ++polls > kWaitLimitPolls) {
+    while (uint32_t((v = load_relaxed(word)) >> 32) != tag) {
+        __builtin_amdgcn_s_sleep(kPollSleep);
+        if ((++polls & 63) == 0 && (wall_clock64() - t0 > kWaitLimitTicks || polls > kWaitLimitPolls)) {
             __hip_atomic_fetch_or(&ws->flags, kFlagWaitTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             break;
         }
@@ -258,193 +308,224 @@ __device__ uint64_t wait_tagged(Workspace* ws, const uint64_t* slot, uint32_t ta
     return v;
 }
 
-// This workgroup's partial loss, tagged for the launch (one 64-bit
-// device-coherent store: a reader sees either the old or the new pair).
+// Thread 0 publishes this workgroup's count / partial for the launch of generation `gen`.
+__device__ __forceinline__ void publish_count(Workspace* ws, uint32_t gen, uint32_t n) {
+    store_relaxed(&ws->slot[blockIdx.x].count, tagged(tag_of(gen), n));
+}
 __device__ __forceinline__ void publish_partial(Workspace* ws, uint32_t gen, float part) {
-    store_relaxed(&ws->partial[blockIdx.x], (uint64_t(tag_of(gen)) << 32) | __float_as_uint(part));
+    store_relaxed(&ws->slot[blockIdx.x].partial, tagged(tag_of(gen), __float_as_uint(part)));
 }
 
-// Sum of the G partials of this launch in workgroup order (each thread a strided
-// run, then the fixed tree); waits for any partial still in flight.
-__device__ float sum_partials(Workspace* ws, uint32_t gen, float* red) {
-    float s = 0.0f;
-    for (uint32_t i = threadIdx.x; i < gridDim.x; i += kThreads)
-        s += __uint_as_float(uint32_t(wait_tagged(ws, &ws->partial[i], tag_of(gen))));
-    return block_sum(s, red);
-}
-
-// Thread 0 of the launch's final ticket holder: every workgroup has read the
-// generation by now, so the next launch may use the next one.
-__device__ __forceinline__ void advance_generation(Workspace* ws, uint32_t gen) {
-    store_relaxed(&ws->generation, gen + 1u);
-}
-
-// Device-wide count exchange (thread 0 works, the workgroup waits at the
-// barrier with its outstanding loads in flight).  Every workgroup adds
-// (1<<32 | its count) to ws->arrive; the last arrival publishes
-// ws->release = [tag | N] and re-arms arrive; the others poll release until
-// it carries this launch's tag.  Returns N in every thread and sets
-// *is_last in every thread of the last arrival.  With `finalises`, the
-// workgroup's partial is published first and the last arrival ends the launch
-// (advances the generation).  `gen` is thread 0's copy of the launch
-// generation; on return every thread holds it.
-__device__ uint32_t grid_count_exchange(Workspace* ws, uint32_t& gen, uint32_t n_wg, bool finalises,
-                                        float part, uint32_t* lds, bool* is_last) {
-    if (threadIdx.x == 0) {
-        lds[2] = gen;
-        const uint32_t G = gridDim.x;
-        if (finalises) publish_partial(ws, gen, part);
-        const uint64_t prev = atomic_add_relaxed(&ws->arrive, after((uint64_t(1) << 32) | n_wg, gen));
-        uint32_t total;
-        lds[1] = 0;
-        if (uint32_t(prev >> 32) == G - 1) {
-            total = uint32_t(prev) + n_wg;
-            store_relaxed(&ws->release, (uint64_t(tag_of(gen)) << 32) | total);
-            store_relaxed(&ws->arrive, uint64_t(0));
-            if (finalises) advance_generation(ws, gen);
-            lds[1] = 1;
-        } else {
-            // Bounded wait: the grid never exceeds the co-resident capacity, so every
-            // workgroup arrives within microseconds; give up after ~1 s of the 100 MHz
-            // clock (or, should that clock not advance, after kWaitLimitPolls polls).
-            const uint64_t t0 = wall_clock64();
-            uint32_t polls = 0;
-            uint64_t rel;
-            while (uint32_t((rel = load_relaxed(&ws->release)) >> 32) != tag_of(gen)) {
-                __builtin_amdgcn_s_sleep(1);
-                if (wall_clock64() - t0 > kWaitLimitTicks || ++polls > kWaitLimitPolls) {
-                    __hip_atomic_fetch_or(&ws->flags, kFlagWaitTimeout, __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT);
-                    break;
-                }
+// Sum over the G slots of this launch's count words (COUNTS) or partial words
+// (otherwise), in every thread.  Each thread owns slots tid, tid+256, ...: eight
+// independent loads in flight, then any word still carrying an older tag is
+// waited for, then the values are added in slot order and reduced with the fixed
+// workgroup tree, so the result is deterministic.
+template <bool COUNTS>
+__device__ auto gather_slots(Workspace* ws, uint32_t gen, float* red_f, uint32_t* red_u) {
+    using V = typename std::conditional<COUNTS, uint32_t, float>::type;
+    constexpr int kBatch = 8;
+    const uint32_t G = gridDim.x;
+    const uint32_t tag = tag_of(gen);
+    V s = 0;
+    for (uint32_t base = threadIdx.x; base < G; base += kThreads * kBatch) {
+        uint64_t v[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const uint32_t i = base + u * kThreads;
+            const uint64_t* w = COUNTS ? &ws->slot[i].count : &ws->slot[i].partial;
+            v[u] = i < G ? load_relaxed(w) : tagged(tag, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const uint32_t i = base + u * kThreads;
+            const uint64_t* w = COUNTS ? &ws->slot[i].count : &ws->slot[i].partial;
+            if (i < G && uint32_t(v[u] >> 32) != tag) v[u] = wait_tagged(ws, w, tag);
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            if (base + u * kThreads < G) {
+                if constexpr (COUNTS) s += uint32_t(v[u]);
+                else s += __uint_as_float(uint32_t(v[u]));
             }
-            total = uint32_t(rel);
         }
-        lds[0] = total;
     }
-    __syncthreads();
-    *is_last = lds[1] != 0;
-    gen = lds[2];
-    return lds[0];
+    if constexpr (COUNTS) return block_sum(s, red_u);
+    else return block_sum(s, red_f);
 }
 
-// Publish this workgroup's partial and take a finish ticket on ws->depart
-// ([63:32 done | 31:0 count]).  Returns true in every thread of the last
-// workgroup, which re-arms depart, advances the generation and owns the
-// finalise; lds[0] then holds the sum of the counts passed by all workgroups.
-// `gen` as for grid_count_exchange.
-__device__ bool finish_ticket(Workspace* ws, uint32_t& gen, float part, uint32_t n_wg, uint32_t* lds) {
-    if (threadIdx.x == 0) {
-        lds[2] = gen;
-        publish_partial(ws, gen, part);
-        const uint64_t prev = atomic_add_relaxed(&ws->depart, after((uint64_t(1) << 32) | n_wg, gen));
-        const bool last = uint32_t(prev >> 32) == gridDim.x - 1;
-        if (last) {
-            lds[0] = uint32_t(prev) + n_wg;
-            store_relaxed(&ws->depart, uint64_t(0));
-            advance_generation(ws, gen);
-        }
-        lds[1] = last;
-    }
+// The global count: workgroup 0 gathers every count word and publishes the
+// total on the release line; every other workgroup reads the release line
+// (one poller per workgroup on one line, one reader per slot line).  Called by
+// every thread; LEADER_DONE means workgroup 0 already gathered (`n_leader`).
+__device__ __forceinline__ void release_count(Workspace* ws, uint32_t gen, uint32_t n) {
+    if (threadIdx.x == 0) store_relaxed(&ws->release, tagged(tag_of(gen), n));
+}
+__device__ uint32_t await_count(Workspace* ws, uint32_t gen, uint32_t* word) {
     __syncthreads();
-    gen = lds[2];
-    return lds[1] != 0;
+    if (threadIdx.x == 0) *word = uint32_t(wait_tagged(ws, &ws->release, tag_of(gen)));
+    __syncthreads();
+    return *word;
 }
 
-// ----------------------------------------------------------------------------- row cursor
+// Workgroup 0, once it has read every partial of the launch: every workgroup
+// has read the generation by then, so the next launch may use the next one.
+__device__ __forceinline__ void advance_generation(Workspace* ws, uint32_t gen) {
+    if (threadIdx.x == 0) store_relaxed(&ws->generation, gen + 1u);
+}
+
+// Thread 0's generation, made known to the whole workgroup (call where every
+// thread passes; `word` is LDS).
+__device__ __forceinline__ uint32_t share_generation(uint32_t gen, uint32_t* word) {
+    __syncthreads();
+    if (threadIdx.x == 0) *word = gen;
+    __syncthreads();
+    return *word;
+}
+
+// ----------------------------------------------------------------------------- rows
+
+// Row of slot s: s / seq_len by multiply-shift with the host's exact magic
+// constant (valid for every s < 2^31).
+__device__ __forceinline__ uint32_t row_of(const Args& a, uint32_t s) {
+    return uint32_t((uint64_t(s) * a.row_magic) >> a.row_shift);
+}
 
 template <typename T>
-__device__ __forceinline__ float load_adv(const T* adv, int32_t r) {
-    if constexpr (sizeof(T) == 4) return reinterpret_cast<const float*>(adv)[r];
-    else return Elem<T>::to_f32(reinterpret_cast<const uint16_t*>(adv)[r]);
+__device__ __forceinline__ float load_adv(const void* adv, uint32_t r) {
+    if constexpr (sizeof(T) == 4) return static_cast<const float*>(adv)[r];
+    else {
+        const uint32_t w = static_cast<const uint16_t*>(adv)[r];
+        return Elem<T>::get(&w, 0);
+    }
 }
 
 // ----------------------------------------------------------------------------- one tile of one lane
 
-// Computes c and g for the lane's 16 slots starting at s; returns the lane's
-// partial sum of c over valid slots.  g[k] is left at 0 for masked slots.
-template <typename T, int MODE, bool HAS_KL>
-__device__ __forceinline__ float lane_terms(const Args& a, int64_t s, const Mask16& m,
-                                            const Vec16<T>& lp, const Vec16<T>& old,
-                                            const Vec16<T>& ref, const float* row_scale_lds,
-                                            int32_t row_base, float g[kVec]) {
-    float part = 0.0f;
-    if (!m.any()) {
-#pragma unroll
-        for (int k = 0; k < kVec; ++k) g[k] = 0.0f;
-        return part;
+template <typename T, int VEC>
+struct Lane {
+    Mask<VEC> m;
+    Plane<T, VEC> lp, old, ref;
+};
+
+// Issues one lane's mask and plane loads (mask first) and returns its valid
+// count.  A lane entirely in range takes straight-line code in which the count
+// waits for the mask load only, while the plane loads are still in flight; the
+// lane that runs past `slots` (one per launch at most) loads element by element.
+// No workgroup barrier inside, so the divergent branch is safe.
+template <typename T, int MODE, bool HAS_KL, int VEC>
+__device__ __forceinline__ uint32_t load_lane_count(const Args& a, uint32_t s, Lane<T, VEC>& L) {
+    const uint32_t slots = uint32_t(a.slots);
+    if (s + VEC <= slots) {
+        L.m.d.load(a.mask + s);
+        L.lp.d.load(static_cast<const T*>(a.lp) + s);
+        if constexpr (MODE != kModeRKL) L.old.d.load(static_cast<const T*>(a.old) + s);
+        if constexpr (HAS_KL) L.ref.d.load(static_cast<const T*>(a.ref) + s);
+        return L.m.count();
     }
-    const T* adv = static_cast<const T*>(a.adv);
-    // s < slots < 2^31 here (a lane past the end has an all-zero mask).
-    int32_t r = int32_t(uint32_t(s) / uint32_t(a.seq_len));
-    int32_t t = int32_t(s) - r * a.seq_len;
+    L.m.load(a.mask, s, slots);
+    L.lp.load(static_cast<const T*>(a.lp), s, slots);
+    if constexpr (MODE != kModeRKL) L.old.load(static_cast<const T*>(a.old), s, slots);
+    if constexpr (HAS_KL) L.ref.load(static_cast<const T*>(a.ref), s, slots);
+    return L.m.count();
+}
+
+// Loads one lane's mask and planes.  SPECULATIVE issues the plane loads
+// together with the mask load (one memory round trip; used when each
+// workgroup owns one tile and the call is latency-bound); otherwise the plane
+// loads wait for the mask and are skipped when all its bytes are zero.
+template <typename T, int MODE, bool HAS_KL, int VEC, bool SPECULATIVE>
+__device__ __forceinline__ void load_planes(const Args& a, uint32_t s, Lane<T, VEC>& L) {
+    if (SPECULATIVE || L.m.any()) {
+        L.lp.load(static_cast<const T*>(a.lp), s, a.slots);
+        if constexpr (MODE != kModeRKL) L.old.load(static_cast<const T*>(a.old), s, a.slots);
+        if constexpr (HAS_KL) L.ref.load(static_cast<const T*>(a.ref), s, a.slots);
+    }
+}
+
+// Per-slot terms of one lane (slots s .. s+VEC-1): returns the lane's sum of c
+// over valid slots and leaves the unscaled derivative of every slot in g (the
+// store selects masked slots to +0).  GRPO folds each row's 1/(max(n_r,1)*bs)
+// (row_scale[r - row_base], LDS) into c and g.
+template <typename T, int MODE, bool HAS_KL, int VEC>
+__device__ __forceinline__ float lane_terms(const Args& a, uint32_t s, const Lane<T, VEC>& L,
+                                            const float* row_scale, uint32_t row_base, float (&g)[VEC]) {
+    float part = 0.0f;
+    if (!L.m.any()) return part;
+    const uint32_t T_len = uint32_t(a.seq_len);
+    uint32_t r = row_of(a, s);
+    uint32_t t = s - r * T_len;
     float A = 0.0f, scale = 1.0f;
-    if constexpr (MODE != kModeRKL) A = load_adv<T>(adv, r);
-    if constexpr (MODE == kModeGRPO) scale = row_scale_lds[r - row_base];
+    if constexpr (MODE != kModeRKL) A = load_adv<T>(a.adv, r);
+    if constexpr (MODE == kModeGRPO) scale = row_scale[r - row_base];
+    if (t + VEC <= T_len) {
+        // All VEC slots in one row (always, when seq_len is a multiple of VEC): branch-free.
 #pragma unroll
-    for (int k = 0; k < kVec; ++k) {
-        float c = 0.0f, gk = 0.0f;
-        if (m.valid(k)) {
-            token_terms<MODE, HAS_KL>(lp.get(k), MODE == kModeRKL ? 0.0f : old.get(k),
-                                      HAS_KL ? ref.get(k) : 0.0f, A, a.beta, a.lo, a.hi, c, gk);
+        for (int k = 0; k < VEC; ++k) {
+            float c, gk;
+            token_terms<MODE, HAS_KL>(L.lp.get(k), MODE == kModeRKL ? 0.0f : L.old.get(k),
+                                      HAS_KL ? L.ref.get(k) : 0.0f, A, a.beta, a.lo, a.hi, c, gk);
             if constexpr (MODE == kModeGRPO) { c *= scale; gk *= scale; }
-            part += c;
+            part += L.m.valid(k) ? c : 0.0f;
+            g[k] = gk;
         }
-        g[k] = gk;
-        if (k + 1 < kVec && ++t == a.seq_len) {
-            t = 0;
-            ++r;
-            if (r < a.bs) {
-                if constexpr (MODE != kModeRKL) A = load_adv<T>(adv, r);
-                if constexpr (MODE == kModeGRPO) scale = row_scale_lds[r - row_base];
+    } else {
+        // The lane crosses a row boundary: track the row slot by slot.
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) {
+            float c, gk;
+            token_terms<MODE, HAS_KL>(L.lp.get(k), MODE == kModeRKL ? 0.0f : L.old.get(k),
+                                      HAS_KL ? L.ref.get(k) : 0.0f, A, a.beta, a.lo, a.hi, c, gk);
+            if constexpr (MODE == kModeGRPO) { c *= scale; gk *= scale; }
+            part += L.m.valid(k) ? c : 0.0f;
+            g[k] = gk;
+            if (k + 1 < VEC && ++t == T_len) {
+                t = 0;
+                ++r;
+                if (r < uint32_t(a.bs)) {
+                    if constexpr (MODE != kModeRKL) A = load_adv<T>(a.adv, r);
+                    if constexpr (MODE == kModeGRPO) scale = row_scale[r - row_base];
+                }
             }
         }
     }
     return part;
 }
 
-template <typename T, bool HAS_KL, int MODE>
-__device__ __forceinline__ void load_planes(const Args& a, int64_t s, Vec16<T>& lp, Vec16<T>& old,
-                                            Vec16<T>& ref) {
-    lp.load(static_cast<const T*>(a.lp), s, a.slots);
-    if constexpr (MODE != kModeRKL) old.load(static_cast<const T*>(a.old), s, a.slots);
-    if constexpr (HAS_KL) ref.load(static_cast<const T*>(a.ref), s, a.slots);
-}
-
-template <typename T>
-__device__ __forceinline__ void store_grad(const Args& a, int64_t s, const Mask16& m,
-                                           const float g[kVec], float scale) {
-    Vec16<T> out;
+template <typename T, int VEC>
+__device__ __forceinline__ void store_grad(const Args& a, uint32_t s, const Mask<VEC>& m,
+                                           const float (&g)[VEC], float scale) {
+    float v[VEC];
 #pragma unroll
-    for (int k = 0; k < kVec; ++k) out.set(k, m.valid(k) ? g[k] * scale : 0.0f);
-    out.store(static_cast<T*>(a.grad), s, a.slots);
+    for (int k = 0; k < VEC; ++k) v[k] = m.valid(k) ? g[k] * scale : 0.0f;
+    store_values<T, VEC>(static_cast<T*>(a.grad), s, a.slots, v);
 }
 
 // ----------------------------------------------------------------------------- GRPO row counts
 
 // For the tile [s0, s1): counts the mask of every row the tile touches into
 // cnt[row - r_first] (LDS), then turns each count into the row's gradient
-// scale 1 / (max(n_r, 1) * bs).  Writes n_out for rows that start in the tile.
-__device__ void grpo_row_scales(const Args& a, int64_t s0, int64_t s1, uint32_t* cnt,
-                                int32_t& r_first) {
-    const int64_t T = a.seq_len;
-    r_first = int32_t(uint32_t(s0) / uint32_t(T));
-    const int32_t r_last = int32_t(uint32_t(s1 - 1) / uint32_t(T));
-    const int32_t nrows = r_last - r_first + 1;
-    const int64_t e0 = int64_t(r_first) * T, e1 = int64_t(r_last + 1) * T;
-    for (int i = threadIdx.x; i < nrows; i += kThreads) cnt[i] = 0;
+// scale 1 / (max(n_r, 1) * bs) in place.  Writes n_out for rows that start in
+// the tile (exactly one tile per row does).
+__device__ void grpo_row_scales(const Args& a, uint32_t s0, uint32_t s1, uint32_t* cnt,
+                                uint32_t& r_first) {
+    const uint32_t T = uint32_t(a.seq_len);
+    r_first = row_of(a, s0);
+    const uint32_t r_last = row_of(a, s1 - 1);
+    const uint32_t nrows = r_last - r_first + 1;
+    const uint32_t e0 = r_first * T, e1 = (r_last + 1) * T;
+    for (uint32_t i = threadIdx.x; i < nrows; i += kThreads) cnt[i] = 0;
     __syncthreads();
-    for (int64_t c = (e0 & ~int64_t(kVec - 1)) + int64_t(threadIdx.x) * kVec; c < e1;
-         c += int64_t(kThreads) * kVec) {
-        Mask16 m;
-        m.load(a.mask, c, a.slots);
+    for (uint32_t c = (e0 & ~15u) + threadIdx.x * 16u; c < e1; c += kThreads * 16u) {
+        Mask<16> m;
+        m.load(a.mask, c, uint32_t(a.slots));
         if (!m.any()) continue;
-        int32_t r = int32_t(uint32_t(c) / uint32_t(T));
-        int64_t row_end = int64_t(r + 1) * T;
+        uint32_t r = row_of(a, c);
+        uint32_t row_end = (r + 1) * T;
         uint32_t run = 0;
 #pragma unroll
-        for (int k = 0; k < kVec; ++k) {
-            const int64_t i = c + k;
+        for (int k = 0; k < 16; ++k) {
+            const uint32_t i = c + k;
             if (i == row_end) {
                 if (run && r >= r_first && r <= r_last) atomicAdd(&cnt[r - r_first], run);
                 run = 0;
@@ -456,54 +537,16 @@ __device__ void grpo_row_scales(const Args& a, int64_t s0, int64_t s1, uint32_t*
         if (run && r >= r_first && r <= r_last) atomicAdd(&cnt[r - r_first], run);
     }
     __syncthreads();
-    // Each thread turns its own entries from counts into scales in place.
-    for (int i = threadIdx.x; i < nrows; i += kThreads) {
+    for (uint32_t i = threadIdx.x; i < nrows; i += kThreads) {
         const uint32_t n = cnt[i];
-        const float scale = 1.0f / (float(n > 0 ? n : 1u) * float(a.bs));
-        cnt[i] = __float_as_uint(scale);
-        const int32_t r = r_first + i;
-        if (a.n_out && int64_t(r) * T >= s0 && int64_t(r) * T < s1) a.n_out[r] = n;
+        cnt[i] = __float_as_uint(1.0f / (float(n > 0 ? n : 1u) * float(a.bs)));
+        const uint32_t r = r_first + i;
+        if (a.n_out && r * T >= s0 && r * T < s1) a.n_out[r] = n;
     }
     __syncthreads();
 }
 
 // ----------------------------------------------------------------------------- the kernel
-
-// Loads one lane's mask and planes.  SPECULATIVE issues the plane loads
-// together with the mask load (one memory round trip; used when each
-// workgroup owns one tile and the call is latency-bound); otherwise the plane
-// loads wait for the mask and are skipped when all 16 bytes are zero (no plane
-// bytes move for masked slots; used when streaming many tiles).
-template <typename T, int MODE, bool HAS_KL, bool SPECULATIVE>
-__device__ __forceinline__ void load_lane(const Args& a, int64_t s, Mask16& m, Vec16<T>& lp,
-                                          Vec16<T>& old, Vec16<T>& ref) {
-    m.load(a.mask, s, a.slots);
-    if (SPECULATIVE || m.any()) load_planes<T, HAS_KL, MODE>(a, s, lp, old, ref);
-}
-
-template <typename T, int MODE, bool HAS_KL, bool WRITE_GRAD, bool SPECULATIVE>
-__device__ __forceinline__ void stream_tiles(const Args& a, uint32_t* row_lds, float& part,
-                                             uint32_t& n_lane, float scale) {
-    const int64_t G = gridDim.x;
-    const int64_t lane_off = int64_t(threadIdx.x) * kVec;
-    for (int64_t tile = blockIdx.x; tile < a.tiles; tile += G) {
-        const int64_t s = tile * kTile + lane_off;
-        int32_t row_base = 0;
-        if constexpr (MODE == kModeGRPO) {
-            const int64_t s0 = tile * kTile;
-            const int64_t s1 = s0 + kTile < a.slots ? s0 + kTile : a.slots;
-            grpo_row_scales(a, s0, s1, row_lds, row_base);
-        }
-        Mask16 m;
-        Vec16<T> lp, old, ref;
-        load_lane<T, MODE, HAS_KL, SPECULATIVE>(a, s, m, lp, old, ref);
-        n_lane += m.count();
-        float g[kVec];
-        part += lane_terms<T, MODE, HAS_KL>(a, s, m, lp, old, ref,
-                                            reinterpret_cast<const float*>(row_lds), row_base, g);
-        if constexpr (WRITE_GRAD) store_grad<T>(a, s, m, g, scale);
-    }
-}
 
 template <int MODE>
 __device__ __forceinline__ float inv_count(uint32_t N) {
@@ -518,89 +561,144 @@ __device__ __forceinline__ float final_loss(float total, uint32_t N) {
     else return total / float(N > 0 ? N : 1u);
 }
 
-template <typename T, int MODE, bool HAS_KL, bool WRITE_GRAD>
+// Streams the workgroup's tiles (wg, wg+G, ...): per tile, the lane's terms,
+// its count and (WRITE_GRAD) the scaled gradient.  With SPECULATIVE (one tile
+// per workgroup) the plane loads go out with the mask load; otherwise they
+// wait for it, and the next tile's mask is fetched during the current tile.
+template <typename T, int MODE, bool HAS_KL, bool WRITE_GRAD, int VEC, bool SPECULATIVE>
+__device__ __forceinline__ void stream_tiles(const Args& a, uint32_t* row_lds, float& part,
+                                             uint32_t& n_lane, float scale) {
+    constexpr uint32_t kTileV = kThreads * VEC;
+    const uint32_t G = gridDim.x;
+    const uint32_t lane_off = threadIdx.x * VEC;
+    const uint32_t slots = uint32_t(a.slots);
+    uint32_t tile = blockIdx.x;
+    Mask<VEC> next;
+    if (tile < a.tiles) next.load(a.mask, tile * kTileV + lane_off, slots);
+    for (; tile < a.tiles; tile += G) {
+        const uint32_t s = tile * kTileV + lane_off;
+        uint32_t row_base = 0;
+        if constexpr (MODE == kModeGRPO) {
+            const uint32_t s0 = tile * kTileV;
+            grpo_row_scales(a, s0, s0 + kTileV < slots ? s0 + kTileV : slots, row_lds, row_base);
+        }
+        Lane<T, VEC> L;
+        L.m = next;
+        if (tile + G < a.tiles) next.load(a.mask, (tile + G) * kTileV + lane_off, slots);
+        load_planes<T, MODE, HAS_KL, VEC, SPECULATIVE>(a, s, L);
+        n_lane += L.m.count();
+        float g[VEC];
+        part += lane_terms<T, MODE, HAS_KL, VEC>(a, s, L, reinterpret_cast<const float*>(row_lds),
+                                                 row_base, g);
+        if constexpr (WRITE_GRAD) store_grad<T, VEC>(a, s, L.m, g, scale);
+    }
+}
+
+template <typename T, int MODE, bool HAS_KL, bool WRITE_GRAD, int VEC>
 __global__ void __launch_bounds__(kThreads) loss_kernel(const Args a) {
+    constexpr uint32_t kTileV = kThreads * VEC;
     __shared__ float red_f[kWaves];
     __shared__ uint32_t red_u[kWaves];
-    __shared__ uint32_t word[3];
+    __shared__ uint32_t word[1];
     // GRPO: per-row counts, then per-row scales, of the rows a tile touches.
-    constexpr int kRowLds = (MODE == kModeGRPO) ? kTile + 2 : 1;
+    constexpr int kRowLds = (MODE == kModeGRPO) ? int(kTileV) + 2 : 1;
     __shared__ uint32_t row_lds[kRowLds];
 
     Workspace* ws = a.ws;
-    // The launch generation tags this launch's partials and count release; thread 0
-    // reads it first so that the read is in flight together with the data loads.
+    // The launch generation tags everything this launch publishes; thread 0 reads it
+    // first so that the read is in flight together with the data loads.  Every word
+    // a workgroup publishes carries a value derived from it, so its stores cannot be
+    // issued before the read has returned.
     uint32_t gen = 0;
     if (threadIdx.x == 0) gen = load_relaxed(&ws->generation);
 
-    const int64_t G = gridDim.x;
+    const uint32_t G = gridDim.x;
     const bool one_tile = a.tiles <= G;     // uniform: each workgroup owns at most one tile
+    const uint32_t slots = uint32_t(a.slots);
     constexpr bool kGlobalN = MODE != kModeGRPO;
     constexpr bool kExchange = kGlobalN && WRITE_GRAD;
 
     float part = 0.0f;
     uint32_t n_lane = 0;
+    uint32_t N = 0;
 
     if constexpr (kExchange) {
         if (one_tile) {
-            // The tile stays in registers across the count exchange.  The partial loss is
-            // published with the arrival, so the last arrival also finalises the loss and
-            // no workgroup waits for anything after the exchange.
-            const int64_t s = int64_t(blockIdx.x) * kTile + int64_t(threadIdx.x) * kVec;
-            Mask16 m;
-            Vec16<T> lp, old, ref;
-            load_lane<T, MODE, HAS_KL, true>(a, s, m, lp, old, ref);
-            float g[kVec];
-            part = lane_terms<T, MODE, HAS_KL>(a, s, m, lp, old, ref, nullptr, 0, g);
-            const uint32_t n_wg = block_sum(m.count(), red_u);
-            const float part_wg = block_sum(part, red_f);
-            bool last;
-            const uint32_t N = grid_count_exchange(ws, gen, n_wg, true, part_wg, word, &last);
-            store_grad<T>(a, s, m, g, inv_count<MODE>(N));
-            if (last) {
-                const float total = sum_partials(ws, gen, red_f);
-                if (threadIdx.x == 0) {
-                    *a.loss = final_loss<MODE>(total, N);
-                    if (a.n_out) a.n_out[0] = N;
-                }
+            // The tile stays in registers across the count exchange.  The count is
+            // published as soon as the mask (loaded first) has arrived, so the exchange
+            // runs while the planes are still arriving and being computed on; the
+            // partial loss follows as the slot's second word.
+            const uint32_t s = blockIdx.x * kTileV + threadIdx.x * VEC;
+            Lane<T, VEC> L;
+            const uint32_t n_wg = block_sum(load_lane_count<T, MODE, HAS_KL, VEC>(a, s, L), red_u);
+            gen = share_generation(gen, word);
+            if (threadIdx.x == 0) publish_count(ws, gen, n_wg);
+            if (blockIdx.x == 0) {
+                // The leader gathers the counts first and releases N before computing.
+                N = gather_slots<true>(ws, gen, red_f, red_u);
+                release_count(ws, gen, N);
             }
+            float g[VEC];
+            part = lane_terms<T, MODE, HAS_KL, VEC>(a, s, L, nullptr, 0, g);
+            const float part_wg = block_sum(part, red_f);
+            if (threadIdx.x == 0) publish_partial(ws, gen, part_wg);
+            if (blockIdx.x != 0) N = await_count(ws, gen, word);
+            store_grad<T, VEC>(a, s, L.m, g, inv_count<MODE>(N));
         } else {
-            // Several tiles per workgroup: count every owned mask, exchange, then stream.
-            const int64_t lane_off = int64_t(threadIdx.x) * kVec;
-            for (int64_t tile = blockIdx.x; tile < a.tiles; tile += G) {
-                Mask16 m;
-                m.load(a.mask, tile * kTile + lane_off, a.slots);
+            // Several tiles per workgroup: count every owned mask (eight loads in flight
+            // per lane), exchange, then stream.
+            const uint32_t lane_off = threadIdx.x * VEC;
+            uint32_t tile = blockIdx.x;
+            for (; tile + 7 * G < a.tiles; tile += 8 * G) {
+                Mask<VEC> m[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) m[u].load(a.mask, (tile + u * G) * kTileV + lane_off, slots);
+#pragma unroll
+                for (int u = 0; u < 8; ++u) n_lane += m[u].count();
+            }
+            for (; tile < a.tiles; tile += G) {
+                Mask<VEC> m;
+                m.load(a.mask, tile * kTileV + lane_off, slots);
                 n_lane += m.count();
             }
-            bool unused_last;
-            const uint32_t N = grid_count_exchange(ws, gen, block_sum(n_lane, red_u), false, 0.0f,
-                                                   word, &unused_last);
-            uint32_t unused_n = 0;
-            stream_tiles<T, MODE, HAS_KL, true, false>(a, row_lds, part, unused_n, inv_count<MODE>(N));
-            if (finish_ticket(ws, gen, block_sum(part, red_f), 0u, word)) {
-                const float total = sum_partials(ws, gen, red_f);
-                if (threadIdx.x == 0) {
-                    *a.loss = final_loss<MODE>(total, N);
-                    if (a.n_out) a.n_out[0] = N;
-                }
+            gen = share_generation(gen, word);
+            const uint32_t n_wg = block_sum(n_lane, red_u);
+            if (threadIdx.x == 0) publish_count(ws, gen, n_wg);
+            if (blockIdx.x == 0) {
+                N = gather_slots<true>(ws, gen, red_f, red_u);
+                release_count(ws, gen, N);
+            } else {
+                N = await_count(ws, gen, word);
             }
+            uint32_t unused_n = 0;
+            stream_tiles<T, MODE, HAS_KL, true, VEC, false>(a, row_lds, part, unused_n, inv_count<MODE>(N));
+            const float part_wg = block_sum(part, red_f);
+            if (threadIdx.x == 0) publish_partial(ws, gen, part_wg);
         }
     } else {
         // Forward-only (any mode) and GRPO fwd+bwd: one streaming pass, no exchange.
-        if (one_tile) stream_tiles<T, MODE, HAS_KL, WRITE_GRAD, true>(a, row_lds, part, n_lane, 1.0f);
-        else stream_tiles<T, MODE, HAS_KL, WRITE_GRAD, false>(a, row_lds, part, n_lane, 1.0f);
+        if (one_tile) stream_tiles<T, MODE, HAS_KL, WRITE_GRAD, VEC, true>(a, row_lds, part, n_lane, 1.0f);
+        else stream_tiles<T, MODE, HAS_KL, WRITE_GRAD, VEC, false>(a, row_lds, part, n_lane, 1.0f);
+        gen = share_generation(gen, word);
+        const float part_wg = block_sum(part, red_f);
         uint32_t n_wg = 0;
         if constexpr (kGlobalN) n_wg = block_sum(n_lane, red_u);
-        if (finish_ticket(ws, gen, block_sum(part, red_f), n_wg, word)) {
-            const uint32_t N = word[0];
-            const float total = sum_partials(ws, gen, red_f);
-            if (threadIdx.x == 0) {
-                if constexpr (MODE == kModeGRPO) {
-                    *a.loss = total;
-                } else {
-                    *a.loss = final_loss<MODE>(total, N);
-                    if (a.n_out) a.n_out[0] = N;
-                }
+        if (threadIdx.x == 0) {
+            if constexpr (kGlobalN) publish_count(ws, gen, n_wg);
+            publish_partial(ws, gen, part_wg);
+        }
+        if (kGlobalN && blockIdx.x == 0) N = gather_slots<true>(ws, gen, red_f, red_u);
+    }
+    // Workgroup 0 reads every partial, in slot order, and writes the loss.
+    if (blockIdx.x == 0) {
+        const float total = gather_slots<false>(ws, gen, red_f, red_u);
+        advance_generation(ws, gen);
+        if (threadIdx.x == 0) {
+            if constexpr (MODE == kModeGRPO) {
+                *a.loss = total;
+            } else {
+                *a.loss = final_loss<MODE>(total, N);
+                if (a.n_out) a.n_out[0] = N;
             }
         }
     }
@@ -609,30 +707,32 @@ __global__ void __launch_bounds__(kThreads) loss_kernel(const Args a) {
 // ----------------------------------------------------------------------------- host-side table
 
 template <typename T, int MODE, bool HAS_KL, bool WRITE_GRAD>
-static const void* kernel_ptr() {
-    return reinterpret_cast<const void*>(&loss_kernel<T, MODE, HAS_KL, WRITE_GRAD>);
+static const void* kernel_ptr(int vec) {
+    return vec == 4 ? reinterpret_cast<const void*>(&loss_kernel<T, MODE, HAS_KL, WRITE_GRAD, 4>)
+                    : reinterpret_cast<const void*>(&loss_kernel<T, MODE, HAS_KL, WRITE_GRAD, 16>);
 }
 
 template <typename T>
-static const void* pick_typed(int mode, bool has_kl, bool write_grad) {
+static const void* pick_typed(int mode, bool has_kl, bool write_grad, int vec) {
     switch (mode) {
     case kModeBNPO:
-        if (has_kl) return write_grad ? kernel_ptr<T, kModeBNPO, true, true>() : kernel_ptr<T, kModeBNPO, true, false>();
-        return write_grad ? kernel_ptr<T, kModeBNPO, false, true>() : kernel_ptr<T, kModeBNPO, false, false>();
+        if (has_kl) return write_grad ? kernel_ptr<T, kModeBNPO, true, true>(vec) : kernel_ptr<T, kModeBNPO, true, false>(vec);
+        return write_grad ? kernel_ptr<T, kModeBNPO, false, true>(vec) : kernel_ptr<T, kModeBNPO, false, false>(vec);
     case kModeGRPO:
-        if (has_kl) return write_grad ? kernel_ptr<T, kModeGRPO, true, true>() : kernel_ptr<T, kModeGRPO, true, false>();
-        return write_grad ? kernel_ptr<T, kModeGRPO, false, true>() : kernel_ptr<T, kModeGRPO, false, false>();
+        if (has_kl) return write_grad ? kernel_ptr<T, kModeGRPO, true, true>(vec) : kernel_ptr<T, kModeGRPO, true, false>(vec);
+        return write_grad ? kernel_ptr<T, kModeGRPO, false, true>(vec) : kernel_ptr<T, kModeGRPO, false, false>(vec);
     case kModeRKL:
-        return write_grad ? kernel_ptr<T, kModeRKL, true, true>() : kernel_ptr<T, kModeRKL, true, false>();
+        return write_grad ? kernel_ptr<T, kModeRKL, true, true>(vec) : kernel_ptr<T, kModeRKL, true, false>(vec);
     }
     return nullptr;
 }
 
-const void* pick_kernel(int dtype, int mode, bool has_kl, bool write_grad) {
+const void* pick_kernel(int dtype, int mode, bool has_kl, bool write_grad, int vec) {
+    if (vec != 4 && vec != 16) return nullptr;
     switch (dtype) {
-    case kF32: return pick_typed<float>(mode, has_kl, write_grad);
-    case kF16: return pick_typed<_Float16>(mode, has_kl, write_grad);
-    case kBF16: return pick_typed<__bf16>(mode, has_kl, write_grad);
+    case kF32: return pick_typed<float>(mode, has_kl, write_grad, vec);
+    case kF16: return pick_typed<_Float16>(mode, has_kl, write_grad, vec);
+    case kBF16: return pick_typed<__bf16>(mode, has_kl, write_grad, vec);
     }
     return nullptr;
 }

@@ -138,13 +138,21 @@ def test_repeated_calls_are_bitwise_identical_and_rearm_the_workspace():
         assert torch.equal(g1.view(torch.int16), g0.view(torch.int16))
     torch.cuda.synchronize()
     ws = rl.workspace_for(DEV, torch.cuda.current_stream(DEV).cuda_stream, "bnpo")
-    head = ws[:1280].cpu()
+    head = ws[:768 + 256 * 64].cpu()
     gen = int(head[0:4].view(torch.int32)[0]) & 0xFFFFFFFF
-    w64 = head.view(torch.int64).numpy()
-    arrive, release, depart = int(w64[32]), int(w64[64]) & (2**64 - 1), int(w64[96])
-    assert arrive == 0 and depart == 0                 # count exchange and tickets re-armed
-    assert (release >> 32) == gen                      # last exchange's tag = its generation + 1
-    assert int(head[1024:1028].view(torch.int32)[0]) == 0   # no timeout flag
+    assert int(head[256:260].view(torch.int32)[0]) == 0   # no timeout flag
+    release = int(head[512:520].view(torch.int64)[0]) & (2**64 - 1)
+    assert release >> 32 == gen                           # the last release carries its tag
+    assert release & 0xFFFFFFFF == int(torch.count_nonzero(x["mask"]))
+    w64 = head[768:].view(torch.int64).numpy()
+    # every slot (256 B apart) the last fused call used carries its tag (= gen now)
+    n_used = 0
+    for i in range(64):
+        words = [int(w64[32 * i]) & (2**64 - 1), int(w64[32 * i + 1]) & (2**64 - 1)]
+        if words[0] >> 32 == gen:
+            assert words[1] >> 32 == gen
+            n_used += 1
+    assert n_used >= 16
     import ctypes
     flags = ctypes.c_uint32(7)
     assert rl.library().rlpl_workspace_flags(ws.data_ptr(), ctypes.byref(flags),
@@ -290,4 +298,27 @@ def test_fresh_workspace_first_calls_and_generation_wraparound(start_gen):
         got = _all_ops(xb, xr, ws)
         for a, b in zip(got, ref):
             assert torch.equal(a, b)
-    assert int(ws[1024:1028].cpu().view(torch.int32)[0]) == 0
+    assert int(ws[256:260].cpu().view(torch.int32)[0]) == 0
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16", "fp16"])
+def test_non_finite_values_in_masked_slots_change_nothing(dtype):
+    # Masked slots are computed with everything else and selected away: NaN or inf
+    # there must not reach the loss, the gradient or the counts.
+    x = _custom("bnpo", dtype, 7, 1000, "random", seed=77)
+    xr = {"student": x["policy"].clone(), "teacher": x["ref"].clone(), "mask": x["mask"]}
+    poisoned = {k: v.clone() for k, v in x.items() if isinstance(v, torch.Tensor)}
+    masked = x["mask"] == 0
+    for k, val in (("policy", float("nan")), ("old", float("inf")), ("ref", float("-inf"))):
+        poisoned[k][masked] = val
+    a, b = dev(x), dev(poisoned)
+    kw = dict(epsilon=0.2, epsilon_high=0.28, beta=0.04)
+    for fn in (rl.bnpo_loss, rl.grpo_loss):
+        o1 = fn(a["policy"], a["old"], a["ref"], a["advantages"], a["mask"], **kw)
+        o2 = fn(b["policy"], b["old"], b["ref"], b["advantages"], b["mask"], **kw)
+        assert torch.equal(o1[0], o2[0]) and torch.equal(o1[1], o2[1])
+    pr = dev(xr)
+    pp = {"student": b["policy"], "teacher": b["ref"], "mask": b["mask"]}
+    o1 = rl.reverse_kl(pr["student"], pr["teacher"], pr["mask"])
+    o2 = rl.reverse_kl(pp["student"], pp["teacher"], pp["mask"])
+    assert torch.equal(o1[0], o2[0]) and torch.equal(o1[1], o2[1])
