@@ -83,7 +83,7 @@ def test_workspace_bytes(lib):
 def _bnpo_args(**over):
     a = dict(lp=A, old=A + 0x100000, ref=A + 0x200000, adv=A + 0x300000, mask=A + 0x400000,
              bs=4, T=64, dtype=2, mask_dtype=1, beta=0.04, eps=0.2, eps_high=0.28,
-             loss=A + 0x500000, grad=A + 0x600000, n=A + 0x700000, ws=WS, ws_bytes=1 << 20,
+             loss=A + 0x500000, grad=A + 0x600000, n=A + 0x700000, ws=WS, ws_bytes=8 << 20,
              stream=None)
     a.update(over)
     return a
@@ -154,7 +154,7 @@ def test_fused_needs_grad_and_grad_alignment(lib):
     for fn in (lib.grpo_loss,):
         a = _bnpo_args(grad=None)
         assert rl.STATUS[fn(a["lp"], a["old"], a["ref"], a["adv"], a["mask"], 4, 64, 2, 1, 0.04,
-                            0.2, 0.28, a["loss"], None, None, WS, 1 << 20, None)] == "RLPL_ERR_NULL"
+                            0.2, 0.28, a["loss"], None, None, WS, 8 << 20, None)] == "RLPL_ERR_NULL"
 
 
 def test_rkl_validation(lib):
