@@ -54,6 +54,33 @@ def algorithmic_bytes(op: str, slots: int, valid: int, bs: int, elem: int, has_k
     return b
 
 
+def kernel_source_hash() -> str:
+    """sha256 over rl_post_loss_amd/csrc/* (sorted; each file's name, then its bytes)."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "rl_post_loss_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per launch (read + written) recorded from rocprofv3 counters for this
+    workload, or None when none is recorded for the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    digest = kernel_source_hash()
+    with open(path) as fh:
+        for line in fh:
+            parts = line.split()
+            if len(parts) == 4 and not line.startswith("#") and parts[0] == workload and parts[1] == digest:
+                return int(parts[2]) + int(parts[3])
+    return None
+
+
 def timed(fn, calls, K, W, stream, torch):
     """W warmup calls, then K timed back-to-back calls; returns (ms per step wall, ms per launch GPU)."""
     n = len(calls)
@@ -196,7 +223,9 @@ def main() -> int:
     alg = algorithmic_bytes(op, w.slots, valid, w.bs, elem, is_rkl or w.beta != 0, fused)
     achieved = alg / (ms_gpu * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBS, 5), "traffic": None}
+                "frac": round(achieved / PEAK_HBM_GBS, 5),
+                "traffic": recorded_traffic(w.name) if headline else None,
+                "traffic_unit": "HBM bytes per launch (read + written), calibrated rocprofv3 counters"}
 
     cpu = None
     if headline and not args.no_cpu_baseline:

@@ -31,16 +31,16 @@
 //    read-modify-write atomics, never an L2-wide writeback or invalidate.
 //    The grid never exceeds the co-resident capacity; every wait is bounded
 //    in time anyway and sets a sticky flag if it ever gives up.
-//    When a workgroup owns a single tile, its plane loads are issued with its
-//    mask load, its count is published as soon as the mask has arrived, and
-//    the tile never leaves registers; with more tiles it counts its masks
-//    first (eight loads in flight) and streams after.
+//    When a workgroup owns a single tile, its count is published as soon as
+//    its mask has arrived (the exchange then overlaps the plane loads and the
+//    per-token math) and the tile never leaves registers; with more tiles it
+//    counts its masks first (eight loads in flight) and streams after.
 //  * GRPO needs only each row's own count: a workgroup counts the mask of
 //    every row its tile touches into LDS (no cross-workgroup exchange before
 //    the gradient is scaled), as the card's one-block-per-row design does.
-//  * When streaming several tiles per workgroup, plane loads wait for the
-//    mask and are skipped for lanes whose mask bytes are all zero, and the
-//    next tile's mask is fetched while the current tile is computed.
+//  * Plane loads wait for the mask and are skipped for lanes whose mask
+//    bytes are all zero; when streaming several tiles per workgroup, the next
+//    tile's mask is fetched while the current tile is computed.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -409,19 +409,31 @@ struct Lane {
 };
 
 // Issues one lane's mask and plane loads (mask first) and returns its valid
-// count.  A lane entirely in range takes straight-line code in which the count
-// waits for the mask load only, while the plane loads are still in flight; the
-// lane that runs past `slots` (one per launch at most) loads element by element.
-// No workgroup barrier inside, so the divergent branch is safe.
+// count.  By default the plane loads wait for the mask and are skipped when
+// all of its bytes are zero (no plane bytes move for masked lanes; measured
+// faster than issuing them together with the mask, as well as leaner).  A lane
+// entirely in range takes straight-line code; the lane that runs past `slots`
+// (one per launch at most) loads element by element.  No workgroup barrier
+// inside, so the divergent branch is safe.
 template <typename T, int MODE, bool HAS_KL, int VEC>
 __device__ __forceinline__ uint32_t load_lane_count(const Args& a, uint32_t s, Lane<T, VEC>& L) {
     const uint32_t slots = uint32_t(a.slots);
     if (s + VEC <= slots) {
         L.m.d.load(a.mask + s);
-        L.lp.d.load(static_cast<const T*>(a.lp) + s);
-        if constexpr (MODE != kModeRKL) L.old.d.load(static_cast<const T*>(a.old) + s);
-        if constexpr (HAS_KL) L.ref.d.load(static_cast<const T*>(a.ref) + s);
-        return L.m.count();
+        if constexpr (kSpeculativeLoads) {
+            L.lp.d.load(static_cast<const T*>(a.lp) + s);
+            if constexpr (MODE != kModeRKL) L.old.d.load(static_cast<const T*>(a.old) + s);
+            if constexpr (HAS_KL) L.ref.d.load(static_cast<const T*>(a.ref) + s);
+            return L.m.count();
+        } else {
+            const uint32_t n = L.m.count();
+            if (n) {
+                L.lp.d.load(static_cast<const T*>(a.lp) + s);
+                if constexpr (MODE != kModeRKL) L.old.d.load(static_cast<const T*>(a.old) + s);
+                if constexpr (HAS_KL) L.ref.d.load(static_cast<const T*>(a.ref) + s);
+            }
+            return n;
+        }
     }
     L.m.load(a.mask, s, slots);
     L.lp.load(static_cast<const T*>(a.lp), s, slots);
@@ -677,7 +689,7 @@ __global__ void __launch_bounds__(kThreads) loss_kernel(const Args a) {
         }
     } else {
         // Forward-only (any mode) and GRPO fwd+bwd: one streaming pass, no exchange.
-        if (one_tile) stream_tiles<T, MODE, HAS_KL, WRITE_GRAD, VEC, true>(a, row_lds, part, n_lane, 1.0f);
+        if (one_tile) stream_tiles<T, MODE, HAS_KL, WRITE_GRAD, VEC, kSpeculativeLoads>(a, row_lds, part, n_lane, 1.0f);
         else stream_tiles<T, MODE, HAS_KL, WRITE_GRAD, VEC, false>(a, row_lds, part, n_lane, 1.0f);
         gen = share_generation(gen, word);
         const float part_wg = block_sum(part, red_f);
