@@ -168,6 +168,16 @@ int reverse_kl_fwd(const void* student_lp, const void* teacher_lp, const void* m
 /* Bytes of workspace an `op` call on a (bs, seq_len) problem needs (0 for a bad op). */
 size_t rlpl_workspace_bytes(int64_t bs, int64_t seq_len, int op);
 
+/* Launch shape a call of `op` on a (bs, seq_len) problem of `dtype` would use
+ * on the current device (host pointers, written): workgroups in the grid (one
+ * coordinator plus one worker per tile when tiles < grid; else every
+ * workgroup strides over the tiles), consecutive slots per lane (4 or 16) and
+ * tiles of 256 lanes.  For
+ * profiling and tests; enqueues nothing.  Returns RLPL_OK, or an rlpl_status
+ * for bad arguments or no usable device. */
+int rlpl_launch_shape(int64_t bs, int64_t seq_len, int dtype, int op, int* grid_out, int* vec_out,
+                      int* tiles_out);
+
 /* Sticky error bits the kernels left in a workspace (host pointer `flags_out`
  * receives them; synchronises `stream`).  Bit 0: a cross-workgroup wait gave
  * up after its time limit, so that call's results are not valid and the

@@ -34,7 +34,8 @@ import torch  # loaded first so the library binds to torch's HIP runtime
 from . import build as _build
 
 __all__ = ["bnpo_loss", "bnpo_loss_fwd", "grpo_loss", "grpo_loss_fwd", "reverse_kl",
-           "reverse_kl_fwd", "library", "library_path", "RlplError", "STATUS", "workspace_for"]
+           "reverse_kl_fwd", "library", "library_path", "RlplError", "STATUS", "workspace_for",
+           "launch_shape"]
 
 STATUS = {0: "RLPL_OK", 1: "RLPL_ERR_NULL", 2: "RLPL_ERR_SHAPE", 3: "RLPL_ERR_ALIGN",
           4: "RLPL_ERR_DTYPE", 5: "RLPL_ERR_PARAM", 6: "RLPL_ERR_WORKSPACE", 7: "RLPL_ERR_DEVICE",
@@ -74,6 +75,8 @@ def _declare(lib):
     lib.rlpl_workspace_bytes.argtypes, lib.rlpl_workspace_bytes.restype = [i64, i64, i32], sz
     lib.rlpl_workspace_flags.argtypes = [vp, ctypes.POINTER(ctypes.c_uint32), vp]
     lib.rlpl_workspace_flags.restype = ctypes.c_int
+    lib.rlpl_launch_shape.argtypes = [i64, i64, i32, i32] + [ctypes.POINTER(ctypes.c_int)] * 3
+    lib.rlpl_launch_shape.restype = ctypes.c_int
     lib.rlpl_status_string.argtypes, lib.rlpl_status_string.restype = [i32], ctypes.c_char_p
     lib.rlpl_version.argtypes, lib.rlpl_version.restype = [], ctypes.c_int
     return lib
@@ -100,6 +103,14 @@ def workspace_for(device: torch.device, stream_ptr: int, op: str = "bnpo") -> to
         ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
+
+
+def launch_shape(bs: int, seq_len: int, dtype: torch.dtype, op: str = "bnpo"):
+    """(workgroups, slots per lane, tiles) a call would launch with on the current device."""
+    grid, vec, tiles = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
+    _check("rlpl_launch_shape", library().rlpl_launch_shape(bs, seq_len, DTYPE[dtype], OP[op], ctypes.byref(grid),
+                                                            ctypes.byref(vec), ctypes.byref(tiles)))
+    return grid.value, vec.value, tiles.value
 
 
 def _aligned(t: torch.Tensor) -> torch.Tensor:

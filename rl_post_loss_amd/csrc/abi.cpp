@@ -25,12 +25,13 @@ using rlpl::kModeRKL;
 
 constexpr int kAbiVersion = 1;
 constexpr int kMaxDevices = 64;
+constexpr size_t kLdsPerCu = 128 * 1024;   // LDS budget per CU for co-residency
 
 // Per-device launch facts, filled once per device (thread-safe) and then read-only.
 struct DeviceInfo {
     int status = RLPL_ERR_DEVICE;
     int cus = 0;
-    int grid_cap[3][3][2] = {};  // [dtype][mode][vec small/large]: co-resident workgroups
+    int grid_cap[3][3][rlpl::kShapes] = {};  // [dtype][mode][kernel shape]: co-resident workgroups
 };
 DeviceInfo g_info[kMaxDevices];
 std::once_flag g_once[kMaxDevices];
@@ -45,7 +46,7 @@ void init_device(int dev, DeviceInfo& info) {
     info.cus = cus;
     for (int dt = 0; dt < 3; ++dt)
         for (int mode = 0; mode < 3; ++mode)
-            for (int v = 0; v < 2; ++v) {
+            for (int shape = 0; shape < rlpl::kShapes; ++shape) {
                 // The whole family shares one grid size so that its forward-only and
                 // fwd+bwd kernels reduce over identical partitions (identical losses),
                 // and that size never exceeds what is co-resident on the device, which
@@ -53,17 +54,26 @@ void init_device(int dev, DeviceInfo& info) {
                 int occ = 1 << 30;
                 for (int kl = 0; kl < 2; ++kl)
                     for (int wg = 0; wg < 2; ++wg) {
-                        const void* k = rlpl::pick_kernel(dt, mode, kl != 0 || mode == kModeRKL, wg != 0,
-                                                          v ? rlpl::kVecLarge : rlpl::kVecSmall);
+                        const void* k = rlpl::pick_kernel(dt, mode, kl != 0 || mode == kModeRKL, wg != 0, shape);
                         int nb = 0;
+                        hipFuncAttributes attr;
                         if (!k || hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k, rlpl::kThreads, 0) !=
-                                      hipSuccess || nb < 1)
+                                      hipSuccess || nb < 1 ||
+                            hipFuncGetAttributes(&attr, k) != hipSuccess)
                             return;
+                        // Keep the workgroups' LDS within kLdsPerCu: all of a CU's
+                        // 160 KB is not always usable (five workgroups of 32 KB are
+                        // not co-resident on gfx950).
+                        if (attr.sharedSizeBytes > 0) {
+                            const int by_lds = int(kLdsPerCu / attr.sharedSizeBytes);
+                            if (by_lds < nb) nb = by_lds;
+                        }
+                        if (nb < 1) return;
                         if (nb < occ) occ = nb;
                     }
                 long cap = long(occ) * cus;
                 if (cap > rlpl::kMaxGrid) cap = rlpl::kMaxGrid;
-                info.grid_cap[dt][mode][v] = int(cap);
+                info.grid_cap[dt][mode][shape] = int(cap);
             }
     info.status = RLPL_OK;
 }
@@ -113,23 +123,49 @@ int launch(const void* kernel, const Args& a, int64_t grid, hipStream_t stream) 
     return RLPL_OK;
 }
 
-// Shared tail of every entry point: lane width, grid sizing and the launch.
+struct Shape {
+    int kernel;      // rlpl::kShapeSmall / kShapeLarge / kShapeStream
+    int vec;
+    uint32_t tiles;
+    int64_t grid;
+};
+
+// Kernel shape, tile count and grid of a call on this device: one
+// coordinating workgroup plus one worker per tile whenever that many
+// workgroups of the one-tile kernel are co-resident (small problems take the
+// narrow lane so that every compute unit gets a tile), else the striding
+// kernel on as many workgroups as are co-resident (all of them workers).
+int launch_shape(const DeviceInfo* info, int dtype, int mode, int64_t slots, Shape* out) {
+    const int64_t large_tile = int64_t(rlpl::kThreads) * rlpl::kVecLarge;
+    const int64_t small_tile = int64_t(rlpl::kThreads) * rlpl::kVecSmall;
+    const int* cap = info->grid_cap[dtype][mode];
+    const int64_t small_tiles = (slots + small_tile - 1) / small_tile;
+    const int64_t large_tiles = (slots + large_tile - 1) / large_tile;
+    if (slots < int64_t(info->cus) * rlpl::kSmallTilesPerCu * large_tile && small_tiles + 1 <= cap[rlpl::kShapeSmall]) {
+        *out = {rlpl::kShapeSmall, rlpl::kVecSmall, uint32_t(small_tiles), small_tiles + 1};
+    } else if (large_tiles + 1 <= cap[rlpl::kShapeLarge]) {
+        *out = {rlpl::kShapeLarge, rlpl::kVecLarge, uint32_t(large_tiles), large_tiles + 1};
+    } else {
+        const int64_t c = cap[rlpl::kShapeStream];
+        if (c < 1) return RLPL_ERR_DEVICE;
+        *out = {rlpl::kShapeStream, rlpl::kVecLarge, uint32_t(large_tiles), large_tiles < c ? large_tiles : c};
+    }
+    return RLPL_OK;
+}
+
+// Shared tail of every entry point: launch shape, row divisor and the launch.
 int run(int mode, bool write_grad, bool has_kl, Args& a, int dtype, hipStream_t stream) {
     const DeviceInfo* info = nullptr;
-    const int st = current_device(&info);
+    int st = current_device(&info);
     if (st != RLPL_OK) return st;
-    // Small problems take the narrow lane so that every compute unit gets a tile.
-    const int64_t large_tile = int64_t(rlpl::kThreads) * rlpl::kVecLarge;
-    const bool small = a.slots < int64_t(info->cus) * rlpl::kSmallTilesPerCu * large_tile;
-    const int vec = small ? rlpl::kVecSmall : rlpl::kVecLarge;
-    const void* kernel = rlpl::pick_kernel(dtype, mode, has_kl, write_grad, vec);
+    Shape sh;
+    st = launch_shape(info, dtype, mode, a.slots, &sh);
+    if (st != RLPL_OK) return st;
+    const void* kernel = rlpl::pick_kernel(dtype, mode, has_kl, write_grad, sh.kernel);
     if (!kernel) return RLPL_ERR_DTYPE;
-    const int64_t tile = int64_t(rlpl::kThreads) * vec;
-    a.tiles = uint32_t((a.slots + tile - 1) / tile);
+    a.tiles = sh.tiles;
     if (!rlpl::row_divisor(uint32_t(a.seq_len), &a.row_magic, &a.row_shift)) return RLPL_ERR_SHAPE;
-    const int64_t cap = info->grid_cap[dtype][mode][small ? 0 : 1];
-    const int64_t grid = int64_t(a.tiles) < cap ? int64_t(a.tiles) : cap;
-    return launch(kernel, a, grid, stream);
+    return launch(kernel, a, sh.grid, stream);
 }
 
 int policy_loss(int mode, bool write_grad, const void* policy_lp, const void* old_lp,
@@ -257,6 +293,31 @@ size_t rlpl_workspace_bytes(int64_t bs, int64_t seq_len, int op) {
     (void)seq_len;
     if (op < RLPL_OP_BNPO || op > RLPL_OP_RKL_FWD) return 0;
     return rlpl::kWorkspaceBytes;
+}
+
+int rlpl_launch_shape(int64_t bs, int64_t seq_len, int dtype, int op, int* grid_out, int* vec_out,
+                      int* tiles_out) {
+    if (!grid_out || !vec_out || !tiles_out) return RLPL_ERR_NULL;
+    if (bs < 1 || seq_len < 1 || bs > (int64_t(1) << 31) / seq_len || bs * seq_len >= (int64_t(1) << 31))
+        return RLPL_ERR_SHAPE;
+    if (dtype != RLPL_F32 && dtype != RLPL_F16 && dtype != RLPL_BF16) return RLPL_ERR_DTYPE;
+    int mode;
+    switch (op) {
+    case RLPL_OP_BNPO: case RLPL_OP_BNPO_FWD: mode = kModeBNPO; break;
+    case RLPL_OP_GRPO: case RLPL_OP_GRPO_FWD: mode = kModeGRPO; break;
+    case RLPL_OP_RKL: case RLPL_OP_RKL_FWD: mode = kModeRKL; break;
+    default: return RLPL_ERR_PARAM;
+    }
+    const DeviceInfo* info = nullptr;
+    int st = current_device(&info);
+    if (st != RLPL_OK) return st;
+    Shape sh;
+    st = launch_shape(info, dtype, mode, bs * seq_len, &sh);
+    if (st != RLPL_OK) return st;
+    *grid_out = int(sh.grid);
+    *vec_out = sh.vec;
+    *tiles_out = int(sh.tiles);
+    return RLPL_OK;
 }
 
 int rlpl_workspace_flags(const void* workspace, uint32_t* flags_out, hipStream_t stream) {

@@ -15,6 +15,9 @@ constexpr int kWaves = kThreads / 64;
 // per compute unit.  A tile is kThreads * VEC slots.
 constexpr int kVecLarge = 16;
 constexpr int kVecSmall = 4;
+// Kernel shapes: one tile per worker with the narrow or the wide lane, or the
+// wide lane striding over several tiles per worker.
+enum { kShapeSmall = 0, kShapeLarge = 1, kShapeStream = 2, kShapes = 3 };
 #ifndef RLPL_SMALL_TILES_PER_CU
 #define RLPL_SMALL_TILES_PER_CU 1
 #endif
@@ -88,6 +91,6 @@ struct Args {
 };
 
 // The kernel instantiation for (dtype, mode, KL on/off, gradient on/off, VEC), or NULL.
-const void* pick_kernel(int dtype, int mode, bool has_kl, bool write_grad, int vec);
+const void* pick_kernel(int dtype, int mode, bool has_kl, bool write_grad, int shape);
 
 }  // namespace rlpl

@@ -15,18 +15,19 @@
 //    bytes and its VEC log-probs per plane with 32/64/128-bit loads.  VEC is
 //    16 for large problems and 4 for small ones, so that a small problem
 //    still spreads over every compute unit.
-//  * A persistent grid of G <= (co-resident workgroups) takes tiles
-//    wg, wg+G, wg+2G, ...  Per-token math is fp32 in registers and
+//  * A persistent grid of G <= (co-resident workgroups): workgroup 0
+//    coordinates, workers 1..G-1 take tiles w, w+(G-1), ...  Per-token math
+//    is fp32 in registers and
 //    branch-free: every slot of a lane is computed and masked slots are
 //    selected away (their values never reach a result).
 //  * Reductions: per-lane sums -> wavefront shuffle tree -> LDS across the
-//    4 waves -> one partial per workgroup in the workspace.  The partial that
-//    finishes last sums the G partials in workgroup order, so the loss is
-//    deterministic and identical between the fwd+bwd and forward-only kernels.
+//    4 waves -> one partial per worker in the workspace.  The coordinator
+//    sums the partials in worker order, so the loss is deterministic and
+//    identical between the fwd+bwd and forward-only kernels.
 //  * BNPO / RKL fwd+bwd need the global valid count N before any gradient is
-//    scaled: each workgroup publishes its count in a slot of its own;
-//    workgroup 0 gathers them and publishes N on a release line that the
-//    others read once their own tile is computed.  All cross-workgroup
+//    scaled: each worker publishes its count in a slot of its own; the
+//    coordinator gathers them and publishes N on a release line that the
+//    workers read once their own tile is computed.  All cross-workgroup
 //    traffic is device-coherent loads/stores of generation-tagged words: no
 //    read-modify-write atomics, never an L2-wide writeback or invalidate.
 //    The grid never exceeds the co-resident capacity; every wait is bounded
@@ -308,24 +309,23 @@ __device__ uint64_t wait_tagged(Workspace* ws, const uint64_t* word, uint32_t ta
     return v;
 }
 
-// Thread 0 publishes this workgroup's count / partial for the launch of generation `gen`.
-__device__ __forceinline__ void publish_count(Workspace* ws, uint32_t gen, uint32_t n) {
-    store_relaxed(&ws->slot[blockIdx.x].count, tagged(tag_of(gen), n));
+// Thread 0 of worker `w` publishes its count / partial for the launch of generation `gen`.
+__device__ __forceinline__ void publish_count(Workspace* ws, uint32_t w, uint32_t gen, uint32_t n) {
+    store_relaxed(&ws->slot[w].count, tagged(tag_of(gen), n));
 }
-__device__ __forceinline__ void publish_partial(Workspace* ws, uint32_t gen, float part) {
-    store_relaxed(&ws->slot[blockIdx.x].partial, tagged(tag_of(gen), __float_as_uint(part)));
+__device__ __forceinline__ void publish_partial(Workspace* ws, uint32_t w, uint32_t gen, float part) {
+    store_relaxed(&ws->slot[w].partial, tagged(tag_of(gen), __float_as_uint(part)));
 }
 
-// Sum over the G slots of this launch's count words (COUNTS) or partial words
-// (otherwise), in every thread.  Each thread owns slots tid, tid+256, ...: eight
+// Sum over the W workers' slots of this launch's count words (COUNTS) or
+// partial words (otherwise), in every thread.  Each thread owns slots tid, tid+256, ...: eight
 // independent loads in flight, then any word still carrying an older tag is
 // waited for, then the values are added in slot order and reduced with the fixed
 // workgroup tree, so the result is deterministic.
 template <bool COUNTS>
-__device__ auto gather_slots(Workspace* ws, uint32_t gen, float* red_f, uint32_t* red_u) {
+__device__ auto gather_slots(Workspace* ws, uint32_t G, uint32_t gen, float* red_f, uint32_t* red_u) {
     using V = typename std::conditional<COUNTS, uint32_t, float>::type;
     constexpr int kBatch = 8;
-    const uint32_t G = gridDim.x;
     const uint32_t tag = tag_of(gen);
     V s = 0;
     for (uint32_t base = threadIdx.x; base < G; base += kThreads * kBatch) {
@@ -354,10 +354,9 @@ __device__ auto gather_slots(Workspace* ws, uint32_t gen, float* red_f, uint32_t
     else return block_sum(s, red_f);
 }
 
-// The global count: workgroup 0 gathers every count word and publishes the
-// total on the release line; every other workgroup reads the release line
-// (one poller per workgroup on one line, one reader per slot line).  Called by
-// every thread; LEADER_DONE means workgroup 0 already gathered (`n_leader`).
+// The global count: the coordinator gathers every count word and publishes the
+// total on the release line; every worker reads the release line (one poller
+// per workgroup on one line, one reader per slot line).
 __device__ __forceinline__ void release_count(Workspace* ws, uint32_t gen, uint32_t n) {
     if (threadIdx.x == 0) store_relaxed(&ws->release, tagged(tag_of(gen), n));
 }
@@ -368,7 +367,7 @@ __device__ uint32_t await_count(Workspace* ws, uint32_t gen, uint32_t* word) {
     return *word;
 }
 
-// Workgroup 0, once it has read every partial of the launch: every workgroup
+// The coordinator, once it has read every partial of the launch: every workgroup
 // has read the generation by then, so the next launch may use the next one.
 __device__ __forceinline__ void advance_generation(Workspace* ws, uint32_t gen) {
     if (threadIdx.x == 0) store_relaxed(&ws->generation, gen + 1u);
@@ -442,13 +441,11 @@ __device__ __forceinline__ uint32_t load_lane_count(const Args& a, uint32_t s, L
     return L.m.count();
 }
 
-// Loads one lane's mask and planes.  SPECULATIVE issues the plane loads
-// together with the mask load (one memory round trip; used when each
-// workgroup owns one tile and the call is latency-bound); otherwise the plane
-// loads wait for the mask and are skipped when all its bytes are zero.
-template <typename T, int MODE, bool HAS_KL, int VEC, bool SPECULATIVE>
+// Loads one lane's planes once its mask has arrived; skipped when all of the
+// mask's bytes are zero.
+template <typename T, int MODE, bool HAS_KL, int VEC>
 __device__ __forceinline__ void load_planes(const Args& a, uint32_t s, Lane<T, VEC>& L) {
-    if (SPECULATIVE || L.m.any()) {
+    if (L.m.any()) {
         L.lp.load(static_cast<const T*>(a.lp), s, a.slots);
         if constexpr (MODE != kModeRKL) L.old.load(static_cast<const T*>(a.old), s, a.slots);
         if constexpr (HAS_KL) L.ref.load(static_cast<const T*>(a.ref), s, a.slots);
@@ -526,6 +523,9 @@ __device__ void grpo_row_scales(const Args& a, uint32_t s0, uint32_t s1, uint32_
     const uint32_t r_last = row_of(a, s1 - 1);
     const uint32_t nrows = r_last - r_first + 1;
     const uint32_t e0 = r_first * T, e1 = (r_last + 1) * T;
+    // cnt[] still holds the previous tile's scales, which other threads may be
+    // reading: clear it only once every thread is done with them.
+    __syncthreads();
     for (uint32_t i = threadIdx.x; i < nrows; i += kThreads) cnt[i] = 0;
     __syncthreads();
     for (uint32_t c = (e0 & ~15u) + threadIdx.x * 16u; c < e1; c += kThreads * 16u) {
@@ -573,18 +573,30 @@ __device__ __forceinline__ float final_loss(float total, uint32_t N) {
     else return total / float(N > 0 ? N : 1u);
 }
 
-// Streams the workgroup's tiles (wg, wg+G, ...): per tile, the lane's terms,
-// its count and (WRITE_GRAD) the scaled gradient.  With SPECULATIVE (one tile
-// per workgroup) the plane loads go out with the mask load; otherwise they
-// wait for it, and the next tile's mask is fetched during the current tile.
-template <typename T, int MODE, bool HAS_KL, bool WRITE_GRAD, int VEC, bool SPECULATIVE>
-__device__ __forceinline__ void stream_tiles(const Args& a, uint32_t* row_lds, float& part,
-                                             uint32_t& n_lane, float scale) {
+// Thread 0 of the coordinating workgroup: the loss (and for the global-count
+// losses, the valid-token count N).
+template <int MODE>
+__device__ __forceinline__ void write_results(const Args& a, float total, uint32_t N) {
+    if constexpr (MODE == kModeGRPO) {
+        *a.loss = total;
+    } else {
+        *a.loss = final_loss<MODE>(total, N);
+        if (a.n_out) a.n_out[0] = N;
+    }
+}
+
+// Streams worker `worker`'s tiles (worker, worker+G, ... for G workers): per
+// tile, the lane's terms, its count and (WRITE_GRAD) the scaled gradient.  The
+// plane loads wait for the mask, and the next tile's mask is fetched during
+// the current tile.
+template <typename T, int MODE, bool HAS_KL, bool WRITE_GRAD, int VEC>
+__device__ __forceinline__ void stream_tiles(const Args& a, uint32_t worker, uint32_t G,
+                                             uint32_t* row_lds, float& part, uint32_t& n_lane,
+                                             float scale) {
     constexpr uint32_t kTileV = kThreads * VEC;
-    const uint32_t G = gridDim.x;
     const uint32_t lane_off = threadIdx.x * VEC;
     const uint32_t slots = uint32_t(a.slots);
-    uint32_t tile = blockIdx.x;
+    uint32_t tile = worker;
     Mask<VEC> next;
     if (tile < a.tiles) next.load(a.mask, tile * kTileV + lane_off, slots);
     for (; tile < a.tiles; tile += G) {
@@ -597,7 +609,7 @@ __device__ __forceinline__ void stream_tiles(const Args& a, uint32_t* row_lds, f
         Lane<T, VEC> L;
         L.m = next;
         if (tile + G < a.tiles) next.load(a.mask, (tile + G) * kTileV + lane_off, slots);
-        load_planes<T, MODE, HAS_KL, VEC, SPECULATIVE>(a, s, L);
+        load_planes<T, MODE, HAS_KL, VEC>(a, s, L);
         n_lane += L.m.count();
         float g[VEC];
         part += lane_terms<T, MODE, HAS_KL, VEC>(a, s, L, reinterpret_cast<const float*>(row_lds),
@@ -606,7 +618,14 @@ __device__ __forceinline__ void stream_tiles(const Args& a, uint32_t* row_lds, f
     }
 }
 
-template <typename T, int MODE, bool HAS_KL, bool WRITE_GRAD, int VEC>
+// Workgroup 0 coordinates: it gathers the workers' counts, releases N (fwd+bwd
+// BNPO / reverse-KL), gathers their partials in worker order, writes the loss
+// and advances the generation.  ONE_TILE kernels are launched with exactly one
+// tile per worker and a coordinator that owns no tile (G = tiles + 1), and
+// keep the tile in registers in straight-line code.  The others (G at most the
+// co-resident capacity, G <= tiles) stride over any number of tiles per
+// worker, which costs registers, and workgroup 0 is a worker as well.
+template <typename T, int MODE, bool HAS_KL, bool WRITE_GRAD, int VEC, bool ONE_TILE>
 __global__ void __launch_bounds__(kThreads) loss_kernel(const Args a) {
     constexpr uint32_t kTileV = kThreads * VEC;
     __shared__ float red_f[kWaves];
@@ -624,94 +643,118 @@ __global__ void __launch_bounds__(kThreads) loss_kernel(const Args a) {
     uint32_t gen = 0;
     if (threadIdx.x == 0) gen = load_relaxed(&ws->generation);
 
-    const uint32_t G = gridDim.x;
-    const bool one_tile = a.tiles <= G;     // uniform: each workgroup owns at most one tile
-    const uint32_t slots = uint32_t(a.slots);
     constexpr bool kGlobalN = MODE != kModeGRPO;
     constexpr bool kExchange = kGlobalN && WRITE_GRAD;
-
+    const uint32_t slots = uint32_t(a.slots);
     float part = 0.0f;
     uint32_t n_lane = 0;
-    uint32_t N = 0;
 
-    if constexpr (kExchange) {
-        if (one_tile) {
+    if constexpr (ONE_TILE) {
+        // Workgroup 0 coordinates only; workgroup w > 0 is worker w - 1 and owns tile w - 1.
+        const uint32_t W = gridDim.x - 1;
+        if (blockIdx.x == 0) {
+            gen = share_generation(gen, word);
+            uint32_t N = 0;
+            if constexpr (kGlobalN) N = gather_slots<true>(ws, W, gen, red_f, red_u);
+            if constexpr (kExchange) release_count(ws, gen, N);
+            const float total = gather_slots<false>(ws, W, gen, red_f, red_u);
+            advance_generation(ws, gen);
+            if (threadIdx.x == 0) write_results<MODE>(a, total, N);
+            return;
+        }
+        const uint32_t worker = blockIdx.x - 1;
+        const uint32_t s = worker * kTileV + threadIdx.x * VEC;
+        Lane<T, VEC> L;
+        if constexpr (kExchange) {
             // The tile stays in registers across the count exchange.  The count is
             // published as soon as the mask (loaded first) has arrived, so the exchange
             // runs while the planes are still arriving and being computed on; the
             // partial loss follows as the slot's second word.
-            const uint32_t s = blockIdx.x * kTileV + threadIdx.x * VEC;
-            Lane<T, VEC> L;
             const uint32_t n_wg = block_sum(load_lane_count<T, MODE, HAS_KL, VEC>(a, s, L), red_u);
             gen = share_generation(gen, word);
-            if (threadIdx.x == 0) publish_count(ws, gen, n_wg);
-            if (blockIdx.x == 0) {
-                // The leader gathers the counts first and releases N before computing.
-                N = gather_slots<true>(ws, gen, red_f, red_u);
-                release_count(ws, gen, N);
-            }
+            if (threadIdx.x == 0) publish_count(ws, worker, gen, n_wg);
             float g[VEC];
             part = lane_terms<T, MODE, HAS_KL, VEC>(a, s, L, nullptr, 0, g);
             const float part_wg = block_sum(part, red_f);
-            if (threadIdx.x == 0) publish_partial(ws, gen, part_wg);
-            if (blockIdx.x != 0) N = await_count(ws, gen, word);
+            if (threadIdx.x == 0) publish_partial(ws, worker, gen, part_wg);
+            const uint32_t N = await_count(ws, gen, word);
             store_grad<T, VEC>(a, s, L.m, g, inv_count<MODE>(N));
         } else {
-            // Several tiles per workgroup: count every owned mask (eight loads in flight
-            // per lane), exchange, then stream.
+            // Forward-only (any mode) and GRPO fwd+bwd.  GRPO first scans the masks of
+            // the rows the tile touches (measured faster than overlapping the scan with
+            // the tile's plane loads, whose completion the scan's loads would wait for).
+            uint32_t row_base = 0;
+            if constexpr (MODE == kModeGRPO) {
+                const uint32_t s0 = worker * kTileV;
+                grpo_row_scales(a, s0, s0 + kTileV < slots ? s0 + kTileV : slots, row_lds, row_base);
+            }
+            n_lane = load_lane_count<T, MODE, HAS_KL, VEC>(a, s, L);
+            float g[VEC];
+            part = lane_terms<T, MODE, HAS_KL, VEC>(a, s, L, reinterpret_cast<const float*>(row_lds),
+                                                    row_base, g);
+            if constexpr (WRITE_GRAD) store_grad<T, VEC>(a, s, L.m, g, 1.0f);
+            gen = share_generation(gen, word);
+            const float part_wg = block_sum(part, red_f);
+            uint32_t n_wg = 0;
+            if constexpr (kGlobalN) n_wg = block_sum(n_lane, red_u);
+            if (threadIdx.x == 0) {
+                if constexpr (kGlobalN) publish_count(ws, worker, gen, n_wg);
+                publish_partial(ws, worker, gen, part_wg);
+            }
+        }
+    } else {
+        // Every workgroup is a worker striding over the tiles; workgroup 0 also
+        // coordinates (a dedicated coordinator would take one of the co-resident
+        // slots, and with it a whole extra tile from some worker's share).
+        const uint32_t W = gridDim.x;
+        const uint32_t worker = blockIdx.x;
+        uint32_t N = 0;
+        if constexpr (kExchange) {
+            // Count every owned mask (eight loads in flight per lane), exchange, then stream.
             const uint32_t lane_off = threadIdx.x * VEC;
-            uint32_t tile = blockIdx.x;
-            for (; tile + 7 * G < a.tiles; tile += 8 * G) {
+            uint32_t tile = worker;
+            for (; tile + 7 * W < a.tiles; tile += 8 * W) {
                 Mask<VEC> m[8];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) m[u].load(a.mask, (tile + u * G) * kTileV + lane_off, slots);
+                for (int u = 0; u < 8; ++u) m[u].load(a.mask, (tile + u * W) * kTileV + lane_off, slots);
 #pragma unroll
                 for (int u = 0; u < 8; ++u) n_lane += m[u].count();
             }
-            for (; tile < a.tiles; tile += G) {
+            for (; tile < a.tiles; tile += W) {
                 Mask<VEC> m;
                 m.load(a.mask, tile * kTileV + lane_off, slots);
                 n_lane += m.count();
             }
             gen = share_generation(gen, word);
             const uint32_t n_wg = block_sum(n_lane, red_u);
-            if (threadIdx.x == 0) publish_count(ws, gen, n_wg);
+            if (threadIdx.x == 0) publish_count(ws, worker, gen, n_wg);
             if (blockIdx.x == 0) {
-                N = gather_slots<true>(ws, gen, red_f, red_u);
+                N = gather_slots<true>(ws, W, gen, red_f, red_u);
                 release_count(ws, gen, N);
             } else {
                 N = await_count(ws, gen, word);
             }
             uint32_t unused_n = 0;
-            stream_tiles<T, MODE, HAS_KL, true, VEC, false>(a, row_lds, part, unused_n, inv_count<MODE>(N));
+            stream_tiles<T, MODE, HAS_KL, true, VEC>(a, worker, W, row_lds, part, unused_n, inv_count<MODE>(N));
             const float part_wg = block_sum(part, red_f);
-            if (threadIdx.x == 0) publish_partial(ws, gen, part_wg);
-        }
-    } else {
-        // Forward-only (any mode) and GRPO fwd+bwd: one streaming pass, no exchange.
-        if (one_tile) stream_tiles<T, MODE, HAS_KL, WRITE_GRAD, VEC, kSpeculativeLoads>(a, row_lds, part, n_lane, 1.0f);
-        else stream_tiles<T, MODE, HAS_KL, WRITE_GRAD, VEC, false>(a, row_lds, part, n_lane, 1.0f);
-        gen = share_generation(gen, word);
-        const float part_wg = block_sum(part, red_f);
-        uint32_t n_wg = 0;
-        if constexpr (kGlobalN) n_wg = block_sum(n_lane, red_u);
-        if (threadIdx.x == 0) {
-            if constexpr (kGlobalN) publish_count(ws, gen, n_wg);
-            publish_partial(ws, gen, part_wg);
-        }
-        if (kGlobalN && blockIdx.x == 0) N = gather_slots<true>(ws, gen, red_f, red_u);
-    }
-    // Workgroup 0 reads every partial, in slot order, and writes the loss.
-    if (blockIdx.x == 0) {
-        const float total = gather_slots<false>(ws, gen, red_f, red_u);
-        advance_generation(ws, gen);
-        if (threadIdx.x == 0) {
-            if constexpr (MODE == kModeGRPO) {
-                *a.loss = total;
-            } else {
-                *a.loss = final_loss<MODE>(total, N);
-                if (a.n_out) a.n_out[0] = N;
+            if (threadIdx.x == 0) publish_partial(ws, worker, gen, part_wg);
+        } else {
+            // Forward-only (any mode) and GRPO fwd+bwd: one streaming pass, no exchange.
+            stream_tiles<T, MODE, HAS_KL, WRITE_GRAD, VEC>(a, worker, W, row_lds, part, n_lane, 1.0f);
+            gen = share_generation(gen, word);
+            const float part_wg = block_sum(part, red_f);
+            uint32_t n_wg = 0;
+            if constexpr (kGlobalN) n_wg = block_sum(n_lane, red_u);
+            if (threadIdx.x == 0) {
+                if constexpr (kGlobalN) publish_count(ws, worker, gen, n_wg);
+                publish_partial(ws, worker, gen, part_wg);
             }
+            if (kGlobalN && blockIdx.x == 0) N = gather_slots<true>(ws, W, gen, red_f, red_u);
+        }
+        if (blockIdx.x == 0) {
+            const float total = gather_slots<false>(ws, W, gen, red_f, red_u);
+            advance_generation(ws, gen);
+            if (threadIdx.x == 0) write_results<MODE>(a, total, N);
         }
     }
 }
@@ -719,32 +762,35 @@ __global__ void __launch_bounds__(kThreads) loss_kernel(const Args a) {
 // ----------------------------------------------------------------------------- host-side table
 
 template <typename T, int MODE, bool HAS_KL, bool WRITE_GRAD>
-static const void* kernel_ptr(int vec) {
-    return vec == 4 ? reinterpret_cast<const void*>(&loss_kernel<T, MODE, HAS_KL, WRITE_GRAD, 4>)
-                    : reinterpret_cast<const void*>(&loss_kernel<T, MODE, HAS_KL, WRITE_GRAD, 16>);
-}
-
-template <typename T>
-static const void* pick_typed(int mode, bool has_kl, bool write_grad, int vec) {
-    switch (mode) {
-    case kModeBNPO:
-        if (has_kl) return write_grad ? kernel_ptr<T, kModeBNPO, true, true>(vec) : kernel_ptr<T, kModeBNPO, true, false>(vec);
-        return write_grad ? kernel_ptr<T, kModeBNPO, false, true>(vec) : kernel_ptr<T, kModeBNPO, false, false>(vec);
-    case kModeGRPO:
-        if (has_kl) return write_grad ? kernel_ptr<T, kModeGRPO, true, true>(vec) : kernel_ptr<T, kModeGRPO, true, false>(vec);
-        return write_grad ? kernel_ptr<T, kModeGRPO, false, true>(vec) : kernel_ptr<T, kModeGRPO, false, false>(vec);
-    case kModeRKL:
-        return write_grad ? kernel_ptr<T, kModeRKL, true, true>(vec) : kernel_ptr<T, kModeRKL, true, false>(vec);
+static const void* kernel_ptr(int shape) {
+    switch (shape) {
+    case kShapeSmall: return reinterpret_cast<const void*>(&loss_kernel<T, MODE, HAS_KL, WRITE_GRAD, kVecSmall, true>);
+    case kShapeLarge: return reinterpret_cast<const void*>(&loss_kernel<T, MODE, HAS_KL, WRITE_GRAD, kVecLarge, true>);
+    case kShapeStream: return reinterpret_cast<const void*>(&loss_kernel<T, MODE, HAS_KL, WRITE_GRAD, kVecLarge, false>);
     }
     return nullptr;
 }
 
-const void* pick_kernel(int dtype, int mode, bool has_kl, bool write_grad, int vec) {
-    if (vec != 4 && vec != 16) return nullptr;
+template <typename T>
+static const void* pick_typed(int mode, bool has_kl, bool write_grad, int shape) {
+    switch (mode) {
+    case kModeBNPO:
+        if (has_kl) return write_grad ? kernel_ptr<T, kModeBNPO, true, true>(shape) : kernel_ptr<T, kModeBNPO, true, false>(shape);
+        return write_grad ? kernel_ptr<T, kModeBNPO, false, true>(shape) : kernel_ptr<T, kModeBNPO, false, false>(shape);
+    case kModeGRPO:
+        if (has_kl) return write_grad ? kernel_ptr<T, kModeGRPO, true, true>(shape) : kernel_ptr<T, kModeGRPO, true, false>(shape);
+        return write_grad ? kernel_ptr<T, kModeGRPO, false, true>(shape) : kernel_ptr<T, kModeGRPO, false, false>(shape);
+    case kModeRKL:
+        return write_grad ? kernel_ptr<T, kModeRKL, true, true>(shape) : kernel_ptr<T, kModeRKL, true, false>(shape);
+    }
+    return nullptr;
+}
+
+const void* pick_kernel(int dtype, int mode, bool has_kl, bool write_grad, int shape) {
     switch (dtype) {
-    case kF32: return pick_typed<float>(mode, has_kl, write_grad, vec);
-    case kF16: return pick_typed<_Float16>(mode, has_kl, write_grad, vec);
-    case kBF16: return pick_typed<__bf16>(mode, has_kl, write_grad, vec);
+    case kF32: return pick_typed<float>(mode, has_kl, write_grad, shape);
+    case kF16: return pick_typed<_Float16>(mode, has_kl, write_grad, shape);
+    case kBF16: return pick_typed<__bf16>(mode, has_kl, write_grad, shape);
     }
     return nullptr;
 }

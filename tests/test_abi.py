@@ -44,7 +44,7 @@ def test_library_exports_every_declared_function(lib):
     names = declared_functions()
     assert set(names) >= {"bnpo_loss", "bnpo_loss_fwd", "grpo_loss", "grpo_loss_fwd", "reverse_kl",
                           "reverse_kl_fwd", "rlpl_workspace_bytes", "rlpl_workspace_flags",
-                          "rlpl_status_string", "rlpl_version"}
+                          "rlpl_status_string", "rlpl_version", "rlpl_launch_shape"}
     for n in names:
         assert hasattr(lib, n), n
     assert lib.rlpl_version() == 1
@@ -186,3 +186,14 @@ def test_binding_rejects_cpu_tensors():
     x = torch.zeros(2, 16)
     with pytest.raises(TypeError):
         rl.bnpo_loss(x, x, x, torch.zeros(2), torch.ones(2, 16, dtype=torch.bool), beta=0.04)
+
+
+def test_launch_shape_validation(lib):
+    g, v, t = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
+    out = (ctypes.byref(g), ctypes.byref(v), ctypes.byref(t))
+    assert rl.STATUS[lib.rlpl_launch_shape(0, 64, 2, 0, *out)] == "RLPL_ERR_SHAPE"
+    assert rl.STATUS[lib.rlpl_launch_shape(4, 64, 9, 0, *out)] == "RLPL_ERR_DTYPE"
+    assert rl.STATUS[lib.rlpl_launch_shape(4, 64, 2, 17, *out)] == "RLPL_ERR_PARAM"
+    assert rl.STATUS[lib.rlpl_launch_shape(4, 64, 2, 0, None, ctypes.byref(v), ctypes.byref(t))] == "RLPL_ERR_NULL"
+    if not torch.cuda.is_available():
+        assert rl.STATUS[lib.rlpl_launch_shape(4, 64, 2, 0, *out)] == "RLPL_ERR_DEVICE"

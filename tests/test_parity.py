@@ -15,7 +15,8 @@ import torch
 import oracle
 import rl_post_loss_amd as rl
 import synthetic
-from parity import (check_grad, check_loss, check_masked_zero, f32, kink_alternative, kink_tokens)
+from parity import (check_grad, check_loss, check_masked_zero, f32, kink_alternative, kink_tokens,
+                    policy_grad_magnitude, rkl_grad_magnitude)
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -62,7 +63,8 @@ def assert_policy_parity(op, x, beta, eps, eps_high, what, fused=True):
         kinks = kink_tokens(x["policy"], x["old"], x["mask"], eps_high)
         alt = kink_alternative(ref.grad, x["policy"], x["old"], x["advantages"], x["mask"],
                                eps_high, scale)
-        check_grad(grad, ref.grad, dt, what, alt, kinks)
+        mag = policy_grad_magnitude(x["policy"], x["old"], x["ref"], x["advantages"], f32(beta), scale)
+        check_grad(grad, ref.grad, dt, what, alt, kinks, mag)
         check_masked_zero(grad, x["mask"], what)
     return out
 
@@ -77,7 +79,8 @@ def assert_rkl_parity(x, what, fused=True):
     check_loss(float(out[0].cpu()), ref.loss, dt, what)
     assert int(out[-1].cpu()[0]) == ref.n_valid, what
     if fused:
-        check_grad(out[1], ref.grad, dt, what)
+        mag = rkl_grad_magnitude(x["student"], x["teacher"], 1.0 / max(ref.n_valid, 1))
+        check_grad(out[1], ref.grad, dt, what, mag=mag)
         check_masked_zero(out[1], x["mask"], what)
     return out
 
@@ -258,6 +261,52 @@ def test_multi_tile_grid_bnpo_and_rkl():
     assert_policy_parity("bnpo", x, 0.04, 0.2, 0.28, "multi-tile bnpo fwd", fused=False)
     w = synthetic.Workload("edge", "rkl", "bf16", "bool", 1024, 8192, 1, 8192)
     assert_rkl_parity(synthetic.inputs(w), "multi-tile rkl")
+
+
+def _shape_kind(grid, vec, tiles):
+    if tiles >= grid:
+        return "stream"
+    return "one-tile vec%d" % vec
+
+
+@pytest.mark.parametrize("op", ["bnpo", "grpo", "rkl"])
+def test_every_kernel_shape(op):
+    # The three kernel shapes (one tile per worker with the narrow or the wide
+    # lane, and the wide lane striding over several tiles per worker), each in
+    # its fused and forward-only form, reached through problem size alone.
+    kinds = set()
+    for bs, T in [(64, 4096), (1024, 4096), (1024, 8192)]:
+        grid, vec, tiles = rl.launch_shape(bs, T, torch.bfloat16, op)
+        kind = _shape_kind(grid, vec, tiles)
+        kinds.add(kind)
+        what = f"{op} {bs}x{T} {kind} grid={grid} tiles={tiles}"
+        print("[parity]", what, flush=True)
+        if op == "rkl":
+            w = synthetic.Workload("edge", "rkl", "bf16", "bool", bs, T, 1, T, seed=bs + T)
+            x = synthetic.inputs(w)
+            assert_rkl_parity(x, what)
+            assert_rkl_parity(x, what + " fwd", fused=False)
+        else:
+            x = _custom(op, "bf16", bs, T, "prefix", seed=bs + T, lo=0)
+            assert_policy_parity(op, x, 0.04, 0.2, 0.28, what)
+            assert_policy_parity(op, x, 0.04, 0.2, 0.28, what + " fwd", fused=False)
+    assert kinds == {"one-tile vec4", "one-tile vec16", "stream"}, kinds
+
+
+@pytest.mark.parametrize("bs,T", [(2048, 4096), (8192, 1024)])
+def test_grpo_striding_kernel_repeats_bitwise(bs, T):
+    # Each worker streams several tiles and rebuilds the per-row scales in LDS
+    # for every tile: the results must match the oracle and repeat bit for bit.
+    grid, vec, tiles = rl.launch_shape(bs, T, torch.bfloat16, "grpo")
+    assert tiles >= grid, (grid, tiles)
+    x = _custom("grpo", "bf16", bs, T, "prefix", seed=bs + T, lo=0)
+    what = f"grpo striding {bs}x{T} grid={grid} tiles={tiles}"
+    print("[parity]", what, flush=True)
+    first = assert_policy_parity("grpo", x, 0.04, 0.2, 0.28, what)
+    g = dev(x)
+    for _ in range(3):
+        again = gpu_policy("grpo", True, g, 0.04, 0.2, 0.28)
+        assert torch.equal(again[0], first[0]) and torch.equal(again[1], first[1]), what
 
 
 def test_grpo_rows_longer_than_a_tile():
