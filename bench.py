@@ -22,6 +22,16 @@ Options for context measurements (never the headline line's workload):
   --copy-mib M                                   a plain device copy of M MiB
                                                  (streaming ceiling; also the
                                                  reference for traffic counters)
+  --floor                                        back-to-back launches of a
+                                                 one-element fill kernel (the
+                                                 per-launch floor of the GPU)
+  --rotate-gib 0                                 two input sets only, which stay
+                                                 in the last-level cache (a
+                                                 warm-cache figure)
+
+The CPU baseline is the oracle (double precision C) over the same host-side
+batch: once on one thread, then on every host core at once (one whole batch
+per thread; ctypes releases the GIL), about 10 + 20 s of CPU work.
 
 Prints one JSON line.  --gpus above 1 is not supported.
 """
@@ -125,6 +135,48 @@ def copy_ceiling(args, torch):
     return 0
 
 
+def launch_floor(args, torch):
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    xs = [torch.empty(1, dtype=torch.float32, device=dev) for _ in range(2)]
+
+    def fn(x):
+        x.fill_(0.0)
+        return 0
+    ms_wall, ms_gpu = timed(fn, [(x,) for x in xs], args.steps, args.warmup, stream, torch)
+    print(json.dumps({"metric": "per-launch floor: one-element fill kernel, back to back",
+                      "us_per_launch": round(ms_gpu * 1e3, 3), "us_per_step_wall": round(ms_wall * 1e3, 3),
+                      "steps": args.steps}), flush=True)
+    return 0
+
+
+def cpu_threads() -> int:
+    n = os.cpu_count() or 1
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    return max(1, min(n, int(env))) if env.isdigit() else n
+
+
+def oracle_rate(run_once, seconds: float, threads: int):
+    """Batches per second of run_once() with `threads` threads each running whole batches."""
+    import threading
+    counts = [0] * threads
+    stop = time.perf_counter() + seconds
+
+    def worker(i):
+        while True:
+            run_once()
+            counts[i] += 1
+            if time.perf_counter() >= stop:
+                break
+    t0 = time.perf_counter()
+    ts = [threading.Thread(target=worker, args=(i,)) for i in range(threads)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    return sum(counts) / (time.perf_counter() - t0), sum(counts)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -139,6 +191,7 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-mib", type=float, default=None)
+    ap.add_argument("--floor", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported: this build measures one GPU only "
@@ -150,6 +203,8 @@ def main() -> int:
 
     if args.copy_mib is not None:
         return copy_ceiling(args, torch)
+    if args.floor:
+        return launch_floor(args, torch)
 
     import rl_post_loss_amd as rl
     import synthetic
@@ -233,21 +288,22 @@ def main() -> int:
         xs = {k: oracle.to_f64(v) for k, v in x.items() if k in planes or k == "advantages"}
         m8 = oracle.to_mask_u8(x["mask"])
         f32 = lambda v: float(np.float32(v))
-        runs, tc0 = 0, time.perf_counter()
-        while True:
+
+        def run_once():
             if is_rkl:
                 oracle.rkl(xs["student"], xs["teacher"], m8)
             else:
                 fo = oracle.bnpo if op.startswith("bnpo") else oracle.grpo
                 fo(xs["policy"], xs["old"], xs.get("ref"), xs["advantages"], m8, f32(w.beta),
                    f32(w.epsilon), f32(w.epsilon_high), grad=fused)
-            runs += 1
-            if time.perf_counter() - tc0 >= args.cpu_seconds:
-                break
-        tc = (time.perf_counter() - tc0) / runs
-        cpu = {"value": round(w.slots / tc, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-               "sample": f"{runs} full {w.name} batches (loss + grad, double precision, one thread), "
-                         f"{tc * 1e3:.1f} ms each"}
+        rate1, runs1 = oracle_rate(run_once, args.cpu_seconds, 1)
+        nt = cpu_threads()
+        rate_n, runs_n = oracle_rate(run_once, max(1.0, 2.0 * args.cpu_seconds / nt), nt) if nt > 1 else (rate1, runs1)
+        cpu = {"value": round(w.slots * rate_n, 1), "unit": "tokens/s", "cores": nt, "kind": "oracle",
+               "per_core_value": round(w.slots * rate1, 1),
+               "sample": f"full {w.name} batches (loss + grad, double precision): {runs_n} batches on "
+                         f"{nt} threads at once, one batch per thread; {runs1} batches on one thread, "
+                         f"{1e3 / rate1:.1f} ms each"}
 
     out = {
         "metric": METRIC,
