@@ -201,7 +201,6 @@ int policy_loss(int mode, bool write_grad, const void* policy_lp, const void* ol
     a.seq_len = int32_t(seq_len);
     a.bs = int32_t(bs);
     a.beta = beta;
-    a.lo = lo;
     a.hi = hi;
     return run(mode, write_grad, has_kl, a, dtype, stream);
 }

@@ -15,6 +15,18 @@ constexpr int kWaves = kThreads / 64;
 // per compute unit.  A tile is kThreads * VEC slots.
 constexpr int kVecLarge = 16;
 constexpr int kVecSmall = 4;
+// Tiles per worker whose mask bits the striding fwd+bwd kernels keep in LDS
+// (512 B per tile): 56 (28 KB) for BNPO and 40 (20 KB) for reverse-KL, which
+// leaves each kernel's register-bound occupancy (4 and 6 workgroups per CU)
+// within the 128 KB of LDS per CU that the host budgets.
+#ifndef RLPL_BIT_TILES_POLICY
+#define RLPL_BIT_TILES_POLICY 56
+#endif
+#ifndef RLPL_BIT_TILES_RKL
+#define RLPL_BIT_TILES_RKL 40
+#endif
+constexpr int kBitTilesPolicy = RLPL_BIT_TILES_POLICY;
+constexpr int kBitTilesRkl = RLPL_BIT_TILES_RKL;
 // Kernel shapes: one tile per worker with the narrow or the wide lane, or the
 // wide lane striding over several tiles per worker.
 enum { kShapeSmall = 0, kShapeLarge = 1, kShapeStream = 2, kShapes = 3 };
@@ -86,8 +98,7 @@ struct Args {
     uint32_t row_magic;    // s / seq_len == (s * row_magic) >> row_shift for every s < 2^31
     uint32_t row_shift;
     float beta;
-    float lo;              // 1 - epsilon
-    float hi;              // 1 + epsilon_high
+    float hi;              // 1 + epsilon_high (the lower bound 1 - epsilon never changes a result)
 };
 
 // The kernel instantiation for (dtype, mode, KL on/off, gradient on/off, VEC), or NULL.

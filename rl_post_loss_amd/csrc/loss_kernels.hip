@@ -196,6 +196,25 @@ struct Mask {
         }
         return n;
     }
+    // One bit per slot (bit k = slot k valid).  Per dword, the nonzero-byte
+    // flags (bits 7, 15, 23, 31) are shifted to bits 0, 8, 16, 24 and gathered
+    // into bits 21..24 by one multiply by 1 + 2^7 + 2^14 + 2^21 (the sixteen
+    // partial products land on distinct bits, so nothing carries).
+    __device__ __forceinline__ uint32_t bits() const {
+        uint32_t b = 0;
+#pragma unroll
+        for (int i = 0; i < VEC / 4; ++i) {
+            const uint32_t f = ((((d.w[i] & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | d.w[i]) & 0x80808080u) >> 7;
+            b |= ((f * 0x00204081u) >> 21 & 0xFu) << (4 * i);
+        }
+        return b;
+    }
+    // The inverse, with valid slots as byte 1: the same multiply spreads four
+    // bits to bits 0, 8, 16, 24 (again on distinct bits).
+    __device__ __forceinline__ void from_bits(uint32_t b) {
+#pragma unroll
+        for (int i = 0; i < VEC / 4; ++i) d.w[i] = ((b >> (4 * i)) & 0xFu) * 0x00204081u & 0x01010101u;
+    }
 };
 
 // ----------------------------------------------------------------------------- per-token math
@@ -203,26 +222,36 @@ struct Mask {
 // exp on the hardware base-2 exponential unit.
 __device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 
+// Per-row coefficients of the per-token terms: c = ac*min(ratio, hi) + bc*kl
+// and g = [ratio <= hi]*ag*ratio - bg*(exp(ref - lp) - 1), where ac = -A and
+// bc = beta, and ag, bg are the same times the gradient's scale wherever that
+// is known before the tile is computed.  GRPO's per-row scale (an LDS value)
+// multiplies c and g afterwards: folded into the coefficients it made every
+// product wait for the LDS read and cost 17 VGPRs (one fewer wave per SIMD).
+struct Coef {
+    float ac, ag, bc, bg;
+};
+
 // Per-token contribution c = per_token + beta*kl and its derivative g in lp.
+// min(ratio, clip(ratio, lo, hi)) equals min(ratio, hi) for every ratio, so the
+// lower clip bound never enters; ties at ratio == hi take the unclipped branch.
 template <int MODE, bool HAS_KL>
-__device__ __forceinline__ void token_terms(float lp, float old, float ref, float A,
-                                            float beta, float lo, float hi, float& c, float& g) {
+__device__ __forceinline__ void token_terms(float lp, float old, float ref, const Coef& k, float hi,
+                                            float& c, float& g) {
     if constexpr (MODE == kModeRKL) {
         const float x = ref - lp;                 // teacher - student
         const float em1 = fast_exp(x) - 1.0f;
         c = em1 - x;                              // exp(x) - x - 1
-        g = -em1;                                 // d/dstudent = 1 - exp(x)
+        g = em1 * k.ag;                           // ag = -scale: d/dstudent = 1 - exp(x)
     } else {
         const float ratio = fast_exp(lp - old);
-        const float clipped = __builtin_amdgcn_fmed3f(ratio, lo, hi);   // clip, lo <= hi
-        const float chosen = fminf(ratio, clipped);
-        c = -A * chosen;
-        g = (ratio <= clipped) ? -A * ratio : 0.0f;   // ties take the unclipped branch
+        c = k.ac * fminf(ratio, hi);
+        g = (ratio <= hi) ? k.ag * ratio : 0.0f;
         if constexpr (HAS_KL) {
             const float x = ref - lp;
             const float em1 = fast_exp(x) - 1.0f;
-            c = fmaf(beta, em1 - x, c);
-            g = fmaf(-beta, em1, g);
+            c = fmaf(k.bc, em1 - x, c);
+            g = fmaf(-k.bg, em1, g);
         }
     }
 }
@@ -453,47 +482,69 @@ __device__ __forceinline__ void load_planes(const Args& a, uint32_t s, Lane<T, V
 }
 
 // Per-slot terms of one lane (slots s .. s+VEC-1): returns the lane's sum of c
-// over valid slots and leaves the unscaled derivative of every slot in g (the
-// store selects masked slots to +0).  GRPO folds each row's 1/(max(n_r,1)*bs)
-// (row_scale[r - row_base], LDS) into c and g.
+// over valid slots and leaves the derivative of every slot, times gscale, in g
+// (the store selects masked slots to +0).  GRPO multiplies c and g by each
+// row's 1/(max(n_r,1)*bs) (row_scale[r - row_base], LDS).
+template <int MODE>
+__device__ __forceinline__ Coef row_coef(const Args& a, float A, float row_scale, float gscale) {
+    Coef k;
+    if constexpr (MODE == kModeRKL) {
+        k.ac = k.bc = 0.0f;
+        k.ag = -gscale;
+        k.bg = 0.0f;
+    } else if constexpr (MODE == kModeGRPO) {
+        k.ac = k.ag = -A;                 // the row scale multiplies c and g afterwards
+        k.bc = k.bg = a.beta;
+    } else {
+        k.ac = -A;
+        k.bc = a.beta;
+        k.ag = -A * gscale;
+        k.bg = a.beta * gscale;
+    }
+    return k;
+}
+
 template <typename T, int MODE, bool HAS_KL, int VEC>
 __device__ __forceinline__ float lane_terms(const Args& a, uint32_t s, const Lane<T, VEC>& L,
-                                            const float* row_scale, uint32_t row_base, float (&g)[VEC]) {
+                                            const float* row_scale, uint32_t row_base, float gscale,
+                                            float (&g)[VEC]) {
     float part = 0.0f;
     if (!L.m.any()) return part;
     const uint32_t T_len = uint32_t(a.seq_len);
     uint32_t r = row_of(a, s);
     uint32_t t = s - r * T_len;
-    float A = 0.0f, scale = 1.0f;
+    float A = 0.0f, rs = 1.0f;
     if constexpr (MODE != kModeRKL) A = load_adv<T>(a.adv, r);
-    if constexpr (MODE == kModeGRPO) scale = row_scale[r - row_base];
+    if constexpr (MODE == kModeGRPO) rs = row_scale[r - row_base];
+    Coef k = row_coef<MODE>(a, A, rs, gscale);
     if (t + VEC <= T_len) {
         // All VEC slots in one row (always, when seq_len is a multiple of VEC): branch-free.
 #pragma unroll
-        for (int k = 0; k < VEC; ++k) {
-            float c, gk;
-            token_terms<MODE, HAS_KL>(L.lp.get(k), MODE == kModeRKL ? 0.0f : L.old.get(k),
-                                      HAS_KL ? L.ref.get(k) : 0.0f, A, a.beta, a.lo, a.hi, c, gk);
-            if constexpr (MODE == kModeGRPO) { c *= scale; gk *= scale; }
-            part += L.m.valid(k) ? c : 0.0f;
-            g[k] = gk;
+        for (int i = 0; i < VEC; ++i) {
+            float c, gi;
+            token_terms<MODE, HAS_KL>(L.lp.get(i), MODE == kModeRKL ? 0.0f : L.old.get(i),
+                                      HAS_KL ? L.ref.get(i) : 0.0f, k, a.hi, c, gi);
+            if constexpr (MODE == kModeGRPO) { c *= rs; gi *= rs; }
+            part += L.m.valid(i) ? c : 0.0f;
+            g[i] = gi;
         }
     } else {
         // The lane crosses a row boundary: track the row slot by slot.
 #pragma unroll
-        for (int k = 0; k < VEC; ++k) {
-            float c, gk;
-            token_terms<MODE, HAS_KL>(L.lp.get(k), MODE == kModeRKL ? 0.0f : L.old.get(k),
-                                      HAS_KL ? L.ref.get(k) : 0.0f, A, a.beta, a.lo, a.hi, c, gk);
-            if constexpr (MODE == kModeGRPO) { c *= scale; gk *= scale; }
-            part += L.m.valid(k) ? c : 0.0f;
-            g[k] = gk;
-            if (k + 1 < VEC && ++t == T_len) {
+        for (int i = 0; i < VEC; ++i) {
+            float c, gi;
+            token_terms<MODE, HAS_KL>(L.lp.get(i), MODE == kModeRKL ? 0.0f : L.old.get(i),
+                                      HAS_KL ? L.ref.get(i) : 0.0f, k, a.hi, c, gi);
+            if constexpr (MODE == kModeGRPO) { c *= rs; gi *= rs; }
+            part += L.m.valid(i) ? c : 0.0f;
+            g[i] = gi;
+            if (i + 1 < VEC && ++t == T_len) {
                 t = 0;
                 ++r;
                 if (r < uint32_t(a.bs)) {
                     if constexpr (MODE != kModeRKL) A = load_adv<T>(a.adv, r);
-                    if constexpr (MODE == kModeGRPO) scale = row_scale[r - row_base];
+                    if constexpr (MODE == kModeGRPO) rs = row_scale[r - row_base];
+                    k = row_coef<MODE>(a, A, rs, gscale);
                 }
             }
         }
@@ -501,14 +552,17 @@ __device__ __forceinline__ float lane_terms(const Args& a, uint32_t s, const Lan
     return part;
 }
 
-template <typename T, int VEC>
+// Stores one lane's gradient, masked slots as +0; SCALE multiplies by `scale`
+// first (the one-tile fwd+bwd path, whose N arrives after the terms are formed).
+template <typename T, int VEC, bool SCALE>
 __device__ __forceinline__ void store_grad(const Args& a, uint32_t s, const Mask<VEC>& m,
                                            const float (&g)[VEC], float scale) {
     float v[VEC];
 #pragma unroll
-    for (int k = 0; k < VEC; ++k) v[k] = m.valid(k) ? g[k] * scale : 0.0f;
+    for (int k = 0; k < VEC; ++k) v[k] = m.valid(k) ? (SCALE ? g[k] * scale : g[k]) : 0.0f;
     store_values<T, VEC>(static_cast<T*>(a.grad), s, a.slots, v);
 }
+
 
 // ----------------------------------------------------------------------------- GRPO row counts
 
@@ -592,14 +646,17 @@ __device__ __forceinline__ void write_results(const Args& a, float total, uint32
 template <typename T, int MODE, bool HAS_KL, bool WRITE_GRAD, int VEC>
 __device__ __forceinline__ void stream_tiles(const Args& a, uint32_t worker, uint32_t G,
                                              uint32_t* row_lds, float& part, uint32_t& n_lane,
-                                             float scale) {
+                                             float scale, const uint16_t* bits = nullptr,
+                                             uint32_t n_bits = 0) {
     constexpr uint32_t kTileV = kThreads * VEC;
     const uint32_t lane_off = threadIdx.x * VEC;
     const uint32_t slots = uint32_t(a.slots);
     uint32_t tile = worker;
+    // The worker's first n_bits tiles take their masks from `bits` (this lane's
+    // entry of each, in LDS); later ones read the mask bytes again.
     Mask<VEC> next;
-    if (tile < a.tiles) next.load(a.mask, tile * kTileV + lane_off, slots);
-    for (; tile < a.tiles; tile += G) {
+    if (tile < a.tiles && n_bits == 0) next.load(a.mask, tile * kTileV + lane_off, slots);
+    for (uint32_t j = 0; tile < a.tiles; tile += G, ++j) {
         const uint32_t s = tile * kTileV + lane_off;
         uint32_t row_base = 0;
         if constexpr (MODE == kModeGRPO) {
@@ -607,14 +664,15 @@ __device__ __forceinline__ void stream_tiles(const Args& a, uint32_t worker, uin
             grpo_row_scales(a, s0, s0 + kTileV < slots ? s0 + kTileV : slots, row_lds, row_base);
         }
         Lane<T, VEC> L;
-        L.m = next;
-        if (tile + G < a.tiles) next.load(a.mask, (tile + G) * kTileV + lane_off, slots);
+        if (j < n_bits) L.m.from_bits(bits[j * kThreads + threadIdx.x]);
+        else L.m = next;
+        if (tile + G < a.tiles && j + 1 >= n_bits) next.load(a.mask, (tile + G) * kTileV + lane_off, slots);
         load_planes<T, MODE, HAS_KL, VEC>(a, s, L);
         n_lane += L.m.count();
         float g[VEC];
         part += lane_terms<T, MODE, HAS_KL, VEC>(a, s, L, reinterpret_cast<const float*>(row_lds),
-                                                 row_base, g);
-        if constexpr (WRITE_GRAD) store_grad<T, VEC>(a, s, L.m, g, scale);
+                                                 row_base, scale, g);
+        if constexpr (WRITE_GRAD) store_grad<T, VEC, false>(a, s, L.m, g, 1.0f);
     }
 }
 
@@ -634,6 +692,12 @@ __global__ void __launch_bounds__(kThreads) loss_kernel(const Args a) {
     // GRPO: per-row counts, then per-row scales, of the rows a tile touches.
     constexpr int kRowLds = (MODE == kModeGRPO) ? int(kTileV) + 2 : 1;
     __shared__ uint32_t row_lds[kRowLds];
+    // Striding fwd+bwd BNPO / reverse-KL: the counting pass keeps each lane's
+    // mask bits of the worker's first kBitTiles tiles, so that the streaming
+    // pass does not read those mask bytes again.
+    constexpr bool kKeepBits = !ONE_TILE && MODE != kModeGRPO && WRITE_GRAD;
+    constexpr int kBitTiles = kKeepBits ? (MODE == kModeRKL ? kBitTilesRkl : kBitTilesPolicy) : 1;
+    __shared__ uint16_t mask_bits[kBitTiles * kThreads];
 
     Workspace* ws = a.ws;
     // The launch generation tags everything this launch publishes; thread 0 reads it
@@ -674,11 +738,11 @@ __global__ void __launch_bounds__(kThreads) loss_kernel(const Args a) {
             gen = share_generation(gen, word);
             if (threadIdx.x == 0) publish_count(ws, worker, gen, n_wg);
             float g[VEC];
-            part = lane_terms<T, MODE, HAS_KL, VEC>(a, s, L, nullptr, 0, g);
+            part = lane_terms<T, MODE, HAS_KL, VEC>(a, s, L, nullptr, 0, 1.0f, g);
             const float part_wg = block_sum(part, red_f);
             if (threadIdx.x == 0) publish_partial(ws, worker, gen, part_wg);
             const uint32_t N = await_count(ws, gen, word);
-            store_grad<T, VEC>(a, s, L.m, g, inv_count<MODE>(N));
+            store_grad<T, VEC, true>(a, s, L.m, g, inv_count<MODE>(N));
         } else {
             // Forward-only (any mode) and GRPO fwd+bwd.  GRPO first scans the masks of
             // the rows the tile touches (measured faster than overlapping the scan with
@@ -691,8 +755,8 @@ __global__ void __launch_bounds__(kThreads) loss_kernel(const Args a) {
             n_lane = load_lane_count<T, MODE, HAS_KL, VEC>(a, s, L);
             float g[VEC];
             part = lane_terms<T, MODE, HAS_KL, VEC>(a, s, L, reinterpret_cast<const float*>(row_lds),
-                                                    row_base, g);
-            if constexpr (WRITE_GRAD) store_grad<T, VEC>(a, s, L.m, g, 1.0f);
+                                                    row_base, 1.0f, g);
+            if constexpr (WRITE_GRAD) store_grad<T, VEC, false>(a, s, L.m, g, 1.0f);
             gen = share_generation(gen, word);
             const float part_wg = block_sum(part, red_f);
             uint32_t n_wg = 0;
@@ -710,21 +774,29 @@ __global__ void __launch_bounds__(kThreads) loss_kernel(const Args a) {
         const uint32_t worker = blockIdx.x;
         uint32_t N = 0;
         if constexpr (kExchange) {
-            // Count every owned mask (eight loads in flight per lane), exchange, then stream.
+            // Count every owned mask (eight loads in flight per lane) and keep the
+            // bits of the first kBitTiles tiles, exchange, then stream.
             const uint32_t lane_off = threadIdx.x * VEC;
-            uint32_t tile = worker;
-            for (; tile + 7 * W < a.tiles; tile += 8 * W) {
+            uint32_t tile = worker, j = 0;
+            for (; tile + 7 * W < a.tiles; tile += 8 * W, j += 8) {
                 Mask<VEC> m[8];
 #pragma unroll
                 for (int u = 0; u < 8; ++u) m[u].load(a.mask, (tile + u * W) * kTileV + lane_off, slots);
 #pragma unroll
-                for (int u = 0; u < 8; ++u) n_lane += m[u].count();
+                for (int u = 0; u < 8; ++u) {
+                    const uint32_t b = m[u].bits();
+                    n_lane += __builtin_popcount(b);
+                    if (j + u < uint32_t(kBitTiles)) mask_bits[(j + u) * kThreads + threadIdx.x] = uint16_t(b);
+                }
             }
-            for (; tile < a.tiles; tile += W) {
+            for (; tile < a.tiles; tile += W, ++j) {
                 Mask<VEC> m;
                 m.load(a.mask, tile * kTileV + lane_off, slots);
-                n_lane += m.count();
+                const uint32_t b = m.bits();
+                n_lane += __builtin_popcount(b);
+                if (j < uint32_t(kBitTiles)) mask_bits[j * kThreads + threadIdx.x] = uint16_t(b);
             }
+            const uint32_t n_bits = j < uint32_t(kBitTiles) ? j : uint32_t(kBitTiles);
             gen = share_generation(gen, word);
             const uint32_t n_wg = block_sum(n_lane, red_u);
             if (threadIdx.x == 0) publish_count(ws, worker, gen, n_wg);
@@ -735,7 +807,8 @@ __global__ void __launch_bounds__(kThreads) loss_kernel(const Args a) {
                 N = await_count(ws, gen, word);
             }
             uint32_t unused_n = 0;
-            stream_tiles<T, MODE, HAS_KL, true, VEC>(a, worker, W, row_lds, part, unused_n, inv_count<MODE>(N));
+            stream_tiles<T, MODE, HAS_KL, true, VEC>(a, worker, W, row_lds, part, unused_n, inv_count<MODE>(N),
+                                                     mask_bits, n_bits);
             const float part_wg = block_sum(part, red_f);
             if (threadIdx.x == 0) publish_partial(ws, worker, gen, part_wg);
         } else {
