@@ -52,7 +52,8 @@ def _load():
     lib.rlpl_oracle_bnpo.argtypes = [i64, i64, dp, dp, dp, dp, u8p, d, d, d, dp, dp, i64p]
     lib.rlpl_oracle_grpo.argtypes = [i64, i64, dp, dp, dp, dp, u8p, d, d, d, dp, dp, i64p]
     lib.rlpl_oracle_rkl.argtypes = [i64, i64, dp, dp, u8p, dp, dp, i64p]
-    for f in (lib.rlpl_oracle_bnpo, lib.rlpl_oracle_grpo, lib.rlpl_oracle_rkl):
+    lib.rlpl_oracle_rkl_logits.argtypes = [i64, i64, dp, dp, u8p, dp, dp, i64p, dp]
+    for f in (lib.rlpl_oracle_bnpo, lib.rlpl_oracle_grpo, lib.rlpl_oracle_rkl, lib.rlpl_oracle_rkl_logits):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -142,3 +143,33 @@ def rkl(student, teacher, mask, grad=True) -> Result:
     if rc != 0:
         raise ValueError("oracle rejected its arguments")
     return Result(loss.value, g, int(n[0]))
+
+
+@dataclass
+class VocabResult:
+    loss: float
+    grad: Optional[np.ndarray]      # float64, shape of the logits, or None
+    n_valid: int
+    kl_rows: np.ndarray             # float64 (rows,): kl of each valid row, 0 for masked rows
+
+
+def rkl_logits(student, teacher, mask, grad=True) -> VocabResult:
+    """Full-vocab reverse KL between the softmaxes of two (*, V) logit slabs, the
+    unclamped mean over valid rows, and d loss / d student logits."""
+    s, t = to_f64(student), to_f64(teacher)
+    shape = s.shape
+    V = shape[-1]
+    s2, t2 = s.reshape(-1, V), t.reshape(-1, V)
+    rows = s2.shape[0]
+    m = to_mask_u8(mask).reshape(rows)
+    loss = ctypes.c_double(0.0)
+    g = np.empty((rows, V), dtype=np.float64) if grad else None
+    n = np.zeros(1, dtype=np.int64)
+    kl = np.zeros(rows, dtype=np.float64)
+    rc = _load().rlpl_oracle_rkl_logits(rows, V, _p(s2, ctypes.c_double), _p(t2, ctypes.c_double),
+                                        _p(m, ctypes.c_uint8), ctypes.byref(loss),
+                                        _p(g, ctypes.c_double), _p(n, ctypes.c_int64),
+                                        _p(kl, ctypes.c_double))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    return VocabResult(loss.value, None if g is None else g.reshape(shape), int(n[0]), kl)

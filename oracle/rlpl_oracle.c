@@ -17,7 +17,11 @@
  *     global token-mean  loss = sum((per_token + beta*kl)*mask) / max(sum(mask), 1);
  *   - section "GRPO Loss": per-response normalisation
  *     loss = mean_r( sum_t((per_token + beta*kl)*mask) / max(sum_t(mask), 1) );
- *   - section "Reverse KL": global token mean with an unclamped 1/sum(mask).
+ *   - section "Reverse KL": KL(student || teacher) between the softmaxes of two
+ *     (rows, vocab) logit slabs, kl_row = sum_v p_v (log p_v - log q_v),
+ *     loss = (mask * kl_row).sum() / mask.sum() (unclamped), and the analytic
+ *     gradient p_v (log p_v - log q_v - kl_row) * mask[r] / mask.sum(); the
+ *     same normalisation for the per-token estimator below.
  *
  * Readings of points the card leaves open (each is also listed with its
  * reason in the design notes):
@@ -38,7 +42,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#define RLPL_ORACLE_VERSION 1
+#define RLPL_ORACLE_VERSION 2
 
 int rlpl_oracle_version(void) { return RLPL_ORACLE_VERSION; }
 
@@ -190,5 +194,63 @@ int rlpl_oracle_rkl(int64_t bs, int64_t seq_len, const double *student, const do
             k3_kl(student[i], teacher[i], &slope);
             grad[i] = slope / (double)n;
         }
+    return 0;
+}
+
+/* log(sum_v exp(x_v)) of one row, as max + log(sum exp(x_v - max)): the same
+ * number, written so that no exp overflows. */
+static double log_sum_exp(const double *x, int64_t n)
+{
+    double m = x[0];
+    for (int64_t v = 1; v < n; ++v)
+        if (x[v] > m) m = x[v];
+    double z = 0.0;
+    for (int64_t v = 0; v < n; ++v) z += exp(x[v] - m);
+    return m + log(z);
+}
+
+/*
+ * Reverse KL over full logit rows ("Reverse KL"): for each row r of the
+ * (rows, vocab) slabs, p = softmax(student[r]), q = softmax(teacher[r]),
+ * kl_r = sum_v p_v (log p_v - log q_v).  N = number of rows with a nonzero
+ * mask byte; loss = sum_r mask_r kl_r / N, not clamped (0/0 = NaN when every
+ * row is masked).  grad (rows*vocab, optional) = p_v (log p_v - log q_v - kl_r)
+ * / N on valid rows and +0 on masked rows, whose logits are never read.
+ * kl_rows (rows, optional) receives kl_r for valid rows and 0 for masked rows.
+ */
+int rlpl_oracle_rkl_logits(int64_t rows, int64_t vocab, const double *student,
+                           const double *teacher, const uint8_t *mask, double *loss,
+                           double *grad, int64_t *n_valid, double *kl_rows)
+{
+    if (rows < 0 || vocab < 1 || !student || !teacher || !mask || !loss || !n_valid) return -1;
+    int64_t n = 0;
+    for (int64_t r = 0; r < rows; ++r)
+        if (mask[r] != 0) ++n;
+    double sum = 0.0;
+    for (int64_t r = 0; r < rows; ++r) {
+        const double *s = student + r * vocab, *t = teacher + r * vocab;
+        double *g = grad ? grad + r * vocab : NULL;
+        if (mask[r] == 0) {
+            if (g)
+                for (int64_t v = 0; v < vocab; ++v) g[v] = 0.0;
+            if (kl_rows) kl_rows[r] = 0.0;
+            continue;
+        }
+        const double lse_s = log_sum_exp(s, vocab), lse_t = log_sum_exp(t, vocab);
+        double kl = 0.0;
+        for (int64_t v = 0; v < vocab; ++v) {
+            const double log_p = s[v] - lse_s, log_q = t[v] - lse_t;
+            kl += exp(log_p) * (log_p - log_q);
+        }
+        sum += kl;
+        if (kl_rows) kl_rows[r] = kl;
+        if (g)
+            for (int64_t v = 0; v < vocab; ++v) {
+                const double log_p = s[v] - lse_s, log_q = t[v] - lse_t;
+                g[v] = exp(log_p) * (log_p - log_q - kl) / (double)n;
+            }
+    }
+    *loss = sum / (double)n;   /* not clamped: 0/0 is NaN when no row is valid */
+    *n_valid = n;
     return 0;
 }

@@ -12,6 +12,7 @@ import pytest
 
 import oracle
 import test_oracle
+import test_oracle_vocab
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "rlpl_oracle.c")
 
@@ -33,12 +34,27 @@ MUTANTS = {
     "grpo grad misses 1/bs": ("grad[i] = slope / (denom * (double)bs);", "grad[i] = slope / denom;"),
     "grpo mean over valid rows": None,   # built by hand below
     "rkl grad not normalised": ("grad[i] = slope / (double)n;", "grad[i] = slope;"),
+    "vocab forward KL instead of reverse": ("kl += exp(log_p) * (log_p - log_q);",
+                                            "kl += exp(log_q) * (log_q - log_p);"),
+    "vocab grad misses -kl_row": ("g[v] = exp(log_p) * (log_p - log_q - kl) / (double)n;",
+                                  "g[v] = exp(log_p) * (log_p - log_q) / (double)n;"),
+    "vocab grad weighted by q": ("g[v] = exp(log_p) * (log_p - log_q - kl) / (double)n;",
+                                 "g[v] = exp(log_q) * (log_p - log_q - kl) / (double)n;"),
+    "vocab grad sign": ("g[v] = exp(log_p) * (log_p - log_q - kl) / (double)n;",
+                        "g[v] = exp(log_p) * (log_q - log_p + kl) / (double)n;"),
+    "vocab mean over all rows": ("*loss = sum / (double)n;   /* not clamped: 0/0 is NaN when no row is valid */",
+                                 "*loss = sum / (double)rows;"),
+    "vocab counts masked rows": ("        if (mask[r] != 0) ++n;\n", "        ++n;\n"),
+    "vocab teacher normaliser from student": ("lse_t = log_sum_exp(t, vocab);", "lse_t = log_sum_exp(s, vocab);"),
+    "vocab log-sum-exp drops the max": ("    return m + log(z);", "    return log(z);"),
+    "vocab grad row offset": ("double *g = grad ? grad + r * vocab : NULL;", "double *g = grad ? grad + r : NULL;"),
     "rkl reads masked tokens": ("        if (mask[i] == 0) continue;\n        ++n;\n        sum += k3_kl(", "        if (mask[i] == 0) { sum += 0.0 * student[i]; continue; }\n        ++n;\n        sum += k3_kl("),
 }
 
 
 def _pins():
-    return [(name, fn) for name, fn in inspect.getmembers(test_oracle, inspect.isfunction)
+    return [(name, fn) for mod in (test_oracle, test_oracle_vocab)
+            for name, fn in inspect.getmembers(mod, inspect.isfunction)
             if name.startswith("test_") and "generator" not in name]
 
 
