@@ -22,6 +22,11 @@ Options for context measurements (never the headline line's workload):
   --copy-mib M                                   a plain device copy of M MiB
                                                  (streaming ceiling; also the
                                                  reference for traffic counters)
+  --op rkl_logits|rkl_logits_fwd [--rows R --vocab V]
+                                                 full-vocab reverse KL over
+                                                 (R, V) logit slabs (default the
+                                                 card's example, 1024 x 248320
+                                                 bf16, rows valid with p = 0.8)
   --floor                                        back-to-back launches of a
                                                  one-element fill kernel (the
                                                  per-launch floor of the GPU)
@@ -177,13 +182,78 @@ def oracle_rate(run_once, seconds: float, threads: int):
     return sum(counts) / (time.perf_counter() - t0), sum(counts)
 
 
+def vocab_bench(args, torch):
+    """Full-vocab reverse KL: logits drawn on the device, rotating sets >= 1 GiB."""
+    import rl_post_loss_amd as rl
+    import synthetic
+    rows, V = args.rows or 1024, args.vocab or 248320
+    dtype = "bf16"
+    fused = args.op == "rkl_logits"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream
+    lib = rl.library()
+    x = synthetic.device_vocab_inputs(rows, V, dtype, "bool", 0, "cuda:0")
+    valid = int(torch.count_nonzero(x["mask"]))
+    elem = 2
+    set_bytes = 2 * rows * V * elem + (rows * V * elem if fused else 0)
+    nsets = max(1, math.ceil(args.rotate_gib * (1 << 30) / set_bytes))
+    nsets = max(nsets, 2) if set_bytes < (1 << 30) else nsets
+    ws = rl.workspace_for(dev, sptr, "rkl_logits")
+    fn = lib.reverse_kl_logits if fused else lib.reverse_kl_logits_fwd
+    sets, calls = [], []
+    for i in range(nsets):
+        st = x if i == 0 else {k: v.clone() for k, v in x.items()}
+        st = dict(st)
+        st["grad"] = torch.empty(rows, V, dtype=torch.bfloat16, device=dev) if fused else None
+        st["loss"] = torch.empty((), dtype=torch.float32, device=dev)
+        st["n"] = torch.empty(1, dtype=torch.int32, device=dev)
+        sets.append(st)
+        a = [st["student"].data_ptr(), st["teacher"].data_ptr(), st["mask"].data_ptr(), rows, V,
+             rl.DTYPE[torch.bfloat16], rl.MASK_DTYPE[torch.bool], st["loss"].data_ptr()]
+        if fused:
+            a.append(st["grad"].data_ptr())
+        calls.append(tuple(a + [st["n"].data_ptr(), ws.data_ptr(), ws.numel(), sptr]))
+    torch.cuda.synchronize()
+    ms_per_step, ms_gpu = timed(fn, calls, args.steps, args.warmup, stream, torch)
+    n0 = int(sets[(args.warmup + args.steps - 1) % nsets]["n"][0].cpu())
+    if n0 != valid:
+        raise RuntimeError(f"valid rows {n0} != {valid}")
+    # The method must read each valid row's two logit planes once and (fwd+bwd)
+    # write every gradient element; the mask and the loss are negligible.
+    alg = 2 * valid * V * elem + rows + 4 + (rows * V * elem if fused else 0)
+    moved = alg + (2 * valid * V * elem if fused else 0)      # what these kernels read: twice when fused
+    achieved = alg / (ms_gpu * 1e-3) / 1e9
+    grid, vec, _ = rl.launch_shape(rows, V, torch.bfloat16, args.op)
+    print(json.dumps({
+        "metric": "full-vocab reverse KL: logit elements/s and achieved HBM GB/s (% of peak)",
+        "value": round(rows * V / (ms_per_step * 1e-3), 1), "unit": "logits/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
+        "config": {"workload": f"rkl_logits_{dtype}_{rows}x{V}", "op": "fwd+bwd" if fused else "fwd-only",
+                   "rows": rows, "vocab": V, "valid_rows": valid, "mask": "bool, U(0,1) > 0.2",
+                   "inputs": "device-generated, independent N(0,1) logits", "rotating_sets": nsets,
+                   "grid": grid, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 5), "traffic": None},
+        "kernel_us_per_launch": round(ms_gpu * 1e3, 3), "algorithmic_bytes_per_launch": alg,
+        "bytes_read_and_written_by_design": moved,
+        "design_GBs": round(moved / (ms_gpu * 1e-3) / 1e9, 2),
+        "context_only": True}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="bnpo_bf16_64x4096")
-    ap.add_argument("--op", default=None, choices=["bnpo", "bnpo_fwd", "grpo", "grpo_fwd", "rkl", "rkl_fwd"])
+    ap.add_argument("--op", default=None, choices=["bnpo", "bnpo_fwd", "grpo", "grpo_fwd", "rkl", "rkl_fwd",
+                                                   "rkl_logits", "rkl_logits_fwd"])
+    ap.add_argument("--rows", type=int, default=None)
+    ap.add_argument("--vocab", type=int, default=None)
     ap.add_argument("--bs", type=int, default=None)
     ap.add_argument("--seq-len", type=int, default=None)
     ap.add_argument("--beta", type=float, default=None)
@@ -205,6 +275,8 @@ def main() -> int:
         return copy_ceiling(args, torch)
     if args.floor:
         return launch_floor(args, torch)
+    if args.op in ("rkl_logits", "rkl_logits_fwd"):
+        return vocab_bench(args, torch)
 
     import rl_post_loss_amd as rl
     import synthetic

@@ -61,16 +61,17 @@ typedef struct ihipStream_t* hipStream_t;
 enum rlpl_dtype { RLPL_F32 = 0, RLPL_F16 = 1, RLPL_BF16 = 2 };
 enum rlpl_mask_dtype { RLPL_MASK_BOOL = 0, RLPL_MASK_INT8 = 1 };
 
-/* Operation selector for rlpl_workspace_bytes. */
+/* Operation selector for rlpl_workspace_bytes and rlpl_launch_shape. */
 enum rlpl_op {
     RLPL_OP_BNPO = 0, RLPL_OP_BNPO_FWD = 1, RLPL_OP_GRPO = 2, RLPL_OP_GRPO_FWD = 3,
-    RLPL_OP_RKL = 4, RLPL_OP_RKL_FWD = 5
+    RLPL_OP_RKL = 4, RLPL_OP_RKL_FWD = 5, RLPL_OP_RKL_LOGITS = 6, RLPL_OP_RKL_LOGITS_FWD = 7
 };
 
 enum rlpl_status {
     RLPL_OK = 0,
     RLPL_ERR_NULL = 1,       /* a required pointer is NULL                                 */
-    RLPL_ERR_SHAPE = 2,      /* bs < 1, seq_len < 1, or bs*seq_len >= 2^31                  */
+    RLPL_ERR_SHAPE = 2,      /* bs < 1, seq_len < 1, or bs*seq_len >= 2^31 (for the logit    */
+                             /* slabs: rows < 1, vocab < 1, rows >= 2^31 or rows*vocab > 2^62)*/
     RLPL_ERR_ALIGN = 3,      /* a plane, mask or grad pointer is not 16-byte aligned, or     */
                              /* advantages / loss / counts / workspace misaligned            */
     RLPL_ERR_DTYPE = 4,      /* unknown dtype or mask_dtype                                  */
@@ -165,6 +166,44 @@ int reverse_kl_fwd(const void* student_lp, const void* teacher_lp, const void* m
                    float* loss_out, uint32_t* n_valid_out,
                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Reverse KL over full logit rows, fused forward + backward (model card,
+ * "Reverse KL"): for each row r of the (rows, vocab) slabs,
+ *
+ *   p = softmax(student_logits[r]),  q = softmax(teacher_logits[r])
+ *   kl_r = sum_v p_v (log p_v - log q_v)
+ *   loss = sum_r mask[r] kl_r / N,  N = number of rows with a nonzero mask byte
+ *   grad_out[r][v] = mask[r] ? p_v (log p_v - log q_v - kl_r) / N : +0
+ *
+ * N is not clamped (as on the card): with no valid row the loss is NaN and
+ * the gradient all +0; that is not an error.  Rows whose mask byte is zero are
+ * never read.  The fused kernel reads a valid row twice (softmax sums, then
+ * the gradient), reverse_kl_logits_fwd once.  With fewer rows than the device
+ * holds workgroups, a row is split among several workgroups that exchange
+ * their softmax sums through the workspace.
+ *
+ * student_logits, teacher_logits : (rows, vocab) `dtype`, dense row-major,
+ *                                  16-byte aligned (rows themselves need not
+ *                                  start on a 16-byte boundary); finite
+ * mask        : (rows,) bytes (the card's completions_mask over the leading
+ *               dims of the logits, flattened), 16-byte aligned
+ * loss_out    : 1 float (written)
+ * grad_out    : (rows, vocab) `dtype`, 16-byte aligned (written, every element)
+ * n_valid_out : 1 uint32 = N (written), or NULL
+ * workspace   : as for bnpo_loss
+ */
+int reverse_kl_logits(const void* student_logits, const void* teacher_logits, const void* mask,
+                      int64_t rows, int64_t vocab, int dtype, int mask_dtype,
+                      float* loss_out, void* grad_out, uint32_t* n_valid_out,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Reverse KL over full logit rows, forward only: the same loss as
+ * reverse_kl_logits (bit-identical), one read of each valid row, no gradient. */
+int reverse_kl_logits_fwd(const void* student_logits, const void* teacher_logits, const void* mask,
+                          int64_t rows, int64_t vocab, int dtype, int mask_dtype,
+                          float* loss_out, uint32_t* n_valid_out,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Bytes of workspace an `op` call on a (bs, seq_len) problem needs (0 for a bad op). */
 size_t rlpl_workspace_bytes(int64_t bs, int64_t seq_len, int op);
 
@@ -172,7 +211,8 @@ size_t rlpl_workspace_bytes(int64_t bs, int64_t seq_len, int op);
  * on the current device (host pointers, written): workgroups in the grid (one
  * coordinator plus one worker per tile when tiles < grid; else every
  * workgroup strides over the tiles), consecutive slots per lane (4 or 16) and
- * tiles of 256 lanes.  For
+ * tiles of 256 lanes.  For the logit-slab ops, bs and seq_len are rows and
+ * vocab, tiles are rows, and the lane width is elements per 32-byte step.  For
  * profiling and tests; enqueues nothing.  Returns RLPL_OK, or an rlpl_status
  * for bad arguments or no usable device. */
 int rlpl_launch_shape(int64_t bs, int64_t seq_len, int dtype, int op, int* grid_out, int* vec_out,

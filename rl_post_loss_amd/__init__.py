@@ -15,6 +15,9 @@ Entry points (model card "Geometric-AI Kernels": sections "BNPO Loss",
 * ``bnpo_loss_fwd(...)`` -> loss
 * ``grpo_loss(...)`` -> (loss, grad);  ``grpo_loss_fwd(...)`` -> loss
 * ``reverse_kl(student_lp, teacher_lp, mask)`` -> (loss, grad);  ``reverse_kl_fwd(...)`` -> loss
+  (per-token log-probs, the card's per-token KL estimator)
+* ``reverse_kl_logits(student_logits, teacher_logits, mask)`` -> (loss, grad);
+  ``reverse_kl_logits_fwd(...)`` -> loss  (full (*, V) logit rows, the card's softmax form)
 
 ``loss`` is a 0-d float32 tensor on the device; ``grad`` has the dtype and
 shape of the policy/student log-probs.  Pass ``return_n_valid=True`` to also
@@ -35,14 +38,15 @@ from . import build as _build
 
 __all__ = ["bnpo_loss", "bnpo_loss_fwd", "grpo_loss", "grpo_loss_fwd", "reverse_kl",
            "reverse_kl_fwd", "library", "library_path", "RlplError", "STATUS", "workspace_for",
-           "launch_shape"]
+           "launch_shape", "reverse_kl_logits", "reverse_kl_logits_fwd"]
 
 STATUS = {0: "RLPL_OK", 1: "RLPL_ERR_NULL", 2: "RLPL_ERR_SHAPE", 3: "RLPL_ERR_ALIGN",
           4: "RLPL_ERR_DTYPE", 5: "RLPL_ERR_PARAM", 6: "RLPL_ERR_WORKSPACE", 7: "RLPL_ERR_DEVICE",
           8: "RLPL_ERR_LAUNCH"}
 DTYPE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 MASK_DTYPE = {torch.bool: 0, torch.int8: 1, torch.uint8: 1}
-OP = {"bnpo": 0, "bnpo_fwd": 1, "grpo": 2, "grpo_fwd": 3, "rkl": 4, "rkl_fwd": 5}
+OP = {"bnpo": 0, "bnpo_fwd": 1, "grpo": 2, "grpo_fwd": 3, "rkl": 4, "rkl_fwd": 5, "rkl_logits": 6,
+      "rkl_logits_fwd": 7}
 
 
 class RlplError(RuntimeError):
@@ -70,6 +74,9 @@ def _declare(lib):
     rkl_fwd = [vp, vp, vp, i64, i64, i32, i32, vp, vp, vp, sz, vp]
     for name, args in (("bnpo_loss", policy), ("grpo_loss", policy), ("bnpo_loss_fwd", policy_fwd),
                        ("grpo_loss_fwd", policy_fwd), ("reverse_kl", rkl), ("reverse_kl_fwd", rkl_fwd)):
+        f = getattr(lib, name)
+        f.argtypes, f.restype = args, ctypes.c_int
+    for name, args in (("reverse_kl_logits", rkl), ("reverse_kl_logits_fwd", rkl_fwd)):
         f = getattr(lib, name)
         f.argtypes, f.restype = args, ctypes.c_int
     lib.rlpl_workspace_bytes.argtypes, lib.rlpl_workspace_bytes.restype = [i64, i64, i32], sz
@@ -252,3 +259,49 @@ def reverse_kl_fwd(student_logprobs, teacher_logprobs, completions_mask, *, retu
                    workspace=None):
     """Per-token reverse KL, forward only: the scalar loss."""
     return _rkl(False, student_logprobs, teacher_logprobs, completions_mask, return_n_valid, workspace)
+
+
+def _rkl_logits(fused: bool, student_logits, teacher_logits, completions_mask, return_n_valid, workspace):
+    s = student_logits.detach()
+    if not isinstance(s, torch.Tensor) or not s.is_cuda or s.dtype not in DTYPE or s.dim() < 1:
+        raise TypeError("student_logits must be a float32, float16 or bfloat16 CUDA (HIP) tensor")
+    t = teacher_logits.detach()
+    if not isinstance(t, torch.Tensor) or t.shape != s.shape or t.dtype != s.dtype or t.device != s.device:
+        raise ValueError("teacher_logits must match student_logits in shape, dtype and device")
+    m = completions_mask.detach()
+    if m.dtype not in MASK_DTYPE or tuple(m.shape) != tuple(s.shape[:-1]) or m.device != s.device:
+        raise ValueError(f"completions_mask must be a bool/int8 tensor of shape {tuple(s.shape[:-1])}")
+    V = s.shape[-1]
+    rows = s.numel() // V if V else 0
+    s2, t2 = _aligned(s.reshape(rows, V)), _aligned(t.reshape(rows, V))
+    m2 = _aligned(m.reshape(rows))
+    dev = s.device
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    ws = _workspace(dev, stream, "rkl_logits", workspace)
+    loss = torch.empty((), dtype=torch.float32, device=dev)
+    grad = torch.empty_like(s2) if fused else None
+    n = torch.empty(1, dtype=torch.int32, device=dev) if return_n_valid else None
+    args = [s2.data_ptr(), t2.data_ptr(), m2.data_ptr(), rows, V, DTYPE[s.dtype], MASK_DTYPE[m2.dtype],
+            loss.data_ptr()]
+    if fused:
+        args.append(grad.data_ptr())
+    args += [None if n is None else n.data_ptr(), ws.data_ptr(), ws.numel(), stream]
+    name = "reverse_kl_logits" if fused else "reverse_kl_logits_fwd"
+    _check(name, getattr(library(), name)(*args))
+    out = (loss, grad.reshape(s.shape)) if fused else (loss,)
+    if return_n_valid:
+        out = out + (n,)
+    return out if len(out) > 1 else out[0]
+
+
+def reverse_kl_logits(student_logits, teacher_logits, completions_mask, *, return_n_valid=False,
+                      workspace=None):
+    """Reverse KL(student || teacher) over full (*, V) logit rows, fused forward+backward:
+    (loss, d loss / d student_logits) from one launch."""
+    return _rkl_logits(True, student_logits, teacher_logits, completions_mask, return_n_valid, workspace)
+
+
+def reverse_kl_logits_fwd(student_logits, teacher_logits, completions_mask, *, return_n_valid=False,
+                          workspace=None):
+    """Reverse KL over full logit rows, forward only: the scalar loss (one read of each valid row)."""
+    return _rkl_logits(False, student_logits, teacher_logits, completions_mask, return_n_valid, workspace)

@@ -15,6 +15,7 @@
 #include "loss_kernels.h"
 #include "rl_post_loss.h"
 #include "row_divisor.h"
+#include "vocab_kernels.h"
 
 namespace {
 
@@ -32,7 +33,25 @@ struct DeviceInfo {
     int status = RLPL_ERR_DEVICE;
     int cus = 0;
     int grid_cap[3][3][rlpl::kShapes] = {};  // [dtype][mode][kernel shape]: co-resident workgroups
+    int vocab_cap[3] = {};                   // [dtype]: co-resident workgroups of the full-vocab kernels
 };
+
+// Co-resident workgroups of `kernel` per CU: the occupancy query, limited so
+// that the workgroups' LDS stays within kLdsPerCu (all of a CU's 160 KB is
+// not always usable: five workgroups of 32 KB are not co-resident on gfx950).
+// 0 when the query fails.
+int blocks_per_cu(const void* kernel) {
+    int nb = 0;
+    hipFuncAttributes attr;
+    if (!kernel || hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, rlpl::kThreads, 0) != hipSuccess ||
+        nb < 1 || hipFuncGetAttributes(&attr, kernel) != hipSuccess)
+        return 0;
+    if (attr.sharedSizeBytes > 0) {
+        const int by_lds = int(kLdsPerCu / attr.sharedSizeBytes);
+        if (by_lds < nb) nb = by_lds;
+    }
+    return nb;
+}
 DeviceInfo g_info[kMaxDevices];
 std::once_flag g_once[kMaxDevices];
 
@@ -54,20 +73,8 @@ void init_device(int dev, DeviceInfo& info) {
                 int occ = 1 << 30;
                 for (int kl = 0; kl < 2; ++kl)
                     for (int wg = 0; wg < 2; ++wg) {
-                        const void* k = rlpl::pick_kernel(dt, mode, kl != 0 || mode == kModeRKL, wg != 0, shape);
-                        int nb = 0;
-                        hipFuncAttributes attr;
-                        if (!k || hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k, rlpl::kThreads, 0) !=
-                                      hipSuccess || nb < 1 ||
-                            hipFuncGetAttributes(&attr, k) != hipSuccess)
-                            return;
-                        // Keep the workgroups' LDS within kLdsPerCu: all of a CU's
-                        // 160 KB is not always usable (five workgroups of 32 KB are
-                        // not co-resident on gfx950).
-                        if (attr.sharedSizeBytes > 0) {
-                            const int by_lds = int(kLdsPerCu / attr.sharedSizeBytes);
-                            if (by_lds < nb) nb = by_lds;
-                        }
+                        const int nb = blocks_per_cu(
+                            rlpl::pick_kernel(dt, mode, kl != 0 || mode == kModeRKL, wg != 0, shape));
                         if (nb < 1) return;
                         if (nb < occ) occ = nb;
                     }
@@ -75,6 +82,15 @@ void init_device(int dev, DeviceInfo& info) {
                 if (cap > rlpl::kMaxGrid) cap = rlpl::kMaxGrid;
                 info.grid_cap[dt][mode][shape] = int(cap);
             }
+    for (int dt = 0; dt < 3; ++dt) {
+        // fwd+bwd and forward-only share one grid size (identical losses).
+        const int a = blocks_per_cu(rlpl::pick_vocab_kernel(dt, true));
+        const int b = blocks_per_cu(rlpl::pick_vocab_kernel(dt, false));
+        if (a < 1 || b < 1) return;
+        long cap = long(a < b ? a : b) * cus;
+        if (cap > rlpl::kMaxGrid) cap = rlpl::kMaxGrid;
+        info.vocab_cap[dt] = int(cap);
+    }
     info.status = RLPL_OK;
 }
 
@@ -112,8 +128,9 @@ int check_common(const void* mask, int64_t bs, int64_t seq_len, int dtype, int m
 // device (and, with other work present, becomes resident as that work drains;
 // the exchange wait is also bounded in time).  A cooperative launch would
 // guarantee the same but costs ~16 us of extra dispatch latency per call here.
-int launch(const void* kernel, const Args& a, int64_t grid, hipStream_t stream) {
-    void* params[] = {const_cast<Args*>(&a)};
+template <typename A>
+int launch(const void* kernel, const A& a, int64_t grid, hipStream_t stream) {
+    void* params[] = {const_cast<A*>(&a)};
     const hipError_t e =
         hipLaunchKernel(kernel, dim3(unsigned(grid)), dim3(rlpl::kThreads), params, 0, stream);
     if (e != hipSuccess) {
@@ -230,9 +247,67 @@ int rkl_loss(bool write_grad, const void* student_lp, const void* teacher_lp, co
     return run(kModeRKL, write_grad, true, a, dtype, stream);
 }
 
+// Full-vocab reverse KL: shape limits of the (rows, vocab) slabs.
+bool vocab_shape_ok(int64_t rows, int64_t vocab) {
+    return rows >= 1 && vocab >= 1 && rows < (int64_t(1) << 31) && vocab <= (int64_t(1) << 62) / rows;
+}
+
+int vocab_loss(bool write_grad, const void* student, const void* teacher, const void* mask,
+               int64_t rows, int64_t vocab, int dtype, int mask_dtype, float* loss_out, void* grad_out,
+               uint32_t* n_valid_out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!student || !teacher || !mask || !loss_out || (write_grad && !grad_out)) return RLPL_ERR_NULL;
+    if (!vocab_shape_ok(rows, vocab)) return RLPL_ERR_SHAPE;
+    if (dtype != RLPL_F32 && dtype != RLPL_F16 && dtype != RLPL_BF16) return RLPL_ERR_DTYPE;
+    if (mask_dtype != RLPL_MASK_BOOL && mask_dtype != RLPL_MASK_INT8) return RLPL_ERR_DTYPE;
+    if (!aligned(student, 16) || !aligned(teacher, 16) || !aligned(mask, 16) ||
+        (write_grad && !aligned(grad_out, 16)) || !aligned(loss_out, 4) ||
+        (n_valid_out && !aligned(n_valid_out, 4)))
+        return RLPL_ERR_ALIGN;
+    if (!workspace || workspace_bytes < rlpl::kWorkspaceBytes) return RLPL_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return RLPL_ERR_ALIGN;
+    const DeviceInfo* info = nullptr;
+    const int st = current_device(&info);
+    if (st != RLPL_OK) return st;
+    const int64_t cap = info->vocab_cap[dtype];
+    if (cap < 1) return RLPL_ERR_DEVICE;
+    // groups of `chunks` workgroups (one per piece of a row), all co-resident.
+    const rlpl::VocabSplit sp = rlpl::vocab_split(rows, vocab, int(elem_bytes(dtype)), cap);
+    rlpl::VocabArgs a{};
+    a.student = student;
+    a.teacher = teacher;
+    a.mask = static_cast<const uint8_t*>(mask);
+    a.grad = write_grad ? grad_out : nullptr;
+    a.loss = loss_out;
+    a.n_out = n_valid_out;
+    a.ws = static_cast<rlpl::Workspace*>(workspace);
+    a.rows = rows;
+    a.vocab = vocab;
+    a.chunks = uint32_t(sp.chunks);
+    a.chunk_blocks = uint64_t(sp.chunk_blocks);
+    const void* kernel = rlpl::pick_vocab_kernel(dtype, write_grad);
+    if (!kernel) return RLPL_ERR_DTYPE;
+    return launch(kernel, a, sp.groups * sp.chunks, stream);
+}
+
 }  // namespace
 
 extern "C" {
+
+int reverse_kl_logits(const void* student_logits, const void* teacher_logits, const void* mask,
+                      int64_t rows, int64_t vocab, int dtype, int mask_dtype, float* loss_out,
+                      void* grad_out, uint32_t* n_valid_out, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+    return vocab_loss(true, student_logits, teacher_logits, mask, rows, vocab, dtype, mask_dtype,
+                      loss_out, grad_out, n_valid_out, workspace, workspace_bytes, stream);
+}
+
+int reverse_kl_logits_fwd(const void* student_logits, const void* teacher_logits, const void* mask,
+                          int64_t rows, int64_t vocab, int dtype, int mask_dtype, float* loss_out,
+                          uint32_t* n_valid_out, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+    return vocab_loss(false, student_logits, teacher_logits, mask, rows, vocab, dtype, mask_dtype,
+                      loss_out, nullptr, n_valid_out, workspace, workspace_bytes, stream);
+}
 
 int bnpo_loss(const void* policy_lp, const void* old_lp, const void* ref_lp, const void* advantages,
               const void* mask, int64_t bs, int64_t seq_len, int dtype, int mask_dtype, float beta,
@@ -290,16 +365,29 @@ int reverse_kl_fwd(const void* student_lp, const void* teacher_lp, const void* m
 size_t rlpl_workspace_bytes(int64_t bs, int64_t seq_len, int op) {
     (void)bs;
     (void)seq_len;
-    if (op < RLPL_OP_BNPO || op > RLPL_OP_RKL_FWD) return 0;
+    if (op < RLPL_OP_BNPO || op > RLPL_OP_RKL_LOGITS_FWD) return 0;
     return rlpl::kWorkspaceBytes;
 }
 
 int rlpl_launch_shape(int64_t bs, int64_t seq_len, int dtype, int op, int* grid_out, int* vec_out,
                       int* tiles_out) {
     if (!grid_out || !vec_out || !tiles_out) return RLPL_ERR_NULL;
+    if (dtype != RLPL_F32 && dtype != RLPL_F16 && dtype != RLPL_BF16) return RLPL_ERR_DTYPE;
+    if (op == RLPL_OP_RKL_LOGITS || op == RLPL_OP_RKL_LOGITS_FWD) {
+        if (!vocab_shape_ok(bs, seq_len)) return RLPL_ERR_SHAPE;
+        const DeviceInfo* info = nullptr;
+        const int st = current_device(&info);
+        if (st != RLPL_OK) return st;
+        const int64_t cap = info->vocab_cap[dtype];
+        if (cap < 1) return RLPL_ERR_DEVICE;
+        const rlpl::VocabSplit sp = rlpl::vocab_split(bs, seq_len, int(elem_bytes(dtype)), cap);
+        *grid_out = int(sp.groups * sp.chunks);
+        *vec_out = int(32 / elem_bytes(dtype));
+        *tiles_out = int(bs * sp.chunks > INT32_MAX ? INT32_MAX : bs * sp.chunks);
+        return RLPL_OK;
+    }
     if (bs < 1 || seq_len < 1 || bs > (int64_t(1) << 31) / seq_len || bs * seq_len >= (int64_t(1) << 31))
         return RLPL_ERR_SHAPE;
-    if (dtype != RLPL_F32 && dtype != RLPL_F16 && dtype != RLPL_BF16) return RLPL_ERR_DTYPE;
     int mode;
     switch (op) {
     case RLPL_OP_BNPO: case RLPL_OP_BNPO_FWD: mode = kModeBNPO; break;

@@ -61,6 +61,8 @@ enum { kF32 = 0, kF16 = 1, kBF16 = 2 };
 struct alignas(256) Slot {
     uint64_t count;            // valid-token count of the workgroup's tiles
     uint64_t partial;          // float bits of the workgroup's partial loss
+    uint64_t stats[2][5];      // full-vocab reverse KL: a row chunk's online sums,
+                               // double-buffered by round (tag = generation + 1 + round)
 };
 
 // Device workspace.  Zero-filled once by the caller; every launch advances

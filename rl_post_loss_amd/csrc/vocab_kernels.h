@@ -1,0 +1,53 @@
+// Internal interface between the C ABI layer (abi.cpp) and the full-vocab
+// reverse-KL kernels (vocab_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "loss_kernels.h"
+
+namespace rlpl {
+
+struct VocabArgs {
+    const void* student;   // (rows, vocab) logits
+    const void* teacher;   // (rows, vocab) logits
+    const uint8_t* mask;   // (rows,)
+    void* grad;            // (rows, vocab) d loss / d student logits (fwd+bwd only)
+    float* loss;
+    uint32_t* n_out;       // valid-row count or NULL
+    Workspace* ws;
+    int64_t rows;          // < 2^31
+    int64_t vocab;         // rows * vocab < 2^62
+    uint32_t chunks;       // workgroups per row (gridDim.x is a multiple of it)
+    uint64_t chunk_blocks; // 32-byte blocks per piece of a row
+};
+
+constexpr int kVocabMaxChunks = 256;      // pieces per row
+constexpr int kVocabMinPieceBlocks = 1024; // a piece is at least 1024 blocks (4 per lane)
+
+// How a (rows, vocab) problem is spread over `cap` co-resident workgroups:
+// one workgroup per row when there are at least as many rows as workgroups,
+// else rows split into pieces of at least kVocabMinPieceBlocks blocks, as many
+// as fill the device.  Every row, wherever it starts, spans at most
+// floor(vocab / per_block) + 2 blocks of per_block elements.
+struct VocabSplit {
+    int64_t chunks, chunk_blocks, groups;
+};
+inline VocabSplit vocab_split(int64_t rows, int64_t vocab, int elem, int64_t cap) {
+    const int64_t per_block = 32 / elem;
+    const int64_t blocks = vocab % per_block == 0 ? vocab / per_block : vocab / per_block + 2;
+    int64_t c = rows >= cap ? 1 : cap / rows;
+    const int64_t most = (blocks + kVocabMinPieceBlocks - 1) / kVocabMinPieceBlocks;
+    if (c > most) c = most;
+    if (c > kVocabMaxChunks) c = kVocabMaxChunks;
+    if (c < 1) c = 1;
+    const int64_t chunk_blocks = (blocks + c - 1) / c;
+    const int64_t groups = cap / c < rows ? cap / c : rows;
+    return VocabSplit{c, chunk_blocks, groups};
+}
+
+// Kernel for <dtype, fwd+bwd or forward-only>, or nullptr.
+const void* pick_vocab_kernel(int dtype, bool write_grad);
+
+}  // namespace rlpl

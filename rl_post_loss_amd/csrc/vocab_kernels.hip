@@ -1,0 +1,367 @@
+// Full-vocab reverse KL between the softmaxes of two (rows, vocab) logit slabs
+// for gfx950 (MI355X).
+//
+// Operation (model card "Geometric-AI Kernels", section "Reverse KL"): for
+// each row r, p = softmax(student[r]), q = softmax(teacher[r]),
+//   kl_r = sum_v p_v (log p_v - log q_v),
+//   loss = sum_r mask_r kl_r / N,  N = number of rows with a nonzero mask byte
+//   (unclamped: 0/0 = NaN when no row is valid),
+//   grad_v = mask_r / N * p_v (log p_v - log q_v - kl_r).
+// Since log p_v - log q_v = (s_v - t_v) - (lse_s - lse_t), the last factor is
+// d_v - E_p[d] with d = s - t, and kl_r = E_p[d] - lse_s + lse_t, formed as
+// (E_p[d] - (m_s - m_t)) - (ln z_s - ln z_t) with m the row maxima and z the
+// sums of exp(x - m): each bracket is of the size of the logits' spread, not
+// of lse, and both are exactly 0 when the rows are equal or vocab is 1.
+//
+// Design (HBM-bound streaming; no contraction, so no MFMA):
+//  * A persistent grid of G = min(rows, co-resident capacity) workgroups;
+//    workgroup w takes rows w, w+G, ...  Rows whose mask byte is zero are
+//    never read (the fwd+bwd kernel writes their gradient as +0).
+//  * Pass 1 reads a row once: each lane keeps, for its elements, the running
+//    maximum of s and of t and the sums sum e^(s-m_s),
+//    sum e^(t-m_t) and sum e^(s-m_s) (s - t), rescaled when a maximum grows
+//    (the online normaliser of Milakov and Gimelshein, 2018).  Four
+//    interleaved accumulators per lane (sharing the maxima) keep the
+//    dependency chains short and each float32 sum to a quarter of a lane's
+//    terms.  Lanes are merged with the same rule over the wavefront, then
+//    over the four waves in LDS.
+//  * The forward-only kernel stops there.  The fwd+bwd kernel reads the row
+//    a second time and writes grad_v = p_v (d_v - E_p[d]) / N.
+//  * N needs no exchange: every workgroup counts the (rows-byte) mask itself.
+//    The loss is the fixed-order sum of per-workgroup partials that
+//    workgroup 0 gathers from the workspace (the protocol of the policy-loss
+//    kernels), so the fused and forward-only losses are bit-identical.
+//  * Rows need not start on a 16-byte boundary: a row covers the aligned
+//    16-byte blocks it touches, full blocks move with 128-bit accesses and the
+//    one or two partial blocks element by element.
+#include <hip/hip_runtime.h>
+#include <float.h>
+#include <stdint.h>
+
+#include "device_common.h"
+#include "loss_kernels.h"
+#include "vocab_kernels.h"
+
+// No implicit a*b+c contraction in this file: the forward-only and fwd+bwd
+// kernels must round pass 1 identically (their losses are bit-identical), and
+// the compiler contracts differently in the two instantiations.  The fmaf
+// calls below are the intended fused operations.
+#pragma clang fp contract(off)
+
+namespace rlpl {
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNone = -FLT_MAX;   // logit of a position outside the row: never the maximum, weight 0
+
+// Online sums of one lane (or, after merging, of a wavefront or a workgroup).
+struct Stats {
+    float ms, mt;       // running maxima of s and t
+    float zs, zt;       // sum exp(s - ms), sum exp(t - mt)
+    float as;           // sum exp(s - ms) * (s - t)
+};
+
+// exp(x) for x <= 0 on the hardware base-2 unit; exp(0) is exactly 1.
+__device__ __forceinline__ float exp_le0(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+
+__device__ __forceinline__ Stats merge(const Stats& a, const Stats& b) {
+    Stats r;
+    r.ms = fmaxf(a.ms, b.ms);
+    r.mt = fmaxf(a.mt, b.mt);
+    const float fa = exp_le0(a.ms - r.ms), fb = exp_le0(b.ms - r.ms);
+    const float ga = exp_le0(a.mt - r.mt), gb = exp_le0(b.mt - r.mt);
+    r.zs = a.zs * fa + b.zs * fb;
+    r.as = a.as * fa + b.as * fb;
+    r.zt = a.zt * ga + b.zt * gb;
+    return r;
+}
+
+__device__ __forceinline__ Stats shfl_xor(const Stats& a, int off) {
+    return Stats{__shfl_xor(a.ms, off, 64), __shfl_xor(a.mt, off, 64), __shfl_xor(a.zs, off, 64),
+                 __shfl_xor(a.zt, off, 64), __shfl_xor(a.as, off, 64)};
+}
+
+// Merge over the workgroup in a fixed order; the result is valid in every thread.
+__device__ __forceinline__ Stats block_merge(Stats v, Stats* red) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v = merge(v, shfl_xor(v, off));
+    __syncthreads();                        // red[] may still be read by the previous row
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    Stats t = red[0];
+#pragma unroll
+    for (int i = 1; i < kWaves; ++i) t = merge(t, red[i]);
+    return t;
+}
+
+// Valid rows: the number of nonzero bytes of mask[0, rows), summed by the whole workgroup.
+__device__ __forceinline__ uint32_t count_rows(const uint8_t* __restrict__ mask, uint32_t rows, uint32_t* red) {
+    uint32_t n = 0;
+    for (uint32_t i = threadIdx.x * 16u; i < rows; i += kThreads * 16u) {
+        Dwords<4> d;
+        if (i + 16u <= rows) {
+            d.load(mask + i);
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) d.w[q] = 0;
+#pragma unroll
+            for (int k = 0; k < 16; ++k)
+                if (i + k < rows) d.w[k >> 2] |= uint32_t(mask[i + k]) << (8 * (k & 3));
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t x = ((d.w[q] & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | d.w[q];
+            n += __builtin_popcount(x & 0x80808080u);
+        }
+    }
+    return block_sum(n, red);
+}
+
+constexpr int kAcc = 4;   // interleaved accumulators per lane
+
+// Positions of block b (elements b*VEC .. b*VEC+VEC-1) inside [lo, hi), as a
+// bitmask (bit k = position k); all VEC bits for a block inside the row.
+template <int VEC>
+__device__ __forceinline__ uint32_t block_bits(uint64_t b, uint64_t lo, uint64_t hi) {
+    const uint64_t e0 = b * VEC;
+    const uint32_t first = lo > e0 ? uint32_t(lo - e0) : 0u;                 // < VEC for a block of the row
+    const uint32_t end = hi < e0 + VEC ? uint32_t(hi - e0) : uint32_t(VEC);  // > first
+    return ((1u << end) - 1u) & ~((1u << first) - 1u);
+}
+
+constexpr uint32_t all_bits(int vec) { return (1u << vec) - 1u; }
+
+// One 32-byte block of a plane as floats; positions whose bit is clear read as kNone.
+template <typename T, int VEC>
+__device__ __forceinline__ void block_values(const Plane<T, VEC>& p, uint32_t bits, float (&x)[VEC]) {
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) x[k] = p.get(k);
+    if (bits != all_bits(VEC)) {
+#pragma unroll
+        for (int k = 0; k < VEC; ++k)
+            if (!((bits >> k) & 1u)) x[k] = kNone;
+    }
+}
+
+// Raw words of block b: one 128-bit path for a block inside the row, else
+// element by element for the positions whose bit is set (others left 0).
+template <typename T, int VEC>
+__device__ __forceinline__ void load_raw(const T* __restrict__ base, uint64_t b, uint32_t bits,
+                                         Plane<T, VEC>& p) {
+    const T* __restrict__ q = base + b * VEC;
+    if (bits == all_bits(VEC)) {
+        p.d.load(q);
+    } else {
+#pragma unroll
+        for (int i = 0; i < Plane<T, VEC>::kWords; ++i) p.d.w[i] = 0;
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) {
+            if ((bits >> k) & 1u) {
+                if constexpr (sizeof(T) == 4) p.d.w[k] = reinterpret_cast<const uint32_t*>(q)[k];
+                else p.d.w[k >> 1] |= uint32_t(reinterpret_cast<const uint16_t*>(q)[k]) << (16 * (k & 1));
+            }
+        }
+    }
+}
+
+// Stores VEC gradient values of block b, only the positions whose bit is set.
+template <typename T, int VEC>
+__device__ __forceinline__ void store_bits(T* __restrict__ base, uint64_t b, uint32_t bits, const float (&v)[VEC]) {
+    T* __restrict__ q = base + b * VEC;
+    Dwords<VEC * int(sizeof(T)) / 4> out;
+    if constexpr (sizeof(T) == 4) {
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) out.w[k] = __float_as_uint(v[k]);
+    } else {
+#pragma unroll
+        for (int k = 0; k < VEC; k += 2) out.w[k >> 1] = Elem<T>::pack(v[k], v[k + 1]);
+    }
+    if (bits == all_bits(VEC)) {
+        out.store(q);
+    } else {
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) {
+            if ((bits >> k) & 1u) {
+                if constexpr (sizeof(T) == 4) reinterpret_cast<uint32_t*>(q)[k] = out.w[k];
+                else reinterpret_cast<uint16_t*>(q)[k] = uint16_t(out.w[k >> 1] >> (16 * (k & 1)));
+            }
+        }
+    }
+}
+
+}  // namespace
+
+// Rows are split into `chunks` pieces of `chunk_blocks` 32-byte blocks (one
+// piece, the whole row, when there are enough rows to fill the device);
+// workgroup w owns piece w % chunks of rows w / chunks, w / chunks + R, ...
+// (R = gridDim.x / chunks), one row per round.  With several pieces, their
+// online sums go to the workspace and are merged in piece order (so every
+// workgroup of the row, and the forward-only kernel, gets the same bits).  The
+// fwd+bwd kernel then reads its piece again to write the gradient.  All
+// workgroups are co-resident and a round's waits are among workgroups of that
+// round only.
+template <typename T, bool WRITE_GRAD>
+__global__ void __launch_bounds__(kThreads) vocab_kernel(const VocabArgs a) {
+    constexpr int VEC = 32 / int(sizeof(T));   // elements per 32-byte block
+    static_assert(VEC % kAcc == 0, "accumulators split a block's elements");
+    const uint64_t chunk_blocks = a.chunk_blocks;
+    __shared__ float red_f[kWaves];
+    __shared__ uint32_t red_u[kWaves];
+    __shared__ uint32_t word[1];
+    __shared__ Stats red_s[kWaves];
+    __shared__ float peer[kVocabMaxChunks * 5];
+
+    Workspace* ws = a.ws;
+    uint32_t gen = 0;
+    if (threadIdx.x == 0) gen = load_relaxed(&ws->generation);
+
+    const uint32_t C = a.chunks;
+    const uint32_t R = gridDim.x / C;
+    const uint32_t grp = blockIdx.x / C, c = blockIdx.x % C;
+    const uint32_t rows = uint32_t(a.rows);
+    const uint64_t V = uint64_t(a.vocab);
+    const T* __restrict__ S = static_cast<const T*>(a.student);
+    const T* __restrict__ Tt = static_cast<const T*>(a.teacher);
+    const uint32_t N = count_rows(a.mask, rows, red_u);
+    gen = share_generation(gen, word);
+    const float inv_n = 1.0f / float(N);        // unclamped: inf when N == 0, used by no row then
+    float part = 0.0f;                          // sum of kl_r over the rows whose chunk 0 this is
+    const uint32_t rounds = (rows + R - 1) / R;
+    // Exchanges so far: the stats buffer alternates per exchange (not per round:
+    // masked rows exchange nothing), so a workgroup writes a buffer only after
+    // every peer has finished reading it (each peer published the exchange in
+    // between only after it had read the one before).
+    uint32_t exch = 0;
+
+    for (uint32_t round = 0, r = grp; r < rows; ++round, r += R) {
+        const uint64_t lo = uint64_t(r) * V, hi = lo + V;
+        const uint64_t rb1 = (hi + VEC - 1) / VEC;
+        const uint64_t cb0 = lo / VEC + c * chunk_blocks;
+        const uint64_t cb1 = cb0 + chunk_blocks < rb1 ? cb0 + chunk_blocks : rb1;
+        if (a.mask[r] == 0) {
+            if constexpr (WRITE_GRAD) {
+                float z[VEC];
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) z[k] = 0.0f;
+                for (uint64_t b = cb0 + threadIdx.x; b < cb1; b += kThreads)
+                    store_bits<T, VEC>(static_cast<T*>(a.grad), b, block_bits<VEC>(b, lo, hi), z);
+            }
+            continue;
+        }
+        // Online sums of the chunk (blocks cb0 + tid, cb0 + tid + kThreads, ...).
+        // The lane's four accumulators share one running maximum per plane,
+        // rescaled only when it grows.
+        float ms = kNone, mt = kNone;
+        float zs[kAcc], zt[kAcc], as[kAcc];
+#pragma unroll
+        for (int q = 0; q < kAcc; ++q) zs[q] = zt[q] = as[q] = 0.0f;
+        for (uint64_t b = cb0 + threadIdx.x; b < cb1; b += kThreads) {
+            const uint32_t bits = block_bits<VEC>(b, lo, hi);
+            Plane<T, VEC> ps, pt;
+            load_raw<T, VEC>(S, b, bits, ps);
+            load_raw<T, VEC>(Tt, b, bits, pt);
+            float s[VEC], t[VEC];
+            block_values<T, VEC>(ps, bits, s);
+            block_values<T, VEC>(pt, bits, t);
+            float bs = kNone, bt = kNone;
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) { bs = fmaxf(bs, s[k]); bt = fmaxf(bt, t[k]); }
+            const float ns = fmaxf(ms, bs), nt = fmaxf(mt, bt);
+            if (ns > ms || nt > mt) {
+                const float fs = exp_le0(ms - ns), ft = exp_le0(mt - nt);
+#pragma unroll
+                for (int q = 0; q < kAcc; ++q) { zs[q] *= fs; as[q] *= fs; zt[q] *= ft; }
+                ms = ns;
+                mt = nt;
+            }
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) {
+                const float es = exp_le0(s[k] - ms);
+                const float et = exp_le0(t[k] - mt);
+                zs[k % kAcc] += es;
+                zt[k % kAcc] += et;
+                as[k % kAcc] = fmaf(es, s[k] - t[k], as[k % kAcc]);
+            }
+        }
+        Stats st{ms, mt, zs[0], zt[0], as[0]};
+#pragma unroll
+        for (int q = 1; q < kAcc; ++q) { st.zs += zs[q]; st.zt += zt[q]; st.as += as[q]; }
+        st = block_merge(st, red_s);
+        Stats row = st;
+        if (C > 1) {
+            // Publish the chunk's sums, read every chunk's of this row, merge them in chunk order.
+            const uint32_t tag = gen + 1u + round;
+            const uint32_t buf = exch++ & 1u;
+            uint64_t* mine = &ws->slot[blockIdx.x].stats[buf][0];
+            if (threadIdx.x < 5) {
+                const float v[5] = {st.ms, st.mt, st.zs, st.zt, st.as};
+                store_relaxed(mine + threadIdx.x, tagged(tag, __float_as_uint(v[threadIdx.x])));
+            }
+            for (uint32_t i = threadIdx.x; i < 5 * C; i += kThreads) {
+                const uint64_t* w = &ws->slot[grp * C + i / 5].stats[buf][i % 5];
+                uint64_t x = load_relaxed(w);
+                if (uint32_t(x >> 32) != tag) x = wait_tagged(ws, w, tag);
+                peer[i] = __uint_as_float(uint32_t(x));
+            }
+            __syncthreads();
+            row = Stats{peer[0], peer[1], peer[2], peer[3], peer[4]};
+            for (uint32_t q = 1; q < C; ++q)
+                row = merge(row, Stats{peer[5 * q], peer[5 * q + 1], peer[5 * q + 2], peer[5 * q + 3],
+                                       peer[5 * q + 4]});
+            __syncthreads();                    // peer[] is rewritten next round
+        }
+        // ln z = log2(z) * ln 2 (v_log_f32 is base 2); z >= 1.
+        const float ln_zs = __builtin_amdgcn_logf(row.zs) * kLn2;
+        const float ln_zt = __builtin_amdgcn_logf(row.zt) * kLn2;
+        const float ed = row.as / row.zs;                       // E_p[s - t]
+        if (c == 0) part += (ed - (row.ms - row.mt)) - (ln_zs - ln_zt);   // kl_r
+        if constexpr (WRITE_GRAD) {
+            // grad_v = p_v (d_v - E_p[d]) / N, p_v = exp(s_v - lse_s).
+            const float lse_s = row.ms + ln_zs;
+            for (uint64_t b = cb0 + threadIdx.x; b < cb1; b += kThreads) {
+                const uint32_t bits = block_bits<VEC>(b, lo, hi);
+                Plane<T, VEC> ps, pt;
+                load_raw<T, VEC>(S, b, bits, ps);
+                load_raw<T, VEC>(Tt, b, bits, pt);
+                float s[VEC], t[VEC], g[VEC];
+                block_values<T, VEC>(ps, bits, s);
+                block_values<T, VEC>(pt, bits, t);
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) {
+                    const float p = exp_le0(s[k] - lse_s);
+                    g[k] = p * ((s[k] - t[k]) - ed) * inv_n;
+                }
+                store_bits<T, VEC>(static_cast<T*>(a.grad), b, bits, g);
+            }
+        }
+    }
+
+    if (threadIdx.x == 0) publish_partial(ws, blockIdx.x, gen, part);
+    if (blockIdx.x == 0) {
+        const float total = gather_slots<false>(ws, gridDim.x, gen, red_f, red_u);
+        // This launch used tags gen + 1 .. gen + rounds; the next starts above them.
+        advance_generation(ws, gen, rounds + 1u);
+        if (threadIdx.x == 0) {
+            *a.loss = total / float(N);                         // 0/0 = NaN when no row is valid
+            if (a.n_out) a.n_out[0] = N;
+        }
+    }
+}
+
+// ----------------------------------------------------------------------------- host-side table
+
+const void* pick_vocab_kernel(int dtype, bool write_grad) {
+    switch (dtype) {
+    case kF32: return write_grad ? reinterpret_cast<const void*>(&vocab_kernel<float, true>)
+                                 : reinterpret_cast<const void*>(&vocab_kernel<float, false>);
+    case kF16: return write_grad ? reinterpret_cast<const void*>(&vocab_kernel<_Float16, true>)
+                                 : reinterpret_cast<const void*>(&vocab_kernel<_Float16, false>);
+    case kBF16: return write_grad ? reinterpret_cast<const void*>(&vocab_kernel<__bf16, true>)
+                                  : reinterpret_cast<const void*>(&vocab_kernel<__bf16, false>);
+    }
+    return nullptr;
+}
+
+}  // namespace rlpl

@@ -17,6 +17,9 @@ mask of shape (bs, seq_len)):
 * completion mask = a prefix of integer length U[lo, hi] (both ends
   inclusive) per row; optionally a fixed number of rows fully masked;
 * reverse-KL: student = -|N(0,1)|, teacher = student + N(0, 0.3).
+* full-vocab reverse-KL ("Reverse KL" example): student and teacher logits
+  are independent N(0,1) draws of shape (rows, vocab), rounded to the dtype;
+  the row mask is U(0,1) > 0.2 (about 80 % of rows valid).
 
 All draws come from ``numpy.random.default_rng(seed)`` (PCG64) in float64, in
 the fixed order listed in ``policy_inputs`` / ``rkl_inputs``.
@@ -148,3 +151,31 @@ def device_policy_inputs(w: Workload, device: str) -> dict:
     lengths = torch.randint(w.len_lo, w.len_hi + 1, (w.bs,), generator=g, device=device)
     mask = (torch.arange(w.seq_len, device=device)[None, :] < lengths[:, None]).to(MASK_DTYPES[w.mask_dtype])
     return {"policy": policy, "old": old, "ref": ref, "advantages": adv, "mask": mask}
+
+
+def vocab_inputs(rows: int, vocab: int, dtype: str = "bf16", mask_dtype: str = "bool", seed: int = 0,
+                 p_valid: float = 0.8) -> dict:
+    """Inputs of the full-vocab reverse-KL loss, as CPU tensors.
+
+    Draw order: z1 (rows, vocab) -> student; z2 (rows, vocab) -> teacher;
+    u (rows,) -> mask = u > 1 - p_valid.
+    """
+    rng = np.random.default_rng(seed)
+    student = _round(rng.standard_normal((rows, vocab)), dtype)
+    teacher = _round(rng.standard_normal((rows, vocab)), dtype)
+    u = rng.random(rows)
+    mask = torch.from_numpy(u > 1.0 - p_valid).to(MASK_DTYPES[mask_dtype])
+    return {"student": student, "teacher": teacher, "mask": mask}
+
+
+def device_vocab_inputs(rows: int, vocab: int, dtype: str, mask_dtype: str, seed: int, device: str,
+                        p_valid: float = 0.8) -> dict:
+    """Large full-vocab inputs drawn on the device with torch's seeded generator
+    (same distributions as ``vocab_inputs``, not the same values)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    dt = DTYPES[dtype]
+    student = torch.randn((rows, vocab), generator=g, device=device, dtype=torch.float32).to(dt)
+    teacher = torch.randn((rows, vocab), generator=g, device=device, dtype=torch.float32).to(dt)
+    mask = (torch.rand(rows, generator=g, device=device) > 1.0 - p_valid).to(MASK_DTYPES[mask_dtype])
+    return {"student": student, "teacher": teacher, "mask": mask}

@@ -44,7 +44,8 @@ def test_library_exports_every_declared_function(lib):
     names = declared_functions()
     assert set(names) >= {"bnpo_loss", "bnpo_loss_fwd", "grpo_loss", "grpo_loss_fwd", "reverse_kl",
                           "reverse_kl_fwd", "rlpl_workspace_bytes", "rlpl_workspace_flags",
-                          "rlpl_status_string", "rlpl_version", "rlpl_launch_shape"}
+                          "rlpl_status_string", "rlpl_version", "rlpl_launch_shape",
+                          "reverse_kl_logits", "reverse_kl_logits_fwd"}
     for n in names:
         assert hasattr(lib, n), n
     assert lib.rlpl_version() == 1
@@ -73,10 +74,10 @@ def test_status_strings(lib):
 
 
 def test_workspace_bytes(lib):
-    for op in range(6):
+    for op in range(8):
         n = lib.rlpl_workspace_bytes(64, 4096, op)
         assert n >= 256 + 4 * 1024 and n % 256 == 0
-    assert lib.rlpl_workspace_bytes(64, 4096, 6) == 0
+    assert lib.rlpl_workspace_bytes(64, 4096, 8) == 0
     assert lib.rlpl_workspace_bytes(64, 4096, -1) == 0
 
 
@@ -197,3 +198,59 @@ def test_launch_shape_validation(lib):
     assert rl.STATUS[lib.rlpl_launch_shape(4, 64, 2, 0, None, ctypes.byref(v), ctypes.byref(t))] == "RLPL_ERR_NULL"
     if not torch.cuda.is_available():
         assert rl.STATUS[lib.rlpl_launch_shape(4, 64, 2, 0, *out)] == "RLPL_ERR_DEVICE"
+
+
+def call_vocab(lib, fused=True, **over):
+    a = dict(s=A, t=A + 0x100000, mask=A + 0x200000, rows=8, V=1000, dtype=2, mask_dtype=0,
+             loss=A + 0x300000, grad=A + 0x400000, n=A + 0x500000, ws=WS, ws_bytes=8 << 20, stream=None)
+    a.update(over)
+    args = [a["s"], a["t"], a["mask"], a["rows"], a["V"], a["dtype"], a["mask_dtype"], a["loss"]]
+    if fused:
+        args.append(a["grad"])
+    args += [a["n"], a["ws"], a["ws_bytes"], a["stream"]]
+    return (lib.reverse_kl_logits if fused else lib.reverse_kl_logits_fwd)(*args)
+
+
+VOCAB_CASES = [
+    ("RLPL_ERR_NULL", dict(s=None)),
+    ("RLPL_ERR_NULL", dict(t=None)),
+    ("RLPL_ERR_NULL", dict(mask=None)),
+    ("RLPL_ERR_NULL", dict(loss=None)),
+    ("RLPL_ERR_SHAPE", dict(rows=0)),
+    ("RLPL_ERR_SHAPE", dict(V=0)),
+    ("RLPL_ERR_SHAPE", dict(rows=1 << 31)),
+    ("RLPL_ERR_SHAPE", dict(rows=1 << 20, V=(1 << 42) + 1)),   # rows * vocab > 2^62
+    ("RLPL_ERR_DTYPE", dict(dtype=5)),
+    ("RLPL_ERR_DTYPE", dict(mask_dtype=3)),
+    ("RLPL_ERR_ALIGN", dict(s=A + 2)),
+    ("RLPL_ERR_ALIGN", dict(t=A + 0x100000 + 8)),
+    ("RLPL_ERR_ALIGN", dict(mask=A + 0x200000 + 1)),
+    ("RLPL_ERR_ALIGN", dict(loss=A + 0x300000 + 2)),
+    ("RLPL_ERR_ALIGN", dict(n=A + 0x500000 + 1)),
+    ("RLPL_ERR_WORKSPACE", dict(ws=None)),
+    ("RLPL_ERR_WORKSPACE", dict(ws_bytes=4096)),
+    ("RLPL_ERR_ALIGN", dict(ws=WS + 64)),
+]
+
+
+@pytest.mark.parametrize("want,over", VOCAB_CASES, ids=[f"{w}-{list(o)[0]}" for w, o in VOCAB_CASES])
+def test_reverse_kl_logits_validation(lib, want, over):
+    assert rl.STATUS[call_vocab(lib, **over)] == want
+    assert rl.STATUS[call_vocab(lib, fused=False, **over)] == want
+
+
+def test_reverse_kl_logits_grad_pointer(lib):
+    assert rl.STATUS[call_vocab(lib, grad=None)] == "RLPL_ERR_NULL"
+    assert rl.STATUS[call_vocab(lib, grad=A + 0x400000 + 4)] == "RLPL_ERR_ALIGN"
+    if not torch.cuda.is_available():
+        # valid arguments stop at the device check on a host with no GPU
+        assert rl.STATUS[call_vocab(lib)] == "RLPL_ERR_DEVICE"
+        assert rl.STATUS[call_vocab(lib, rows=3, V=50257, dtype=0)] == "RLPL_ERR_DEVICE"
+
+
+def test_launch_shape_vocab_validation(lib):
+    g, v, t = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
+    out = (ctypes.byref(g), ctypes.byref(v), ctypes.byref(t))
+    # vocab ops take (rows, vocab): 2^31 slots and more are fine there
+    assert rl.STATUS[lib.rlpl_launch_shape(1 << 20, 1 << 20, 2, 6, *out)] in ("RLPL_OK", "RLPL_ERR_DEVICE")
+    assert rl.STATUS[lib.rlpl_launch_shape(0, 1000, 2, 7, *out)] == "RLPL_ERR_SHAPE"
