@@ -52,8 +52,11 @@ def _load():
     lib.rlpl_oracle_bnpo.argtypes = [i64, i64, dp, dp, dp, dp, u8p, d, d, d, dp, dp, i64p]
     lib.rlpl_oracle_grpo.argtypes = [i64, i64, dp, dp, dp, dp, u8p, d, d, d, dp, dp, i64p]
     lib.rlpl_oracle_rkl.argtypes = [i64, i64, dp, dp, u8p, dp, dp, i64p]
+    lib.rlpl_oracle_bnpo_ppo.argtypes = [i64, i64, dp, dp, dp, dp, u8p, d, d, d, dp, dp, i64p]
+    lib.rlpl_oracle_grpo_ppo.argtypes = [i64, i64, dp, dp, dp, dp, u8p, d, d, d, dp, dp, i64p]
     lib.rlpl_oracle_rkl_logits.argtypes = [i64, i64, dp, dp, u8p, dp, dp, i64p, dp]
-    for f in (lib.rlpl_oracle_bnpo, lib.rlpl_oracle_grpo, lib.rlpl_oracle_rkl, lib.rlpl_oracle_rkl_logits):
+    for f in (lib.rlpl_oracle_bnpo, lib.rlpl_oracle_grpo, lib.rlpl_oracle_rkl, lib.rlpl_oracle_rkl_logits,
+              lib.rlpl_oracle_bnpo_ppo, lib.rlpl_oracle_grpo_ppo):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -117,16 +120,21 @@ def _policy_call(fn, policy, old, ref, advantages, mask, beta, epsilon, epsilon_
     return Result(loss.value, g, n if per_row else int(n[0]))
 
 
-def bnpo(policy, old, ref, advantages, mask, beta, epsilon, epsilon_high, grad=True) -> Result:
-    """BNPO loss (global token mean) and d loss / d policy."""
-    return _policy_call(_load().rlpl_oracle_bnpo, policy, old, ref, advantages, mask,
-                        beta, epsilon, epsilon_high, grad, per_row=False)
+def bnpo(policy, old, ref, advantages, mask, beta, epsilon, epsilon_high, grad=True,
+         sign_aware=False) -> Result:
+    """BNPO loss (global token mean) and d loss / d policy; sign_aware takes the
+    PPO form -min(A*ratio, A*clipped) for per_token."""
+    lib = _load()
+    return _policy_call(lib.rlpl_oracle_bnpo_ppo if sign_aware else lib.rlpl_oracle_bnpo, policy, old,
+                        ref, advantages, mask, beta, epsilon, epsilon_high, grad, per_row=False)
 
 
-def grpo(policy, old, ref, advantages, mask, beta, epsilon, epsilon_high, grad=True) -> Result:
+def grpo(policy, old, ref, advantages, mask, beta, epsilon, epsilon_high, grad=True,
+         sign_aware=False) -> Result:
     """GRPO loss (per-response token mean, then mean over rows) and d loss / d policy."""
-    return _policy_call(_load().rlpl_oracle_grpo, policy, old, ref, advantages, mask,
-                        beta, epsilon, epsilon_high, grad, per_row=True)
+    lib = _load()
+    return _policy_call(lib.rlpl_oracle_grpo_ppo if sign_aware else lib.rlpl_oracle_grpo, policy, old,
+                        ref, advantages, mask, beta, epsilon, epsilon_high, grad, per_row=True)
 
 
 def rkl(student, teacher, mask, grad=True) -> Result:

@@ -28,6 +28,9 @@
  *   - per_token = -A * min(ratio, clip(ratio, 1-eps, 1+eps_high)) literally;
  *     when ratio equals its clipped value the unclipped branch is taken, so
  *     d per_token / d lp = -A*ratio unless clipping lowered ratio to 1+eps_high.
+ *     The *_ppo functions take the sign-aware PPO form
+ *     -min(A*ratio, A*clip(ratio, 1-eps, 1+eps_high)) instead (the card calls
+ *     per_token "PPO-clipped"); ties again take the unclipped branch.
  *   - masked slots are selected out: they add nothing, their gradient is +0 and
  *     their log-probs are never read.  Any nonzero mask byte means "valid".
  *   - GRPO averages over all bs rows; a fully masked row adds 0 and still counts.
@@ -42,7 +45,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#define RLPL_ORACLE_VERSION 2
+#define RLPL_ORACLE_VERSION 3
 
 int rlpl_oracle_version(void) { return RLPL_ORACLE_VERSION; }
 
@@ -67,6 +70,27 @@ static double clipped_ratio_term(double lp, double old, double adv, double lo, d
     return -adv * chosen;
 }
 
+/* Sign-aware PPO ratio term of one token: per_token = -min(A*ratio, A*clipped),
+ * the standard PPO clipped objective that the card's "PPO-clipped" names (for
+ * A >= 0 it equals the literal form above; for A < 0 the lower bound 1-eps
+ * is the one that clips).  Ties take the unclipped branch.  *slope receives
+ * d per_token / d lp. */
+static double ppo_ratio_term(double lp, double old, double adv, double lo, double hi,
+                             double *slope)
+{
+    double ratio = exp(lp - old);
+    double clipped = ratio;
+    if (clipped < lo) clipped = lo;
+    if (clipped > hi) clipped = hi;
+    double unclipped_obj = adv * ratio, clipped_obj = adv * clipped;
+    if (unclipped_obj <= clipped_obj) {
+        *slope = -adv * ratio;   /* the unclipped objective is the minimum (ties included) */
+        return -unclipped_obj;
+    }
+    *slope = 0.0;                /* the clipped objective is a constant in lp */
+    return -clipped_obj;
+}
+
 /* k3 KL estimator of one token ("BNPO Loss": kl), x = ref - lp.
  * Returns kl; *slope receives d kl / d lp = -(exp(x) - 1). */
 static double k3_kl(double lp, double ref, double *slope)
@@ -77,13 +101,15 @@ static double k3_kl(double lp, double ref, double *slope)
     return e - x - 1.0;
 }
 
-/* Per-token loss contribution (per_token + beta*kl) and its derivative in lp. */
+/* Per-token loss contribution (per_token + beta*kl) and its derivative in lp;
+ * sign_aware selects the sign-aware PPO ratio term. */
 static double token_term(const double *lp, const double *old, const double *ref,
                          double adv, int64_t i, double beta, double lo, double hi,
-                         double *slope)
+                         int sign_aware, double *slope)
 {
     double dpol;
-    double term = clipped_ratio_term(lp[i], old[i], adv, lo, hi, &dpol);
+    double term = sign_aware ? ppo_ratio_term(lp[i], old[i], adv, lo, hi, &dpol)
+                             : clipped_ratio_term(lp[i], old[i], adv, lo, hi, &dpol);
     double dkl = 0.0;
     if (beta != 0.0) {
         double kl = k3_kl(lp[i], ref[i], &dkl);
@@ -99,10 +125,10 @@ static double token_term(const double *lp, const double *old, const double *ref,
  * (loss only).  ref may be NULL when beta == 0.  *n_valid = sum(mask != 0).
  * Returns 0, or -1 on a NULL required pointer / bad shape.
  */
-int rlpl_oracle_bnpo(int64_t bs, int64_t seq_len, const double *lp, const double *old,
-                     const double *ref, const double *adv, const uint8_t *mask,
-                     double beta, double eps, double eps_high,
-                     double *loss, double *grad, int64_t *n_valid)
+static int bnpo(int64_t bs, int64_t seq_len, const double *lp, const double *old,
+                const double *ref, const double *adv, const uint8_t *mask,
+                double beta, double eps, double eps_high, int sign_aware,
+                double *loss, double *grad, int64_t *n_valid)
 {
     if (bs < 0 || seq_len < 0 || !lp || !old || !adv || !mask || !loss || !n_valid) return -1;
     if (beta != 0.0 && !ref) return -1;
@@ -114,7 +140,7 @@ int rlpl_oracle_bnpo(int64_t bs, int64_t seq_len, const double *lp, const double
             int64_t i = r * seq_len + t;
             if (mask[i] == 0) continue;
             ++n;
-            sum += token_term(lp, old, ref, adv[r], i, beta, lo, hi, &slope);
+            sum += token_term(lp, old, ref, adv[r], i, beta, lo, hi, sign_aware, &slope);
         }
     double denom = (double)n;
     if (denom < 1.0) denom = 1.0;   /* max(mask.sum(), 1) */
@@ -125,7 +151,7 @@ int rlpl_oracle_bnpo(int64_t bs, int64_t seq_len, const double *lp, const double
             for (int64_t t = 0; t < seq_len; ++t) {
                 int64_t i = r * seq_len + t;
                 if (mask[i] == 0) { grad[i] = 0.0; continue; }
-                token_term(lp, old, ref, adv[r], i, beta, lo, hi, &slope);
+                token_term(lp, old, ref, adv[r], i, beta, lo, hi, sign_aware, &slope);
                 grad[i] = slope / denom;
             }
     return 0;
@@ -135,10 +161,10 @@ int rlpl_oracle_bnpo(int64_t bs, int64_t seq_len, const double *lp, const double
  * GRPO: loss = (1/bs) * sum_r [ sum_t((per_token + beta*kl) * mask) / max(sum_t(mask), 1) ].
  * grad[i] = d loss / d lp[i].  n_valid has bs entries (per-row counts).
  */
-int rlpl_oracle_grpo(int64_t bs, int64_t seq_len, const double *lp, const double *old,
-                     const double *ref, const double *adv, const uint8_t *mask,
-                     double beta, double eps, double eps_high,
-                     double *loss, double *grad, int64_t *n_valid)
+static int grpo(int64_t bs, int64_t seq_len, const double *lp, const double *old,
+                const double *ref, const double *adv, const uint8_t *mask,
+                double beta, double eps, double eps_high, int sign_aware,
+                double *loss, double *grad, int64_t *n_valid)
 {
     if (bs < 0 || seq_len < 0 || !lp || !old || !adv || !mask || !loss || !n_valid) return -1;
     if (beta != 0.0 && !ref) return -1;
@@ -151,7 +177,7 @@ int rlpl_oracle_grpo(int64_t bs, int64_t seq_len, const double *lp, const double
             int64_t i = r * seq_len + t;
             if (mask[i] == 0) continue;
             ++n;
-            row_sum += token_term(lp, old, ref, adv[r], i, beta, lo, hi, &slope);
+            row_sum += token_term(lp, old, ref, adv[r], i, beta, lo, hi, sign_aware, &slope);
         }
         double denom = (double)n;
         if (denom < 1.0) denom = 1.0;   /* max(mask.sum(-1), 1) */
@@ -161,12 +187,46 @@ int rlpl_oracle_grpo(int64_t bs, int64_t seq_len, const double *lp, const double
             for (int64_t t = 0; t < seq_len; ++t) {
                 int64_t i = r * seq_len + t;
                 if (mask[i] == 0) { grad[i] = 0.0; continue; }
-                token_term(lp, old, ref, adv[r], i, beta, lo, hi, &slope);
+                token_term(lp, old, ref, adv[r], i, beta, lo, hi, sign_aware, &slope);
                 grad[i] = slope / (denom * (double)bs);
             }
     }
     *loss = bs > 0 ? total / (double)bs : 0.0;   /* mean over the bs rows */
     return 0;
+}
+
+/* The card's literal per_token (-A * min(ratio, clipped)) ... */
+int rlpl_oracle_bnpo(int64_t bs, int64_t seq_len, const double *lp, const double *old,
+                     const double *ref, const double *adv, const uint8_t *mask,
+                     double beta, double eps, double eps_high,
+                     double *loss, double *grad, int64_t *n_valid)
+{
+    return bnpo(bs, seq_len, lp, old, ref, adv, mask, beta, eps, eps_high, 0, loss, grad, n_valid);
+}
+
+int rlpl_oracle_grpo(int64_t bs, int64_t seq_len, const double *lp, const double *old,
+                     const double *ref, const double *adv, const uint8_t *mask,
+                     double beta, double eps, double eps_high,
+                     double *loss, double *grad, int64_t *n_valid)
+{
+    return grpo(bs, seq_len, lp, old, ref, adv, mask, beta, eps, eps_high, 0, loss, grad, n_valid);
+}
+
+/* ... and the sign-aware PPO per_token (-min(A*ratio, A*clipped)), same normalisations. */
+int rlpl_oracle_bnpo_ppo(int64_t bs, int64_t seq_len, const double *lp, const double *old,
+                         const double *ref, const double *adv, const uint8_t *mask,
+                         double beta, double eps, double eps_high,
+                         double *loss, double *grad, int64_t *n_valid)
+{
+    return bnpo(bs, seq_len, lp, old, ref, adv, mask, beta, eps, eps_high, 1, loss, grad, n_valid);
+}
+
+int rlpl_oracle_grpo_ppo(int64_t bs, int64_t seq_len, const double *lp, const double *old,
+                         const double *ref, const double *adv, const uint8_t *mask,
+                         double beta, double eps, double eps_high,
+                         double *loss, double *grad, int64_t *n_valid)
+{
+    return grpo(bs, seq_len, lp, old, ref, adv, mask, beta, eps, eps_high, 1, loss, grad, n_valid);
 }
 
 /*

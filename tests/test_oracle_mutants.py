@@ -12,6 +12,7 @@ import pytest
 
 import oracle
 import test_oracle
+import test_oracle_ppo
 import test_oracle_vocab
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "rlpl_oracle.c")
@@ -28,12 +29,17 @@ MUTANTS = {
     "upper bound uses eps": ("hi = 1.0 + eps_high;", "hi = 1.0 + eps;"),
     "beta dropped": ("term += beta * kl;", "term += kl;"),
     "advantage of row 0 everywhere": (
-        "sum += token_term(lp, old, ref, adv[r], i, beta, lo, hi, &slope);",
-        "sum += token_term(lp, old, ref, adv[0], i, beta, lo, hi, &slope);"),
+        "sum += token_term(lp, old, ref, adv[r], i, beta, lo, hi, sign_aware, &slope);",
+        "sum += token_term(lp, old, ref, adv[0], i, beta, lo, hi, sign_aware, &slope);"),
     "bnpo denominator not clamped": ("    if (denom < 1.0) denom = 1.0;   /* max(mask.sum(), 1) */\n", ""),
     "grpo grad misses 1/bs": ("grad[i] = slope / (denom * (double)bs);", "grad[i] = slope / denom;"),
     "grpo mean over valid rows": None,   # built by hand below
     "rkl grad not normalised": ("grad[i] = slope / (double)n;", "grad[i] = slope;"),
+    "ppo picks the max objective": ("if (unclipped_obj <= clipped_obj) {", "if (unclipped_obj >= clipped_obj) {"),
+    "ppo clipped branch has a slope": ("    *slope = 0.0;                /* the clipped objective is a constant in lp */",
+                                       "    *slope = -adv * clipped;"),
+    "ppo uses the literal min for every sign": ("double unclipped_obj = adv * ratio, clipped_obj = adv * clipped;",
+                                                "double unclipped_obj = ratio, clipped_obj = clipped;"),
     "vocab forward KL instead of reverse": ("kl += exp(log_p) * (log_p - log_q);",
                                             "kl += exp(log_q) * (log_q - log_p);"),
     "vocab grad misses -kl_row": ("g[v] = exp(log_p) * (log_p - log_q - kl) / (double)n;",
@@ -53,23 +59,29 @@ MUTANTS = {
 
 
 def _pins():
-    return [(name, fn) for mod in (test_oracle, test_oracle_vocab)
+    return [(name, fn) for mod in (test_oracle, test_oracle_ppo, test_oracle_vocab)
             for name, fn in inspect.getmembers(mod, inspect.isfunction)
             if name.startswith("test_") and "generator" not in name]
+
+
+def _param_sets(fn):
+    """Keyword-argument sets of a pin: the product of its parametrize marks."""
+    sets = [{}]
+    for m in getattr(fn, "pytestmark", []):
+        if m.name != "parametrize":
+            continue
+        names = [n.strip() for n in m.args[0].split(",")] if isinstance(m.args[0], str) else list(m.args[0])
+        vals = [v if len(names) > 1 else (v,) for v in m.args[1]]
+        sets = [dict(s, **dict(zip(names, v))) for s in sets for v in vals]
+    return sets
 
 
 def _run_pins():
     failed = []
     for name, fn in _pins():
-        sig = inspect.signature(fn)
-        params = [[]]
-        mark = getattr(fn, "pytestmark", [])
-        for m in mark:
-            if m.name == "parametrize":
-                params = [[v] for v in m.args[1]]
-        for p in params:
+        for kw in _param_sets(fn):
             try:
-                fn(*p)
+                fn(**kw)
             except (AssertionError, ValueError):
                 failed.append(name)
                 break
