@@ -142,6 +142,35 @@ int grpo_loss_fwd(const void* policy_lp, const void* old_lp, const void* ref_lp,
                   float* loss_out, uint32_t* n_valid_out,
                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Flags of rlpl_policy_loss. */
+enum rlpl_flags {
+    RLPL_CLIP_SIGN_AWARE = 1   /* per_token = -min(A*ratio, A*clipped) (see below) */
+};
+
+/*
+ * The policy losses with options (model card, "BNPO Loss" and "GRPO Loss").
+ * op is RLPL_OP_BNPO, RLPL_OP_BNPO_FWD, RLPL_OP_GRPO or RLPL_OP_GRPO_FWD;
+ * flags 0 gives exactly the corresponding entry point above (grad_out is
+ * ignored, and may be NULL, for the _FWD ops).
+ *
+ * RLPL_CLIP_SIGN_AWARE replaces the card's literal per_token
+ * -A*min(ratio, clipped) by the standard PPO clipped objective that the card
+ * calls "PPO-clipped":
+ *
+ *   per_token = -min(A*ratio, A*clip(ratio, 1 - epsilon, 1 + epsilon_high))
+ *
+ * which is the same where A >= 0 and -A*max(ratio, 1 - epsilon) where A < 0
+ * (so epsilon matters).  Where the two objectives tie, the unclipped branch
+ * is taken: the policy part of the gradient is -A*ratio on the unclipped
+ * branch and 0 on the clipped one.  Unknown flag bits give RLPL_ERR_PARAM;
+ * every other argument is as for bnpo_loss / grpo_loss.
+ */
+int rlpl_policy_loss(int op, uint32_t flags, const void* policy_lp, const void* old_lp,
+                     const void* ref_lp, const void* advantages, const void* mask, int64_t bs,
+                     int64_t seq_len, int dtype, int mask_dtype, float beta, float epsilon,
+                     float epsilon_high, float* loss_out, void* grad_out, uint32_t* n_valid_out,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /*
  * Reverse KL(student || teacher) self-distillation on per-token log-probs
  * (model card, "Reverse KL": global token mean with the unclamped

@@ -19,6 +19,15 @@ Entry points (model card "Geometric-AI Kernels": sections "BNPO Loss",
 * ``reverse_kl_logits(student_logits, teacher_logits, mask)`` -> (loss, grad);
   ``reverse_kl_logits_fwd(...)`` -> loss  (full (*, V) logit rows, the card's softmax form)
 
+Autograd-aware forms (``rl_post_loss_amd.autograd``): ``bnpo_loss_autograd``,
+``grpo_loss_autograd``, ``reverse_kl_autograd`` and ``reverse_kl_logits_autograd``
+return the loss as a differentiable tensor (torch custom ops over the same
+kernels; ``loss.backward()`` and ``torch.compile(fullgraph=True)`` work).
+
+The policy losses take ``clip="literal"`` (the card's per_token
+-A*min(ratio, clipped)) or ``clip="sign_aware"`` (the standard PPO
+-min(A*ratio, A*clipped); C entry point ``rlpl_policy_loss``).
+
 ``loss`` is a 0-d float32 tensor on the device; ``grad`` has the dtype and
 shape of the policy/student log-probs.  Pass ``return_n_valid=True`` to also
 get the valid-token count(s) as an int32 tensor (one entry, or bs for GRPO).
@@ -38,7 +47,8 @@ from . import build as _build
 
 __all__ = ["bnpo_loss", "bnpo_loss_fwd", "grpo_loss", "grpo_loss_fwd", "reverse_kl",
            "reverse_kl_fwd", "library", "library_path", "RlplError", "STATUS", "workspace_for",
-           "launch_shape", "reverse_kl_logits", "reverse_kl_logits_fwd"]
+           "launch_shape", "reverse_kl_logits", "reverse_kl_logits_fwd", "bnpo_loss_autograd",
+           "grpo_loss_autograd", "reverse_kl_autograd", "reverse_kl_logits_autograd"]
 
 STATUS = {0: "RLPL_OK", 1: "RLPL_ERR_NULL", 2: "RLPL_ERR_SHAPE", 3: "RLPL_ERR_ALIGN",
           4: "RLPL_ERR_DTYPE", 5: "RLPL_ERR_PARAM", 6: "RLPL_ERR_WORKSPACE", 7: "RLPL_ERR_DEVICE",
@@ -79,6 +89,8 @@ def _declare(lib):
     for name, args in (("reverse_kl_logits", rkl), ("reverse_kl_logits_fwd", rkl_fwd)):
         f = getattr(lib, name)
         f.argtypes, f.restype = args, ctypes.c_int
+    lib.rlpl_policy_loss.argtypes = [i32, ctypes.c_uint32] + policy
+    lib.rlpl_policy_loss.restype = ctypes.c_int
     lib.rlpl_workspace_bytes.argtypes, lib.rlpl_workspace_bytes.restype = [i64, i64, i32], sz
     lib.rlpl_workspace_flags.argtypes = [vp, ctypes.POINTER(ctypes.c_uint32), vp]
     lib.rlpl_workspace_flags.restype = ctypes.c_int
@@ -154,8 +166,11 @@ def _workspace(dev, stream, op, workspace):
     return workspace
 
 
+CLIP = {"literal": 0, "sign_aware": 1}   # rlpl_policy_loss flags (RLPL_CLIP_SIGN_AWARE)
+
+
 def _policy(op: str, fused: bool, policy_logprobs, old_policy_logprobs, ref_logprobs, advantages,
-            completions_mask, epsilon, epsilon_high, beta, return_n_valid, workspace):
+            completions_mask, epsilon, epsilon_high, beta, return_n_valid, workspace, clip="literal"):
     lp = policy_logprobs.detach()
     if lp.dtype not in DTYPE:
         raise TypeError("log-probs must be float32, float16 or bfloat16")
@@ -178,15 +193,22 @@ def _policy(op: str, fused: bool, policy_logprobs, old_policy_logprobs, ref_logp
     grad = torch.empty_like(lp) if fused else None
     n = torch.empty(bs if op.startswith("grpo") else 1, dtype=torch.int32, device=dev) \
         if return_n_valid else None
+    if clip not in CLIP:
+        raise ValueError(f"clip must be one of {sorted(CLIP)}")
     lib = library()
     name = f"{op}_loss" + ("" if fused else "_fwd")
     args = [lp.data_ptr(), old.data_ptr(), None if ref is None else ref.data_ptr(), adv.data_ptr(),
             mask.data_ptr(), bs, T, DTYPE[lp.dtype], MASK_DTYPE[mask.dtype], beta, float(epsilon),
             float(eps_high), loss.data_ptr()]
-    if fused:
-        args.append(grad.data_ptr())
-    args += [None if n is None else n.data_ptr(), ws.data_ptr(), ws.numel(), stream]
-    _check(name, getattr(lib, name)(*args))
+    if clip == "literal":
+        if fused:
+            args.append(grad.data_ptr())
+        args += [None if n is None else n.data_ptr(), ws.data_ptr(), ws.numel(), stream]
+        _check(name, getattr(lib, name)(*args))
+    else:
+        args.append(grad.data_ptr() if fused else None)
+        args += [None if n is None else n.data_ptr(), ws.data_ptr(), ws.numel(), stream]
+        _check("rlpl_policy_loss", lib.rlpl_policy_loss(OP[op if fused else op + "_fwd"], CLIP[clip], *args))
     out = (loss, grad) if fused else (loss,)
     if return_n_valid:
         out = out + (n,)
@@ -194,31 +216,35 @@ def _policy(op: str, fused: bool, policy_logprobs, old_policy_logprobs, ref_logp
 
 
 def bnpo_loss(policy_logprobs, old_policy_logprobs, ref_logprobs, advantages, completions_mask, *,
-              epsilon=0.2, epsilon_high=None, beta=0.0, return_n_valid=False, workspace=None):
+              epsilon=0.2, epsilon_high=None, beta=0.0, return_n_valid=False, workspace=None,
+              clip="literal"):
     """BNPO fused forward+backward: (loss, d loss / d policy_logprobs) from one launch."""
     return _policy("bnpo", True, policy_logprobs, old_policy_logprobs, ref_logprobs, advantages,
-                   completions_mask, epsilon, epsilon_high, beta, return_n_valid, workspace)
+                   completions_mask, epsilon, epsilon_high, beta, return_n_valid, workspace, clip)
 
 
 def bnpo_loss_fwd(policy_logprobs, old_policy_logprobs, ref_logprobs, advantages, completions_mask,
-                  *, epsilon=0.2, epsilon_high=None, beta=0.0, return_n_valid=False, workspace=None):
+                  *, epsilon=0.2, epsilon_high=None, beta=0.0, return_n_valid=False, workspace=None,
+                  clip="literal"):
     """BNPO forward only: the scalar loss, no gradient buffer."""
     return _policy("bnpo", False, policy_logprobs, old_policy_logprobs, ref_logprobs, advantages,
-                   completions_mask, epsilon, epsilon_high, beta, return_n_valid, workspace)
+                   completions_mask, epsilon, epsilon_high, beta, return_n_valid, workspace, clip)
 
 
 def grpo_loss(policy_logprobs, old_policy_logprobs, ref_logprobs, advantages, completions_mask, *,
-              epsilon=0.2, epsilon_high=None, beta=0.0, return_n_valid=False, workspace=None):
+              epsilon=0.2, epsilon_high=None, beta=0.0, return_n_valid=False, workspace=None,
+              clip="literal"):
     """GRPO (per-response normalised) fused forward+backward: (loss, grad)."""
     return _policy("grpo", True, policy_logprobs, old_policy_logprobs, ref_logprobs, advantages,
-                   completions_mask, epsilon, epsilon_high, beta, return_n_valid, workspace)
+                   completions_mask, epsilon, epsilon_high, beta, return_n_valid, workspace, clip)
 
 
 def grpo_loss_fwd(policy_logprobs, old_policy_logprobs, ref_logprobs, advantages, completions_mask,
-                  *, epsilon=0.2, epsilon_high=None, beta=0.0, return_n_valid=False, workspace=None):
+                  *, epsilon=0.2, epsilon_high=None, beta=0.0, return_n_valid=False, workspace=None,
+                  clip="literal"):
     """GRPO forward only: the scalar loss."""
     return _policy("grpo", False, policy_logprobs, old_policy_logprobs, ref_logprobs, advantages,
-                   completions_mask, epsilon, epsilon_high, beta, return_n_valid, workspace)
+                   completions_mask, epsilon, epsilon_high, beta, return_n_valid, workspace, clip)
 
 
 def _rkl(fused: bool, student_logprobs, teacher_logprobs, completions_mask, return_n_valid, workspace):
@@ -305,3 +331,7 @@ def reverse_kl_logits_fwd(student_logits, teacher_logits, completions_mask, *, r
                           workspace=None):
     """Reverse KL over full logit rows, forward only: the scalar loss (one read of each valid row)."""
     return _rkl_logits(False, student_logits, teacher_logits, completions_mask, return_n_valid, workspace)
+
+
+from .autograd import (bnpo_loss_autograd, grpo_loss_autograd, reverse_kl_autograd,  # noqa: E402
+                       reverse_kl_logits_autograd)

@@ -1,0 +1,113 @@
+"""Autograd-aware entry points (model card "Geometric-AI Kernels", section
+"Entry points": ``<name>_autograd``, the same kernel registered as a torch
+custom op with an autograd formula, so that ``loss.backward()`` works and the
+call traces under ``torch.compile(fullgraph=True)``).
+
+Each op runs the fused forward+backward launch of the C ABI once, returns the
+loss and keeps the gradient the launch wrote; backward multiplies that
+gradient by the incoming scalar gradient of the loss (the chain rule for a
+scalar loss).  There is no other computation and no fallback: the ops call the
+same HIP kernels as the direct entry points.
+
+The direct entry points stay the lowest-overhead path; these add the custom-op
+dispatch (and, under compile, a graph break-free call).
+"""
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import torch
+
+from . import _policy, _rkl, _rkl_logits
+
+__all__ = ["bnpo_loss_autograd", "grpo_loss_autograd", "reverse_kl_autograd",
+           "reverse_kl_logits_autograd"]
+
+_LIB = "rlpl"
+
+
+def _policy_op(op: str):
+    @torch.library.custom_op(f"{_LIB}::{op}_loss", mutates_args=())
+    def fused(policy_logprobs: torch.Tensor, old_policy_logprobs: torch.Tensor,
+              ref_logprobs: Optional[torch.Tensor], advantages: torch.Tensor,
+              completions_mask: torch.Tensor, epsilon: float, epsilon_high: float,
+              beta: float, sign_aware: bool) -> Tuple[torch.Tensor, torch.Tensor]:
+        loss, grad = _policy(op, True, policy_logprobs, old_policy_logprobs, ref_logprobs, advantages,
+                             completions_mask, epsilon, epsilon_high, beta, False, None,
+                             "sign_aware" if sign_aware else "literal")
+        return loss, grad
+
+    @fused.register_fake
+    def _(policy_logprobs, old_policy_logprobs, ref_logprobs, advantages, completions_mask, epsilon,
+          epsilon_high, beta, sign_aware):
+        return (policy_logprobs.new_empty((), dtype=torch.float32), torch.empty_like(policy_logprobs))
+
+    def setup_context(ctx, inputs, output):
+        ctx.save_for_backward(output[1])
+
+    def backward(ctx, grad_loss, _grad_of_grad):
+        (g,) = ctx.saved_tensors
+        return (g * grad_loss.to(g.dtype), None, None, None, None, None, None, None, None)
+
+    fused.register_autograd(backward, setup_context=setup_context)
+    return fused
+
+
+def _rkl_op(name: str, direct):
+    @torch.library.custom_op(f"{_LIB}::{name}", mutates_args=())
+    def fused(student: torch.Tensor, teacher: torch.Tensor,
+              completions_mask: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
+        loss, grad = direct(True, student, teacher, completions_mask, False, None)
+        return loss, grad
+
+    @fused.register_fake
+    def _(student, teacher, completions_mask):
+        return student.new_empty((), dtype=torch.float32), torch.empty_like(student)
+
+    def setup_context(ctx, inputs, output):
+        ctx.save_for_backward(output[1])
+
+    def backward(ctx, grad_loss, _grad_of_grad):
+        (g,) = ctx.saved_tensors
+        return g * grad_loss.to(g.dtype), None, None
+
+    fused.register_autograd(backward, setup_context=setup_context)
+    return fused
+
+
+_bnpo = _policy_op("bnpo")
+_grpo = _policy_op("grpo")
+_rkl_tok = _rkl_op("reverse_kl", _rkl)
+_rkl_vocab = _rkl_op("reverse_kl_logits", _rkl_logits)
+
+
+def bnpo_loss_autograd(policy_logprobs, old_policy_logprobs, ref_logprobs, advantages, completions_mask, *,
+                       epsilon=0.2, epsilon_high=None, beta=0.0, clip="literal"):
+    """BNPO loss as a differentiable 0-d float32 tensor (gradient flows to policy_logprobs)."""
+    eh = epsilon if epsilon_high is None else epsilon_high
+    return _bnpo(policy_logprobs, old_policy_logprobs, ref_logprobs, advantages, completions_mask,
+                 float(epsilon), float(eh), float(beta), _sign_aware(clip))[0]
+
+
+def grpo_loss_autograd(policy_logprobs, old_policy_logprobs, ref_logprobs, advantages, completions_mask, *,
+                       epsilon=0.2, epsilon_high=None, beta=0.0, clip="literal"):
+    """GRPO loss as a differentiable 0-d float32 tensor."""
+    eh = epsilon if epsilon_high is None else epsilon_high
+    return _grpo(policy_logprobs, old_policy_logprobs, ref_logprobs, advantages, completions_mask,
+                 float(epsilon), float(eh), float(beta), _sign_aware(clip))[0]
+
+
+def _sign_aware(clip: str) -> bool:
+    if clip not in ("literal", "sign_aware"):
+        raise ValueError("clip must be 'literal' or 'sign_aware'")
+    return clip == "sign_aware"
+
+
+def reverse_kl_autograd(student_logprobs, teacher_logprobs, completions_mask):
+    """Per-token reverse KL as a differentiable 0-d float32 tensor (gradient flows to the student)."""
+    return _rkl_tok(student_logprobs, teacher_logprobs, completions_mask)[0]
+
+
+def reverse_kl_logits_autograd(student_logits, teacher_logits, completions_mask):
+    """Full-vocab reverse KL as a differentiable 0-d float32 tensor (gradient flows to the student logits)."""
+    return _rkl_vocab(student_logits, teacher_logits, completions_mask)[0]

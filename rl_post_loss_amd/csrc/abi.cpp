@@ -185,7 +185,7 @@ int run(int mode, bool write_grad, bool has_kl, Args& a, int dtype, hipStream_t 
     return launch(kernel, a, sh.grid, stream);
 }
 
-int policy_loss(int mode, bool write_grad, const void* policy_lp, const void* old_lp,
+int policy_loss(int mode, bool write_grad, bool sign_aware, const void* policy_lp, const void* old_lp,
                 const void* ref_lp, const void* advantages, const void* mask, int64_t bs,
                 int64_t seq_len, int dtype, int mask_dtype, float beta, float epsilon,
                 float epsilon_high, float* loss_out, void* grad_out, uint32_t* n_valid_out,
@@ -218,7 +218,9 @@ int policy_loss(int mode, bool write_grad, const void* policy_lp, const void* ol
     a.seq_len = int32_t(seq_len);
     a.bs = int32_t(bs);
     a.beta = beta;
+    a.lo = lo;
     a.hi = hi;
+    a.sign_aware = sign_aware ? 1u : 0u;
     return run(mode, write_grad, has_kl, a, dtype, stream);
 }
 
@@ -313,7 +315,7 @@ int bnpo_loss(const void* policy_lp, const void* old_lp, const void* ref_lp, con
               const void* mask, int64_t bs, int64_t seq_len, int dtype, int mask_dtype, float beta,
               float epsilon, float epsilon_high, float* loss_out, void* grad_out,
               uint32_t* n_valid_out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    return policy_loss(kModeBNPO, true, policy_lp, old_lp, ref_lp, advantages, mask, bs, seq_len,
+    return policy_loss(kModeBNPO, true, false, policy_lp, old_lp, ref_lp, advantages, mask, bs, seq_len,
                        dtype, mask_dtype, beta, epsilon, epsilon_high, loss_out, grad_out,
                        n_valid_out, workspace, workspace_bytes, stream);
 }
@@ -323,7 +325,7 @@ int bnpo_loss_fwd(const void* policy_lp, const void* old_lp, const void* ref_lp,
                   int mask_dtype, float beta, float epsilon, float epsilon_high, float* loss_out,
                   uint32_t* n_valid_out, void* workspace, size_t workspace_bytes,
                   hipStream_t stream) {
-    return policy_loss(kModeBNPO, false, policy_lp, old_lp, ref_lp, advantages, mask, bs, seq_len,
+    return policy_loss(kModeBNPO, false, false, policy_lp, old_lp, ref_lp, advantages, mask, bs, seq_len,
                        dtype, mask_dtype, beta, epsilon, epsilon_high, loss_out, nullptr,
                        n_valid_out, workspace, workspace_bytes, stream);
 }
@@ -332,7 +334,7 @@ int grpo_loss(const void* policy_lp, const void* old_lp, const void* ref_lp, con
               const void* mask, int64_t bs, int64_t seq_len, int dtype, int mask_dtype, float beta,
               float epsilon, float epsilon_high, float* loss_out, void* grad_out,
               uint32_t* n_valid_out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    return policy_loss(kModeGRPO, true, policy_lp, old_lp, ref_lp, advantages, mask, bs, seq_len,
+    return policy_loss(kModeGRPO, true, false, policy_lp, old_lp, ref_lp, advantages, mask, bs, seq_len,
                        dtype, mask_dtype, beta, epsilon, epsilon_high, loss_out, grad_out,
                        n_valid_out, workspace, workspace_bytes, stream);
 }
@@ -342,8 +344,29 @@ int grpo_loss_fwd(const void* policy_lp, const void* old_lp, const void* ref_lp,
                   int mask_dtype, float beta, float epsilon, float epsilon_high, float* loss_out,
                   uint32_t* n_valid_out, void* workspace, size_t workspace_bytes,
                   hipStream_t stream) {
-    return policy_loss(kModeGRPO, false, policy_lp, old_lp, ref_lp, advantages, mask, bs, seq_len,
+    return policy_loss(kModeGRPO, false, false, policy_lp, old_lp, ref_lp, advantages, mask, bs, seq_len,
                        dtype, mask_dtype, beta, epsilon, epsilon_high, loss_out, nullptr,
+                       n_valid_out, workspace, workspace_bytes, stream);
+}
+
+int rlpl_policy_loss(int op, uint32_t flags, const void* policy_lp, const void* old_lp,
+                     const void* ref_lp, const void* advantages, const void* mask, int64_t bs,
+                     int64_t seq_len, int dtype, int mask_dtype, float beta, float epsilon,
+                     float epsilon_high, float* loss_out, void* grad_out, uint32_t* n_valid_out,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if ((flags & ~uint32_t(RLPL_CLIP_SIGN_AWARE)) != 0u) return RLPL_ERR_PARAM;
+    const bool sign_aware = (flags & RLPL_CLIP_SIGN_AWARE) != 0u;
+    int mode;
+    bool fused;
+    switch (op) {
+    case RLPL_OP_BNPO: mode = kModeBNPO; fused = true; break;
+    case RLPL_OP_BNPO_FWD: mode = kModeBNPO; fused = false; break;
+    case RLPL_OP_GRPO: mode = kModeGRPO; fused = true; break;
+    case RLPL_OP_GRPO_FWD: mode = kModeGRPO; fused = false; break;
+    default: return RLPL_ERR_PARAM;
+    }
+    return policy_loss(mode, fused, sign_aware, policy_lp, old_lp, ref_lp, advantages, mask, bs, seq_len,
+                       dtype, mask_dtype, beta, epsilon, epsilon_high, loss_out, fused ? grad_out : nullptr,
                        n_valid_out, workspace, workspace_bytes, stream);
 }
 

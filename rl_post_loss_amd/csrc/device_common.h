@@ -97,6 +97,16 @@ struct Plane {
         }
     }
     __device__ __forceinline__ float get(int k) const { return Elem<T>::get(d.w, k); }
+    // Moves every element down one position (element k+1 becomes k; the last
+    // becomes 0), with static register indices only.
+    __device__ __forceinline__ void rotate() {
+#pragma unroll
+        for (int i = 0; i < kWords; ++i) {
+            const uint32_t next = i + 1 < kWords ? d.w[i + 1] : 0u;
+            if constexpr (sizeof(T) == 4) d.w[i] = next;
+            else d.w[i] = __builtin_amdgcn_alignbit(next, d.w[i], 16);
+        }
+    }
 };
 
 // A lane's gradient values, converted to T and stored.

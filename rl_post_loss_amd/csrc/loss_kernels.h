@@ -100,7 +100,9 @@ struct Args {
     uint32_t row_magic;    // s / seq_len == (s * row_magic) >> row_shift for every s < 2^31
     uint32_t row_shift;
     float beta;
-    float hi;              // 1 + epsilon_high (the lower bound 1 - epsilon never changes a result)
+    float lo;              // 1 - epsilon (used only by the sign-aware form, where A < 0)
+    float hi;              // 1 + epsilon_high
+    uint32_t sign_aware;   // per_token = -min(A*ratio, A*clipped) instead of -A*min(ratio, clipped)
 };
 
 // The kernel instantiation for (dtype, mode, KL on/off, gradient on/off, VEC), or NULL.

@@ -74,6 +74,12 @@ struct Mask {
         return o != 0;
     }
     __device__ __forceinline__ bool valid(int k) const { return ((d.w[k >> 2] >> (8 * (k & 3))) & 0xFFu) != 0; }
+    // Moves every byte down one position (byte k+1 becomes k; the last becomes 0).
+    __device__ __forceinline__ void rotate() {
+#pragma unroll
+        for (int i = 0; i < VEC / 4; ++i)
+            d.w[i] = __builtin_amdgcn_alignbit(i + 1 < VEC / 4 ? d.w[i + 1] : 0u, d.w[i], 8);
+    }
     // Number of nonzero bytes: for each byte, (b & 0x7F) + 0x7F sets bit 7 iff the low 7 bits
     // are nonzero; OR-ing b itself covers bit 7.
     __device__ __forceinline__ uint32_t count() const {
@@ -111,21 +117,26 @@ struct Mask {
 // exp on the hardware base-2 exponential unit.
 __device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 
-// Per-row coefficients of the per-token terms: c = ac*min(ratio, hi) + bc*kl
-// and g = [ratio <= hi]*ag*ratio - bg*(exp(ref - lp) - 1), where ac = -A and
+// Per-row coefficients of the per-token terms: c = ac*med3(ratio, L, H) + bc*kl
+// and g = [unclipped]*ag*ratio - bg*(exp(ref - lp) - 1), where ac = -A and
 // bc = beta, and ag, bg are the same times the gradient's scale wherever that
 // is known before the tile is computed.  GRPO's per-row scale (an LDS value)
 // multiplies c and g afterwards: folded into the coefficients it made every
 // product wait for the LDS read and cost 17 VGPRs (one fewer wave per SIMD).
 struct Coef {
     float ac, ag, bc, bg;
+    float L, H;   // clip bounds of the row: (-inf, 1+eps_high), or (1-eps, +inf) where the
+                  // sign-aware form meets A < 0
 };
 
 // Per-token contribution c = per_token + beta*kl and its derivative g in lp.
-// min(ratio, clip(ratio, lo, hi)) equals min(ratio, hi) for every ratio, so the
-// lower clip bound never enters; ties at ratio == hi take the unclipped branch.
+// The literal per_token -A*min(ratio, clip(ratio, lo, hi)) is -A*min(ratio, hi)
+// for every ratio (the lower bound never enters); the sign-aware
+// -min(A*ratio, A*clip(ratio, lo, hi)) is the same where A >= 0 and
+// -A*max(ratio, lo) where A < 0.  Both are ac*med3(ratio, L, H) with the row's
+// bounds, and the unclipped branch (ties included) is exactly chosen == ratio.
 template <int MODE, bool HAS_KL>
-__device__ __forceinline__ void token_terms(float lp, float old, float ref, const Coef& k, float hi,
+__device__ __forceinline__ void token_terms(float lp, float old, float ref, const Coef& k,
                                             float& c, float& g) {
     if constexpr (MODE == kModeRKL) {
         const float x = ref - lp;                 // teacher - student
@@ -134,8 +145,9 @@ __device__ __forceinline__ void token_terms(float lp, float old, float ref, cons
         g = em1 * k.ag;                           // ag = -scale: d/dstudent = 1 - exp(x)
     } else {
         const float ratio = fast_exp(lp - old);
-        c = k.ac * fminf(ratio, hi);
-        g = (ratio <= hi) ? k.ag * ratio : 0.0f;
+        const float chosen = __builtin_amdgcn_fmed3f(ratio, k.L, k.H);
+        c = k.ac * chosen;
+        g = (chosen == ratio) ? k.ag * ratio : 0.0f;
         if constexpr (HAS_KL) {
             const float x = ref - lp;
             const float em1 = fast_exp(x) - 1.0f;
@@ -222,6 +234,9 @@ __device__ __forceinline__ void load_planes(const Args& a, uint32_t s, Lane<T, V
 template <int MODE>
 __device__ __forceinline__ Coef row_coef(const Args& a, float A, float row_scale, float gscale) {
     Coef k;
+    const bool low_clip = a.sign_aware != 0u && A < 0.0f;
+    k.L = low_clip ? a.lo : -__builtin_inff();
+    k.H = low_clip ? __builtin_inff() : a.hi;
     if constexpr (MODE == kModeRKL) {
         k.ac = k.bc = 0.0f;
         k.ag = -gscale;
@@ -251,28 +266,43 @@ __device__ __forceinline__ float lane_terms(const Args& a, uint32_t s, const Lan
     if constexpr (MODE != kModeRKL) A = load_adv<T>(a.adv, r);
     if constexpr (MODE == kModeGRPO) rs = row_scale[r - row_base];
     Coef k = row_coef<MODE>(a, A, rs, gscale);
-    if (t + VEC <= T_len) {
-        // All VEC slots in one row (always, when seq_len is a multiple of VEC): branch-free.
+    if (MODE == kModeRKL || t + VEC <= T_len) {
+        // All VEC slots in one row (always, when seq_len is a multiple of VEC; the
+        // reverse-KL terms do not depend on the row at all): branch-free.
 #pragma unroll
         for (int i = 0; i < VEC; ++i) {
             float c, gi;
             token_terms<MODE, HAS_KL>(L.lp.get(i), MODE == kModeRKL ? 0.0f : L.old.get(i),
-                                      HAS_KL ? L.ref.get(i) : 0.0f, k, a.hi, c, gi);
+                                      HAS_KL ? L.ref.get(i) : 0.0f, k, c, gi);
             if constexpr (MODE == kModeGRPO) { c *= rs; gi *= rs; }
             part += L.m.valid(i) ? c : 0.0f;
             g[i] = gi;
         }
     } else {
-        // The lane crosses a row boundary: track the row slot by slot.
+        // The lane crosses a row boundary: slot by slot, tracking the row.  A rolled
+        // loop keeps one slot's terms live (this path is rare: only lanes that
+        // straddle a row end); it always works on slot 0 of a copy of the lane
+        // that rotates down one slot per step, and the derivatives rotate in at
+        // the top, so that every register index stays static.
+        Lane<T, VEC> R = L;
+        float out[VEC];
 #pragma unroll
+        for (int i = 0; i < VEC; ++i) out[i] = 0.0f;
+#pragma unroll 1
         for (int i = 0; i < VEC; ++i) {
             float c, gi;
-            token_terms<MODE, HAS_KL>(L.lp.get(i), MODE == kModeRKL ? 0.0f : L.old.get(i),
-                                      HAS_KL ? L.ref.get(i) : 0.0f, k, a.hi, c, gi);
+            token_terms<MODE, HAS_KL>(R.lp.get(0), MODE == kModeRKL ? 0.0f : R.old.get(0),
+                                      HAS_KL ? R.ref.get(0) : 0.0f, k, c, gi);
             if constexpr (MODE == kModeGRPO) { c *= rs; gi *= rs; }
-            part += L.m.valid(i) ? c : 0.0f;
-            g[i] = gi;
-            if (i + 1 < VEC && ++t == T_len) {
+            part += R.m.valid(0) ? c : 0.0f;
+#pragma unroll
+            for (int j = 0; j + 1 < VEC; ++j) out[j] = out[j + 1];
+            out[VEC - 1] = gi;
+            R.m.rotate();
+            R.lp.rotate();
+            if constexpr (MODE != kModeRKL) R.old.rotate();
+            if constexpr (HAS_KL) R.ref.rotate();
+            if (++t == T_len) {
                 t = 0;
                 ++r;
                 if (r < uint32_t(a.bs)) {
@@ -282,6 +312,8 @@ __device__ __forceinline__ float lane_terms(const Args& a, uint32_t s, const Lan
                 }
             }
         }
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) g[i] = out[i];
     }
     return part;
 }

@@ -83,6 +83,21 @@ def rkl_grad_magnitude(student, teacher, scale):
     return (1.0 + np.exp(oracle.to_f64(teacher) - oracle.to_f64(student))) * scale
 
 
+def sign_aware_kinks(grad_ref, x, epsilon, epsilon_high, scale):
+    """Kink tokens of the sign-aware form (ratio within 1e-5 of the bound that
+    clips for the token's sign of A) and the oracle gradient with the other
+    branch taken there."""
+    lp, od = oracle.to_f64(x["policy"]), oracle.to_f64(x["old"])
+    a = oracle.to_f64(x["advantages"])[:, None]
+    ratio = np.exp(lp - od)
+    bound = np.where(a < 0, 1.0 - f32(epsilon), 1.0 + f32(epsilon_high))
+    kinks = (np.abs(ratio - bound) <= 1e-5 * bound) & (oracle.to_mask_u8(x["mask"]) != 0)
+    unclipped = np.where(a < 0, ratio >= bound, ratio <= bound)
+    g_pol = -a * ratio * scale
+    alt = np.where(unclipped, grad_ref - g_pol, grad_ref + g_pol)
+    return kinks, alt
+
+
 def check_loss(got: float, want: float, dtype, what=""):
     tol = 1e-5 if dtype == torch.float32 else 1e-3
     if math.isnan(want):

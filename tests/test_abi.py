@@ -45,7 +45,7 @@ def test_library_exports_every_declared_function(lib):
     assert set(names) >= {"bnpo_loss", "bnpo_loss_fwd", "grpo_loss", "grpo_loss_fwd", "reverse_kl",
                           "reverse_kl_fwd", "rlpl_workspace_bytes", "rlpl_workspace_flags",
                           "rlpl_status_string", "rlpl_version", "rlpl_launch_shape",
-                          "reverse_kl_logits", "reverse_kl_logits_fwd"}
+                          "reverse_kl_logits", "reverse_kl_logits_fwd", "rlpl_policy_loss"}
     for n in names:
         assert hasattr(lib, n), n
     assert lib.rlpl_version() == 1
@@ -254,3 +254,21 @@ def test_launch_shape_vocab_validation(lib):
     # vocab ops take (rows, vocab): 2^31 slots and more are fine there
     assert rl.STATUS[lib.rlpl_launch_shape(1 << 20, 1 << 20, 2, 6, *out)] in ("RLPL_OK", "RLPL_ERR_DEVICE")
     assert rl.STATUS[lib.rlpl_launch_shape(0, 1000, 2, 7, *out)] == "RLPL_ERR_SHAPE"
+
+
+def call_ex(lib, op=0, flags=1, **over):
+    a = _bnpo_args(**over)
+    return lib.rlpl_policy_loss(op, flags, a["lp"], a["old"], a["ref"], a["adv"], a["mask"], a["bs"], a["T"],
+                                a["dtype"], a["mask_dtype"], a["beta"], a["eps"], a["eps_high"], a["loss"],
+                                a["grad"], a["n"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+def test_policy_loss_ex_validation(lib):
+    assert rl.STATUS[call_ex(lib, flags=2)] == "RLPL_ERR_PARAM"          # unknown flag bit
+    assert rl.STATUS[call_ex(lib, op=4)] == "RLPL_ERR_PARAM"             # reverse-KL is not a policy op
+    assert rl.STATUS[call_ex(lib, op=0, grad=None)] == "RLPL_ERR_NULL"   # fused needs grad_out
+    assert rl.STATUS[call_ex(lib, op=1, grad=None, lp=None)] == "RLPL_ERR_NULL"
+    assert rl.STATUS[call_ex(lib, op=3, bs=0)] == "RLPL_ERR_SHAPE"
+    assert rl.STATUS[call_ex(lib, op=2, eps=0.5, eps_high=-0.6)] == "RLPL_ERR_PARAM"
+    if not torch.cuda.is_available():
+        assert rl.STATUS[call_ex(lib, op=1, grad=None)] == "RLPL_ERR_DEVICE"   # _FWD ignores grad_out

@@ -16,7 +16,7 @@ import oracle
 import rl_post_loss_amd as rl
 import synthetic
 from parity import (check_grad, check_loss, check_masked_zero, f32, kink_alternative, kink_tokens,
-                    policy_grad_magnitude, rkl_grad_magnitude)
+                    policy_grad_magnitude, rkl_grad_magnitude, sign_aware_kinks)
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -27,25 +27,25 @@ def dev(x):
     return {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
 
 
-def gpu_policy(op, fused, g, beta, eps, eps_high, ref=True):
+def gpu_policy(op, fused, g, beta, eps, eps_high, ref=True, clip="literal"):
     fn = {("bnpo", True): rl.bnpo_loss, ("bnpo", False): rl.bnpo_loss_fwd,
           ("grpo", True): rl.grpo_loss, ("grpo", False): rl.grpo_loss_fwd}[(op, fused)]
     out = fn(g["policy"], g["old"], g["ref"] if ref else None, g["advantages"], g["mask"],
-             epsilon=eps, epsilon_high=eps_high, beta=beta, return_n_valid=True)
+             epsilon=eps, epsilon_high=eps_high, beta=beta, return_n_valid=True, clip=clip)
     torch.cuda.synchronize()
     return out
 
 
-def oracle_policy(op, x, beta, eps, eps_high):
+def oracle_policy(op, x, beta, eps, eps_high, clip="literal"):
     fn = oracle.bnpo if op == "bnpo" else oracle.grpo
     return fn(x["policy"], x["old"], x["ref"], x["advantages"], x["mask"], f32(beta), f32(eps),
-              f32(eps_high))
+              f32(eps_high), sign_aware=clip == "sign_aware")
 
 
-def assert_policy_parity(op, x, beta, eps, eps_high, what, fused=True):
+def assert_policy_parity(op, x, beta, eps, eps_high, what, fused=True, clip="literal"):
     g = dev(x)
-    ref = oracle_policy(op, x, beta, eps, eps_high)
-    out = gpu_policy(op, fused, g, beta, eps, eps_high, ref=beta != 0.0)
+    ref = oracle_policy(op, x, beta, eps, eps_high, clip)
+    out = gpu_policy(op, fused, g, beta, eps, eps_high, ref=beta != 0.0, clip=clip)
     loss, n = (out[0], out[-1])
     dt = x["policy"].dtype
     check_loss(float(loss.cpu()), ref.loss, dt, what)
@@ -60,9 +60,12 @@ def assert_policy_parity(op, x, beta, eps, eps_high, what, fused=True):
             scale = 1.0 / max(ref.n_valid, 1)
         else:
             scale = (1.0 / (np.maximum(ref.n_valid, 1) * x["policy"].shape[0]))[:, None]
-        kinks = kink_tokens(x["policy"], x["old"], x["mask"], eps_high)
-        alt = kink_alternative(ref.grad, x["policy"], x["old"], x["advantages"], x["mask"],
-                               eps_high, scale)
+        if clip == "literal":
+            kinks = kink_tokens(x["policy"], x["old"], x["mask"], eps_high)
+            alt = kink_alternative(ref.grad, x["policy"], x["old"], x["advantages"], x["mask"],
+                                   eps_high, scale)
+        else:
+            kinks, alt = sign_aware_kinks(ref.grad, x, eps, eps_high, scale)
         mag = policy_grad_magnitude(x["policy"], x["old"], x["ref"], x["advantages"], f32(beta), scale)
         check_grad(grad, ref.grad, dt, what, alt, kinks, mag)
         check_masked_zero(grad, x["mask"], what)
@@ -307,6 +310,42 @@ def test_grpo_striding_kernel_repeats_bitwise(bs, T):
     for _ in range(3):
         again = gpu_policy("grpo", True, g, 0.04, 0.2, 0.28)
         assert torch.equal(again[0], first[0]) and torch.equal(again[1], first[1]), what
+
+
+@pytest.mark.parametrize("op", ["bnpo", "grpo"])
+@pytest.mark.parametrize("name", ["bnpo_bf16_64x4096", "bnpo_fp32_4x64", "grpo_fp16_128x2048"])
+def test_sign_aware_clip(op, name):
+    # Standard PPO -min(A*ratio, A*clipped): where A < 0 the lower bound 1-eps clips.
+    # old = policy + N(0, 0.3) here, so that ratios fall outside the clip range on both sides.
+    w = synthetic.WORKLOADS[name]
+    x = synthetic.inputs(w)
+    rng = np.random.default_rng(17)
+    x["old"] = (x["policy"].double() + 0.3 * torch.from_numpy(rng.standard_normal(tuple(x["policy"].shape)))
+                ).to(x["policy"].dtype)
+    what = f"sign-aware {op} {name}"
+    print("[parity]", what, flush=True)
+    assert_policy_parity(op, x, w.beta, w.epsilon, w.epsilon_high, what, clip="sign_aware")
+    assert_policy_parity(op, x, w.beta, w.epsilon, w.epsilon_high, what + " fwd", fused=False, clip="sign_aware")
+    # eps now changes the result (it never does in the literal form)
+    g = dev(x)
+    a = gpu_policy(op, True, g, w.beta, 0.1, w.epsilon_high, clip="sign_aware")
+    b = gpu_policy(op, True, g, w.beta, 0.3, w.epsilon_high, clip="sign_aware")
+    assert not torch.equal(a[0], b[0])
+    # and where every advantage is >= 0 it equals the literal form bit for bit
+    g["advantages"] = g["advantages"].abs()
+    c = gpu_policy(op, True, g, w.beta, w.epsilon, w.epsilon_high, clip="sign_aware")
+    d = gpu_policy(op, True, g, w.beta, w.epsilon, w.epsilon_high)
+    assert torch.equal(c[0], d[0]) and torch.equal(c[1], d[1])
+
+
+@pytest.mark.parametrize("bs,T", [(3, 37), (9, 4095), (2, 4097), (40, 1)])
+def test_sign_aware_clip_row_crossing_lanes(bs, T):
+    x = _custom("bnpo", "bf16", bs, T, "random", seed=bs + T)
+    rng = np.random.default_rng(bs)
+    x["old"] = (x["policy"].double() + 0.3 * torch.from_numpy(rng.standard_normal((bs, T)))).to(torch.bfloat16)
+    x["advantages"] = torch.from_numpy(rng.standard_normal(bs)).to(torch.bfloat16)
+    for op in ("bnpo", "grpo"):
+        assert_policy_parity(op, x, 0.04, 0.2, 0.28, f"sign-aware {op} {bs}x{T}", clip="sign_aware")
 
 
 def test_grpo_rows_longer_than_a_tile():
