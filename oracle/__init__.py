@@ -55,6 +55,8 @@ def _load():
     lib.rlpl_oracle_bnpo_ppo.argtypes = [i64, i64, dp, dp, dp, dp, u8p, d, d, d, dp, dp, i64p]
     lib.rlpl_oracle_grpo_ppo.argtypes = [i64, i64, dp, dp, dp, dp, u8p, d, d, d, dp, dp, i64p]
     lib.rlpl_oracle_rkl_logits.argtypes = [i64, i64, dp, dp, u8p, dp, dp, i64p, dp]
+    lib.rlpl_oracle_selective_logprob.argtypes = [i64, i64, i64, dp, dp, dp, i64p, dp, dp, dp, dp, dp, dp]
+    lib.rlpl_oracle_selective_logprob.restype = ctypes.c_int
     for f in (lib.rlpl_oracle_bnpo, lib.rlpl_oracle_grpo, lib.rlpl_oracle_rkl, lib.rlpl_oracle_rkl_logits,
               lib.rlpl_oracle_bnpo_ppo, lib.rlpl_oracle_grpo_ppo):
         f.restype = ctypes.c_int
@@ -181,3 +183,35 @@ def rkl_logits(student, teacher, mask, grad=True) -> VocabResult:
     if rc != 0:
         raise ValueError("oracle rejected its arguments")
     return VocabResult(loss.value, None if g is None else g.reshape(shape), int(n[0]), kl)
+
+
+@dataclass
+class LogprobResult:
+    logp: np.ndarray                 # (n,)
+    lse: np.ndarray                  # (n,)
+    d_hidden: Optional[np.ndarray]   # (n, h)
+    d_weight: Optional[np.ndarray]   # (vocab, h)
+    d_bias: Optional[np.ndarray]     # (vocab,)
+
+
+def selective_logprob(hidden, weight, bias, targets, grad_logp=None) -> LogprobResult:
+    """Per-token log-probability of the target under softmax(hidden . weight^T + bias), and,
+    for an upstream gradient grad_logp, the gradients of sum(grad_logp * logp)."""
+    x, w = to_f64(hidden), to_f64(weight)
+    n, h = x.shape
+    V = w.shape[0]
+    b = to_f64(bias) if bias is not None else None
+    y = np.ascontiguousarray(np.asarray(targets.cpu() if hasattr(targets, "cpu") else targets, dtype=np.int64))
+    logp, lse = np.empty(n), np.empty(n)
+    g = to_f64(grad_logp) if grad_logp is not None else None
+    dh = np.empty((n, h)) if g is not None else None
+    dw = np.empty((V, h)) if g is not None else None
+    db = np.empty(V) if (g is not None and b is not None) else None
+    rc = _load().rlpl_oracle_selective_logprob(n, h, V, _p(x, ctypes.c_double), _p(w, ctypes.c_double),
+                                               _p(b, ctypes.c_double), _p(y, ctypes.c_int64),
+                                               _p(logp, ctypes.c_double), _p(lse, ctypes.c_double),
+                                               _p(g, ctypes.c_double), _p(dh, ctypes.c_double),
+                                               _p(dw, ctypes.c_double), _p(db, ctypes.c_double))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    return LogprobResult(logp, lse, dh, dw, db)

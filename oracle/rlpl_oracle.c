@@ -39,13 +39,22 @@
  *     with the unclamped 1/N, so an all-masked batch gives 0/0 = NaN loss and
  *     a +0 gradient.
  *
- * Parity pins for every function here live in tests/test_oracle.py.
+ * Selective log-probabilities (the step upstream of the loss, page "Add SM100
+ * CuTe DSL GRPO fast path", section "Summary"): for each token i, the logits
+ * z_i = hidden_i . weight^T (+ bias) over the vocabulary (temperature 1), and
+ * logp_i = z_i[target_i] - log(sum_v exp(z_i[v])).  The backward for an
+ * upstream gradient g_i = d loss / d logp_i: dz_i = g_i (onehot(target_i) -
+ * softmax(z_i)), d hidden_i = dz_i . weight, d weight = sum_i dz_i^T hidden_i,
+ * d bias = sum_i dz_i.
+ *
+ * Parity pins for every function here live in tests/test_oracle*.py.
  */
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
 
-#define RLPL_ORACLE_VERSION 3
+#define RLPL_ORACLE_VERSION 4
 
 int rlpl_oracle_version(void) { return RLPL_ORACLE_VERSION; }
 
@@ -312,5 +321,56 @@ int rlpl_oracle_rkl_logits(int64_t rows, int64_t vocab, const double *student,
     }
     *loss = sum / (double)n;   /* not clamped: 0/0 is NaN when no row is valid */
     *n_valid = n;
+    return 0;
+}
+
+/*
+ * Selective log-probabilities: logp[i] = z_i[target_i] - logsumexp(z_i), with
+ * z_i[v] = sum_k hidden[i][k] * weight[v][k] + (bias ? bias[v] : 0).
+ * hidden (n, h), weight (vocab, h), bias (vocab) or NULL, targets (n) in
+ * [0, vocab).  lse (n, optional) receives logsumexp(z_i).
+ * When grad_logp is not NULL it also writes d_hidden (n, h), d_weight
+ * (vocab, h) and d_bias (vocab, if bias) for the upstream gradient grad_logp
+ * (each of the three outputs may be NULL).  Returns 0, or -1 on bad arguments.
+ */
+int rlpl_oracle_selective_logprob(int64_t n, int64_t h, int64_t vocab, const double *hidden,
+                                  const double *weight, const double *bias, const int64_t *targets,
+                                  double *logp, double *lse, const double *grad_logp,
+                                  double *d_hidden, double *d_weight, double *d_bias)
+{
+    if (n < 0 || h < 1 || vocab < 1 || !hidden || !weight || !targets || !logp) return -1;
+    for (int64_t i = 0; i < n; ++i)
+        if (targets[i] < 0 || targets[i] >= vocab) return -1;
+    if (d_weight)
+        for (int64_t j = 0; j < vocab * h; ++j) d_weight[j] = 0.0;
+    if (d_bias)
+        for (int64_t v = 0; v < vocab; ++v) d_bias[v] = 0.0;
+    double *z = (double *)malloc((size_t)vocab * sizeof(double));
+    if (!z) return -1;
+    for (int64_t i = 0; i < n; ++i) {
+        const double *x = hidden + i * h;
+        for (int64_t v = 0; v < vocab; ++v) {
+            double acc = bias ? bias[v] : 0.0;
+            const double *w = weight + v * h;
+            for (int64_t k = 0; k < h; ++k) acc += x[k] * w[k];
+            z[v] = acc;
+        }
+        const double l = log_sum_exp(z, vocab);
+        logp[i] = z[targets[i]] - l;
+        if (lse) lse[i] = l;
+        if (!grad_logp) continue;
+        if (d_hidden)
+            for (int64_t k = 0; k < h; ++k) d_hidden[i * h + k] = 0.0;
+        for (int64_t v = 0; v < vocab; ++v) {
+            const double dz = grad_logp[i] * ((v == targets[i] ? 1.0 : 0.0) - exp(z[v] - l));
+            const double *w = weight + v * h;
+            if (d_hidden)
+                for (int64_t k = 0; k < h; ++k) d_hidden[i * h + k] += dz * w[k];
+            if (d_weight)
+                for (int64_t k = 0; k < h; ++k) d_weight[v * h + k] += dz * x[k];
+            if (d_bias) d_bias[v] += dz;
+        }
+    }
+    free(z);
     return 0;
 }

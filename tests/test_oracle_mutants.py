@@ -12,6 +12,7 @@ import pytest
 
 import oracle
 import test_oracle
+import test_oracle_logprob
 import test_oracle_ppo
 import test_oracle_vocab
 
@@ -40,6 +41,13 @@ MUTANTS = {
                                        "    *slope = -adv * clipped;"),
     "ppo uses the literal min for every sign": ("double unclipped_obj = adv * ratio, clipped_obj = adv * clipped;",
                                                 "double unclipped_obj = ratio, clipped_obj = clipped;"),
+    "logprob dz sign": ("grad_logp[i] * ((v == targets[i] ? 1.0 : 0.0) - exp(z[v] - l));",
+                        "grad_logp[i] * (exp(z[v] - l) - (v == targets[i] ? 1.0 : 0.0));"),
+    "logprob d_weight uses the weight": ("d_weight[v * h + k] += dz * x[k];", "d_weight[v * h + k] += dz * w[k];"),
+    "logprob bias ignored": ("double acc = bias ? bias[v] : 0.0;", "double acc = 0.0;"),
+    "logprob gathers logit 0": ("logp[i] = z[targets[i]] - l;", "logp[i] = z[0] - l;"),
+    "logprob d_hidden misses the softmax": ("const double dz = grad_logp[i] * ((v == targets[i] ? 1.0 : 0.0) - exp(z[v] - l));",
+                                            "const double dz = grad_logp[i] * (v == targets[i] ? 1.0 : 0.0);"),
     "vocab forward KL instead of reverse": ("kl += exp(log_p) * (log_p - log_q);",
                                             "kl += exp(log_q) * (log_q - log_p);"),
     "vocab grad misses -kl_row": ("g[v] = exp(log_p) * (log_p - log_q - kl) / (double)n;",
@@ -59,7 +67,7 @@ MUTANTS = {
 
 
 def _pins():
-    return [(name, fn) for mod in (test_oracle, test_oracle_ppo, test_oracle_vocab)
+    return [(name, fn) for mod in (test_oracle, test_oracle_logprob, test_oracle_ppo, test_oracle_vocab)
             for name, fn in inspect.getmembers(mod, inspect.isfunction)
             if name.startswith("test_") and "generator" not in name]
 
