@@ -233,6 +233,67 @@ int reverse_kl_logits_fwd(const void* student_logits, const void* teacher_logits
                           float* loss_out, uint32_t* n_valid_out,
                           void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Selective log-probabilities: the producer of the policy log-probs above
+ * (page "Add SM100 CuTe DSL GRPO fast path", section "Summary": the logits of
+ * a group of up to 1024 tokens come from one matrix multiplication, the
+ * cross-entropy is taken in place and the full logits are never kept; the
+ * weight gradient is accumulated in float32 across groups).  For token i,
+ *
+ *   z_i      = hidden[i] . weight^T + bias          (vocab logits, temperature 1)
+ *   lse_i    = log sum_v exp(z_i[v])
+ *   logp_i   = z_i[targets[i]] - lse_i
+ *
+ * and, for an upstream gradient g_i = d L / d logp_i, the gradients of L:
+ *
+ *   dz_i[v]         = g_i ((v == targets[i]) - exp(z_i[v] - lse_i))
+ *   grad_hidden[i]  = sum_v dz_i[v] weight[v]
+ *   grad_weight[v]  = sum_i dz_i[v] hidden[i]
+ *   grad_bias[v]    = sum_i dz_i[v]
+ *
+ * The matrix products run on the matrix cores with `dtype` operands (RLPL_F16
+ * or RLPL_BF16 only) and float32 accumulation.  The forward keeps per token
+ * only lse and logp; the backward recomputes z in groups of 1024 tokens and
+ * forms dz in `dtype` (rounded to nearest even) in the workspace, the operand
+ * of its two gradient products.  Each call enqueues several kernels on
+ * `stream` (no host synchronisation, no allocation); results are
+ * deterministic (fixed reduction orders, no atomics).
+ *
+ * hidden      : (n, hidden_size) `dtype`, dense row-major, 16-byte aligned
+ * weight      : (vocab, hidden_size) `dtype`, dense row-major, 16-byte aligned
+ * bias        : (vocab,) `dtype`, or NULL (no bias)
+ * targets     : (n,) int64 token ids, 8-byte aligned; a target outside
+ *               [0, vocab) gives logp = NaN (forward) and no one-hot term in dz
+ * lse_out     : (n,) float32, written (may be NULL in the forward); the
+ *               backward reads the forward's lse through `lse`
+ * logp_out    : (n,) float32, written
+ * grad_logp   : (n,) float32 upstream gradient g
+ * grad_hidden : (n, hidden_size) `dtype` written, or NULL (not wanted)
+ * grad_weight : (vocab, hidden_size) float32, or NULL; accumulate != 0 adds
+ *               to its contents, else overwrites them
+ * grad_bias   : (vocab,) float32, or NULL; accumulate as for grad_weight
+ * workspace   : device memory of at least
+ *               selective_logprob_workspace_bytes(n, hidden_size, vocab,
+ *               backward) bytes, 256-byte aligned, no initial contents needed;
+ *               one call in flight per workspace
+ *
+ * Shapes: 1 <= n < 2^31, hidden_size a multiple of 8 in [8, 65536],
+ * 1 <= vocab < 2^26; otherwise RLPL_ERR_SHAPE.  Pointers 4-byte aligned
+ * where not stated.  Errors as for the other entry points.
+ */
+size_t selective_logprob_workspace_bytes(int64_t n, int64_t hidden_size, int64_t vocab, int backward);
+
+int selective_logprob_fwd(const void* hidden, const void* weight, const void* bias, const int64_t* targets,
+                          int64_t n, int64_t hidden_size, int64_t vocab, int dtype,
+                          float* logp_out, float* lse_out,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+int selective_logprob_bwd(const void* hidden, const void* weight, const void* bias, const int64_t* targets,
+                          const float* lse, const float* grad_logp,
+                          int64_t n, int64_t hidden_size, int64_t vocab, int dtype,
+                          void* grad_hidden, float* grad_weight, float* grad_bias, int accumulate,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Bytes of workspace an `op` call on a (bs, seq_len) problem needs (0 for a bad op). */
 size_t rlpl_workspace_bytes(int64_t bs, int64_t seq_len, int op);
 

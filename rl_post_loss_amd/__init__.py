@@ -18,6 +18,11 @@ Entry points (model card "Geometric-AI Kernels": sections "BNPO Loss",
   (per-token log-probs, the card's per-token KL estimator)
 * ``reverse_kl_logits(student_logits, teacher_logits, mask)`` -> (loss, grad);
   ``reverse_kl_logits_fwd(...)`` -> loss  (full (*, V) logit rows, the card's softmax form)
+* ``selective_logprob_fwd(hidden, weight, bias, targets)`` -> (logp, lse) and
+  ``selective_logprob_bwd(hidden, weight, bias, targets, lse, grad_logp)`` ->
+  (grad_hidden, grad_weight, grad_bias): the policy log-probs from the last
+  hidden states and the output projection, on the matrix cores (page "Add SM100
+  CuTe DSL GRPO fast path", section "Summary")
 
 Autograd-aware forms (``rl_post_loss_amd.autograd``): ``bnpo_loss_autograd``,
 ``grpo_loss_autograd``, ``reverse_kl_autograd`` and ``reverse_kl_logits_autograd``
@@ -48,7 +53,8 @@ from . import build as _build
 __all__ = ["bnpo_loss", "bnpo_loss_fwd", "grpo_loss", "grpo_loss_fwd", "reverse_kl",
            "reverse_kl_fwd", "library", "library_path", "RlplError", "STATUS", "workspace_for",
            "launch_shape", "reverse_kl_logits", "reverse_kl_logits_fwd", "bnpo_loss_autograd",
-           "grpo_loss_autograd", "reverse_kl_autograd", "reverse_kl_logits_autograd"]
+           "grpo_loss_autograd", "reverse_kl_autograd", "reverse_kl_logits_autograd",
+           "selective_logprob_fwd", "selective_logprob_bwd", "selective_logprob_autograd"]
 
 STATUS = {0: "RLPL_OK", 1: "RLPL_ERR_NULL", 2: "RLPL_ERR_SHAPE", 3: "RLPL_ERR_ALIGN",
           4: "RLPL_ERR_DTYPE", 5: "RLPL_ERR_PARAM", 6: "RLPL_ERR_WORKSPACE", 7: "RLPL_ERR_DEVICE",
@@ -89,6 +95,13 @@ def _declare(lib):
     for name, args in (("reverse_kl_logits", rkl), ("reverse_kl_logits_fwd", rkl_fwd)):
         f = getattr(lib, name)
         f.argtypes, f.restype = args, ctypes.c_int
+    lp_common = [vp, vp, vp, vp]
+    lib.selective_logprob_workspace_bytes.argtypes = [i64, i64, i64, i32]
+    lib.selective_logprob_workspace_bytes.restype = sz
+    lib.selective_logprob_fwd.argtypes = lp_common + [i64, i64, i64, i32, vp, vp, vp, sz, vp]
+    lib.selective_logprob_fwd.restype = ctypes.c_int
+    lib.selective_logprob_bwd.argtypes = lp_common + [vp, vp, i64, i64, i64, i32, vp, vp, vp, i32, vp, sz, vp]
+    lib.selective_logprob_bwd.restype = ctypes.c_int
     lib.rlpl_policy_loss.argtypes = [i32, ctypes.c_uint32] + policy
     lib.rlpl_policy_loss.restype = ctypes.c_int
     lib.rlpl_workspace_bytes.argtypes, lib.rlpl_workspace_bytes.restype = [i64, i64, i32], sz
@@ -333,5 +346,98 @@ def reverse_kl_logits_fwd(student_logits, teacher_logits, completions_mask, *, r
     return _rkl_logits(False, student_logits, teacher_logits, completions_mask, return_n_valid, workspace)
 
 
+
+def _lp_operands(hidden, weight, bias, targets):
+    x, w = hidden.detach(), weight.detach()
+    for name, t in (("hidden", x), ("weight", w)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dim() != 2:
+            raise TypeError(f"{name} must be a 2-d CUDA (HIP) tensor")
+    if x.dtype not in (torch.float16, torch.bfloat16) or w.dtype != x.dtype:
+        raise TypeError("hidden and weight must share a float16 or bfloat16 dtype")
+    if x.shape[1] != w.shape[1] or w.device != x.device:
+        raise ValueError("hidden (n, H) and weight (V, H) must agree in H and device")
+    n, V = x.shape[0], w.shape[0]
+    b = None
+    if bias is not None:
+        b = bias.detach().contiguous()
+        if b.dtype != x.dtype or tuple(b.shape) != (V,) or b.device != x.device:
+            raise ValueError(f"bias must be a ({V},) tensor of the operands' dtype and device")
+    y = targets.detach().contiguous()
+    if y.dtype != torch.int64 or tuple(y.shape) != (n,) or y.device != x.device:
+        raise ValueError(f"targets must be an int64 ({n},) tensor on the operands' device")
+    return _aligned(x), _aligned(w), b, y
+
+
+def _lp_workspace(n, H, V, backward, workspace, dev):
+    nbytes = library().selective_logprob_workspace_bytes(n, H, V, int(backward))
+    if nbytes == 0:
+        _check("selective_logprob_workspace_bytes", 2)
+    if workspace is None:
+        return torch.empty(nbytes + 256, dtype=torch.uint8, device=dev)
+    if workspace.device != dev or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor on the operands' device")
+    return workspace
+
+
+def _ws_ptr(ws: torch.Tensor):
+    p = ws.data_ptr()
+    off = (-p) % 256
+    return p + off, ws.numel() - off
+
+
+def selective_logprob_fwd(hidden, weight, bias, targets, *, workspace=None):
+    """Per-token log-probability of ``targets`` under softmax(hidden . weight^T + bias):
+    (logp, lse), float32 (n,) each.  hidden (n, H) and weight (V, H) float16/bfloat16."""
+    x, w, b, y = _lp_operands(hidden, weight, bias, targets)
+    n, H = x.shape
+    V = w.shape[0]
+    dev = x.device
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    ws = _lp_workspace(n, H, V, False, workspace, dev)
+    logp = torch.empty(n, dtype=torch.float32, device=dev)
+    lse = torch.empty(n, dtype=torch.float32, device=dev)
+    wp, wn = _ws_ptr(ws)
+    _check("selective_logprob_fwd", library().selective_logprob_fwd(
+        x.data_ptr(), w.data_ptr(), None if b is None else b.data_ptr(), y.data_ptr(), n, H, V,
+        DTYPE[x.dtype], logp.data_ptr(), lse.data_ptr(), wp, wn, stream))
+    return logp, lse
+
+
+def selective_logprob_bwd(hidden, weight, bias, targets, lse, grad_logp, *, need_hidden=True,
+                          need_weight=True, grad_weight=None, grad_bias=None, workspace=None):
+    """Gradients of sum(grad_logp * logp): (grad_hidden in the operands' dtype or None,
+    grad_weight float32 (V, H) or None, grad_bias float32 (V,) or None).  Passing
+    ``grad_weight`` / ``grad_bias`` (float32) accumulates into them."""
+    x, w, b, y = _lp_operands(hidden, weight, bias, targets)
+    n, H = x.shape
+    V = w.shape[0]
+    dev = x.device
+    ls = lse.detach().to(torch.float32).contiguous()
+    g = grad_logp.detach().to(torch.float32).contiguous()
+    if tuple(ls.shape) != (n,) or tuple(g.shape) != (n,):
+        raise ValueError(f"lse and grad_logp must have shape ({n},)")
+    accumulate = grad_weight is not None or grad_bias is not None
+    for name, t, shape in (("grad_weight", grad_weight, (V, H)), ("grad_bias", grad_bias, (V,))):
+        if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != shape or not t.is_contiguous()
+                              or t.device != dev):
+            raise ValueError(f"{name} must be a contiguous float32 {shape} tensor on the operands' device")
+    if accumulate and ((need_weight and grad_weight is None) or (b is not None and grad_bias is None)):
+        raise ValueError("to accumulate, pass both grad_weight (when wanted) and grad_bias (with a bias)")
+    dh = torch.empty_like(x) if need_hidden else None
+    dw = grad_weight if grad_weight is not None else (
+        torch.empty((V, H), dtype=torch.float32, device=dev) if need_weight else None)
+    db = grad_bias if grad_bias is not None else (
+        torch.empty(V, dtype=torch.float32, device=dev) if b is not None else None)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    ws = _lp_workspace(n, H, V, True, workspace, dev)
+    wp, wn = _ws_ptr(ws)
+    _check("selective_logprob_bwd", library().selective_logprob_bwd(
+        x.data_ptr(), w.data_ptr(), None if b is None else b.data_ptr(), y.data_ptr(), ls.data_ptr(),
+        g.data_ptr(), n, H, V, DTYPE[x.dtype], None if dh is None else dh.data_ptr(),
+        None if dw is None else dw.data_ptr(), None if db is None else db.data_ptr(), int(accumulate),
+        wp, wn, stream))
+    return dh, dw, db
+
+
 from .autograd import (bnpo_loss_autograd, grpo_loss_autograd, reverse_kl_autograd,  # noqa: E402
-                       reverse_kl_logits_autograd)
+                       reverse_kl_logits_autograd, selective_logprob_autograd)

@@ -18,10 +18,10 @@ from typing import Optional, Tuple
 
 import torch
 
-from . import _policy, _rkl, _rkl_logits
+from . import _policy, _rkl, _rkl_logits, selective_logprob_bwd, selective_logprob_fwd
 
 __all__ = ["bnpo_loss_autograd", "grpo_loss_autograd", "reverse_kl_autograd",
-           "reverse_kl_logits_autograd"]
+           "reverse_kl_logits_autograd", "selective_logprob_autograd"]
 
 _LIB = "rlpl"
 
@@ -111,3 +111,63 @@ def reverse_kl_autograd(student_logprobs, teacher_logprobs, completions_mask):
 def reverse_kl_logits_autograd(student_logits, teacher_logits, completions_mask):
     """Full-vocab reverse KL as a differentiable 0-d float32 tensor (gradient flows to the student logits)."""
     return _rkl_vocab(student_logits, teacher_logits, completions_mask)[0]
+
+
+@torch.library.custom_op(f"{_LIB}::selective_logprob", mutates_args=())
+def _selective(hidden: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor],
+               targets: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
+    return selective_logprob_fwd(hidden, weight, bias, targets)
+
+
+@_selective.register_fake
+def _(hidden, weight, bias, targets):
+    n = hidden.shape[0]
+    return (hidden.new_empty((n,), dtype=torch.float32), hidden.new_empty((n,), dtype=torch.float32))
+
+
+@torch.library.custom_op(f"{_LIB}::selective_logprob_backward", mutates_args=())
+def _selective_bwd(hidden: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor],
+                   targets: torch.Tensor, lse: torch.Tensor, grad_logp: torch.Tensor,
+                   need_hidden: bool, need_weight: bool) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    dh, dw, db = selective_logprob_bwd(hidden, weight, bias, targets, lse, grad_logp,
+                                       need_hidden=need_hidden, need_weight=need_weight)
+    # custom ops return tensors only: empty placeholders stand for the gradients not asked for
+    empty = hidden.new_empty((0,))
+    return (dh if dh is not None else empty, dw if dw is not None else empty.float(),
+            db if db is not None else empty.float())
+
+
+@_selective_bwd.register_fake
+def _(hidden, weight, bias, targets, lse, grad_logp, need_hidden, need_weight):
+    n, H = hidden.shape
+    V = weight.shape[0]
+    dh = hidden.new_empty((n, H)) if need_hidden else hidden.new_empty((0,))
+    dw = hidden.new_empty((V, H), dtype=torch.float32) if need_weight else hidden.new_empty((0,), dtype=torch.float32)
+    db = hidden.new_empty((V,) if bias is not None else (0,), dtype=torch.float32)
+    return dh, dw, db
+
+
+def _selective_setup(ctx, inputs, output):
+    hidden, weight, bias, targets = inputs
+    ctx.has_bias = bias is not None
+    ctx.save_for_backward(hidden, weight, bias, targets, output[1])
+
+
+def _selective_backward(ctx, grad_logp, _grad_lse):
+    hidden, weight, bias, targets, lse = ctx.saved_tensors
+    need_h, need_w = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
+    need_b = ctx.has_bias and ctx.needs_input_grad[2]
+    if not (need_h or need_w or need_b):
+        return None, None, None, None
+    dh, dw, db = _selective_bwd(hidden, weight, bias, targets, lse, grad_logp, need_h, need_w)
+    return (dh if need_h else None, dw.to(weight.dtype) if need_w else None,
+            db.to(bias.dtype) if need_b else None, None)
+
+
+_selective.register_autograd(_selective_backward, setup_context=_selective_setup)
+
+
+def selective_logprob_autograd(hidden, weight, bias, targets):
+    """Per-token target log-probabilities (float32, (n,)) as a differentiable tensor: gradients flow to
+    hidden, weight and bias (the weight and bias gradients are formed in float32, then cast to their dtype)."""
+    return _selective(hidden, weight, bias, targets)[0]

@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "librl_post_loss.so")
-SOURCES = ["loss_kernels.hip", "vocab_kernels.hip", "abi.cpp"]
+SOURCES = ["loss_kernels.hip", "vocab_kernels.hip", "logprob_kernels.hip", "abi.cpp"]
 
 
 def hipcc() -> str:

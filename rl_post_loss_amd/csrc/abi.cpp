@@ -12,6 +12,7 @@
 #include <cstring>
 #include <mutex>
 
+#include "logprob_kernels.h"
 #include "loss_kernels.h"
 #include "rl_post_loss.h"
 #include "row_divisor.h"
@@ -129,10 +130,9 @@ int check_common(const void* mask, int64_t bs, int64_t seq_len, int dtype, int m
 // the exchange wait is also bounded in time).  A cooperative launch would
 // guarantee the same but costs ~16 us of extra dispatch latency per call here.
 template <typename A>
-int launch(const void* kernel, const A& a, int64_t grid, hipStream_t stream) {
+int launch(const void* kernel, const A& a, dim3 grid, hipStream_t stream, int threads = rlpl::kThreads) {
     void* params[] = {const_cast<A*>(&a)};
-    const hipError_t e =
-        hipLaunchKernel(kernel, dim3(unsigned(grid)), dim3(rlpl::kThreads), params, 0, stream);
+    const hipError_t e = hipLaunchKernel(kernel, grid, dim3(threads), params, 0, stream);
     if (e != hipSuccess) {
         (void)hipGetLastError();   // clear the sticky launch error
         return RLPL_ERR_LAUNCH;
@@ -182,7 +182,7 @@ int run(int mode, bool write_grad, bool has_kl, Args& a, int dtype, hipStream_t 
     if (!kernel) return RLPL_ERR_DTYPE;
     a.tiles = sh.tiles;
     if (!rlpl::row_divisor(uint32_t(a.seq_len), &a.row_magic, &a.row_shift)) return RLPL_ERR_SHAPE;
-    return launch(kernel, a, sh.grid, stream);
+    return launch(kernel, a, dim3(unsigned(sh.grid)), stream);
 }
 
 int policy_loss(int mode, bool write_grad, bool sign_aware, const void* policy_lp, const void* old_lp,
@@ -288,12 +288,228 @@ int vocab_loss(bool write_grad, const void* student, const void* teacher, const 
     a.chunk_blocks = uint64_t(sp.chunk_blocks);
     const void* kernel = rlpl::pick_vocab_kernel(dtype, write_grad);
     if (!kernel) return RLPL_ERR_DTYPE;
-    return launch(kernel, a, sp.groups * sp.chunks, stream);
+    return launch(kernel, a, dim3(unsigned(sp.groups * sp.chunks)), stream);
+}
+
+// ----------------------------------------------------------------------------- selective log-probs
+
+constexpr int64_t kLpMaxVocab = int64_t(1) << 26;
+constexpr int64_t kLpMaxHidden = 65536;
+constexpr int64_t kLpMaxTiles = int64_t(1) << 24;   // workgroups per launch (x 256 lanes < 2^32)
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
+
+// Workspace carve-up of a selective log-prob call: per-tile (max, sum) partials
+// and target logits of one group (forward), and the group's logits gradient
+// (ld = vocab rounded up to 8) plus the split-K partial planes of the hidden
+// gradient (backward).
+struct LpLayout {
+    int64_t chunk, tiles_n, ld_dz, k_split;
+    size_t part, target, dz, split, total;
+};
+
+bool lp_shape_ok(int64_t n, int64_t h, int64_t vocab) {
+    if (n < 1 || n >= (int64_t(1) << 31) || h < 8 || h > kLpMaxHidden || h % 8 != 0 || vocab < 1 ||
+        vocab >= kLpMaxVocab)
+        return false;
+    const int64_t chunk = n < rlpl::kLogprobChunk ? n : rlpl::kLogprobChunk;
+    const int64_t tn_v = ceil_div(vocab, rlpl::kGemmBN), tm_v = ceil_div(vocab, rlpl::kGemmBM);
+    const int64_t t_h = ceil_div(h, rlpl::kGemmBN), t_c = ceil_div(chunk, rlpl::kGemmBM);
+    return t_c * tn_v < kLpMaxTiles && tm_v * t_h < kLpMaxTiles && t_c * t_h < kLpMaxTiles;
+}
+
+LpLayout lp_layout(int64_t n, int64_t h, int64_t vocab, int backward) {
+    LpLayout L{};
+    L.chunk = n < rlpl::kLogprobChunk ? n : rlpl::kLogprobChunk;
+    L.tiles_n = ceil_div(vocab, rlpl::kGemmBN);
+    L.ld_dz = (vocab + 7) & ~int64_t(7);
+    L.k_split = ceil_div(ceil_div(vocab, rlpl::kSplitK), rlpl::kGemmBK) * rlpl::kGemmBK;
+    if (!backward) {
+        L.part = round256(size_t(L.chunk) * size_t(L.tiles_n) * 2 * sizeof(float));
+        L.target = round256(size_t(L.chunk) * sizeof(float));
+    } else {
+        L.dz = round256(size_t(L.chunk) * size_t(L.ld_dz) * 2);
+        L.split = round256(size_t(rlpl::kSplitK) * size_t(L.chunk) * size_t(h) * sizeof(float));
+    }
+    L.total = L.part + L.target + L.dz + L.split;
+    return L;
+}
+
+int lp_check(const void* hidden, const void* weight, const void* bias, const int64_t* targets, int64_t n,
+             int64_t h, int64_t vocab, int dtype, const void* workspace, size_t workspace_bytes, int backward) {
+    if (!hidden || !weight || !targets) return RLPL_ERR_NULL;
+    if (!lp_shape_ok(n, h, vocab)) return RLPL_ERR_SHAPE;
+    if (dtype != RLPL_F16 && dtype != RLPL_BF16) return RLPL_ERR_DTYPE;
+    if (!aligned(hidden, 16) || !aligned(weight, 16) || (bias && !aligned(bias, 2)) || !aligned(targets, 8))
+        return RLPL_ERR_ALIGN;
+    if (!workspace || workspace_bytes < lp_layout(n, h, vocab, backward).total) return RLPL_ERR_WORKSPACE;
+    return aligned(workspace, 256) ? RLPL_OK : RLPL_ERR_ALIGN;
+}
+
+int lp_device() {
+    const DeviceInfo* info = nullptr;
+    return current_device(&info);
+}
+
+rlpl::GemmArgs logits_gemm(const void* hidden, const void* weight, const void* bias, const int64_t* targets,
+                           int64_t r0, int64_t m, int64_t h, int64_t vocab, size_t elem) {
+    rlpl::GemmArgs g{};
+    g.a = static_cast<const char*>(hidden) + size_t(r0) * size_t(h) * elem;
+    g.b = weight;
+    g.lda = h;
+    g.ldb = h;
+    g.M = int32_t(m);
+    g.N = int32_t(vocab);
+    g.K = int32_t(h);
+    g.k_split = int32_t(h);
+    g.tiles_m = uint32_t(ceil_div(m, rlpl::kGemmBM));
+    g.tiles_n = uint32_t(ceil_div(vocab, rlpl::kGemmBN));
+    g.bias = bias;
+    g.targets = targets + r0;
+    return g;
+}
+
+int launch_gemm(int dtype, int epi, bool ak, bool bk, const rlpl::GemmArgs& g, unsigned splits,
+                hipStream_t stream) {
+    const void* k = rlpl::pick_gemm_kernel(dtype, epi, ak, bk);
+    if (!k) return RLPL_ERR_DTYPE;
+    return launch(k, g, dim3(g.tiles_m * g.tiles_n, 1, splits), stream, rlpl::kGemmThreads);
 }
 
 }  // namespace
 
 extern "C" {
+
+size_t selective_logprob_workspace_bytes(int64_t n, int64_t hidden_size, int64_t vocab, int backward) {
+    if (!lp_shape_ok(n, hidden_size, vocab)) return 0;
+    return lp_layout(n, hidden_size, vocab, backward).total;
+}
+
+int selective_logprob_fwd(const void* hidden, const void* weight, const void* bias, const int64_t* targets,
+                          int64_t n, int64_t hidden_size, int64_t vocab, int dtype, float* logp_out,
+                          float* lse_out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!logp_out) return RLPL_ERR_NULL;
+    int st = lp_check(hidden, weight, bias, targets, n, hidden_size, vocab, dtype, workspace, workspace_bytes, 0);
+    if (st != RLPL_OK) return st;
+    if (!aligned(logp_out, 4) || (lse_out && !aligned(lse_out, 4))) return RLPL_ERR_ALIGN;
+    if ((st = lp_device()) != RLPL_OK) return st;
+    const LpLayout L = lp_layout(n, hidden_size, vocab, 0);
+    char* ws = static_cast<char*>(workspace);
+    float* part = reinterpret_cast<float*>(ws);
+    float* target = reinterpret_cast<float*>(ws + L.part);
+    const size_t elem = elem_bytes(dtype);
+    for (int64_t r0 = 0; r0 < n; r0 += L.chunk) {
+        const int64_t m = n - r0 < L.chunk ? n - r0 : L.chunk;
+        rlpl::GemmArgs g = logits_gemm(hidden, weight, bias, targets, r0, m, hidden_size, vocab, elem);
+        g.part = part;
+        g.target_logit = target;
+        st = launch_gemm(dtype, rlpl::kEpiLse, true, true, g, 1, stream);
+        if (st != RLPL_OK) return st;
+        rlpl::LseArgs a{};
+        a.part = part;
+        a.target_logit = target;
+        a.targets = targets + r0;
+        a.logp = logp_out + r0;
+        a.lse = lse_out ? lse_out + r0 : nullptr;
+        a.vocab = vocab;
+        a.rows = int32_t(m);
+        a.tiles = int32_t(L.tiles_n);
+        st = launch(rlpl::lse_combine_kernel(), a, dim3(unsigned(m)), stream);
+        if (st != RLPL_OK) return st;
+    }
+    return RLPL_OK;
+}
+
+int selective_logprob_bwd(const void* hidden, const void* weight, const void* bias, const int64_t* targets,
+                          const float* lse, const float* grad_logp, int64_t n, int64_t hidden_size,
+                          int64_t vocab, int dtype, void* grad_hidden, float* grad_weight, float* grad_bias,
+                          int accumulate, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!lse || !grad_logp) return RLPL_ERR_NULL;
+    int st = lp_check(hidden, weight, bias, targets, n, hidden_size, vocab, dtype, workspace, workspace_bytes, 1);
+    if (st != RLPL_OK) return st;
+    if (!aligned(lse, 4) || !aligned(grad_logp, 4) || (grad_hidden && !aligned(grad_hidden, 4)) ||
+        (grad_weight && !aligned(grad_weight, 4)) || (grad_bias && !aligned(grad_bias, 4)))
+        return RLPL_ERR_ALIGN;
+    if ((st = lp_device()) != RLPL_OK) return st;
+    const LpLayout L = lp_layout(n, hidden_size, vocab, 1);
+    char* ws = static_cast<char*>(workspace);
+    void* dz = ws;
+    float* split = reinterpret_cast<float*>(ws + L.dz);
+    const size_t elem = elem_bytes(dtype);
+    for (int64_t r0 = 0; r0 < n; r0 += L.chunk) {
+        const int64_t m = n - r0 < L.chunk ? n - r0 : L.chunk;
+        const int acc = (accumulate || r0 > 0) ? 1 : 0;
+        const void* h0 = static_cast<const char*>(hidden) + size_t(r0) * size_t(hidden_size) * elem;
+        // dz = g (onehot - softmax(z)) for the group's rows.
+        rlpl::GemmArgs g = logits_gemm(hidden, weight, bias, targets, r0, m, hidden_size, vocab, elem);
+        g.c = dz;
+        g.ldc = L.ld_dz;
+        g.lse = lse + r0;
+        g.grad = grad_logp + r0;
+        st = launch_gemm(dtype, rlpl::kEpiDlogits, true, true, g, 1, stream);
+        if (st != RLPL_OK) return st;
+        if (grad_hidden) {
+            // (m x vocab) . (vocab x hidden): split over vocab into fp32 planes, summed in split order.
+            rlpl::GemmArgs d{};
+            d.a = dz;
+            d.b = weight;
+            d.lda = L.ld_dz;
+            d.ldb = hidden_size;
+            d.M = int32_t(m);
+            d.N = int32_t(hidden_size);
+            d.K = int32_t(vocab);
+            d.k_split = int32_t(L.k_split);
+            d.tiles_m = uint32_t(ceil_div(m, rlpl::kGemmBM));
+            d.tiles_n = uint32_t(ceil_div(hidden_size, rlpl::kGemmBN));
+            d.c = split;
+            d.ldc = hidden_size;
+            st = launch_gemm(dtype, rlpl::kEpiSplit, true, false, d, rlpl::kSplitK, stream);
+            if (st != RLPL_OK) return st;
+            rlpl::SplitSumArgs s{};
+            s.part = split;
+            s.out = static_cast<char*>(grad_hidden) + size_t(r0) * size_t(hidden_size) * elem;
+            s.plane = m * hidden_size;
+            s.splits = rlpl::kSplitK;
+            const int64_t blocks = ceil_div(s.plane, rlpl::kThreads);
+            st = launch(rlpl::pick_split_sum_kernel(dtype), s, dim3(unsigned(blocks < 8192 ? blocks : 8192)), stream);
+            if (st != RLPL_OK) return st;
+        }
+        if (grad_weight) {
+            // (vocab x m) . (m x hidden), accumulated in fp32 over the groups.
+            rlpl::GemmArgs w{};
+            w.a = dz;
+            w.b = h0;
+            w.lda = L.ld_dz;
+            w.ldb = hidden_size;
+            w.M = int32_t(vocab);
+            w.N = int32_t(hidden_size);
+            w.K = int32_t(m);
+            w.k_split = int32_t(m);
+            w.tiles_m = uint32_t(ceil_div(vocab, rlpl::kGemmBM));
+            w.tiles_n = uint32_t(ceil_div(hidden_size, rlpl::kGemmBN));
+            w.c = grad_weight;
+            w.ldc = hidden_size;
+            w.accumulate = acc;
+            st = launch_gemm(dtype, rlpl::kEpiAccum, false, false, w, 1, stream);
+            if (st != RLPL_OK) return st;
+        }
+        if (grad_bias) {
+            rlpl::ColSumArgs c{};
+            c.x = dz;
+            c.out = grad_bias;
+            c.ldx = L.ld_dz;
+            c.rows = int32_t(m);
+            c.cols = int32_t(vocab);
+            c.accumulate = acc;
+            st = launch(rlpl::pick_col_sum_kernel(dtype), c, dim3(unsigned(ceil_div(vocab, rlpl::kThreads))), stream);
+            if (st != RLPL_OK) return st;
+        }
+    }
+    return RLPL_OK;
+}
+
+
 
 int reverse_kl_logits(const void* student_logits, const void* teacher_logits, const void* mask,
                       int64_t rows, int64_t vocab, int dtype, int mask_dtype, float* loss_out,

@@ -20,6 +20,11 @@ mask of shape (bs, seq_len)):
 * full-vocab reverse-KL ("Reverse KL" example): student and teacher logits
   are independent N(0,1) draws of shape (rows, vocab), rounded to the dtype;
   the row mask is U(0,1) > 0.2 (about 80 % of rows valid).
+* selective log-probs (page "Add SM100 CuTe DSL GRPO fast path", section
+  "Summary": a group of up to 1024 tokens, hidden size H, vocabulary V): final
+  hidden states N(0, 1) of shape (n, H); output projection N(0, (2/sqrt(H))^2)
+  of shape (V, H), so that logits have a standard deviation near 2; bias
+  N(0, 0.25); target ids uniform on [0, V); upstream gradient N(0, 1)/n.
 
 All draws come from ``numpy.random.default_rng(seed)`` (PCG64) in float64, in
 the fixed order listed in ``policy_inputs`` / ``rkl_inputs``.
@@ -179,3 +184,33 @@ def device_vocab_inputs(rows: int, vocab: int, dtype: str, mask_dtype: str, seed
     teacher = torch.randn((rows, vocab), generator=g, device=device, dtype=torch.float32).to(dt)
     mask = (torch.rand(rows, generator=g, device=device) > 1.0 - p_valid).to(MASK_DTYPES[mask_dtype])
     return {"student": student, "teacher": teacher, "mask": mask}
+
+
+def logprob_inputs(n: int, hidden_size: int, vocab: int, dtype: str = "bf16", seed: int = 0,
+                   bias: bool = True) -> dict:
+    """Inputs of the selective log-probability producer, as CPU tensors.
+
+    Draw order: hidden (n, H); weight (V, H); bias (V,) if wanted; targets (n,); grad_logp (n,).
+    """
+    rng = np.random.default_rng(seed)
+    hidden = _round(rng.standard_normal((n, hidden_size)), dtype)
+    weight = _round(rng.standard_normal((vocab, hidden_size)) * (2.0 / np.sqrt(hidden_size)), dtype)
+    b = _round(0.5 * rng.standard_normal(vocab), dtype) if bias else None
+    targets = torch.from_numpy(rng.integers(0, vocab, size=n).astype(np.int64))
+    grad = torch.from_numpy(rng.standard_normal(n) / max(n, 1)).to(torch.float32)
+    return {"hidden": hidden, "weight": weight, "bias": b, "targets": targets, "grad_logp": grad}
+
+
+def device_logprob_inputs(n: int, hidden_size: int, vocab: int, dtype: str, seed: int, device: str,
+                          bias: bool = True) -> dict:
+    """Large selective log-prob inputs drawn on the device with torch's seeded generator
+    (same distributions as ``logprob_inputs``, not the same values)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    dt = DTYPES[dtype]
+    hidden = torch.randn((n, hidden_size), generator=g, device=device).to(dt)
+    weight = (torch.randn((vocab, hidden_size), generator=g, device=device) * (2.0 / hidden_size ** 0.5)).to(dt)
+    b = (0.5 * torch.randn(vocab, generator=g, device=device)).to(dt) if bias else None
+    targets = torch.randint(0, vocab, (n,), generator=g, device=device, dtype=torch.int64)
+    grad = torch.randn(n, generator=g, device=device) / max(n, 1)
+    return {"hidden": hidden, "weight": weight, "bias": b, "targets": targets, "grad_logp": grad}

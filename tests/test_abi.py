@@ -272,3 +272,64 @@ def test_policy_loss_ex_validation(lib):
     assert rl.STATUS[call_ex(lib, op=2, eps=0.5, eps_high=-0.6)] == "RLPL_ERR_PARAM"
     if not torch.cuda.is_available():
         assert rl.STATUS[call_ex(lib, op=1, grad=None)] == "RLPL_ERR_DEVICE"   # _FWD ignores grad_out
+
+
+def call_lp(lib, backward=False, **over):
+    a = dict(h=A, w=A + 0x100000, b=A + 0x200000, y=A + 0x300000, lse=A + 0x400000, g=A + 0x500000,
+             n=64, H=256, V=1000, dtype=2, logp=A + 0x600000, dh=A + 0x700000, dw=A + 0x800000,
+             db=A + 0x900000, acc=0, ws=WS, ws_bytes=64 << 20, stream=None)
+    a.update(over)
+    if not backward:
+        return lib.selective_logprob_fwd(a["h"], a["w"], a["b"], a["y"], a["n"], a["H"], a["V"], a["dtype"],
+                                         a["logp"], a["lse"], a["ws"], a["ws_bytes"], a["stream"])
+    return lib.selective_logprob_bwd(a["h"], a["w"], a["b"], a["y"], a["lse"], a["g"], a["n"], a["H"], a["V"],
+                                     a["dtype"], a["dh"], a["dw"], a["db"], a["acc"], a["ws"], a["ws_bytes"],
+                                     a["stream"])
+
+
+LP_CASES = [
+    ("RLPL_ERR_NULL", dict(h=None)),
+    ("RLPL_ERR_NULL", dict(w=None)),
+    ("RLPL_ERR_NULL", dict(y=None)),
+    ("RLPL_ERR_SHAPE", dict(n=0)),
+    ("RLPL_ERR_SHAPE", dict(H=12)),              # not a multiple of 8
+    ("RLPL_ERR_SHAPE", dict(H=0)),
+    ("RLPL_ERR_SHAPE", dict(H=65544)),
+    ("RLPL_ERR_SHAPE", dict(V=0)),
+    ("RLPL_ERR_SHAPE", dict(V=1 << 26)),
+    ("RLPL_ERR_DTYPE", dict(dtype=0)),           # fp32 operands are not taken
+    ("RLPL_ERR_DTYPE", dict(dtype=7)),
+    ("RLPL_ERR_ALIGN", dict(h=A + 8)),
+    ("RLPL_ERR_ALIGN", dict(w=A + 0x100000 + 2)),
+    ("RLPL_ERR_ALIGN", dict(b=A + 0x200000 + 1)),
+    ("RLPL_ERR_ALIGN", dict(y=A + 0x300000 + 4)),
+    ("RLPL_ERR_WORKSPACE", dict(ws=None)),
+    ("RLPL_ERR_WORKSPACE", dict(ws_bytes=4096)),
+    ("RLPL_ERR_ALIGN", dict(ws=WS + 64)),
+]
+
+
+@pytest.mark.parametrize("want,over", LP_CASES, ids=[f"{w}-{list(o)[0]}" for w, o in LP_CASES])
+def test_selective_logprob_validation(lib, want, over):
+    assert rl.STATUS[call_lp(lib, **over)] == want
+    assert rl.STATUS[call_lp(lib, backward=True, **over)] == want
+
+
+def test_selective_logprob_outputs_and_workspace(lib):
+    assert rl.STATUS[call_lp(lib, logp=None)] == "RLPL_ERR_NULL"
+    assert rl.STATUS[call_lp(lib, logp=A + 0x600000 + 2)] == "RLPL_ERR_ALIGN"
+    assert rl.STATUS[call_lp(lib, backward=True, lse=None)] == "RLPL_ERR_NULL"
+    assert rl.STATUS[call_lp(lib, backward=True, g=None)] == "RLPL_ERR_NULL"
+    assert rl.STATUS[call_lp(lib, backward=True, dw=A + 0x800000 + 2)] == "RLPL_ERR_ALIGN"
+    fwd = lib.selective_logprob_workspace_bytes(1024, 4096, 128256, 0)
+    bwd = lib.selective_logprob_workspace_bytes(1024, 4096, 128256, 1)
+    # forward: per-tile (max, sum) pairs and target logits of one 1024-token group
+    assert fwd >= 1024 * 1002 * 8 + 1024 * 4 and fwd < 9 << 20
+    # backward: the group's logits gradient (bf16, rows padded to 8) and four fp32 planes of (1024, 4096)
+    assert bwd >= 1024 * 128256 * 2 + 4 * 1024 * 4096 * 4 and bwd < 320 << 20
+    assert lib.selective_logprob_workspace_bytes(5000, 4096, 128256, 1) == bwd   # sized by the group, not n
+    assert lib.selective_logprob_workspace_bytes(0, 4096, 128256, 1) == 0
+    assert lib.selective_logprob_workspace_bytes(8, 100, 1000, 0) == 0
+    if not torch.cuda.is_available():
+        assert rl.STATUS[call_lp(lib)] == "RLPL_ERR_DEVICE"
+        assert rl.STATUS[call_lp(lib, backward=True, dh=None, dw=None, db=None, b=None)] == "RLPL_ERR_DEVICE"
