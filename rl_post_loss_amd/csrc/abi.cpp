@@ -83,6 +83,15 @@ void init_device(int dev, DeviceInfo& info) {
                 if (cap > rlpl::kMaxGrid) cap = rlpl::kMaxGrid;
                 info.grid_cap[dt][mode][shape] = int(cap);
             }
+    // The contraction kernels take their LDS ring as dynamic LDS beyond the default limit.
+    for (int dt : {RLPL_F16, RLPL_BF16})
+        for (int epi = 0; epi < 4; ++epi)
+            for (int ab = 0; ab < 4; ++ab) {
+                const void* k = rlpl::pick_gemm_kernel(dt, epi, ab & 1, ab >> 1);
+                if (k && hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, rlpl::kGemmDynLds) !=
+                             hipSuccess)
+                    return;
+            }
     for (int dt = 0; dt < 3; ++dt) {
         // fwd+bwd and forward-only share one grid size (identical losses).
         const int a = blocks_per_cu(rlpl::pick_vocab_kernel(dt, true));
@@ -130,9 +139,10 @@ int check_common(const void* mask, int64_t bs, int64_t seq_len, int dtype, int m
 // the exchange wait is also bounded in time).  A cooperative launch would
 // guarantee the same but costs ~16 us of extra dispatch latency per call here.
 template <typename A>
-int launch(const void* kernel, const A& a, dim3 grid, hipStream_t stream, int threads = rlpl::kThreads) {
+int launch(const void* kernel, const A& a, dim3 grid, hipStream_t stream, int threads = rlpl::kThreads,
+           size_t dyn_lds = 0) {
     void* params[] = {const_cast<A*>(&a)};
-    const hipError_t e = hipLaunchKernel(kernel, grid, dim3(threads), params, 0, stream);
+    const hipError_t e = hipLaunchKernel(kernel, grid, dim3(threads), params, dyn_lds, stream);
     if (e != hipSuccess) {
         (void)hipGetLastError();   // clear the sticky launch error
         return RLPL_ERR_LAUNCH;
@@ -302,11 +312,11 @@ size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
 
 // Workspace carve-up of a selective log-prob call: per-tile (max, sum) partials
 // and target logits of one group (forward), and the group's logits gradient
-// (ld = vocab rounded up to 8) plus the split-K partial planes of the hidden
-// gradient (backward).
+// (ld = vocab rounded up to 8), the split-K partial planes of the hidden
+// gradient and the per-row-tile column sums of the logits gradient (backward).
 struct LpLayout {
-    int64_t chunk, tiles_n, ld_dz, k_split;
-    size_t part, target, dz, split, total;
+    int64_t chunk, tiles_n, tiles_m, ld_dz, k_split;
+    size_t part, target, dz, split, col, total;
 };
 
 bool lp_shape_ok(int64_t n, int64_t h, int64_t vocab) {
@@ -323,6 +333,7 @@ LpLayout lp_layout(int64_t n, int64_t h, int64_t vocab, int backward) {
     LpLayout L{};
     L.chunk = n < rlpl::kLogprobChunk ? n : rlpl::kLogprobChunk;
     L.tiles_n = ceil_div(vocab, rlpl::kGemmBN);
+    L.tiles_m = ceil_div(L.chunk, rlpl::kGemmBM);
     L.ld_dz = (vocab + 7) & ~int64_t(7);
     L.k_split = ceil_div(ceil_div(vocab, rlpl::kSplitK), rlpl::kGemmBK) * rlpl::kGemmBK;
     if (!backward) {
@@ -331,8 +342,9 @@ LpLayout lp_layout(int64_t n, int64_t h, int64_t vocab, int backward) {
     } else {
         L.dz = round256(size_t(L.chunk) * size_t(L.ld_dz) * 2);
         L.split = round256(size_t(rlpl::kSplitK) * size_t(L.chunk) * size_t(h) * sizeof(float));
+        L.col = round256(size_t(L.tiles_m) * size_t(vocab) * sizeof(float));
     }
-    L.total = L.part + L.target + L.dz + L.split;
+    L.total = L.part + L.target + L.dz + L.split + L.col;
     return L;
 }
 
@@ -374,7 +386,7 @@ int launch_gemm(int dtype, int epi, bool ak, bool bk, const rlpl::GemmArgs& g, u
                 hipStream_t stream) {
     const void* k = rlpl::pick_gemm_kernel(dtype, epi, ak, bk);
     if (!k) return RLPL_ERR_DTYPE;
-    return launch(k, g, dim3(g.tiles_m * g.tiles_n, 1, splits), stream, rlpl::kGemmThreads);
+    return launch(k, g, dim3(g.tiles_m * g.tiles_n, 1, splits), stream, rlpl::kGemmThreads, rlpl::kGemmDynLds);
 }
 
 }  // namespace
@@ -436,6 +448,7 @@ int selective_logprob_bwd(const void* hidden, const void* weight, const void* bi
     char* ws = static_cast<char*>(workspace);
     void* dz = ws;
     float* split = reinterpret_cast<float*>(ws + L.dz);
+    float* col_part = reinterpret_cast<float*>(ws + L.dz + L.split);
     const size_t elem = elem_bytes(dtype);
     for (int64_t r0 = 0; r0 < n; r0 += L.chunk) {
         const int64_t m = n - r0 < L.chunk ? n - r0 : L.chunk;
@@ -447,6 +460,7 @@ int selective_logprob_bwd(const void* hidden, const void* weight, const void* bi
         g.ldc = L.ld_dz;
         g.lse = lse + r0;
         g.grad = grad_logp + r0;
+        g.col_part = grad_bias ? col_part : nullptr;
         st = launch_gemm(dtype, rlpl::kEpiDlogits, true, true, g, 1, stream);
         if (st != RLPL_OK) return st;
         if (grad_hidden) {
@@ -495,14 +509,14 @@ int selective_logprob_bwd(const void* hidden, const void* weight, const void* bi
             if (st != RLPL_OK) return st;
         }
         if (grad_bias) {
+            // the row tiles' column sums of dz, added in row-tile order
             rlpl::ColSumArgs c{};
-            c.x = dz;
+            c.x = col_part;
             c.out = grad_bias;
-            c.ldx = L.ld_dz;
-            c.rows = int32_t(m);
+            c.rows = int32_t(ceil_div(m, rlpl::kGemmBM));
             c.cols = int32_t(vocab);
             c.accumulate = acc;
-            st = launch(rlpl::pick_col_sum_kernel(dtype), c, dim3(unsigned(ceil_div(vocab, rlpl::kThreads))), stream);
+            st = launch(rlpl::col_sum_kernel(), c, dim3(unsigned(ceil_div(vocab, rlpl::kThreads))), stream);
             if (st != RLPL_OK) return st;
         }
     }

@@ -7,11 +7,14 @@
 
 namespace rlpl {
 
-// Tiles of the MFMA contraction: 128 x 128 outputs per workgroup, 32-deep K steps.
-constexpr int kGemmBM = 128;
-constexpr int kGemmBN = 128;
+// Tiles of the MFMA contraction: 256 x 256 outputs per workgroup (four
+// wavefronts of 128 x 128), 32-deep K steps.
+constexpr int kGemmBM = 256;
+constexpr int kGemmBN = 256;
 constexpr int kGemmBK = 32;
 constexpr int kGemmThreads = 256;
+constexpr int kGemmStages = 4;            // LDS ring of K stages (three in flight)
+constexpr int kGemmDynLds = kGemmStages * 2 * kGemmBM * kGemmBK * 2;   // dynamic LDS bytes per workgroup
 constexpr int kLogprobChunk = 1024;       // rows of logits gradient formed at a time (backward)
 constexpr int kSplitK = 4;                // K splits of the hidden-gradient contraction
 
@@ -37,6 +40,7 @@ struct GemmArgs {
     const float* grad;         // (M) (kEpiDlogits)
     float* part;               // (M, tiles_n, 2) per-tile (max, sum exp) (kEpiLse)
     float* target_logit;       // (M) (kEpiLse)
+    float* col_part;           // (tiles_m, N) per-tile column sums of the logits gradient, or NULL (kEpiDlogits)
 };
 
 const void* pick_gemm_kernel(int dtype, int epi, bool a_kcontig, bool b_kcontig);
@@ -62,13 +66,12 @@ struct SplitSumArgs {
 };
 const void* pick_split_sum_kernel(int dtype);
 
-// Column sums of a (rows, cols) dtype plane into an fp32 vector (add or overwrite), in row order.
+// Sums of `rows` per-tile column partials (rows, cols) fp32 into an fp32 vector (add or overwrite), in row order.
 struct ColSumArgs {
-    const void* x;
+    const float* x;
     float* out;
-    int64_t ldx;
     int32_t rows, cols, accumulate;
 };
-const void* pick_col_sum_kernel(int dtype);
+const void* col_sum_kernel();
 
 }  // namespace rlpl

@@ -39,15 +39,13 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
-template <typename T> struct Mfma;
-template <> struct Mfma<__bf16> {
-    static __device__ __forceinline__ floatx16 run(uint4 a, uint4 b, floatx16 c) {
+// One v_mfma_f32_32x32x16 of the operand type (tag argument selects bf16 or fp16).
+template <typename U> struct Mfma {
+    static __device__ __forceinline__ floatx16 run(uint4 a, uint4 b, floatx16 c, __bf16) {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
                                                        c, 0, 0, 0);
     }
-};
-template <> struct Mfma<_Float16> {
-    static __device__ __forceinline__ floatx16 run(uint4 a, uint4 b, floatx16 c) {
+    static __device__ __forceinline__ floatx16 run(uint4 a, uint4 b, floatx16 c, _Float16) {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b),
                                                       c, 0, 0, 0);
     }
@@ -56,87 +54,110 @@ template <> struct Mfma<_Float16> {
 template <typename T> __device__ __forceinline__ float to_f(T x) { return float(x); }
 template <typename T> __device__ __forceinline__ T from_f(float x) { return T(x); }
 
-constexpr int kLdsK = kGemmBK + 8;        // LDS row: 32 K elements + 8 of padding (80 bytes)
-constexpr int kTileElems = kGemmBM * kLdsK;
+constexpr int kWaveTile = 128;            // rows and columns of C per wavefront
+constexpr int kFrag = kWaveTile / 32;     // 32 x 32 MFMA tiles per wavefront side
+constexpr int kOperandBytes = kGemmBM * kGemmBK * 2;   // one operand tile of one stage: 16 KB
+constexpr int kStageBytes = 2 * kOperandBytes;
+constexpr int kDmaPerOperand = kOperandBytes / 1024 / 4;  // 1 KB copies per wavefront per operand tile
 constexpr float kLog2eG = 1.4426950408889634f;
 
-// One 128 x 32 operand tile in flight: eight 32-bit words per thread.
-struct Stage {
-    uint32_t w[8];
-};
+static_assert(kGemmBM == kGemmBN && kGemmBM == 2 * kWaveTile && kGemmThreads == 256 && kGemmBK == 32,
+              "2 x 2 wavefronts of 128 x 128, 32-deep stages");
+static_assert(kGemmStages * kStageBytes == kGemmDynLds, "LDS ring size");
 
-// Global -> registers for the 128-row (M or N) by 32-deep tile at (r0, k0) of
-// an operand with R rows and K depth; out-of-range elements read as 0.
-// KCONTIG (element (r, k) at x[r*ld + k]): two 16-byte pieces, piece c is
-// row c/4, K elements 8*(c%4) .. +8.
-// Otherwise (element (r, k) at x[k*ld + r]): the thread takes the row pair
-// 2*(tid%64), +1 at the eight K rows 8*(tid/64) .. +8, one 32-bit word per
-// K row (a wavefront's load covers 128 contiguous elements of one K row).
-template <typename T, bool KCONTIG>
-__device__ __forceinline__ void load_stage(const T* __restrict__ x, int64_t ld, int R, int K, int r0, int k0,
-                                           Stage& st) {
-    const uint16_t* __restrict__ h = reinterpret_cast<const uint16_t*>(x);
+// LDS layout of one 256 x 32 operand tile (16 KB), filled by 16-byte
+// global->LDS copies (each wavefront copy writes 1 KB contiguously: lane l's
+// 16 bytes at +16*l), with an XOR swizzle of 16-byte chunks that keeps the
+// matrix-core fragment reads free of bank conflicts.
+//
+// K-contiguous operand (element (r, k) at x[r*ld + k]): row r (0..255) is 64
+// bytes; its K chunk c (elements 8c..8c+7) sits in slot c ^ sw(r), sw(r) =
+// ((r >> 1) ^ (r >> 3)) & 3, which spreads any 8 or 16 consecutive rows' reads
+// of one chunk over distinct banks (32 or 64 banks of 4 bytes).  Fragment
+// reads are one 16-byte read per lane.
+//
+// MN-contiguous operand (element (r, k) at x[k*ld + r]): eight 2 KB blocks of
+// 32 r each; in a block, K row k is 64 bytes and its chunk c (r = 8c..8c+7 of
+// the block) sits in slot c ^ (k & 2).  Fragment reads are two transposing
+// 8-byte reads per lane (ds_read_b64_tr_b16).
+__device__ __forceinline__ int kc_swizzle(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+__device__ __forceinline__ int kc_offset(int r, int c) { return r * 64 + 16 * (c ^ kc_swizzle(r)); }
+__device__ __forceinline__ int mn_offset(int k, int r) {
+    return (r >> 5) * 2048 + k * 64 + 16 * (((r & 31) >> 3) ^ (k & 2)) + 2 * (r & 7);
+}
+
+// Per-lane source of the wavefront's 1 KB copies of one operand tile: copy u
+// (0..3) of wavefront w is copy q = 4w + u of the tile.  Returns the element
+// offset of the lane's 16 bytes for the stage at k0; rows past R are clamped to
+// a valid row (they only feed discarded outputs), K past ke to a valid chunk
+// (zeroed in LDS afterwards).
+template <bool KCONTIG>
+__device__ __forceinline__ int64_t dma_source(int q, int lane, int64_t ld, int R, int ke, int r0, int k0) {
     if constexpr (KCONTIG) {
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int c = threadIdx.x + q * kGemmThreads;
-            const int r = r0 + (c >> 2), k = k0 + 8 * (c & 3);
-            uint4 v = make_uint4(0u, 0u, 0u, 0u);
-            if (r < R) {
-                const uint16_t* p = h + int64_t(r) * ld + k;
-                if (k + 8 <= K) {
-                    v = *reinterpret_cast<const uint4*>(p);
-                } else {
-                    uint32_t e[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
-#pragma unroll
-                    for (int j = 0; j < 8; ++j)
-                        if (k + j < K) e[j] = p[j];
-                    v = make_uint4(e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16),
-                                   e[6] | (e[7] << 16));
-                }
-            }
-            st.w[4 * q + 0] = v.x;
-            st.w[4 * q + 1] = v.y;
-            st.w[4 * q + 2] = v.z;
-            st.w[4 * q + 3] = v.w;
-        }
+        const int r = 16 * q + (lane >> 2);
+        const int c = (lane & 3) ^ kc_swizzle(r);
+        const int row = min(r0 + r, R - 1);
+        int k = k0 + 8 * c;
+        if (k >= ke) k = (ke - 1) & ~7;
+        return int64_t(row) * ld + k;
     } else {
-        const int r = r0 + 2 * (threadIdx.x & 63), kg = k0 + 8 * (threadIdx.x >> 6);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            uint32_t w = 0u;
-            if (kg + j < K) {
-                const uint16_t* p = h + int64_t(kg + j) * ld + r;
-                if (r + 1 < R) w = *reinterpret_cast<const uint32_t*>(p);
-                else if (r < R) w = p[0];
-            }
-            st.w[j] = w;
-        }
+        const int cb = q >> 1, k = 16 * (q & 1) + (lane >> 2);
+        const int c = (lane & 3) ^ (k & 2);
+        int r = r0 + 32 * cb + 8 * c;
+        if (r >= R) r = 0;
+        const int kk = min(k0 + k, ke - 1);
+        return int64_t(kk) * ld + r;
     }
 }
 
-// Registers -> LDS tile laid out [row][k] (K contiguous, kLdsK per row),
-// 16-byte stores only (the transposed operand is repacked in registers).
+__device__ __forceinline__ void dma16(const void* src, void* lds) {
+    __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
+}
+
+// Wait until at most `pending` stages of this wavefront's copies are in flight
+// (8 copies per stage), then meet the other wavefronts.
+__device__ __forceinline__ void wait_stages(int pending) {
+    // s_waitcnt immediates (expcnt and lgkmcnt left at their maxima): vmcnt 16, 8, 0
+    if (pending >= 2) __builtin_amdgcn_s_waitcnt(0x4F70);
+    else if (pending == 1) __builtin_amdgcn_s_waitcnt(0x0F78);
+    else __builtin_amdgcn_s_waitcnt(0x0F70);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Zero the K entries k >= kt (0 < kt < 32) of one operand tile in LDS.
 template <bool KCONTIG>
-__device__ __forceinline__ void store_stage(uint16_t* __restrict__ lds, const Stage& st) {
+__device__ __forceinline__ void zero_k_tail(uint16_t* __restrict__ t, int kt) {
+    const int r = threadIdx.x;   // one tile row (MN index) per thread
+    for (int k = kt; k < kGemmBK; ++k) {
+        const int off = KCONTIG ? kc_offset(r, k >> 3) + 2 * (k & 7) : mn_offset(k, r);
+        t[off >> 1] = 0;
+    }
+}
+
+// Matrix-core fragments of stage tile t for wavefront row/column block wb,
+// 32-row tile f, K step kk (16 K): the eight K values lane l needs for
+// row/column wb*128 + f*32 + l%32, K 8*(l/32) .. +8.
+template <bool KCONTIG>
+__device__ __forceinline__ uint4 fragment(const uint16_t* __restrict__ t, int wb, int f, int kk, int lane) {
     if constexpr (KCONTIG) {
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int c = threadIdx.x + q * kGemmThreads;
-            *reinterpret_cast<uint4*>(lds + (c >> 2) * kLdsK + 8 * (c & 3)) =
-                make_uint4(st.w[4 * q], st.w[4 * q + 1], st.w[4 * q + 2], st.w[4 * q + 3]);
-        }
+        const int r = wb * kWaveTile + f * 32 + (lane & 31);
+        return *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(t) + kc_offset(r, kk * 2 + (lane >> 5)));
     } else {
-        const int r = 2 * (threadIdx.x & 63), k = 8 * (threadIdx.x >> 6);
-        uint32_t lo[4], hi[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t a = st.w[2 * j], b = st.w[2 * j + 1];
-            lo[j] = (a & 0xffffu) | (b << 16);           // row r: K elements 2j, 2j+1
-            hi[j] = (a >> 16) | (b & 0xffff0000u);       // row r+1
-        }
-        *reinterpret_cast<uint4*>(lds + r * kLdsK + k) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-        *reinterpret_cast<uint4*>(lds + (r + 1) * kLdsK + k) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+        // 16-lane group G: columns 16*(G%2) .. +16 of the 32-wide tile, K base 8*(G/2).
+        // Input lane q = 4j + t of the group points at K row kbase + j, columns 4t .. 4t+3;
+        // output lane i then holds K rows kbase .. kbase+3 of column i.
+        const int G = lane >> 4, q = lane & 15;
+        const int r = wb * kWaveTile + f * 32 + 16 * (G & 1) + 4 * (q & 3);
+        const int k = kk * 16 + 8 * (G >> 1) + (q >> 2);
+        typedef short v4s __attribute__((ext_vector_type(4)));
+        const char* base = reinterpret_cast<const char*>(t);
+        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4s*)(base + mn_offset(k, r)));
+        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4s*)(base + mn_offset(k + 4, r)));
+        const uint2 a = __builtin_bit_cast(uint2, lo), b = __builtin_bit_cast(uint2, hi);
+        return make_uint4(a.x, a.y, b.x, b.y);
     }
 }
 
@@ -155,11 +176,11 @@ __device__ __forceinline__ void tile_of(uint32_t b, uint32_t tiles_m, uint32_t t
 }  // namespace
 
 template <typename T, int EPI, bool A_KCONTIG, bool B_KCONTIG>
-__global__ void __launch_bounds__(kGemmThreads) gemm_kernel(const GemmArgs g) {
-    __shared__ __attribute__((aligned(16))) uint16_t As[2][kTileElems];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kTileElems];
-    __shared__ float red_max[2][kGemmBM];
-    __shared__ float red_sum[2][kGemmBM];
+__global__ void __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+gemm_kernel(const GemmArgs g) {
+    extern __shared__ __attribute__((aligned(1024))) uint16_t ring[];   // kGemmStages x (A tile, B tile)
+    __shared__ float red_a[2][kGemmBM];
+    __shared__ float red_b[2][kGemmBM];
 
     uint32_t tm, tn;
     tile_of(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
@@ -168,154 +189,243 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_kernel(const GemmArgs g) {
     const int wm = wave >> 1, wn = wave & 1;
     const int kb = EPI == kEpiSplit ? int(blockIdx.z) * g.k_split : 0;
     const int ke = EPI == kEpiSplit ? min(g.K, kb + g.k_split) : g.K;
-    const T* __restrict__ A = static_cast<const T*>(g.a);
-    const T* __restrict__ B = static_cast<const T*>(g.b);
+    const uint16_t* __restrict__ A = static_cast<const uint16_t*>(g.a);
+    const uint16_t* __restrict__ B = static_cast<const uint16_t*>(g.b);
 
-    floatx16 acc[2][2];
+    // Accumulator element e of tile (i, j) is tile row wm*128 + i*32 + 8*(e/4) +
+    // 4*(lane/32) + e%4 and column wn*128 + j*32 + lane%32.
+    auto row_of_e = [&](int i, int e) { return wm * kWaveTile + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3); };
+    auto col_of_j = [&](int j) { return wn * kWaveTile + j * 32 + (lane & 31); };
+
+    floatx16 acc[kFrag][kFrag];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < kFrag; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < kFrag; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    if (kb < ke) {
-        Stage sa, sb;
-        load_stage<T, A_KCONTIG>(A, g.lda, g.M, ke, m0, kb, sa);
-        load_stage<T, B_KCONTIG>(B, g.ldb, g.N, ke, n0, kb, sb);
-        store_stage<A_KCONTIG>(As[0], sa);
-        store_stage<B_KCONTIG>(Bs[0], sb);
-        __syncthreads();
-        int cur = 0;
-        for (int k0 = kb; k0 < ke; k0 += kGemmBK) {
-            const bool more = k0 + kGemmBK < ke;
-            if (more) {
-                load_stage<T, A_KCONTIG>(A, g.lda, g.M, ke, m0, k0 + kGemmBK, sa);
-                load_stage<T, B_KCONTIG>(B, g.ldb, g.N, ke, n0, k0 + kGemmBK, sb);
-            }
+    const int nst = kb < ke ? (ke - kb + kGemmBK - 1) / kGemmBK : 0;
+    // This wavefront's copies of stage s (8 of 1 KB: four of A, four of B) into ring slot s % stages.
+    auto issue = [&](int s) {
+        const int k0 = kb + s * kGemmBK;
+        char* slot = reinterpret_cast<char*>(ring) + (s % kGemmStages) * kStageBytes;
 #pragma unroll
-            for (int kk = 0; kk < kGemmBK / 16; ++kk) {
-                uint4 af[2], bf[2];
-#pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    const int row = wm * 64 + i * 32 + (lane & 31);
-                    af[i] = *reinterpret_cast<const uint4*>(&As[cur][row * kLdsK + kk * 16 + (lane >> 5) * 8]);
-                }
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const int col = wn * 64 + j * 32 + (lane & 31);
-                    bf[j] = *reinterpret_cast<const uint4*>(&Bs[cur][col * kLdsK + kk * 16 + (lane >> 5) * 8]);
-                }
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) acc[i][j] = Mfma<T>::run(af[i], bf[j], acc[i][j]);
-            }
-            if (more) {
-                store_stage<A_KCONTIG>(As[cur ^ 1], sa);
-                store_stage<B_KCONTIG>(Bs[cur ^ 1], sb);
-            }
-            __syncthreads();
-            cur ^= 1;
+        for (int u = 0; u < kDmaPerOperand; ++u) {
+            const int q = wave * kDmaPerOperand + u;
+            dma16(A + dma_source<A_KCONTIG>(q, lane, g.lda, g.M, ke, m0, k0), slot + q * 1024);
+            dma16(B + dma_source<B_KCONTIG>(q, lane, g.ldb, g.N, ke, n0, k0), slot + kOperandBytes + q * 1024);
         }
+    };
+    for (int s = 0; s < kGemmStages - 1 && s < nst; ++s) issue(s);
+    for (int s = 0; s < nst; ++s) {
+        // stages s+1 .. min(nst-1, s+stages-2) may stay in flight
+        wait_stages(min(nst - 1, s + kGemmStages - 2) - s);
+        if (s + kGemmStages - 1 < nst) issue(s + kGemmStages - 1);   // into the slot read in step s-1
+        const uint16_t* at = ring + (s % kGemmStages) * (kStageBytes / 2);
+        const uint16_t* bt = at + kOperandBytes / 2;
+        const int kt = ke - (kb + s * kGemmBK);
+        if (kt < kGemmBK) {   // last stage of a K range that is not a multiple of 32
+            zero_k_tail<A_KCONTIG>(const_cast<uint16_t*>(at), kt);
+            zero_k_tail<B_KCONTIG>(const_cast<uint16_t*>(bt), kt);
+            __syncthreads();
+        }
+        // fragments of both 16-deep K steps are read up front (the second step's
+        // reads overlap the first step's matrix instructions)
+        uint4 af[2][kFrag], bf[2][kFrag];
+#pragma unroll
+        for (int kk = 0; kk < kGemmBK / 16; ++kk) {
+#pragma unroll
+            for (int i = 0; i < kFrag; ++i) af[kk][i] = fragment<A_KCONTIG>(at, wm, i, kk, lane);
+#pragma unroll
+            for (int j = 0; j < kFrag; ++j) bf[kk][j] = fragment<B_KCONTIG>(bt, wn, j, kk, lane);
+        }
+#pragma unroll
+        for (int kk = 0; kk < kGemmBK / 16; ++kk)
+#pragma unroll
+            for (int i = 0; i < kFrag; ++i)
+#pragma unroll
+                for (int j = 0; j < kFrag; ++j)
+                    acc[i][j] = Mfma<uint16_t>::run(af[kk][i], bf[kk][j], acc[i][j], T());
     }
-
-    // Epilogue.  Accumulator element e of tile (i, j) is output row
-    // wm*64 + i*32 + 8*(e/4) + 4*(lane/32) + e%4 and column wn*64 + j*32 + lane%32.
-    auto row_of_e = [&](int i, int e) { return wm * 64 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3); };
-    const int col_l[2] = {wn * 64 + (lane & 31), wn * 64 + 32 + (lane & 31)};
+    __syncthreads();
 
     if constexpr (EPI == kEpiSplit || EPI == kEpiAccum) {
         float* __restrict__ C = static_cast<float*>(g.c);
         if constexpr (EPI == kEpiSplit) C += int64_t(blockIdx.z) * g.M * g.ldc;
+        if (EPI == kEpiAccum && g.accumulate) {
+            // C += acc, one 32-row tile at a time: its 64 reads are issued together.
+            if (m0 + wm * kWaveTile + kWaveTile <= g.M && n0 + wn * kWaveTile + kWaveTile <= g.N) {
+                // the wavefront's 128 x 128 block lies inside C
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+                for (int i = 0; i < kFrag; ++i) {
+                    float* base = C + int64_t(m0 + row_of_e(i, 0)) * g.ldc + n0 + col_of_j(0);
+                    float old[16][kFrag];
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+                    for (int e = 0; e < 16; ++e)
+#pragma unroll
+                        for (int j = 0; j < kFrag; ++j) old[e][j] = base[int64_t(8 * (e >> 2) + (e & 3)) * g.ldc + 32 * j];
+#pragma unroll
+                    for (int e = 0; e < 16; ++e)
+#pragma unroll
+                        for (int j = 0; j < kFrag; ++j)
+                            base[int64_t(8 * (e >> 2) + (e & 3)) * g.ldc + 32 * j] = old[e][j] + acc[i][j][e];
+                }
+                return;
+            }
+            // edge blocks: reads clamped to a valid element outside M x N, where nothing is stored
+#pragma unroll
+            for (int i = 0; i < kFrag; ++i) {
+                float old[16][kFrag];
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
-                    const int row = m0 + row_of_e(i, e), col = n0 + col_l[j];
-                    if (row < g.M && col < g.N) {
-                        float* p = C + int64_t(row) * g.ldc + col;
-                        *p = (EPI == kEpiAccum && g.accumulate) ? *p + acc[i][j][e] : acc[i][j][e];
+                    const int row = min(m0 + row_of_e(i, e), g.M - 1);
+#pragma unroll
+                    for (int j = 0; j < kFrag; ++j)
+                        old[e][j] = C[int64_t(row) * g.ldc + min(n0 + col_of_j(j), g.N - 1)];
+                }
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int row = m0 + row_of_e(i, e);
+                    if (row >= g.M) continue;
+#pragma unroll
+                    for (int j = 0; j < kFrag; ++j) {
+                        const int col = n0 + col_of_j(j);
+                        if (col < g.N) C[int64_t(row) * g.ldc + col] = old[e][j] + acc[i][j][e];
                     }
                 }
+            }
+            return;
+        }
+#pragma unroll
+        for (int i = 0; i < kFrag; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int row = m0 + row_of_e(i, e);
+                if (row >= g.M) continue;
+#pragma unroll
+                for (int j = 0; j < kFrag; ++j) {
+                    const int col = n0 + col_of_j(j);
+                    if (col < g.N) C[int64_t(row) * g.ldc + col] = acc[i][j][e];
+                }
+            }
         return;
     }
 
     // Logits epilogues: z = acc + bias; columns past N are -inf.
     const T* __restrict__ bias = static_cast<const T*>(g.bias);
-    float bcol[2];
+    float bcol[kFrag];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int col = n0 + col_l[j];
+    for (int j = 0; j < kFrag; ++j) {
+        const int col = n0 + col_of_j(j);
         bcol[j] = col < g.N ? (bias ? to_f<T>(bias[col]) : 0.0f) : -__builtin_inff();
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < kFrag; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < kFrag; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] += bcol[j];
 
     if constexpr (EPI == kEpiDlogits) {
+        // dz = g (onehot - exp(z - lse)), exact zeros outside the M x N range, one
+        // 32-row tile at a time.  Stores: lanes 2c and 2c+1 (columns c, c+1 of a
+        // 32-column group) swap one value so that each writes two adjacent columns
+        // of one row (rows r and r+1 of elements e, e+1) as a 32-bit word.
         T* __restrict__ D = static_cast<T*>(g.c);
+        const bool odd = lane & 1;
+        float csum[kFrag] = {};
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < kFrag; ++i) {
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int row = m0 + row_of_e(i, e);
-                if (row >= g.M) continue;
-                const float l = g.lse[row], gr = g.grad[row];
-                const int64_t tgt = g.targets[row];
+            for (int e = 0; e < 16; e += 2) {
+                float dz[2][kFrag];
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const int col = n0 + col_l[j];
-                    if (col >= g.N) continue;
-                    const float p = __builtin_amdgcn_exp2f((acc[i][j][e] - l) * kLog2eG);
-                    const float dz = gr * ((col == tgt ? 1.0f : 0.0f) - p);
-                    D[int64_t(row) * g.ldc + col] = from_f<T>(dz);
+                for (int h = 0; h < 2; ++h) {
+                    const int row = m0 + row_of_e(i, e + h);
+                    const bool in = row < g.M;
+                    const float l = in ? g.lse[row] : 0.0f, gr = in ? g.grad[row] : 0.0f;
+                    const int64_t tgt = in ? g.targets[row] : -1;
+#pragma unroll
+                    for (int j = 0; j < kFrag; ++j) {
+                        const int col = n0 + col_of_j(j);
+                        const float p = __builtin_amdgcn_exp2f((acc[i][j][e + h] - l) * kLog2eG);
+                        dz[h][j] = (in && col < g.N) ? gr * ((col == tgt ? 1.0f : 0.0f) - p) : 0.0f;
+                        csum[j] += dz[h][j];
+                    }
+                }
+                const int row = m0 + row_of_e(i, e) + (odd ? 1 : 0);
+#pragma unroll
+                for (int j = 0; j < kFrag; ++j) {
+                    const float got = __shfl_xor(odd ? dz[0][j] : dz[1][j], 1, 64);
+                    const float lo = odd ? got : dz[0][j];
+                    const float hi = odd ? dz[1][j] : got;
+                    const int col = n0 + col_of_j(j) - (odd ? 1 : 0);   // even column of the pair
+                    if (row < g.M) {
+                        T* p = D + int64_t(row) * g.ldc + col;
+                        if (col + 1 < g.N) {
+                            *reinterpret_cast<uint32_t*>(p) = Elem<T>::pack(lo, hi);
+                        } else if (col < g.N) {
+                            *p = from_f<T>(lo);
+                        }
+                    }
                 }
             }
+        }
+        if (g.col_part) {
+            // Column sums of dz over the tile's 256 rows (fixed order: the lane's rows,
+            // the two lane halves, the two row wavefronts).
+#pragma unroll
+            for (int j = 0; j < kFrag; ++j) {
+                const float s = csum[j] + __shfl_xor(csum[j], 32, 64);
+                if (lane < 32) red_a[wm][col_of_j(j)] = s;
+            }
+            __syncthreads();
+            const int col = n0 + threadIdx.x;
+            if (col < g.N) g.col_part[int64_t(tm) * g.N + col] = red_a[0][threadIdx.x] + red_a[1][threadIdx.x];
+        }
         return;
     }
 
     // kEpiLse: per row of the tile, (max, sum exp(z - max)) over its columns, and the target logit.
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < kFrag; ++i)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-            float m = fmaxf(acc[i][0][e], acc[i][1][e]);
+            float m = acc[i][0][e];
+#pragma unroll
+            for (int j = 1; j < kFrag; ++j) m = fmaxf(m, acc[i][j][e]);
 #pragma unroll
             for (int off = 1; off < 32; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-            if ((lane & 31) == 0) red_max[wn][row_of_e(i, e)] = m;
+            if ((lane & 31) == 0) red_a[wn][row_of_e(i, e)] = m;
             const int row = m0 + row_of_e(i, e);
             if (row < g.M) {
                 const int64_t tgt = g.targets[row];
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    if (int64_t(n0 + col_l[j]) == tgt) g.target_logit[row] = acc[i][j][e];
+                for (int j = 0; j < kFrag; ++j)
+                    if (int64_t(n0 + col_of_j(j)) == tgt) g.target_logit[row] = acc[i][j][e];
             }
         }
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < kFrag; ++i)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             const int r = row_of_e(i, e);
-            const float M = fmaxf(red_max[0][r], red_max[1][r]);
-            float s = __builtin_amdgcn_exp2f((acc[i][0][e] - M) * kLog2eG) +
-                      __builtin_amdgcn_exp2f((acc[i][1][e] - M) * kLog2eG);
+            const float M = fmaxf(red_a[0][r], red_a[1][r]);
+            float s = 0.0f;
+#pragma unroll
+            for (int j = 0; j < kFrag; ++j) s += __builtin_amdgcn_exp2f((acc[i][j][e] - M) * kLog2eG);
 #pragma unroll
             for (int off = 1; off < 32; off <<= 1) s += __shfl_xor(s, off, 64);
-            if ((lane & 31) == 0) red_sum[wn][r] = s;
+            if ((lane & 31) == 0) red_b[wn][r] = s;
         }
     __syncthreads();
-    if (threadIdx.x < kGemmBM) {
+    {
         const int r = threadIdx.x, row = m0 + r;
         if (row < g.M) {
             float2* p = reinterpret_cast<float2*>(g.part) + int64_t(row) * g.tiles_n + tn;
-            *p = make_float2(fmaxf(red_max[0][r], red_max[1][r]), red_sum[0][r] + red_sum[1][r]);
+            *p = make_float2(fmaxf(red_a[0][r], red_a[1][r]), red_b[0][r] + red_b[1][r]);
         }
     }
 }
@@ -358,13 +468,11 @@ __global__ void __launch_bounds__(kThreads) split_sum(const SplitSumArgs a) {
     }
 }
 
-template <typename T>
 __global__ void __launch_bounds__(kThreads) col_sum(const ColSumArgs a) {
     const int col = blockIdx.x * kThreads + threadIdx.x;
     if (col >= a.cols) return;
-    const T* x = static_cast<const T*>(a.x);
     float s = 0.0f;
-    for (int r = 0; r < a.rows; ++r) s += to_f<T>(x[int64_t(r) * a.ldx + col]);
+    for (int r = 0; r < a.rows; ++r) s += a.x[int64_t(r) * a.cols + col];
     a.out[col] = a.accumulate ? a.out[col] + s : s;
 }
 
@@ -402,12 +510,6 @@ const void* pick_split_sum_kernel(int dtype) {
     return nullptr;
 }
 
-const void* pick_col_sum_kernel(int dtype) {
-    switch (dtype) {
-    case kF16: return reinterpret_cast<const void*>(&col_sum<_Float16>);
-    case kBF16: return reinterpret_cast<const void*>(&col_sum<__bf16>);
-    }
-    return nullptr;
-}
+const void* col_sum_kernel() { return reinterpret_cast<const void*>(&col_sum); }
 
 }  // namespace rlpl

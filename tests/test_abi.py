@@ -304,7 +304,7 @@ LP_CASES = [
     ("RLPL_ERR_ALIGN", dict(b=A + 0x200000 + 1)),
     ("RLPL_ERR_ALIGN", dict(y=A + 0x300000 + 4)),
     ("RLPL_ERR_WORKSPACE", dict(ws=None)),
-    ("RLPL_ERR_WORKSPACE", dict(ws_bytes=4096)),
+    ("RLPL_ERR_WORKSPACE", dict(ws_bytes=256)),
     ("RLPL_ERR_ALIGN", dict(ws=WS + 64)),
 ]
 
@@ -324,9 +324,10 @@ def test_selective_logprob_outputs_and_workspace(lib):
     fwd = lib.selective_logprob_workspace_bytes(1024, 4096, 128256, 0)
     bwd = lib.selective_logprob_workspace_bytes(1024, 4096, 128256, 1)
     # forward: per-tile (max, sum) pairs and target logits of one 1024-token group
-    assert fwd >= 1024 * 1002 * 8 + 1024 * 4 and fwd < 9 << 20
-    # backward: the group's logits gradient (bf16, rows padded to 8) and four fp32 planes of (1024, 4096)
-    assert bwd >= 1024 * 128256 * 2 + 4 * 1024 * 4096 * 4 and bwd < 320 << 20
+    assert fwd >= 1024 * 501 * 8 + 1024 * 4 and fwd < 9 << 20
+    # backward: the group's logits gradient (bf16, rows padded to 8), four fp32 planes of
+    # (1024, 4096) and the column sums of four 256-row tiles
+    assert bwd >= 1024 * 128256 * 2 + 4 * 1024 * 4096 * 4 + 4 * 128256 * 4 and bwd < 320 << 20
     assert lib.selective_logprob_workspace_bytes(5000, 4096, 128256, 1) == bwd   # sized by the group, not n
     assert lib.selective_logprob_workspace_bytes(0, 4096, 128256, 1) == 0
     assert lib.selective_logprob_workspace_bytes(8, 100, 1000, 0) == 0
