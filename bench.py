@@ -27,6 +27,12 @@ Options for context measurements (never the headline line's workload):
                                                  (R, V) logit slabs (default the
                                                  card's example, 1024 x 248320
                                                  bf16, rows valid with p = 0.8)
+  --op logprob|logprob_fwd [--rows N --hidden H --vocab V]
+                                                 selective log-probabilities from
+                                                 hidden states and the output
+                                                 projection on the matrix cores
+                                                 (default one 1024-token group,
+                                                 H = 4096, V = 128256, bf16)
   --floor                                        back-to-back launches of a
                                                  one-element fill kernel (the
                                                  per-launch floor of the GPU)
@@ -54,6 +60,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0   # MI355X HBM3E peak
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 / fp16 matrix-core peak
 METRIC = "tokens/s and achieved HBM GB/s (% of peak) for fused loss fwd+bwd"
 
 
@@ -69,14 +76,18 @@ def algorithmic_bytes(op: str, slots: int, valid: int, bs: int, elem: int, has_k
     return b
 
 
+# The sources the per-token loss kernels and their launch are built from (the
+# full-vocab and log-prob kernels live in files of their own).
+LOSS_KERNEL_SOURCES = ("abi.cpp", "device_common.h", "loss_kernels.h", "loss_kernels.hip", "row_divisor.h")
+
+
 def kernel_source_hash() -> str:
-    """sha256 over rl_post_loss_amd/csrc/* (sorted; each file's name, then its bytes)."""
-    import glob
+    """sha256 over the per-token loss kernel sources (sorted; each file's name, then its bytes)."""
     import hashlib
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "rl_post_loss_amd", "csrc", "*"))):
-        h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
+    for name in sorted(LOSS_KERNEL_SOURCES):
+        h.update(name.encode())
+        with open(os.path.join(ROOT, "rl_post_loss_amd", "csrc", name), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
@@ -244,6 +255,80 @@ def vocab_bench(args, torch):
     return 0
 
 
+def logprob_bench(args, torch):
+    """Selective log-probabilities: one group of tokens, weights resident (1 GB at the default size)."""
+    import rl_post_loss_amd as rl
+    import synthetic
+    n, H, V = args.rows or 1024, args.hidden or 4096, args.vocab or 128256
+    fused = args.op == "logprob"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream
+    lib = rl.library()
+    x = synthetic.device_logprob_inputs(n, H, V, "bf16", 0, "cuda:0")
+    align = lambda t: t.data_ptr() + (-t.data_ptr()) % 256
+    ws_f = torch.empty(lib.selective_logprob_workspace_bytes(n, H, V, 0) + 256, dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(lib.selective_logprob_workspace_bytes(n, H, V, 1) + 256, dtype=torch.uint8, device=dev)
+    logp = torch.empty(n, dtype=torch.float32, device=dev)
+    lse = torch.empty(n, dtype=torch.float32, device=dev)
+    dh = torch.empty(n, H, dtype=torch.bfloat16, device=dev)
+    dw = torch.empty(V, H, dtype=torch.float32, device=dev)
+    db = torch.empty(V, dtype=torch.float32, device=dev)
+    bf16 = rl.DTYPE[torch.bfloat16]
+    common = (x["hidden"].data_ptr(), x["weight"].data_ptr(), x["bias"].data_ptr(), x["targets"].data_ptr())
+
+    def fwd():
+        return lib.selective_logprob_fwd(*common, n, H, V, bf16, logp.data_ptr(), lse.data_ptr(), align(ws_f),
+                                         ws_f.numel() - 256, sptr)
+
+    def step():
+        rc = fwd()
+        return rc or lib.selective_logprob_bwd(*common, lse.data_ptr(), x["grad_logp"].data_ptr(), n, H, V, bf16,
+                                               dh.data_ptr(), dw.data_ptr(), db.data_ptr(), 0, align(ws_b),
+                                               ws_b.numel() - 256, sptr)
+    torch.cuda.synchronize()
+    ms_per_step, ms_gpu = timed(step if fused else fwd, [()], args.steps, args.warmup, stream, torch)
+    _, ms_fwd = timed(fwd, [()], args.steps, args.warmup, stream, torch)
+    if not bool(torch.isfinite(logp).all()):
+        raise RuntimeError("non-finite log-probabilities")
+    # The method's contractions: logits (2nVH) forward; hidden and weight gradients (2nVH each) backward.
+    # The backward here also recomputes the logits (another 2nVH) instead of storing them.
+    alg = 2 * n * V * H * (3 if fused else 1)
+    done = 2 * n * V * H * (4 if fused else 1)
+    tflops = alg / (ms_gpu * 1e-3) / 1e12
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        xh, xw, xb = (oracle.to_f64(x[k][:2] if k == "hidden" else x[k]) for k in ("hidden", "weight", "bias"))
+        y = x["targets"][:2].cpu().numpy()
+        g = oracle.to_f64(x["grad_logp"][:2])
+        t0 = time.perf_counter()
+        oracle.selective_logprob(xh, xw, xb, y, g if fused else None)
+        sec = time.perf_counter() - t0
+        cpu = {"value": round(2 / sec, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"2 tokens of the same problem (H = {H}, V = {V}), {'forward + backward' if fused else 'forward'}, "
+                         f"double precision, one thread: {sec:.2f} s"}
+    print(json.dumps({
+        "metric": "selective log-probs: tokens/s and achieved matrix-core TFLOP/s (% of dense bf16 peak)",
+        "value": round(n / (ms_per_step * 1e-3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"logprob_bf16_{n}x{H}x{V}", "op": "fwd+bwd" if fused else "fwd-only",
+                   "tokens": n, "hidden": H, "vocab": V, "bias": True,
+                   "inputs": "device-generated: hidden N(0,1), weight N(0,4/H), bias N(0,1/4), uniform targets",
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_BF16_TFLOPS, 5), "traffic": None},
+        "cpu_baseline": cpu,
+        "gpu_ms_per_step": round(ms_gpu, 4), "gpu_ms_forward": round(ms_fwd, 4),
+        "forward_TFLOPs": round(2 * n * V * H / (ms_fwd * 1e-3) / 1e12, 2),
+        "algorithmic_flops_per_step": alg, "executed_matrix_flops_per_step": done,
+        "executed_TFLOPs": round(done / (ms_gpu * 1e-3) / 1e12, 2),
+        "context_only": True}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -251,9 +336,10 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="bnpo_bf16_64x4096")
     ap.add_argument("--op", default=None, choices=["bnpo", "bnpo_fwd", "grpo", "grpo_fwd", "rkl", "rkl_fwd",
-                                                   "rkl_logits", "rkl_logits_fwd"])
+                                                   "rkl_logits", "rkl_logits_fwd", "logprob", "logprob_fwd"])
     ap.add_argument("--rows", type=int, default=None)
     ap.add_argument("--vocab", type=int, default=None)
+    ap.add_argument("--hidden", type=int, default=None)
     ap.add_argument("--bs", type=int, default=None)
     ap.add_argument("--seq-len", type=int, default=None)
     ap.add_argument("--beta", type=float, default=None)
@@ -277,6 +363,8 @@ def main() -> int:
         return launch_floor(args, torch)
     if args.op in ("rkl_logits", "rkl_logits_fwd"):
         return vocab_bench(args, torch)
+    if args.op in ("logprob", "logprob_fwd"):
+        return logprob_bench(args, torch)
 
     import rl_post_loss_amd as rl
     import synthetic

@@ -278,7 +278,7 @@ int reverse_kl_logits_fwd(const void* student_logits, const void* teacher_logits
  *               one call in flight per workspace
  *
  * Shapes: 1 <= n < 2^31, hidden_size a multiple of 8 in [8, 65536],
- * 1 <= vocab < 2^26; otherwise RLPL_ERR_SHAPE.  Pointers 4-byte aligned
+ * 1 <= vocab < 2^22; otherwise RLPL_ERR_SHAPE.  Pointers 4-byte aligned
  * where not stated.  Errors as for the other entry points.
  */
 size_t selective_logprob_workspace_bytes(int64_t n, int64_t hidden_size, int64_t vocab, int backward);

@@ -303,7 +303,7 @@ int vocab_loss(bool write_grad, const void* student, const void* teacher, const 
 
 // ----------------------------------------------------------------------------- selective log-probs
 
-constexpr int64_t kLpMaxVocab = int64_t(1) << 26;
+constexpr int64_t kLpMaxVocab = int64_t(1) << 22;   // the kernels address a 256-row panel with 32-bit offsets
 constexpr int64_t kLpMaxHidden = 65536;
 constexpr int64_t kLpMaxTiles = int64_t(1) << 24;   // workgroups per launch (x 256 lanes < 2^32)
 

@@ -71,68 +71,68 @@ static_assert(kGemmStages * kStageBytes == kGemmDynLds, "LDS ring size");
 // matrix-core fragment reads free of bank conflicts.
 //
 // K-contiguous operand (element (r, k) at x[r*ld + k]): row r (0..255) is 64
-// bytes; its K chunk c (elements 8c..8c+7) sits in slot c ^ sw(r), sw(r) =
-// ((r >> 1) ^ (r >> 3)) & 3, which spreads any 8 or 16 consecutive rows' reads
-// of one chunk over distinct banks (32 or 64 banks of 4 bytes).  Fragment
-// reads are one 16-byte read per lane.
+// bytes; its K chunk c (elements 8c..8c+7) sits in slot c ^ ((r >> 2) & 3).
+// Rows four apart fall on the same banks in a 16-byte read, so the swizzle
+// gives rows r, r+4, r+8, r+12 different slots (measured free of bank
+// conflicts on gfx950).  Fragment reads are one 16-byte read per lane.
 //
 // MN-contiguous operand (element (r, k) at x[k*ld + r]): eight 2 KB blocks of
 // 32 r each; in a block, K row k is 64 bytes and its chunk c (r = 8c..8c+7 of
 // the block) sits in slot c ^ (k & 2).  Fragment reads are two transposing
 // 8-byte reads per lane (ds_read_b64_tr_b16).
-__device__ __forceinline__ int kc_swizzle(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+__device__ __forceinline__ int kc_swizzle(int r) { return (r >> 2) & 3; }
 __device__ __forceinline__ int kc_offset(int r, int c) { return r * 64 + 16 * (c ^ kc_swizzle(r)); }
 __device__ __forceinline__ int mn_offset(int k, int r) {
     return (r >> 5) * 2048 + k * 64 + 16 * (((r & 31) >> 3) ^ (k & 2)) + 2 * (r & 7);
 }
 
-// Per-lane source of the wavefront's 1 KB copies of one operand tile: copy u
-// (0..3) of wavefront w is copy q = 4w + u of the tile.  Returns the element
-// offset of the lane's 16 bytes for the stage at k0; rows past R are clamped to
-// a valid row (they only feed discarded outputs), K past ke to a valid chunk
-// (zeroed in LDS afterwards).
+// Per-lane source of the wavefront's 1 KB copies of one operand tile: copy q
+// (0..15; wavefront w issues q = 4w .. 4w+3) of the tile whose first element is
+// (r0, k0).  Returns the byte offset of the lane's 16 bytes from that element
+// (the copy goes through a buffer descriptor based there), or kOutOfRange for a
+// chunk of rows past R or of K at or past ke, which the buffer unit reads as
+// zeros.  A chunk that starts before ke is read whole: the caller guarantees
+// that the elements past ke in it are zeros or that ke is a multiple of 8.
+// Offsets stay below 2 * (32 + 256 * ld) bytes.
+constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;
+constexpr int kBufferRecords = 0x7FFFFFF0;
+
 template <bool KCONTIG>
-__device__ __forceinline__ int64_t dma_source(int q, int lane, int64_t ld, int R, int ke, int r0, int k0) {
+__device__ __forceinline__ uint32_t dma_source(int q, int lane, uint32_t ld, int R, int ke, int r0, int k0) {
     if constexpr (KCONTIG) {
         const int r = 16 * q + (lane >> 2);
         const int c = (lane & 3) ^ kc_swizzle(r);
-        const int row = min(r0 + r, R - 1);
-        int k = k0 + 8 * c;
-        if (k >= ke) k = (ke - 1) & ~7;
-        return int64_t(row) * ld + k;
+        const bool ok = r0 + r < R && k0 + 8 * c < ke;
+        return ok ? 2u * (uint32_t(r) * ld + uint32_t(8 * c)) : kOutOfRange;
     } else {
         const int cb = q >> 1, k = 16 * (q & 1) + (lane >> 2);
         const int c = (lane & 3) ^ (k & 2);
-        int r = r0 + 32 * cb + 8 * c;
-        if (r >= R) r = 0;
-        const int kk = min(k0 + k, ke - 1);
-        return int64_t(kk) * ld + r;
+        const int rr = 32 * cb + 8 * c;
+        const bool ok = r0 + rr < R && k0 + k < ke;
+        return ok ? 2u * (uint32_t(k) * ld + uint32_t(rr)) : kOutOfRange;
     }
 }
 
-__device__ __forceinline__ void dma16(const void* src, void* lds) {
-    __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
+// One 16-byte copy per lane from a buffer (offset `off`) into LDS at lds + 16 * lane.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t src, uint32_t off, void* lds) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (__attribute__((address_space(3))) void*)lds, 16, int(off), 0, 0, 0);
+}
+
+// Raw buffer descriptor over the memory from p on (gfx9 raw-buffer flags).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_at(const void* p) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, kBufferRecords, 0x00020000);
 }
 
 // Wait until at most `pending` stages of this wavefront's copies are in flight
 // (8 copies per stage), then meet the other wavefronts.
 __device__ __forceinline__ void wait_stages(int pending) {
-    // s_waitcnt immediates (expcnt and lgkmcnt left at their maxima): vmcnt 16, 8, 0
-    if (pending >= 2) __builtin_amdgcn_s_waitcnt(0x4F70);
+    // s_waitcnt immediates (expcnt and lgkmcnt left at their maxima): vmcnt 24, 16, 8, 0
+    if (pending >= 3) __builtin_amdgcn_s_waitcnt(0x4F78);
+    else if (pending == 2) __builtin_amdgcn_s_waitcnt(0x4F70);
     else if (pending == 1) __builtin_amdgcn_s_waitcnt(0x0F78);
     else __builtin_amdgcn_s_waitcnt(0x0F70);
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-}
-
-// Zero the K entries k >= kt (0 < kt < 32) of one operand tile in LDS.
-template <bool KCONTIG>
-__device__ __forceinline__ void zero_k_tail(uint16_t* __restrict__ t, int kt) {
-    const int r = threadIdx.x;   // one tile row (MN index) per thread
-    for (int k = kt; k < kGemmBK; ++k) {
-        const int off = KCONTIG ? kc_offset(r, k >> 3) + 2 * (k & 7) : mn_offset(k, r);
-        t[off >> 1] = 0;
-    }
 }
 
 // Matrix-core fragments of stage tile t for wavefront row/column block wb,
@@ -159,6 +159,11 @@ __device__ __forceinline__ uint4 fragment(const uint16_t* __restrict__ t, int wb
         const uint2 a = __builtin_bit_cast(uint2, lo), b = __builtin_bit_cast(uint2, hi);
         return make_uint4(a.x, a.y, b.x, b.y);
     }
+}
+
+// The value of the neighbouring lane (lane ^ 1), by a DPP quad permute [1, 0, 3, 2].
+__device__ __forceinline__ float swap_pair(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
 }
 
 // XCD-aware tile order: consecutive block indices go to different XCDs, so
@@ -210,43 +215,69 @@ gemm_kernel(const GemmArgs g) {
     auto issue = [&](int s) {
         const int k0 = kb + s * kGemmBK;
         char* slot = reinterpret_cast<char*>(ring) + (s % kGemmStages) * kStageBytes;
+        // first element (tile row 0, K k0) of each operand's tile
+        const __amdgpu_buffer_rsrc_t a0 =
+            buffer_at(A + (A_KCONTIG ? int64_t(m0) * g.lda + k0 : int64_t(k0) * g.lda + m0));
+        const __amdgpu_buffer_rsrc_t b0 =
+            buffer_at(B + (B_KCONTIG ? int64_t(n0) * g.ldb + k0 : int64_t(k0) * g.ldb + n0));
 #pragma unroll
         for (int u = 0; u < kDmaPerOperand; ++u) {
             const int q = wave * kDmaPerOperand + u;
-            dma16(A + dma_source<A_KCONTIG>(q, lane, g.lda, g.M, ke, m0, k0), slot + q * 1024);
-            dma16(B + dma_source<B_KCONTIG>(q, lane, g.ldb, g.N, ke, n0, k0), slot + kOperandBytes + q * 1024);
+            dma16(a0, dma_source<A_KCONTIG>(q, lane, uint32_t(g.lda), g.M, ke, m0, k0), slot + q * 1024);
+            dma16(b0, dma_source<B_KCONTIG>(q, lane, uint32_t(g.ldb), g.N, ke, n0, k0),
+                  slot + kOperandBytes + q * 1024);
         }
     };
-    for (int s = 0; s < kGemmStages - 1 && s < nst; ++s) issue(s);
-    for (int s = 0; s < nst; ++s) {
-        // stages s+1 .. min(nst-1, s+stages-2) may stay in flight
-        wait_stages(min(nst - 1, s + kGemmStages - 2) - s);
-        if (s + kGemmStages - 1 < nst) issue(s + kGemmStages - 1);   // into the slot read in step s-1
+    // Make stage s readable: wait for its copies (the later issued ones may stay in
+    // flight) and meet the other wavefronts.
+    auto ready = [&](int s, int issued_last) { wait_stages(issued_last - s); };
+    // Fragments of both 16-deep K steps of stage s.
+    typedef uint4 Frags[2][2][kFrag];   // [kk][A, B][tile]
+    auto read = [&](int s, Frags& f) {
         const uint16_t* at = ring + (s % kGemmStages) * (kStageBytes / 2);
         const uint16_t* bt = at + kOperandBytes / 2;
-        const int kt = ke - (kb + s * kGemmBK);
-        if (kt < kGemmBK) {   // last stage of a K range that is not a multiple of 32
-            zero_k_tail<A_KCONTIG>(const_cast<uint16_t*>(at), kt);
-            zero_k_tail<B_KCONTIG>(const_cast<uint16_t*>(bt), kt);
-            __syncthreads();
-        }
-        // fragments of both 16-deep K steps are read up front (the second step's
-        // reads overlap the first step's matrix instructions)
-        uint4 af[2][kFrag], bf[2][kFrag];
 #pragma unroll
         for (int kk = 0; kk < kGemmBK / 16; ++kk) {
 #pragma unroll
-            for (int i = 0; i < kFrag; ++i) af[kk][i] = fragment<A_KCONTIG>(at, wm, i, kk, lane);
+            for (int i = 0; i < kFrag; ++i) f[kk][0][i] = fragment<A_KCONTIG>(at, wm, i, kk, lane);
 #pragma unroll
-            for (int j = 0; j < kFrag; ++j) bf[kk][j] = fragment<B_KCONTIG>(bt, wn, j, kk, lane);
+            for (int j = 0; j < kFrag; ++j) f[kk][1][j] = fragment<B_KCONTIG>(bt, wn, j, kk, lane);
         }
+    };
+    auto mfma = [&](const Frags& f) {
 #pragma unroll
         for (int kk = 0; kk < kGemmBK / 16; ++kk)
 #pragma unroll
             for (int i = 0; i < kFrag; ++i)
 #pragma unroll
                 for (int j = 0; j < kFrag; ++j)
-                    acc[i][j] = Mfma<uint16_t>::run(af[kk][i], bf[kk][j], acc[i][j], T());
+                    acc[i][j] = Mfma<uint16_t>::run(f[kk][0][i], f[kk][1][j], acc[i][j], T());
+    };
+    // Step s: make stage s+1 readable, refill the slot of stage s (read in step s-1)
+    // with stage s+stages, read stage s+1's fragments into `nxt` while the matrix
+    // instructions of stage s run on `cur`.
+    auto step = [&](int s, const Frags& cur, Frags& nxt) {
+        if (s + 1 < nst) {
+            ready(s + 1, min(nst - 1, s + kGemmStages - 1));
+            if (s + kGemmStages < nst) issue(s + kGemmStages);
+            // `cur` was read a whole step ago: settle those reads here (no stall), so
+            // that the matrix instructions below need not wait for the reads of `nxt`
+            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+            read(s + 1, nxt);
+        }
+        mfma(cur);
+    };
+    if (nst > 0) {
+        for (int s = 0; s < kGemmStages && s < nst; ++s) issue(s);
+        Frags f0, f1;
+        ready(0, min(nst - 1, kGemmStages - 1));
+        read(0, f0);
+        int s = 0;
+        for (; s + 1 < nst; s += 2) {
+            step(s, f0, f1);
+            step(s + 1, f1, f0);
+        }
+        if (s < nst) step(s, f0, f1);
     }
     __syncthreads();
 
@@ -329,9 +360,22 @@ gemm_kernel(const GemmArgs g) {
 
     if constexpr (EPI == kEpiDlogits) {
         // dz = g (onehot - exp(z - lse)), exact zeros outside the M x N range, one
-        // 32-row tile at a time.  Stores: lanes 2c and 2c+1 (columns c, c+1 of a
-        // 32-column group) swap one value so that each writes two adjacent columns
-        // of one row (rows r and r+1 of elements e, e+1) as a 32-bit word.
+        // 32-row tile at a time, with the rows' lse, g and target column staged in
+        // LDS.  Stores: lanes 2c and 2c+1 (columns c, c+1 of a 32-column group)
+        // swap one value (DPP quad permute) so that each writes two adjacent
+        // columns of one row (rows r and r+1 of elements e, e+1) as a 32-bit word.
+        float* row_lse = reinterpret_cast<float*>(ring);
+        float* row_g = row_lse + kGemmBM;
+        int* row_tc = reinterpret_cast<int*>(row_g + kGemmBM);
+        {
+            const int row = m0 + int(threadIdx.x);
+            const bool in = row < g.M;
+            const int64_t t = in ? g.targets[row] : -1;
+            row_lse[threadIdx.x] = in ? g.lse[row] : 0.0f;
+            row_g[threadIdx.x] = in ? g.grad[row] : 0.0f;
+            row_tc[threadIdx.x] = (t >= n0 && t < n0 + kGemmBN && t < g.N) ? int(t - n0) : -1;
+        }
+        __syncthreads();
         T* __restrict__ D = static_cast<T*>(g.c);
         const bool odd = lane & 1;
         float csum[kFrag] = {};
@@ -342,33 +386,29 @@ gemm_kernel(const GemmArgs g) {
                 float dz[2][kFrag];
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
-                    const int row = m0 + row_of_e(i, e + h);
-                    const bool in = row < g.M;
-                    const float l = in ? g.lse[row] : 0.0f, gr = in ? g.grad[row] : 0.0f;
-                    const int64_t tgt = in ? g.targets[row] : -1;
+                    const int r = row_of_e(i, e + h);
+                    const bool in = m0 + r < g.M;
+                    const float l = row_lse[r], gr = row_g[r];
+                    const int tc = row_tc[r];
 #pragma unroll
                     for (int j = 0; j < kFrag; ++j) {
-                        const int col = n0 + col_of_j(j);
+                        const int c = col_of_j(j);
                         const float p = __builtin_amdgcn_exp2f((acc[i][j][e + h] - l) * kLog2eG);
-                        dz[h][j] = (in && col < g.N) ? gr * ((col == tgt ? 1.0f : 0.0f) - p) : 0.0f;
+                        dz[h][j] = (in && n0 + c < g.N) ? gr * ((c == tc ? 1.0f : 0.0f) - p) : 0.0f;
                         csum[j] += dz[h][j];
                     }
                 }
                 const int row = m0 + row_of_e(i, e) + (odd ? 1 : 0);
 #pragma unroll
                 for (int j = 0; j < kFrag; ++j) {
-                    const float got = __shfl_xor(odd ? dz[0][j] : dz[1][j], 1, 64);
+                    const float got = swap_pair(odd ? dz[0][j] : dz[1][j]);
                     const float lo = odd ? got : dz[0][j];
                     const float hi = odd ? dz[1][j] : got;
                     const int col = n0 + col_of_j(j) - (odd ? 1 : 0);   // even column of the pair
-                    if (row < g.M) {
-                        T* p = D + int64_t(row) * g.ldc + col;
-                        if (col + 1 < g.N) {
-                            *reinterpret_cast<uint32_t*>(p) = Elem<T>::pack(lo, hi);
-                        } else if (col < g.N) {
-                            *p = from_f<T>(lo);
-                        }
-                    }
+                    // pairs up to the row pitch (a multiple of 8): the padding columns past N
+                    // get zeros, which the hidden-gradient contraction reads as a K tail
+                    if (row < g.M && col < g.ldc)
+                        *reinterpret_cast<uint32_t*>(D + int64_t(row) * g.ldc + col) = Elem<T>::pack(lo, hi);
                 }
             }
         }
@@ -387,46 +427,51 @@ gemm_kernel(const GemmArgs g) {
         return;
     }
 
-    // kEpiLse: per row of the tile, (max, sum exp(z - max)) over its columns, and the target logit.
-#pragma unroll
-    for (int i = 0; i < kFrag; ++i)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            float m = acc[i][0][e];
-#pragma unroll
-            for (int j = 1; j < kFrag; ++j) m = fmaxf(m, acc[i][j][e]);
-#pragma unroll
-            for (int off = 1; off < 32; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-            if ((lane & 31) == 0) red_a[wn][row_of_e(i, e)] = m;
-            const int row = m0 + row_of_e(i, e);
-            if (row < g.M) {
-                const int64_t tgt = g.targets[row];
-#pragma unroll
-                for (int j = 0; j < kFrag; ++j)
-                    if (int64_t(n0 + col_of_j(j)) == tgt) g.target_logit[row] = acc[i][j][e];
-            }
-        }
+    // kEpiLse: per row of the tile, (max, sum exp(z - max)) over its 256 columns, and
+    // the target logit.  Each lane reduces its own four columns of a row; the 64
+    // partials of a row (two column wavefronts x 32 lanes) meet in LDS, laid out
+    // [partial p][row ^ (p % 32)] so that both the writes (32 lanes, one row) and
+    // the reads (one row per thread) are free of bank conflicts; one thread per
+    // row then merges them in partial order.
+    float2* parts = reinterpret_cast<float2*>(ring);   // 64 x 256 float2 = the whole 128 KB ring
+    int* tgt_col = reinterpret_cast<int*>(red_b);       // target column within the tile, or -1
+    {
+        const int row = m0 + int(threadIdx.x);
+        const int64_t t = row < g.M ? g.targets[row] : -1;
+        tgt_col[threadIdx.x] = (t >= n0 && t < n0 + kGemmBN && t < g.N) ? int(t - n0) : -1;
+    }
     __syncthreads();
+    const int pidx = wn * 32 + (lane & 31);
 #pragma unroll
     for (int i = 0; i < kFrag; ++i)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             const int r = row_of_e(i, e);
-            const float M = fmaxf(red_a[0][r], red_a[1][r]);
-            float s = 0.0f;
+            float m = acc[i][0][e];
 #pragma unroll
-            for (int j = 0; j < kFrag; ++j) s += __builtin_amdgcn_exp2f((acc[i][j][e] - M) * kLog2eG);
+            for (int j = 1; j < kFrag; ++j) m = fmaxf(m, acc[i][j][e]);
+            float sum = 0.0f;
+            if (m != -__builtin_inff()) {
 #pragma unroll
-            for (int off = 1; off < 32; off <<= 1) s += __shfl_xor(s, off, 64);
-            if ((lane & 31) == 0) red_b[wn][r] = s;
+                for (int j = 0; j < kFrag; ++j) sum += __builtin_amdgcn_exp2f((acc[i][j][e] - m) * kLog2eG);
+            }
+            parts[pidx * kGemmBM + (r ^ (pidx & 31))] = make_float2(m, sum);
+            const int tc = tgt_col[r];
+#pragma unroll
+            for (int j = 0; j < kFrag; ++j)
+                if (col_of_j(j) == tc && m0 + r < g.M) g.target_logit[m0 + r] = acc[i][j][e];
         }
     __syncthreads();
     {
         const int r = threadIdx.x, row = m0 + r;
-        if (row < g.M) {
-            float2* p = reinterpret_cast<float2*>(g.part) + int64_t(row) * g.tiles_n + tn;
-            *p = make_float2(fmaxf(red_a[0][r], red_a[1][r]), red_b[0][r] + red_b[1][r]);
+        float M = -__builtin_inff();
+        for (int q = 0; q < 64; ++q) M = fmaxf(M, parts[q * kGemmBM + (r ^ (q & 31))].x);
+        float S = 0.0f;
+        for (int q = 0; q < 64; ++q) {
+            const float2 v = parts[q * kGemmBM + (r ^ (q & 31))];
+            S += v.y * __builtin_amdgcn_exp2f((v.x - M) * kLog2eG);
         }
+        if (row < g.M) reinterpret_cast<float2*>(g.part)[int64_t(row) * g.tiles_n + tn] = make_float2(M, S);
     }
 }
 
