@@ -228,9 +228,6 @@ gemm_kernel(const GemmArgs g) {
                   slot + kOperandBytes + q * 1024);
         }
     };
-    // Make stage s readable: wait for its copies (the later issued ones may stay in
-    // flight) and meet the other wavefronts.
-    auto ready = [&](int s, int issued_last) { wait_stages(issued_last - s); };
     // Fragments of both 16-deep K steps of stage s.
     typedef uint4 Frags[2][2][kFrag];   // [kk][A, B][tile]
     auto read = [&](int s, Frags& f) {
@@ -255,22 +252,33 @@ gemm_kernel(const GemmArgs g) {
     };
     // Step s: make stage s+1 readable, refill the slot of stage s (read in step s-1)
     // with stage s+stages, read stage s+1's fragments into `nxt` while the matrix
-    // instructions of stage s run on `cur`.
+    // instructions of stage s run on `cur`.  The step has no branches: copies of
+    // stages past the last are all out of range (they fill a consumed slot with
+    // zeros), and stage nst's fragments are read but never used, so every step
+    // waits for the same count of copies and forms one scheduling region, in
+    // which reads and matrix instructions are interleaved.
     auto step = [&](int s, const Frags& cur, Frags& nxt) {
-        if (s + 1 < nst) {
-            ready(s + 1, min(nst - 1, s + kGemmStages - 1));
-            if (s + kGemmStages < nst) issue(s + kGemmStages);
-            // `cur` was read a whole step ago: settle those reads here (no stall), so
-            // that the matrix instructions below need not wait for the reads of `nxt`
-            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-            read(s + 1, nxt);
-        }
+        wait_stages(kGemmStages - 2);
+        issue(s + kGemmStages);
+        // `cur` was read a whole step ago: settle those reads here (no stall), so
+        // that the matrix instructions below need not wait for the reads of `nxt`
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+        read(s + 1, nxt);
         mfma(cur);
+        // eight groups of (1/8 of the stage's LDS reads, 4 matrix instructions); a
+        // K-contiguous fragment is one 16-byte read, an MN-contiguous one two
+        // transposing 8-byte reads
+        constexpr int kReads = 2 * kFrag * ((A_KCONTIG ? 1 : 2) + (B_KCONTIG ? 1 : 2));
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x100, kReads / 8, 0);   // LDS reads
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);            // matrix instructions
+        }
     };
     if (nst > 0) {
-        for (int s = 0; s < kGemmStages && s < nst; ++s) issue(s);
+        for (int s = 0; s < kGemmStages; ++s) issue(s);
         Frags f0, f1;
-        ready(0, min(nst - 1, kGemmStages - 1));
+        wait_stages(kGemmStages - 1);
         read(0, f0);
         int s = 0;
         for (; s + 1 < nst; s += 2) {
