@@ -33,6 +33,11 @@ Options for context measurements (never the headline line's workload):
                                                  projection on the matrix cores
                                                  (default one 1024-token group,
                                                  H = 4096, V = 128256, bf16)
+  --op grpo_chain [--bs B]                       the chain policy + reference
+                                                 log-probs -> GRPO loss -> backward
+                                                 into the policy's hidden states,
+                                                 projection and bias (B sequences
+                                                 of 1024 tokens, default 1)
   --floor                                        back-to-back launches of a
                                                  one-element fill kernel (the
                                                  per-launch floor of the GPU)
@@ -329,6 +334,78 @@ def logprob_bench(args, torch):
     return 0
 
 
+def chain_bench(args, torch):
+    """Policy and reference log-probs -> GRPO loss -> policy backward, B sequences of 1024 tokens."""
+    import rl_post_loss_amd as rl
+    import synthetic
+    bs, T, H, V = args.bs or 1, 1024, args.hidden or 4096, args.vocab or 128256
+    n = bs * T
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream
+    lib = rl.library()
+    pol = synthetic.device_logprob_inputs(n, H, V, "bf16", 0, "cuda:0")
+    refm = synthetic.device_logprob_inputs(n, H, V, "bf16", 1, "cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(2)
+    adv = torch.randn(bs, generator=g, device=dev)
+    lengths = torch.randint(T // 4, T + 1, (bs,), generator=g, device=dev)
+    mask = (torch.arange(T, device=dev)[None, :] < lengths[:, None]).to(torch.int8)
+    align = lambda t: t.data_ptr() + (-t.data_ptr()) % 256
+    ws_f = torch.empty(lib.selective_logprob_workspace_bytes(n, H, V, 0) + 256, dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(lib.selective_logprob_workspace_bytes(n, H, V, 1) + 256, dtype=torch.uint8, device=dev)
+    ws_l = rl.workspace_for(dev, sptr, "grpo")
+    lp, lse = torch.empty(n, device=dev), torch.empty(n, device=dev)
+    ref, ref_lse = torch.empty(n, device=dev), torch.empty(n, device=dev)
+    loss, grad = torch.empty((), device=dev), torch.empty(n, device=dev)
+    dh = torch.empty(n, H, dtype=torch.bfloat16, device=dev)
+    dw = torch.empty(V, H, dtype=torch.float32, device=dev)
+    db = torch.empty(V, dtype=torch.float32, device=dev)
+    bf16, f32, i8 = rl.DTYPE[torch.bfloat16], rl.DTYPE[torch.float32], rl.MASK_DTYPE[torch.int8]
+    P = lambda d: (d["hidden"].data_ptr(), d["weight"].data_ptr(), d["bias"].data_ptr(), pol["targets"].data_ptr())
+
+    def fwd(d, out, out_lse):
+        return lib.selective_logprob_fwd(*P(d), n, H, V, bf16, out.data_ptr(), out_lse.data_ptr(), align(ws_f),
+                                         ws_f.numel() - 256, sptr)
+    # behaviour log-probs: the policy's own, slightly perturbed (inputs only, outside the timed region)
+    fwd(pol, lp, lse)
+    torch.cuda.synchronize()
+    old = (lp + 0.05 * torch.randn(n, generator=g, device=dev)).contiguous()
+
+    def step():
+        rc = fwd(pol, lp, lse) or fwd(refm, ref, ref_lse)
+        rc = rc or lib.grpo_loss(lp.data_ptr(), old.data_ptr(), ref.data_ptr(), adv.data_ptr(), mask.data_ptr(),
+                                 bs, T, f32, i8, 0.04, 0.2, 0.28, loss.data_ptr(), grad.data_ptr(), None,
+                                 ws_l.data_ptr(), ws_l.numel(), sptr)
+        return rc or lib.selective_logprob_bwd(*P(pol), lse.data_ptr(), grad.data_ptr(), n, H, V, bf16,
+                                               dh.data_ptr(), dw.data_ptr(), db.data_ptr(), 0, align(ws_b),
+                                               ws_b.numel() - 256, sptr)
+    torch.cuda.synchronize()
+    ms_per_step, ms_gpu = timed(step, [()], args.steps, args.warmup, stream, torch)
+    if not bool(torch.isfinite(loss)):
+        raise RuntimeError("non-finite loss")
+    alg = 2 * n * V * H * 4          # policy and reference logits, hidden and weight gradients
+    done = 2 * n * V * H * 5         # plus the logits recomputed in the backward
+    tflops = alg / (ms_gpu * 1e-3) / 1e12
+    print(json.dumps({
+        "metric": "log-prob -> GRPO chain (policy + reference log-probs, loss, backward): tokens/s and "
+                  "achieved matrix-core TFLOP/s",
+        "value": round(n / (ms_per_step * 1e-3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"grpo_chain_bf16_{bs}x{T}_H{H}_V{V}", "sequences": bs, "tokens": n, "hidden": H,
+                   "vocab": V, "beta": 0.04, "epsilon": 0.2, "epsilon_high": 0.28,
+                   "mask": f"int8 prefix U[{T // 4},{T}]", "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_BF16_TFLOPS, 5), "traffic": None},
+        "cpu_baseline": None,
+        "gpu_ms_per_step": round(ms_gpu, 4), "algorithmic_flops_per_step": alg,
+        "executed_matrix_flops_per_step": done, "executed_TFLOPs": round(done / (ms_gpu * 1e-3) / 1e12, 2),
+        "context_only": True}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -336,7 +413,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="bnpo_bf16_64x4096")
     ap.add_argument("--op", default=None, choices=["bnpo", "bnpo_fwd", "grpo", "grpo_fwd", "rkl", "rkl_fwd",
-                                                   "rkl_logits", "rkl_logits_fwd", "logprob", "logprob_fwd"])
+                                                   "rkl_logits", "rkl_logits_fwd", "logprob", "logprob_fwd",
+                                                   "grpo_chain"])
     ap.add_argument("--rows", type=int, default=None)
     ap.add_argument("--vocab", type=int, default=None)
     ap.add_argument("--hidden", type=int, default=None)
@@ -365,6 +443,8 @@ def main() -> int:
         return vocab_bench(args, torch)
     if args.op in ("logprob", "logprob_fwd"):
         return logprob_bench(args, torch)
+    if args.op == "grpo_chain":
+        return chain_bench(args, torch)
 
     import rl_post_loss_amd as rl
     import synthetic

@@ -25,6 +25,13 @@ mask of shape (bs, seq_len)):
   hidden states N(0, 1) of shape (n, H); output projection N(0, (2/sqrt(H))^2)
   of shape (V, H), so that logits have a standard deviation near 2; bias
   N(0, 0.25); target ids uniform on [0, V); upstream gradient N(0, 1)/n.
+* the log-prob -> GRPO chain (same page, "Summary": policy and reference
+  log-probs, the GRPO loss and its backward): the policy's operands as above;
+  the reference model's hidden states and projection are the policy's plus
+  N(0, 0.1^2) and N(0, (0.1 * 2/sqrt(H))^2) perturbations, same bias;
+  advantages N(0, 1) per row; prefix completion lengths U[lo, seq_len]; and
+  N(0, 0.05^2) noise that the caller adds to the policy's log-probs to form
+  the behaviour (old) log-probs.
 
 All draws come from ``numpy.random.default_rng(seed)`` (PCG64) in float64, in
 the fixed order listed in ``policy_inputs`` / ``rkl_inputs``.
@@ -214,3 +221,26 @@ def device_logprob_inputs(n: int, hidden_size: int, vocab: int, dtype: str, seed
     targets = torch.randint(0, vocab, (n,), generator=g, device=device, dtype=torch.int64)
     grad = torch.randn(n, generator=g, device=device) / max(n, 1)
     return {"hidden": hidden, "weight": weight, "bias": b, "targets": targets, "grad_logp": grad}
+
+
+def chain_inputs(bs: int, seq_len: int, hidden_size: int, vocab: int, dtype: str = "bf16", seed: int = 0,
+                 len_lo: int = 1) -> dict:
+    """Inputs of the log-prob -> GRPO chain over bs x seq_len tokens, as CPU tensors.
+
+    Draw order: the policy's operands (``logprob_inputs`` order, n = bs * seq_len); reference
+    hidden noise (n, H); reference weight noise (V, H); advantages (bs,); prefix lengths;
+    behaviour noise (bs, seq_len).
+    """
+    n = bs * seq_len
+    x = logprob_inputs(n, hidden_size, vocab, dtype, seed, bias=True)
+    rng = np.random.default_rng([seed, 1])
+    h64, w64 = x["hidden"].to(torch.float64).numpy(), x["weight"].to(torch.float64).numpy()
+    ref_hidden = _round(h64 + 0.1 * rng.standard_normal((n, hidden_size)), dtype)
+    ref_weight = _round(w64 + 0.1 * (2.0 / np.sqrt(hidden_size)) * rng.standard_normal((vocab, hidden_size)), dtype)
+    adv = torch.from_numpy(rng.standard_normal(bs)).to(torch.float32)
+    lengths = rng.integers(len_lo, seq_len + 1, size=bs)
+    mask = _prefix_mask(lengths, seq_len, "int8")
+    noise = torch.from_numpy(0.05 * rng.standard_normal((bs, seq_len)))
+    return {"hidden": x["hidden"], "weight": x["weight"], "bias": x["bias"], "targets": x["targets"],
+            "ref_hidden": ref_hidden, "ref_weight": ref_weight, "advantages": adv, "mask": mask,
+            "behaviour_noise": noise}

@@ -42,8 +42,9 @@ def _f64(t):
     return None if t is None else oracle.to_f64(t)
 
 
-def _bounds(x, w, b, y, g, lse_o, dtype, rows=None):
-    """Per-element allowances (logp, grad_hidden, grad_weight, grad_bias) for the given inputs (float64)."""
+def _bounds(x, w, b, y, g, lse_o, dtype, rows=None, g_err=None):
+    """Per-element allowances (logp, grad_hidden, grad_weight, grad_bias) for the given inputs (float64).
+    g_err: a bound on the error of the upstream gradient g itself, per token (or None)."""
     n, H = x.shape
     V = w.shape[0]
     u, sub = UNIT[dtype], SUB[dtype]
@@ -63,6 +64,8 @@ def _bounds(x, w, b, y, g, lse_o, dtype, rows=None):
     dz = g[:, None] * (onehot - p)
     ag = np.abs(g)[:, None]
     edz = ag * dp + 2 * EPS32 * ag * (onehot + p) + u * (np.abs(dz) + ag * dp) + sub
+    if g_err is not None:
+        edz = edz + (1.0 + u) * g_err[:, None] * (onehot + p)
     dh = dz @ w
     dh_tol = edz @ np.abs(w) + (V + 8) * EPS32 * (np.abs(dz) @ np.abs(w)) + u * np.abs(dh) + sub
     wr = slice(None) if rows is None else rows
@@ -79,7 +82,8 @@ def _check(what, got, want, tol):
         i = np.unravel_index(np.argmax(np.where(np.isfinite(err), err / tol, np.inf)), err.shape)
         raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} elements out of tolerance; worst at {i}: "
                              f"got {got[i]!r} oracle {want[i]!r} (allowed {tol[i]:.3e})")
-    return float((err / tol).max()) if err.size else 0.0
+    pos = tol > 0
+    return float((err[pos] / tol[pos]).max()) if pos.any() else 0.0
 
 
 def _to_dev(x):
