@@ -54,23 +54,28 @@ template <typename U> struct Mfma {
 template <typename T> __device__ __forceinline__ float to_f(T x) { return float(x); }
 template <typename T> __device__ __forceinline__ T from_f(float x) { return T(x); }
 
-constexpr int kWaveTile = 128;            // rows and columns of C per wavefront
-constexpr int kFrag = kWaveTile / 32;     // 32 x 32 MFMA tiles per wavefront side
-constexpr int kOperandBytes = kGemmBM * kGemmBK * 2;   // one operand tile of one stage: 16 KB
-constexpr int kStageBytes = 2 * kOperandBytes;
-constexpr int kDmaPerOperand = kOperandBytes / 1024 / 4;  // 1 KB copies per wavefront per operand tile
+constexpr int kWaveM = kGemmBM / 2;      // rows of C per wavefront
+constexpr int kWaveN = kGemmBN / 2;      // columns of C per wavefront
+constexpr int kFragM = kWaveM / 32;      // 32 x 32 MFMA tiles per wavefront, rows
+constexpr int kFragN = kWaveN / 32;      // and columns
+constexpr int kBytesA = kGemmBM * kGemmBK * 2;   // A tile of one stage
+constexpr int kBytesB = kGemmBN * kGemmBK * 2;   // B tile of one stage
+constexpr int kStageBytes = kBytesA + kBytesB;
+constexpr int kDmaA = kBytesA / 1024 / 4;        // 1 KB copies per wavefront for the A tile
+constexpr int kDmaB = kBytesB / 1024 / 4;        // and for the B tile
 constexpr float kLog2eG = 1.4426950408889634f;
 
-static_assert(kGemmBM == kGemmBN && kGemmBM == 2 * kWaveTile && kGemmThreads == 256 && kGemmBK == 32,
-              "2 x 2 wavefronts of 128 x 128, 32-deep stages");
+static_assert(kGemmThreads == 256 && kGemmBK == 32 && kWaveM % 32 == 0 && kWaveN % 32 == 0,
+              "2 x 2 wavefronts, 32-deep stages");
 static_assert(kGemmStages * kStageBytes == kGemmDynLds, "LDS ring size");
+static_assert(kGemmBN == 256 && kGemmBM <= 256, "the epilogues use one thread per tile column / row");
 
-// LDS layout of one 256 x 32 operand tile (16 KB), filled by 16-byte
+// LDS layout of one R x 32 operand tile (R = 128 or 256 rows), filled by 16-byte
 // global->LDS copies (each wavefront copy writes 1 KB contiguously: lane l's
 // 16 bytes at +16*l), with an XOR swizzle of 16-byte chunks that keeps the
 // matrix-core fragment reads free of bank conflicts.
 //
-// K-contiguous operand (element (r, k) at x[r*ld + k]): row r (0..255) is 64
+// K-contiguous operand (element (r, k) at x[r*ld + k]): row r (0..R-1) is 64
 // bytes; its K chunk c (elements 8c..8c+7) sits in slot c ^ ((r >> 2) & 3).
 // Rows four apart fall on the same banks in a 16-byte read, so the swizzle
 // gives rows r, r+4, r+8, r+12 different slots (measured free of bank
@@ -87,7 +92,7 @@ __device__ __forceinline__ int mn_offset(int k, int r) {
 }
 
 // Per-lane source of the wavefront's 1 KB copies of one operand tile: copy q
-// (0..15; wavefront w issues q = 4w .. 4w+3) of the tile whose first element is
+// (0 .. R/16-1; each wavefront issues a quarter of them) of the tile whose first element is
 // (r0, k0).  Returns the byte offset of the lane's 16 bytes from that element
 // (the copy goes through a buffer descriptor based there), or kOutOfRange for a
 // chunk of rows past R or of K at or past ke, which the buffer unit reads as
@@ -123,32 +128,32 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_at(const void* p) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, kBufferRecords, 0x00020000);
 }
 
-// Wait until at most `pending` stages of this wavefront's copies are in flight
-// (8 copies per stage), then meet the other wavefronts.
-__device__ __forceinline__ void wait_stages(int pending) {
-    // s_waitcnt immediates (expcnt and lgkmcnt left at their maxima): vmcnt 24, 16, 8, 0
-    if (pending >= 3) __builtin_amdgcn_s_waitcnt(0x4F78);
-    else if (pending == 2) __builtin_amdgcn_s_waitcnt(0x4F70);
-    else if (pending == 1) __builtin_amdgcn_s_waitcnt(0x0F78);
-    else __builtin_amdgcn_s_waitcnt(0x0F70);
+// s_waitcnt immediate that waits for vmcnt <= v (expcnt and lgkmcnt left at their maxima).
+constexpr int vmcnt_imm(int v) { return 0x0F70 | (v & 15) | ((v >> 4) << 14); }
+
+// Wait until at most `pending` (compile-time) stages of this wavefront's copies
+// (kDmaA + kDmaB per stage) are in flight, then meet the other wavefronts.
+template <int PENDING>
+__device__ __forceinline__ void wait_stages() {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(PENDING * (kDmaA + kDmaB)));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 }
 
-// Matrix-core fragments of stage tile t for wavefront row/column block wb,
-// 32-row tile f, K step kk (16 K): the eight K values lane l needs for
-// row/column wb*128 + f*32 + l%32, K 8*(l/32) .. +8.
-template <bool KCONTIG>
+// Matrix-core fragments of stage tile t for wavefront row/column block wb (of
+// WT rows), 32-row tile f, K step kk (16 K): the eight K values lane l needs
+// for row/column wb*WT + f*32 + l%32, K 8*(l/32) .. +8.
+template <bool KCONTIG, int WT>
 __device__ __forceinline__ uint4 fragment(const uint16_t* __restrict__ t, int wb, int f, int kk, int lane) {
     if constexpr (KCONTIG) {
-        const int r = wb * kWaveTile + f * 32 + (lane & 31);
+        const int r = wb * WT + f * 32 + (lane & 31);
         return *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(t) + kc_offset(r, kk * 2 + (lane >> 5)));
     } else {
         // 16-lane group G: columns 16*(G%2) .. +16 of the 32-wide tile, K base 8*(G/2).
         // Input lane q = 4j + t of the group points at K row kbase + j, columns 4t .. 4t+3;
         // output lane i then holds K rows kbase .. kbase+3 of column i.
         const int G = lane >> 4, q = lane & 15;
-        const int r = wb * kWaveTile + f * 32 + 16 * (G & 1) + 4 * (q & 3);
+        const int r = wb * WT + f * 32 + 16 * (G & 1) + 4 * (q & 3);
         const int k = kk * 16 + 8 * (G >> 1) + (q >> 2);
         typedef short v4s __attribute__((ext_vector_type(4)));
         const char* base = reinterpret_cast<const char*>(t);
@@ -181,11 +186,11 @@ __device__ __forceinline__ void tile_of(uint32_t b, uint32_t tiles_m, uint32_t t
 }  // namespace
 
 template <typename T, int EPI, bool A_KCONTIG, bool B_KCONTIG>
-__global__ void __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm_kernel(const GemmArgs g) {
     extern __shared__ __attribute__((aligned(1024))) uint16_t ring[];   // kGemmStages x (A tile, B tile)
-    __shared__ float red_a[2][kGemmBM];
-    __shared__ float red_b[2][kGemmBM];
+    __shared__ float red_a[2][kGemmBN];
+    __shared__ float red_b[2][kGemmBN];
 
     uint32_t tm, tn;
     tile_of(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
@@ -197,21 +202,23 @@ gemm_kernel(const GemmArgs g) {
     const uint16_t* __restrict__ A = static_cast<const uint16_t*>(g.a);
     const uint16_t* __restrict__ B = static_cast<const uint16_t*>(g.b);
 
-    // Accumulator element e of tile (i, j) is tile row wm*128 + i*32 + 8*(e/4) +
-    // 4*(lane/32) + e%4 and column wn*128 + j*32 + lane%32.
-    auto row_of_e = [&](int i, int e) { return wm * kWaveTile + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3); };
-    auto col_of_j = [&](int j) { return wn * kWaveTile + j * 32 + (lane & 31); };
+    // Accumulator element e of tile (i, j) is tile row wm*kWaveM + i*32 + 8*(e/4) +
+    // 4*(lane/32) + e%4 and column wn*kWaveN + j*32 + lane%32.
+    auto row_of_e = [&](int i, int e) { return wm * kWaveM + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3); };
+    auto col_of_j = [&](int j) { return wn * kWaveN + j * 32 + (lane & 31); };
 
-    floatx16 acc[kFrag][kFrag];
+    floatx16 acc[kFragM][kFragN];
 #pragma unroll
-    for (int i = 0; i < kFrag; ++i)
+    for (int i = 0; i < kFragM; ++i)
 #pragma unroll
-        for (int j = 0; j < kFrag; ++j)
+        for (int j = 0; j < kFragN; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
     const int nst = kb < ke ? (ke - kb + kGemmBK - 1) / kGemmBK : 0;
-    // This wavefront's copies of stage s (8 of 1 KB: four of A, four of B) into ring slot s % stages.
+    // This wavefront's copies of stage s (kDmaA of the A tile, kDmaB of the B tile,
+    // 1 KB each) into ring slot s % stages.  Copies of a stage past the last are all
+    // out of range (zeros).
     auto issue = [&](int s) {
         const int k0 = kb + s * kGemmBK;
         char* slot = reinterpret_cast<char*>(ring) + (s % kGemmStages) * kStageBytes;
@@ -221,71 +228,40 @@ gemm_kernel(const GemmArgs g) {
         const __amdgpu_buffer_rsrc_t b0 =
             buffer_at(B + (B_KCONTIG ? int64_t(n0) * g.ldb + k0 : int64_t(k0) * g.ldb + n0));
 #pragma unroll
-        for (int u = 0; u < kDmaPerOperand; ++u) {
-            const int q = wave * kDmaPerOperand + u;
+        for (int u = 0; u < kDmaA; ++u) {
+            const int q = wave * kDmaA + u;
             dma16(a0, dma_source<A_KCONTIG>(q, lane, uint32_t(g.lda), g.M, ke, m0, k0), slot + q * 1024);
-            dma16(b0, dma_source<B_KCONTIG>(q, lane, uint32_t(g.ldb), g.N, ke, n0, k0),
-                  slot + kOperandBytes + q * 1024);
+        }
+#pragma unroll
+        for (int u = 0; u < kDmaB; ++u) {
+            const int q = wave * kDmaB + u;
+            dma16(b0, dma_source<B_KCONTIG>(q, lane, uint32_t(g.ldb), g.N, ke, n0, k0), slot + kBytesA + q * 1024);
         }
     };
-    // Fragments of both 16-deep K steps of stage s.
-    typedef uint4 Frags[2][2][kFrag];   // [kk][A, B][tile]
-    auto read = [&](int s, Frags& f) {
-        const uint16_t* at = ring + (s % kGemmStages) * (kStageBytes / 2);
-        const uint16_t* bt = at + kOperandBytes / 2;
-#pragma unroll
-        for (int kk = 0; kk < kGemmBK / 16; ++kk) {
-#pragma unroll
-            for (int i = 0; i < kFrag; ++i) f[kk][0][i] = fragment<A_KCONTIG>(at, wm, i, kk, lane);
-#pragma unroll
-            for (int j = 0; j < kFrag; ++j) f[kk][1][j] = fragment<B_KCONTIG>(bt, wn, j, kk, lane);
-        }
-    };
-    auto mfma = [&](const Frags& f) {
-#pragma unroll
-        for (int kk = 0; kk < kGemmBK / 16; ++kk)
-#pragma unroll
-            for (int i = 0; i < kFrag; ++i)
-#pragma unroll
-                for (int j = 0; j < kFrag; ++j)
-                    acc[i][j] = Mfma<uint16_t>::run(f[kk][0][i], f[kk][1][j], acc[i][j], T());
-    };
-    // Step s: make stage s+1 readable, refill the slot of stage s (read in step s-1)
-    // with stage s+stages, read stage s+1's fragments into `nxt` while the matrix
-    // instructions of stage s run on `cur`.  The step has no branches: copies of
-    // stages past the last are all out of range (they fill a consumed slot with
-    // zeros), and stage nst's fragments are read but never used, so every step
-    // waits for the same count of copies and forms one scheduling region, in
-    // which reads and matrix instructions are interleaved.
-    auto step = [&](int s, const Frags& cur, Frags& nxt) {
-        wait_stages(kGemmStages - 2);
-        issue(s + kGemmStages);
-        // `cur` was read a whole step ago: settle those reads here (no stall), so
-        // that the matrix instructions below need not wait for the reads of `nxt`
-        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-        read(s + 1, nxt);
-        mfma(cur);
-        // eight groups of (1/8 of the stage's LDS reads, 4 matrix instructions); a
-        // K-contiguous fragment is one 16-byte read, an MN-contiguous one two
-        // transposing 8-byte reads
-        constexpr int kReads = 2 * kFrag * ((A_KCONTIG ? 1 : 2) + (B_KCONTIG ? 1 : 2));
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x100, kReads / 8, 0);   // LDS reads
-            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);            // matrix instructions
-        }
-    };
+    // Step s: wait for stage s's copies (stage s+1's may stay in flight), meet the
+    // other wavefronts (so every one is done with stage s-1), refill stage s-1's slot
+    // with stage s+2, then the matrix instructions of stage s, one 16-deep K step at a
+    // time.  The other workgroup on the compute unit covers the waits.
     if (nst > 0) {
-        for (int s = 0; s < kGemmStages; ++s) issue(s);
-        Frags f0, f1;
-        wait_stages(kGemmStages - 1);
-        read(0, f0);
-        int s = 0;
-        for (; s + 1 < nst; s += 2) {
-            step(s, f0, f1);
-            step(s + 1, f1, f0);
+        for (int s = 0; s < kGemmStages - 1; ++s) issue(s);
+        for (int s = 0; s < nst; ++s) {
+            wait_stages<kGemmStages - 2>();
+            issue(s + kGemmStages - 1);
+            const uint16_t* at = ring + (s % kGemmStages) * (kStageBytes / 2);
+            const uint16_t* bt = at + kBytesA / 2;
+#pragma unroll
+            for (int kk = 0; kk < kGemmBK / 16; ++kk) {
+                uint4 af[kFragM], bf[kFragN];
+#pragma unroll
+                for (int i = 0; i < kFragM; ++i) af[i] = fragment<A_KCONTIG, kWaveM>(at, wm, i, kk, lane);
+#pragma unroll
+                for (int j = 0; j < kFragN; ++j) bf[j] = fragment<B_KCONTIG, kWaveN>(bt, wn, j, kk, lane);
+#pragma unroll
+                for (int i = 0; i < kFragM; ++i)
+#pragma unroll
+                    for (int j = 0; j < kFragN; ++j) acc[i][j] = Mfma<uint16_t>::run(af[i], bf[j], acc[i][j], T());
+            }
         }
-        if (s < nst) step(s, f0, f1);
     }
     __syncthreads();
 
@@ -294,33 +270,33 @@ gemm_kernel(const GemmArgs g) {
         if constexpr (EPI == kEpiSplit) C += int64_t(blockIdx.z) * g.M * g.ldc;
         if (EPI == kEpiAccum && g.accumulate) {
             // C += acc, one 32-row tile at a time: its 64 reads are issued together.
-            if (m0 + wm * kWaveTile + kWaveTile <= g.M && n0 + wn * kWaveTile + kWaveTile <= g.N) {
+            if (m0 + wm * kWaveM + kWaveM <= g.M && n0 + wn * kWaveN + kWaveN <= g.N) {
                 // the wavefront's 128 x 128 block lies inside C
 #pragma unroll
-                for (int i = 0; i < kFrag; ++i) {
+                for (int i = 0; i < kFragM; ++i) {
                     float* base = C + int64_t(m0 + row_of_e(i, 0)) * g.ldc + n0 + col_of_j(0);
-                    float old[16][kFrag];
+                    float old[16][kFragN];
 #pragma unroll
                     for (int e = 0; e < 16; ++e)
 #pragma unroll
-                        for (int j = 0; j < kFrag; ++j) old[e][j] = base[int64_t(8 * (e >> 2) + (e & 3)) * g.ldc + 32 * j];
+                        for (int j = 0; j < kFragN; ++j) old[e][j] = base[int64_t(8 * (e >> 2) + (e & 3)) * g.ldc + 32 * j];
 #pragma unroll
                     for (int e = 0; e < 16; ++e)
 #pragma unroll
-                        for (int j = 0; j < kFrag; ++j)
+                        for (int j = 0; j < kFragN; ++j)
                             base[int64_t(8 * (e >> 2) + (e & 3)) * g.ldc + 32 * j] = old[e][j] + acc[i][j][e];
                 }
                 return;
             }
             // edge blocks: reads clamped to a valid element outside M x N, where nothing is stored
 #pragma unroll
-            for (int i = 0; i < kFrag; ++i) {
-                float old[16][kFrag];
+            for (int i = 0; i < kFragM; ++i) {
+                float old[16][kFragN];
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     const int row = min(m0 + row_of_e(i, e), g.M - 1);
 #pragma unroll
-                    for (int j = 0; j < kFrag; ++j)
+                    for (int j = 0; j < kFragN; ++j)
                         old[e][j] = C[int64_t(row) * g.ldc + min(n0 + col_of_j(j), g.N - 1)];
                 }
 #pragma unroll
@@ -328,7 +304,7 @@ gemm_kernel(const GemmArgs g) {
                     const int row = m0 + row_of_e(i, e);
                     if (row >= g.M) continue;
 #pragma unroll
-                    for (int j = 0; j < kFrag; ++j) {
+                    for (int j = 0; j < kFragN; ++j) {
                         const int col = n0 + col_of_j(j);
                         if (col < g.N) C[int64_t(row) * g.ldc + col] = old[e][j] + acc[i][j][e];
                     }
@@ -337,13 +313,13 @@ gemm_kernel(const GemmArgs g) {
             return;
         }
 #pragma unroll
-        for (int i = 0; i < kFrag; ++i)
+        for (int i = 0; i < kFragM; ++i)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int row = m0 + row_of_e(i, e);
                 if (row >= g.M) continue;
 #pragma unroll
-                for (int j = 0; j < kFrag; ++j) {
+                for (int j = 0; j < kFragN; ++j) {
                     const int col = n0 + col_of_j(j);
                     if (col < g.N) C[int64_t(row) * g.ldc + col] = acc[i][j][e];
                 }
@@ -353,16 +329,16 @@ gemm_kernel(const GemmArgs g) {
 
     // Logits epilogues: z = acc + bias; columns past N are -inf.
     const T* __restrict__ bias = static_cast<const T*>(g.bias);
-    float bcol[kFrag];
+    float bcol[kFragN];
 #pragma unroll
-    for (int j = 0; j < kFrag; ++j) {
+    for (int j = 0; j < kFragN; ++j) {
         const int col = n0 + col_of_j(j);
         bcol[j] = col < g.N ? (bias ? to_f<T>(bias[col]) : 0.0f) : -__builtin_inff();
     }
 #pragma unroll
-    for (int i = 0; i < kFrag; ++i)
+    for (int i = 0; i < kFragM; ++i)
 #pragma unroll
-        for (int j = 0; j < kFrag; ++j)
+        for (int j = 0; j < kFragN; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] += bcol[j];
 
@@ -375,7 +351,7 @@ gemm_kernel(const GemmArgs g) {
         float* row_lse = reinterpret_cast<float*>(ring);
         float* row_g = row_lse + kGemmBM;
         int* row_tc = reinterpret_cast<int*>(row_g + kGemmBM);
-        {
+        if (threadIdx.x < kGemmBM) {
             const int row = m0 + int(threadIdx.x);
             const bool in = row < g.M;
             const int64_t t = in ? g.targets[row] : -1;
@@ -386,12 +362,12 @@ gemm_kernel(const GemmArgs g) {
         __syncthreads();
         T* __restrict__ D = static_cast<T*>(g.c);
         const bool odd = lane & 1;
-        float csum[kFrag] = {};
+        float csum[kFragN] = {};
 #pragma unroll
-        for (int i = 0; i < kFrag; ++i) {
+        for (int i = 0; i < kFragM; ++i) {
 #pragma unroll
             for (int e = 0; e < 16; e += 2) {
-                float dz[2][kFrag];
+                float dz[2][kFragN];
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const int r = row_of_e(i, e + h);
@@ -399,7 +375,7 @@ gemm_kernel(const GemmArgs g) {
                     const float l = row_lse[r], gr = row_g[r];
                     const int tc = row_tc[r];
 #pragma unroll
-                    for (int j = 0; j < kFrag; ++j) {
+                    for (int j = 0; j < kFragN; ++j) {
                         const int c = col_of_j(j);
                         const float p = __builtin_amdgcn_exp2f((acc[i][j][e + h] - l) * kLog2eG);
                         dz[h][j] = (in && n0 + c < g.N) ? gr * ((c == tc ? 1.0f : 0.0f) - p) : 0.0f;
@@ -408,7 +384,7 @@ gemm_kernel(const GemmArgs g) {
                 }
                 const int row = m0 + row_of_e(i, e) + (odd ? 1 : 0);
 #pragma unroll
-                for (int j = 0; j < kFrag; ++j) {
+                for (int j = 0; j < kFragN; ++j) {
                     const float got = swap_pair(odd ? dz[0][j] : dz[1][j]);
                     const float lo = odd ? got : dz[0][j];
                     const float hi = odd ? dz[1][j] : got;
@@ -424,7 +400,7 @@ gemm_kernel(const GemmArgs g) {
             // Column sums of dz over the tile's 256 rows (fixed order: the lane's rows,
             // the two lane halves, the two row wavefronts).
 #pragma unroll
-            for (int j = 0; j < kFrag; ++j) {
+            for (int j = 0; j < kFragN; ++j) {
                 const float s = csum[j] + __shfl_xor(csum[j], 32, 64);
                 if (lane < 32) red_a[wm][col_of_j(j)] = s;
             }
@@ -441,9 +417,10 @@ gemm_kernel(const GemmArgs g) {
     // [partial p][row ^ (p % 32)] so that both the writes (32 lanes, one row) and
     // the reads (one row per thread) are free of bank conflicts; one thread per
     // row then merges them in partial order.
-    float2* parts = reinterpret_cast<float2*>(ring);   // 64 x 256 float2 = the whole 128 KB ring
+    float2* parts = reinterpret_cast<float2*>(ring);   // 64 x kGemmBM float2, inside the ring
     int* tgt_col = reinterpret_cast<int*>(red_b);       // target column within the tile, or -1
-    {
+    static_assert(64 * kGemmBM * 8 <= kGemmDynLds && kGemmBM <= 2 * kGemmBN, "partials fit");
+    if (threadIdx.x < kGemmBM) {
         const int row = m0 + int(threadIdx.x);
         const int64_t t = row < g.M ? g.targets[row] : -1;
         tgt_col[threadIdx.x] = (t >= n0 && t < n0 + kGemmBN && t < g.N) ? int(t - n0) : -1;
@@ -451,26 +428,26 @@ gemm_kernel(const GemmArgs g) {
     __syncthreads();
     const int pidx = wn * 32 + (lane & 31);
 #pragma unroll
-    for (int i = 0; i < kFrag; ++i)
+    for (int i = 0; i < kFragM; ++i)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             const int r = row_of_e(i, e);
             float m = acc[i][0][e];
 #pragma unroll
-            for (int j = 1; j < kFrag; ++j) m = fmaxf(m, acc[i][j][e]);
+            for (int j = 1; j < kFragN; ++j) m = fmaxf(m, acc[i][j][e]);
             float sum = 0.0f;
             if (m != -__builtin_inff()) {
 #pragma unroll
-                for (int j = 0; j < kFrag; ++j) sum += __builtin_amdgcn_exp2f((acc[i][j][e] - m) * kLog2eG);
+                for (int j = 0; j < kFragN; ++j) sum += __builtin_amdgcn_exp2f((acc[i][j][e] - m) * kLog2eG);
             }
             parts[pidx * kGemmBM + (r ^ (pidx & 31))] = make_float2(m, sum);
             const int tc = tgt_col[r];
 #pragma unroll
-            for (int j = 0; j < kFrag; ++j)
+            for (int j = 0; j < kFragN; ++j)
                 if (col_of_j(j) == tc && m0 + r < g.M) g.target_logit[m0 + r] = acc[i][j][e];
         }
     __syncthreads();
-    {
+    if (threadIdx.x < kGemmBM) {
         const int r = threadIdx.x, row = m0 + r;
         float M = -__builtin_inff();
         for (int q = 0; q < 64; ++q) M = fmaxf(M, parts[q * kGemmBM + (r ^ (q & 31))].x);
