@@ -93,7 +93,7 @@ void init_device(int dev, DeviceInfo& info) {
                     return;
             }
     for (int dt = 0; dt < 3; ++dt) {
-        // fwd+bwd and forward-only share one grid size (identical losses).
+        // fwd+bwd and forward-only share one co-resident capacity (the smaller one).
         const int a = blocks_per_cu(rlpl::pick_vocab_kernel(dt, true));
         const int b = blocks_per_cu(rlpl::pick_vocab_kernel(dt, false));
         if (a < 1 || b < 1) return;
@@ -283,7 +283,7 @@ int vocab_loss(bool write_grad, const void* student, const void* teacher, const 
     const int64_t cap = info->vocab_cap[dtype];
     if (cap < 1) return RLPL_ERR_DEVICE;
     // groups of `chunks` workgroups (one per piece of a row), all co-resident.
-    const rlpl::VocabSplit sp = rlpl::vocab_split(rows, vocab, int(elem_bytes(dtype)), cap);
+    const rlpl::VocabSplit sp = rlpl::vocab_split(rows, vocab, int(elem_bytes(dtype)), cap, write_grad);
     rlpl::VocabArgs a{};
     a.student = student;
     a.teacher = teacher;
@@ -633,7 +633,8 @@ int rlpl_launch_shape(int64_t bs, int64_t seq_len, int dtype, int op, int* grid_
         if (st != RLPL_OK) return st;
         const int64_t cap = info->vocab_cap[dtype];
         if (cap < 1) return RLPL_ERR_DEVICE;
-        const rlpl::VocabSplit sp = rlpl::vocab_split(bs, seq_len, int(elem_bytes(dtype)), cap);
+        const rlpl::VocabSplit sp =
+            rlpl::vocab_split(bs, seq_len, int(elem_bytes(dtype)), cap, op == RLPL_OP_RKL_LOGITS);
         *grid_out = int(sp.groups * sp.chunks);
         *vec_out = int(32 / elem_bytes(dtype));
         *tiles_out = int(bs * sp.chunks > INT32_MAX ? INT32_MAX : bs * sp.chunks);

@@ -26,20 +26,26 @@ struct VocabArgs {
 constexpr int kVocabMaxChunks = 256;      // pieces per row
 constexpr int kVocabMinPieceBlocks = 1024; // a piece is at least 1024 blocks (4 per lane)
 
-// How a (rows, vocab) problem is spread over `cap` co-resident workgroups:
-// one workgroup per row when there are at least as many rows as workgroups,
-// else rows split into pieces of at least kVocabMinPieceBlocks blocks, as many
-// as fill the device.  Every row, wherever it starts, spans at most
-// floor(vocab / per_block) + 2 blocks of per_block elements.
+// How a (rows, vocab) problem is spread over `cap` co-resident workgroups.
+// Forward only (one read of each row): one workgroup per row when there are at
+// least as many rows as workgroups, else rows split into pieces of at least
+// kVocabMinPieceBlocks blocks, as many as fill the device.  Fused (each piece
+// read twice): always pieces of about kVocabMinPieceBlocks blocks (64 KB of
+// both slabs at 16-bit), so that the second read of a piece finds it in L2
+// (measured at 1024 x 248320 bf16: 450 -> 370 us); the forward-only kernel
+// keeps its split (the finer one costs it 155 -> 219 us), so the two losses
+// agree to float32 summation rounding rather than bit for bit when the splits
+// differ.  Every row, wherever it starts, spans at most floor(vocab /
+// per_block) + 2 blocks of per_block elements.
 struct VocabSplit {
     int64_t chunks, chunk_blocks, groups;
 };
-inline VocabSplit vocab_split(int64_t rows, int64_t vocab, int elem, int64_t cap) {
+inline VocabSplit vocab_split(int64_t rows, int64_t vocab, int elem, int64_t cap, bool fused) {
     const int64_t per_block = 32 / elem;
     const int64_t blocks = vocab % per_block == 0 ? vocab / per_block : vocab / per_block + 2;
     int64_t c = rows >= cap ? 1 : cap / rows;
     const int64_t most = (blocks + kVocabMinPieceBlocks - 1) / kVocabMinPieceBlocks;
-    if (c > most) c = most;
+    if (c > most || fused) c = most;
     if (c > kVocabMaxChunks) c = kVocabMaxChunks;
     if (c < 1) c = 1;
     const int64_t chunk_blocks = (blocks + c - 1) / c;

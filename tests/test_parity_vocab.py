@@ -178,7 +178,13 @@ def test_vocab_card_example_size_sampled_rows():
                                          g["mask"].view(4, 256), return_n_valid=True)
     fwd = rl.reverse_kl_logits_fwd(g["student"], g["teacher"], g["mask"])
     torch.cuda.synchronize()
-    assert torch.equal(loss, fwd)
+    # Here the fused kernel splits each row into pieces of ~1024 blocks and the
+    # forward-only kernel reads whole rows, so their float32 sums differ in
+    # order: each is within about (V/1024 + 64) * 2^-24 (relative, per row, of
+    # the row's softmax sums and so of kl_r) of the exact loss; doubled for the
+    # difference of the two, and again as margin.
+    bound = 4 * (V / 1024 + 64) * 2.0 ** -24
+    assert abs(float(loss) - float(fwd)) <= bound * abs(float(loss)), (float(loss), float(fwd), bound)
     m = oracle.to_mask_u8(x["mask"])
     ref = oracle.rkl_logits(x["student"], x["teacher"], m, grad=False)
     assert int(n.cpu()[0]) == ref.n_valid
