@@ -93,11 +93,14 @@ void init_device(int dev, DeviceInfo& info) {
                     return;
             }
     for (int dt = 0; dt < 3; ++dt) {
-        // fwd+bwd and forward-only share one co-resident capacity (the smaller one).
-        const int a = blocks_per_cu(rlpl::pick_vocab_kernel(dt, true));
-        const int b = blocks_per_cu(rlpl::pick_vocab_kernel(dt, false));
-        if (a < 1 || b < 1) return;
-        long cap = long(a < b ? a : b) * cus;
+        // Every variant shares one co-resident capacity (the smallest one).
+        int occ = 0;
+        for (int mode : {rlpl::kVocabFwd, rlpl::kVocabResident, rlpl::kVocabStream}) {
+            const int nb = blocks_per_cu(rlpl::pick_vocab_kernel(dt, mode));
+            if (nb < 1) return;
+            if (occ == 0 || nb < occ) occ = nb;
+        }
+        long cap = long(occ) * cus;
         if (cap > rlpl::kMaxGrid) cap = rlpl::kMaxGrid;
         info.vocab_cap[dt] = int(cap);
     }
@@ -296,7 +299,7 @@ int vocab_loss(bool write_grad, const void* student, const void* teacher, const 
     a.vocab = vocab;
     a.chunks = uint32_t(sp.chunks);
     a.chunk_blocks = uint64_t(sp.chunk_blocks);
-    const void* kernel = rlpl::pick_vocab_kernel(dtype, write_grad);
+    const void* kernel = rlpl::pick_vocab_kernel(dtype, rlpl::vocab_mode(write_grad, sp.chunk_blocks));
     if (!kernel) return RLPL_ERR_DTYPE;
     return launch(kernel, a, dim3(unsigned(sp.groups * sp.chunks)), stream);
 }

@@ -29,14 +29,15 @@ constexpr int kVocabMinPieceBlocks = 1024; // a piece is at least 1024 blocks (4
 // How a (rows, vocab) problem is spread over `cap` co-resident workgroups.
 // Forward only (one read of each row): one workgroup per row when there are at
 // least as many rows as workgroups, else rows split into pieces of at least
-// kVocabMinPieceBlocks blocks, as many as fill the device.  Fused (each piece
-// read twice): always pieces of about kVocabMinPieceBlocks blocks (64 KB of
-// both slabs at 16-bit), so that the second read of a piece finds it in L2
-// (measured at 1024 x 248320 bf16: 450 -> 370 us); the forward-only kernel
-// keeps its split (the finer one costs it 155 -> 219 us), so the two losses
-// agree to float32 summation rounding rather than bit for bit when the splits
-// differ.  Every row, wherever it starts, spans at most floor(vocab /
-// per_block) + 2 blocks of per_block elements.
+// kVocabMinPieceBlocks blocks, as many as fill the device.  Fused: always
+// pieces of about kVocabMinPieceBlocks blocks (64 KB of both slabs at 16-bit),
+// which a workgroup keeps in registers between its two passes (a longer piece,
+// when a row needs more than kVocabMaxChunks pieces, is read a second time).
+// The forward-only kernel keeps its own split (pieces cost it 155 -> 219 us at
+// 1024 x 248320 bf16), so the two losses agree to float32 summation rounding
+// rather than bit for bit when the splits differ.  Every row, wherever it
+// starts, spans at most floor(vocab / per_block) + 2 blocks of per_block
+// elements.
 struct VocabSplit {
     int64_t chunks, chunk_blocks, groups;
 };
@@ -53,7 +54,17 @@ inline VocabSplit vocab_split(int64_t rows, int64_t vocab, int elem, int64_t cap
     return VocabSplit{c, chunk_blocks, groups};
 }
 
-// Kernel for <dtype, fwd+bwd or forward-only>, or nullptr.
-const void* pick_vocab_kernel(int dtype, bool write_grad);
+// Kernel variants: forward only; fwd+bwd with each piece kept in registers
+// between its two passes (pieces of at most kVocabResidentBlocks blocks, four
+// per lane); fwd+bwd reading its piece a second time (longer pieces).
+enum { kVocabFwd = 0, kVocabResident = 1, kVocabStream = 2 };
+constexpr int64_t kVocabResidentBlocks = 1024;
+
+inline int vocab_mode(bool write_grad, int64_t chunk_blocks) {
+    return !write_grad ? kVocabFwd : chunk_blocks <= kVocabResidentBlocks ? kVocabResident : kVocabStream;
+}
+
+// Kernel for <dtype, mode>, or nullptr.
+const void* pick_vocab_kernel(int dtype, int mode);
 
 }  // namespace rlpl

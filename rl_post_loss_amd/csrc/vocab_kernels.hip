@@ -14,26 +14,35 @@
 // of lse, and both are exactly 0 when the rows are equal or vocab is 1.
 //
 // Design (HBM-bound streaming; no contraction, so no MFMA):
-//  * A persistent grid of G = min(rows, co-resident capacity) workgroups;
-//    workgroup w takes rows w, w+G, ...  Rows whose mask byte is zero are
-//    never read (the fwd+bwd kernel writes their gradient as +0).
-//  * Pass 1 reads a row once: each lane keeps, for its elements, the running
-//    maximum of s and of t and the sums sum e^(s-m_s),
-//    sum e^(t-m_t) and sum e^(s-m_s) (s - t), rescaled when a maximum grows
-//    (the online normaliser of Milakov and Gimelshein, 2018).  Four
-//    interleaved accumulators per lane (sharing the maxima) keep the
-//    dependency chains short and each float32 sum to a quarter of a lane's
-//    terms.  Lanes are merged with the same rule over the wavefront, then
-//    over the four waves in LDS.
-//  * The forward-only kernel stops there.  The fwd+bwd kernel reads the row
-//    a second time and writes grad_v = p_v (d_v - E_p[d]) / N.
+//  * A persistent grid of co-resident workgroups, each taking one piece of a
+//    row per round (the whole row when rows are plentiful and the kernel is
+//    forward only).  Rows whose mask byte is zero are never read (the fwd+bwd
+//    kernel writes their gradient as +0).
+//  * Pass 1 reads a row once.  Each lane takes its blocks in groups of four
+//    (loaded together), and keeps for its elements the running maximum of s
+//    and of t and the sums sum e^(s-m_s), sum e^(t-m_t) and
+//    sum e^(s-m_s) (s - t), rescaled when a group raises a maximum (the
+//    online normaliser of Milakov and Gimelshein, 2018).  Four interleaved
+//    accumulators per lane (sharing the maxima) keep the dependency chains
+//    short and each float32 sum to a quarter of a lane's terms.  Lanes are
+//    merged with the same rule over the wavefront, then over the four waves
+//    in LDS.
+//  * The forward-only kernel stops there.  The fwd+bwd kernel then writes
+//    grad_v = p_v (d_v - E_p[d]) / N: from the registers that still hold its
+//    piece of the row (one group per lane), or, for rows too long for that,
+//    by reading the piece a second time.
 //  * N needs no exchange: every workgroup counts the (rows-byte) mask itself.
 //    The loss is the fixed-order sum of per-workgroup partials that
 //    workgroup 0 gathers from the workspace (the protocol of the policy-loss
-//    kernels), so the fused and forward-only losses are bit-identical.
-//  * Rows need not start on a 16-byte boundary: a row covers the aligned
-//    16-byte blocks it touches, full blocks move with 128-bit accesses and the
-//    one or two partial blocks element by element.
+//    kernels), so the fused and forward-only losses are bit-identical when
+//    both split the rows alike.
+//  * Rows need not start on a block boundary: a row covers the 32-byte
+//    blocks (counted from the slab's start) it touches, all read with 128-bit
+//    buffer loads (positions of neighbouring rows are masked in registers; a
+//    read past the slab's end returns zeros); the one or two partial blocks
+//    are written element by element.
+//  * At most 168 VGPRs per lane (three wavefronts per SIMD), so that three
+//    workgroups share a compute unit.
 #include <hip/hip_runtime.h>
 #include <float.h>
 #include <stdint.h>
@@ -145,27 +154,6 @@ __device__ __forceinline__ void block_values(const Plane<T, VEC>& p, uint32_t bi
     }
 }
 
-// Raw words of block b: one 128-bit path for a block inside the row, else
-// element by element for the positions whose bit is set (others left 0).
-template <typename T, int VEC>
-__device__ __forceinline__ void load_raw(const T* __restrict__ base, uint64_t b, uint32_t bits,
-                                         Plane<T, VEC>& p) {
-    const T* __restrict__ q = base + b * VEC;
-    if (bits == all_bits(VEC)) {
-        p.d.load(q);
-    } else {
-#pragma unroll
-        for (int i = 0; i < Plane<T, VEC>::kWords; ++i) p.d.w[i] = 0;
-#pragma unroll
-        for (int k = 0; k < VEC; ++k) {
-            if ((bits >> k) & 1u) {
-                if constexpr (sizeof(T) == 4) p.d.w[k] = reinterpret_cast<const uint32_t*>(q)[k];
-                else p.d.w[k >> 1] |= uint32_t(reinterpret_cast<const uint16_t*>(q)[k]) << (16 * (k & 1));
-            }
-        }
-    }
-}
-
 // Stores VEC gradient values of block b, only the positions whose bit is set.
 template <typename T, int VEC>
 __device__ __forceinline__ void store_bits(T* __restrict__ base, uint64_t b, uint32_t bits, const float (&v)[VEC]) {
@@ -191,6 +179,161 @@ __device__ __forceinline__ void store_bits(T* __restrict__ base, uint64_t b, uin
     }
 }
 
+// Running sums of one lane: one maximum per plane, kAcc interleaved sums.
+struct LaneSums {
+    float ms, mt;
+    float zs[kAcc], zt[kAcc], as[kAcc];
+};
+
+__device__ __forceinline__ void lane_init(LaneSums& L) {
+    L.ms = L.mt = kNone;
+#pragma unroll
+    for (int q = 0; q < kAcc; ++q) L.zs[q] = L.zt[q] = L.as[q] = 0.0f;
+}
+
+constexpr int kGroup = 4;   // blocks a lane loads at once (kThreads apart)
+
+// kGroup blocks of both planes held by one lane: blocks b0 + j * kThreads,
+// j < kGroup; bits[j] == 0 marks a block past the piece's end (not loaded).
+template <typename T, int VEC>
+struct Group {
+    Plane<T, VEC> s[kGroup], t[kGroup];
+    uint32_t bits[kGroup];
+};
+
+// Buffer view of a slab from byte `first` on, `bytes` long (at most 1 GiB):
+// reads at or past its end return zeros without touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slab_view(const void* base, uint64_t first, uint64_t bytes) {
+    const uint32_t n = bytes < (uint64_t(1) << 30) ? uint32_t(bytes) : (1u << 30);
+    return __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(static_cast<const char*>(base) + first), 0, int(n), 0x00020000);
+}
+
+constexpr uint32_t kOffView = 0x80000000u;   // a view offset past every view's end
+
+template <typename T, int VEC>
+__device__ __forceinline__ void set_plane(Plane<T, VEC>& p, const __attribute__((ext_vector_type(4))) uint32_t& h0,
+                                          const __attribute__((ext_vector_type(4))) uint32_t& h1) {
+    static_assert(Plane<T, VEC>::kWords == 8, "a block is 32 bytes");
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { p.d.w[i] = h0[i]; p.d.w[4 + i] = h1[i]; }
+}
+
+// The group of blocks g0 + tid + j * kThreads.  g0 is the same in the whole
+// workgroup; `end16` is the slab's size in bytes rounded up to 16, so a read
+// that starts before the slab's end stays in its last (mapped) page, and one
+// that starts after it returns zeros.  Positions outside the row are masked
+// later, by block_values; blocks past the piece are not read (zeros).
+template <typename T, int VEC>
+__device__ __forceinline__ void load_group(Group<T, VEC>& G, const T* __restrict__ S, const T* __restrict__ Tt,
+                                           uint64_t g0, uint64_t cb1, uint64_t lo, uint64_t hi, uint64_t end16) {
+    const uint64_t first = g0 * 32u;
+    const __amdgpu_buffer_rsrc_t rs = slab_view(S, first, end16 - first);
+    const __amdgpu_buffer_rsrc_t rt = slab_view(Tt, first, end16 - first);
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) {
+        const uint64_t b = g0 + threadIdx.x + uint64_t(j) * kThreads;
+        G.bits[j] = b < cb1 ? block_bits<VEC>(b, lo, hi) : 0u;
+        // view offsets of the two halves (< 32 KB), or past the view's end
+        const uint32_t off = G.bits[j] ? (threadIdx.x + uint32_t(j) * kThreads) * 32u : kOffView;
+        const auto s0 = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+        const auto s1 = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16u, 0, 0);
+        const auto t0 = __builtin_amdgcn_raw_buffer_load_b128(rt, off, 0, 0);
+        const auto t1 = __builtin_amdgcn_raw_buffer_load_b128(rt, off + 16u, 0, 0);
+        set_plane(G.s[j], s0, s1);
+        set_plane(G.t[j], t0, t1);
+    }
+}
+
+// The held words are declared rewritten, so later uses convert them again
+// instead of keeping float copies (twice the registers) alive.
+template <typename T, int VEC>
+__device__ __forceinline__ void opaque(Group<T, VEC>& G) {
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j)
+#pragma unroll
+        for (int i = 0; i < Plane<T, VEC>::kWords; ++i) asm volatile("" : "+v"(G.s[j].d.w[i]), "+v"(G.t[j].d.w[i]));
+}
+
+// Adds a group: the maxima take the whole group first, so the sums are
+// rescaled at most once per group.
+template <typename T, int VEC>
+__device__ __forceinline__ void lane_add(LaneSums& L, Group<T, VEC>& G) {
+    float bs = kNone, bt = kNone;
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) {
+        if (G.bits[j]) {
+            float s[VEC], t[VEC];
+            block_values<T, VEC>(G.s[j], G.bits[j], s);
+            block_values<T, VEC>(G.t[j], G.bits[j], t);
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) { bs = fmaxf(bs, s[k]); bt = fmaxf(bt, t[k]); }
+        }
+    }
+    opaque(G);
+    const float ns = fmaxf(L.ms, bs), nt = fmaxf(L.mt, bt);
+    if (ns > L.ms || nt > L.mt) {
+        const float fs = exp_le0(L.ms - ns), ft = exp_le0(L.mt - nt);
+#pragma unroll
+        for (int q = 0; q < kAcc; ++q) { L.zs[q] *= fs; L.as[q] *= fs; L.zt[q] *= ft; }
+        L.ms = ns;
+        L.mt = nt;
+    }
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) {
+        if (G.bits[j]) {
+            float s[VEC], t[VEC];
+            block_values<T, VEC>(G.s[j], G.bits[j], s);
+            block_values<T, VEC>(G.t[j], G.bits[j], t);
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) {
+                const float es = exp_le0(s[k] - L.ms);
+                const float et = exp_le0(t[k] - L.mt);
+                L.zs[k % kAcc] += es;
+                L.zt[k % kAcc] += et;
+                L.as[k % kAcc] = fmaf(es, s[k] - t[k], L.as[k % kAcc]);
+            }
+        }
+        // one block's floats at a time: the scheduler may not hoist the next block's work
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+__device__ __forceinline__ Stats lane_total(const LaneSums& L) {
+    Stats st{L.ms, L.mt, L.zs[0], L.zt[0], L.as[0]};
+#pragma unroll
+    for (int q = 1; q < kAcc; ++q) { st.zs += L.zs[q]; st.zt += L.zt[q]; st.as += L.as[q]; }
+    return st;
+}
+
+// grad_v = p_v (d_v - E_p[d]) / N for the positions of one block (others unused).
+template <typename T, int VEC>
+__device__ __forceinline__ void grad_block(const Plane<T, VEC>& ps, const Plane<T, VEC>& pt, uint32_t bits,
+                                           float lse_s, float ed, float inv_n, float (&g)[VEC]) {
+    float s[VEC], t[VEC];
+    block_values<T, VEC>(ps, bits, s);
+    block_values<T, VEC>(pt, bits, t);
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) {
+        const float p = exp_le0(s[k] - lse_s);
+        g[k] = p * ((s[k] - t[k]) - ed) * inv_n;
+    }
+}
+
+// The gradient of a group's blocks (g0 as in load_group).
+template <typename T, int VEC>
+__device__ __forceinline__ void grad_group(const Group<T, VEC>& G, T* __restrict__ grad, uint64_t g0, float lse_s,
+                                           float ed, float inv_n) {
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) {
+        if (G.bits[j]) {
+            float g[VEC];
+            grad_block<T, VEC>(G.s[j], G.t[j], G.bits[j], lse_s, ed, inv_n, g);
+            store_bits<T, VEC>(grad, g0 + threadIdx.x + uint64_t(j) * kThreads, G.bits[j], g);
+        }
+    }
+}
+
 }  // namespace
 
 // Rows are split into `chunks` pieces of `chunk_blocks` 32-byte blocks (one
@@ -199,13 +342,17 @@ __device__ __forceinline__ void store_bits(T* __restrict__ base, uint64_t b, uin
 // (R = gridDim.x / chunks), one row per round.  With several pieces, their
 // online sums go to the workspace and are merged in piece order (so every
 // workgroup of the row, and the forward-only kernel, gets the same bits).  The
-// fwd+bwd kernel then reads its piece again to write the gradient.  All
+// fwd+bwd kernel then writes the gradient of its piece: from the registers
+// that still hold it (kVocabResident, pieces of at most kVocabResidentBlocks
+// blocks), or by reading it again (kVocabStream, longer pieces).  All
 // workgroups are co-resident and a round's waits are among workgroups of that
 // round only.
-template <typename T, bool WRITE_GRAD>
-__global__ void __launch_bounds__(kThreads) vocab_kernel(const VocabArgs a) {
+template <typename T, int MODE>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) vocab_kernel(const VocabArgs a) {
     constexpr int VEC = 32 / int(sizeof(T));   // elements per 32-byte block
+    constexpr bool WRITE_GRAD = MODE != kVocabFwd;
     static_assert(VEC % kAcc == 0, "accumulators split a block's elements");
+    static_assert(kGroup * kThreads == kVocabResidentBlocks, "a resident piece is one group per lane");
     const uint64_t chunk_blocks = a.chunk_blocks;
     __shared__ float red_f[kWaves];
     __shared__ uint32_t red_u[kWaves];
@@ -222,6 +369,7 @@ __global__ void __launch_bounds__(kThreads) vocab_kernel(const VocabArgs a) {
     const uint32_t grp = blockIdx.x / C, c = blockIdx.x % C;
     const uint32_t rows = uint32_t(a.rows);
     const uint64_t V = uint64_t(a.vocab);
+    const uint64_t end16 = (uint64_t(rows) * V * sizeof(T) + 15u) & ~uint64_t(15);   // slab bytes, rounded up
     const T* __restrict__ S = static_cast<const T*>(a.student);
     const T* __restrict__ Tt = static_cast<const T*>(a.teacher);
     const uint32_t N = count_rows(a.mask, rows, red_u);
@@ -250,45 +398,24 @@ __global__ void __launch_bounds__(kThreads) vocab_kernel(const VocabArgs a) {
             }
             continue;
         }
-        // Online sums of the chunk (blocks cb0 + tid, cb0 + tid + kThreads, ...).
-        // The lane's four accumulators share one running maximum per plane,
-        // rescaled only when it grows.
-        float ms = kNone, mt = kNone;
-        float zs[kAcc], zt[kAcc], as[kAcc];
-#pragma unroll
-        for (int q = 0; q < kAcc; ++q) zs[q] = zt[q] = as[q] = 0.0f;
-        for (uint64_t b = cb0 + threadIdx.x; b < cb1; b += kThreads) {
-            const uint32_t bits = block_bits<VEC>(b, lo, hi);
-            Plane<T, VEC> ps, pt;
-            load_raw<T, VEC>(S, b, bits, ps);
-            load_raw<T, VEC>(Tt, b, bits, pt);
-            float s[VEC], t[VEC];
-            block_values<T, VEC>(ps, bits, s);
-            block_values<T, VEC>(pt, bits, t);
-            float bs = kNone, bt = kNone;
-#pragma unroll
-            for (int k = 0; k < VEC; ++k) { bs = fmaxf(bs, s[k]); bt = fmaxf(bt, t[k]); }
-            const float ns = fmaxf(ms, bs), nt = fmaxf(mt, bt);
-            if (ns > ms || nt > mt) {
-                const float fs = exp_le0(ms - ns), ft = exp_le0(mt - nt);
-#pragma unroll
-                for (int q = 0; q < kAcc; ++q) { zs[q] *= fs; as[q] *= fs; zt[q] *= ft; }
-                ms = ns;
-                mt = nt;
-            }
-#pragma unroll
-            for (int k = 0; k < VEC; ++k) {
-                const float es = exp_le0(s[k] - ms);
-                const float et = exp_le0(t[k] - mt);
-                zs[k % kAcc] += es;
-                zt[k % kAcc] += et;
-                as[k % kAcc] = fmaf(es, s[k] - t[k], as[k % kAcc]);
+        // Online sums of the chunk: blocks cb0 + tid, cb0 + tid + kThreads, ...,
+        // a group of kGroup at a time, in the same order in every variant.
+        LaneSums acc;
+        lane_init(acc);
+        Group<T, VEC> G;
+        if constexpr (MODE == kVocabResident) {
+            // The piece is one group (at most kGroup * kThreads blocks); it stays
+            // in registers for the gradient.
+            load_group<T, VEC>(G, S, Tt, cb0, cb1, lo, hi, end16);
+            lane_add<T, VEC>(acc, G);
+            opaque(G);
+        } else {
+            for (uint64_t g0 = cb0; g0 < cb1; g0 += kGroup * kThreads) {
+                load_group<T, VEC>(G, S, Tt, g0, cb1, lo, hi, end16);
+                lane_add<T, VEC>(acc, G);
             }
         }
-        Stats st{ms, mt, zs[0], zt[0], as[0]};
-#pragma unroll
-        for (int q = 1; q < kAcc; ++q) { st.zs += zs[q]; st.zt += zt[q]; st.as += as[q]; }
-        st = block_merge(st, red_s);
+        Stats st = block_merge(lane_total(acc), red_s);
         Stats row = st;
         if (C > 1) {
             // Publish the chunk's sums, read every chunk's of this row, merge them in chunk order.
@@ -320,20 +447,13 @@ __global__ void __launch_bounds__(kThreads) vocab_kernel(const VocabArgs a) {
         if constexpr (WRITE_GRAD) {
             // grad_v = p_v (d_v - E_p[d]) / N, p_v = exp(s_v - lse_s).
             const float lse_s = row.ms + ln_zs;
-            for (uint64_t b = cb0 + threadIdx.x; b < cb1; b += kThreads) {
-                const uint32_t bits = block_bits<VEC>(b, lo, hi);
-                Plane<T, VEC> ps, pt;
-                load_raw<T, VEC>(S, b, bits, ps);
-                load_raw<T, VEC>(Tt, b, bits, pt);
-                float s[VEC], t[VEC], g[VEC];
-                block_values<T, VEC>(ps, bits, s);
-                block_values<T, VEC>(pt, bits, t);
-#pragma unroll
-                for (int k = 0; k < VEC; ++k) {
-                    const float p = exp_le0(s[k] - lse_s);
-                    g[k] = p * ((s[k] - t[k]) - ed) * inv_n;
+            if constexpr (MODE == kVocabResident) {
+                grad_group<T, VEC>(G, static_cast<T*>(a.grad), cb0, lse_s, ed, inv_n);
+            } else {
+                for (uint64_t g0 = cb0; g0 < cb1; g0 += kGroup * kThreads) {
+                    load_group<T, VEC>(G, S, Tt, g0, cb1, lo, hi, end16);
+                    grad_group<T, VEC>(G, static_cast<T*>(a.grad), g0, lse_s, ed, inv_n);
                 }
-                store_bits<T, VEC>(static_cast<T*>(a.grad), b, bits, g);
             }
         }
     }
@@ -352,14 +472,21 @@ __global__ void __launch_bounds__(kThreads) vocab_kernel(const VocabArgs a) {
 
 // ----------------------------------------------------------------------------- host-side table
 
-const void* pick_vocab_kernel(int dtype, bool write_grad) {
+template <typename T>
+const void* vocab_kernel_of(int mode) {
+    switch (mode) {
+    case kVocabFwd: return reinterpret_cast<const void*>(&vocab_kernel<T, kVocabFwd>);
+    case kVocabResident: return reinterpret_cast<const void*>(&vocab_kernel<T, kVocabResident>);
+    case kVocabStream: return reinterpret_cast<const void*>(&vocab_kernel<T, kVocabStream>);
+    }
+    return nullptr;
+}
+
+const void* pick_vocab_kernel(int dtype, int mode) {
     switch (dtype) {
-    case kF32: return write_grad ? reinterpret_cast<const void*>(&vocab_kernel<float, true>)
-                                 : reinterpret_cast<const void*>(&vocab_kernel<float, false>);
-    case kF16: return write_grad ? reinterpret_cast<const void*>(&vocab_kernel<_Float16, true>)
-                                 : reinterpret_cast<const void*>(&vocab_kernel<_Float16, false>);
-    case kBF16: return write_grad ? reinterpret_cast<const void*>(&vocab_kernel<__bf16, true>)
-                                  : reinterpret_cast<const void*>(&vocab_kernel<__bf16, false>);
+    case kF32: return vocab_kernel_of<float>(mode);
+    case kF16: return vocab_kernel_of<_Float16>(mode);
+    case kBF16: return vocab_kernel_of<__bf16>(mode);
     }
     return nullptr;
 }

@@ -123,6 +123,23 @@ def test_vocab_rows_split_across_workgroups(dtype, rows, V):
         assert torch.equal(c[0], a) and torch.equal(c[1], ga)
 
 
+@pytest.mark.parametrize("dtype,rows,V", [("bf16", 2, 4_300_000), ("fp32", 1, 2_200_001)])
+def test_vocab_long_pieces_read_twice(dtype, rows, V):
+    # Rows so long that, at the largest number of pieces per row, a piece is
+    # longer than the 1024 32-byte blocks a workgroup keeps in registers: the
+    # fused kernel then reads its piece a second time for the gradient.
+    grid, vec, tiles = rl.launch_shape(rows, V, synthetic.DTYPES[dtype], "rkl_logits")
+    chunks = tiles // rows
+    blocks = V // vec if V % vec == 0 else V // vec + 2
+    assert -(-blocks // chunks) > 1024, (chunks, blocks)
+    x = synthetic.vocab_inputs(rows, V, dtype, "bool", seed=V % 1000, p_valid=1.0)
+    what = f"rkl_logits long pieces {dtype} {rows}x{V} pieces={chunks}"
+    print("[parity]", what, flush=True)
+    a, _ = assert_vocab_parity(x, what)
+    b, _ = assert_vocab_parity(x, what + " fwd", fused=False)
+    assert a.cpu().view(torch.int32).item() == b.cpu().view(torch.int32).item()
+
+
 def test_vocab_leading_dims_and_shifted_logits():
     x = synthetic.vocab_inputs(24, 3000, "fp32", "bool", seed=4)
     x = {"student": (x["student"] + 40.0).reshape(2, 3, 4, 3000),
