@@ -5,7 +5,7 @@
 // weight-gradient accumulation across chunks).
 //
 // Forward: logits tiles z = hidden . weight^T (+ bias) come out of the MFMA
-// contraction and never leave the chip: each 128 x 128 tile's epilogue
+// contraction and never leave the chip: each 128 x 256 tile's epilogue
 // reduces its rows to (max, sum exp(z - max)) partials and picks out the
 // target's logit; a small kernel combines a row's partials into its
 // log-sum-exp and log-probability.
@@ -16,13 +16,15 @@
 // one owner per element) are two more contractions of the same kernel with
 // transposed operand layouts; d bias is a column sum of dz.
 //
-// The contraction: 256 threads (2 x 2 wavefronts), a 128 x 128 output tile,
-// K in steps of 32 staged through LDS (double-buffered, the next step's
-// global loads in flight during the current step's MFMAs), each wavefront a
-// 64 x 64 block of four v_mfma_f32_32x32x16 accumulators.  Operands whose K
-// is contiguous in memory move to LDS with 128-bit stores; the others are
-// transposed on the way in.  Blocks are mapped so that each XCD works on a
-// contiguous run of tiles (shared weight panels stay in its L2).
+// The contraction: 256 threads (2 x 2 wavefronts), a 128 x 256 output tile,
+// each wavefront a 64 x 128 block of eight v_mfma_f32_32x32x16 accumulators
+// held in VGPRs; two workgroups share a compute unit.  K advances in steps of
+// 32 through a ring of three LDS stages filled by buffer-to-LDS copies (two
+// stages in flight while the third is consumed; copies past the operand's end
+// read as zeros).  K-contiguous operands are read from LDS as one 16-byte
+// fragment per lane; MN-contiguous ones with transposing 8-byte LDS reads.
+// Blocks are mapped so that each XCD works on a contiguous run of tiles
+// (shared weight panels stay in its L2).
 #include <hip/hip_runtime.h>
 #include <float.h>
 #include <stdint.h>
