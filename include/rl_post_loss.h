@@ -206,10 +206,11 @@ int reverse_kl_fwd(const void* student_lp, const void* teacher_lp, const void* m
  *
  * N is not clamped (as on the card): with no valid row the loss is NaN and
  * the gradient all +0; that is not an error.  Rows whose mask byte is zero are
- * never read.  The fused kernel reads a valid row twice (softmax sums, then
- * the gradient), reverse_kl_logits_fwd once.  With fewer rows than the device
- * holds workgroups, a row is split among several workgroups that exchange
- * their softmax sums through the workspace.
+ * never read.  A valid row is split among workgroups in pieces of about
+ * 32 KB per slab, which exchange their softmax sums through the workspace;
+ * each holds its piece in registers until the row's sums are known, so the
+ * row is read once.  (Rows of more than 256 such pieces, above about 4.2 M
+ * 16-bit or 2.1 M fp32 logits, are read twice.)
  *
  * student_logits, teacher_logits : (rows, vocab) `dtype`, dense row-major,
  *                                  16-byte aligned (rows themselves need not
@@ -227,7 +228,10 @@ int reverse_kl_logits(const void* student_logits, const void* teacher_logits, co
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Reverse KL over full logit rows, forward only: the same loss as
- * reverse_kl_logits (bit-identical), one read of each valid row, no gradient. */
+ * reverse_kl_logits, one read of each valid row, no gradient.  The two losses
+ * are bit-identical when both split the rows alike (when rows times the
+ * pieces per row fit in the device's co-resident workgroups); otherwise they
+ * agree to float32 summation rounding. */
 int reverse_kl_logits_fwd(const void* student_logits, const void* teacher_logits, const void* mask,
                           int64_t rows, int64_t vocab, int dtype, int mask_dtype,
                           float* loss_out, uint32_t* n_valid_out,

@@ -13,7 +13,9 @@ namespace rlpl {
 constexpr int kGemmBM = 128;
 constexpr int kGemmBN = 256;
 constexpr int kGemmBK = 32;
-constexpr int kGemmThreads = 256;
+constexpr int kGemmWavesM = 2;            // wavefronts along M
+constexpr int kGemmWavesN = 2;            // and along N
+constexpr int kGemmThreads = 64 * kGemmWavesM * kGemmWavesN;
 constexpr int kGemmStages = 3;            // LDS ring of K stages (two in flight)
 constexpr int kGemmDynLds = kGemmStages * (kGemmBM + kGemmBN) * kGemmBK * 2;   // dynamic LDS bytes per workgroup
 constexpr int kLogprobChunk = 1024;       // rows of logits gradient formed at a time (backward)

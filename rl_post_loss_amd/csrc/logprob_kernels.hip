@@ -56,21 +56,24 @@ template <typename U> struct Mfma {
 template <typename T> __device__ __forceinline__ float to_f(T x) { return float(x); }
 template <typename T> __device__ __forceinline__ T from_f(float x) { return T(x); }
 
-constexpr int kWaveM = kGemmBM / 2;      // rows of C per wavefront
-constexpr int kWaveN = kGemmBN / 2;      // columns of C per wavefront
+constexpr int kGemmWaves = kGemmWavesM * kGemmWavesN;
+constexpr int kWaveM = kGemmBM / kGemmWavesM;   // rows of C per wavefront
+constexpr int kWaveN = kGemmBN / kGemmWavesN;   // columns of C per wavefront
 constexpr int kFragM = kWaveM / 32;      // 32 x 32 MFMA tiles per wavefront, rows
 constexpr int kFragN = kWaveN / 32;      // and columns
 constexpr int kBytesA = kGemmBM * kGemmBK * 2;   // A tile of one stage
 constexpr int kBytesB = kGemmBN * kGemmBK * 2;   // B tile of one stage
 constexpr int kStageBytes = kBytesA + kBytesB;
-constexpr int kDmaA = kBytesA / 1024 / 4;        // 1 KB copies per wavefront for the A tile
-constexpr int kDmaB = kBytesB / 1024 / 4;        // and for the B tile
+constexpr int kDmaA = kBytesA / 1024 / kGemmWaves;   // 1 KB copies per wavefront for the A tile
+constexpr int kDmaB = kBytesB / 1024 / kGemmWaves;   // and for the B tile
 constexpr float kLog2eG = 1.4426950408889634f;
 
-static_assert(kGemmThreads == 256 && kGemmBK == 32 && kWaveM % 32 == 0 && kWaveN % 32 == 0,
-              "2 x 2 wavefronts, 32-deep stages");
+static_assert(kGemmBK == 32 && kWaveM % 32 == 0 && kWaveN % 32 == 0, "32 x 32 matrix tiles, 32-deep stages");
+static_assert(kDmaA * kGemmWaves * 1024 == kBytesA && kDmaB * kGemmWaves * 1024 == kBytesB, "whole copies");
 static_assert(kGemmStages * kStageBytes == kGemmDynLds, "LDS ring size");
-static_assert(kGemmBN == 256 && kGemmBM <= 256, "the epilogues use one thread per tile column / row");
+static_assert(kGemmBN == 256 && kGemmBM <= kGemmThreads && kGemmBN <= kGemmThreads,
+              "the epilogues use one thread per tile column / row");
+static_assert(kWaveM == 64 || kWaveM == 128, "log-sum-exp partial layout");
 
 // LDS layout of one R x 32 operand tile (R = 128 or 256 rows), filled by 16-byte
 // global->LDS copies (each wavefront copy writes 1 KB contiguously: lane l's
@@ -191,14 +194,14 @@ template <typename T, int EPI, bool A_KCONTIG, bool B_KCONTIG>
 __global__ void __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm_kernel(const GemmArgs g) {
     extern __shared__ __attribute__((aligned(1024))) uint16_t ring[];   // kGemmStages x (A tile, B tile)
-    __shared__ float red_a[2][kGemmBN];
-    __shared__ float red_b[2][kGemmBN];
+    __shared__ float red_a[kGemmWavesM][kGemmBN];
+    __shared__ int tgt_col[kGemmBM];
 
     uint32_t tm, tn;
     tile_of(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
     const int m0 = int(tm) * kGemmBM, n0 = int(tn) * kGemmBN;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / kGemmWavesN, wn = wave % kGemmWavesN;
     const int kb = EPI == kEpiSplit ? int(blockIdx.z) * g.k_split : 0;
     const int ke = EPI == kEpiSplit ? min(g.K, kb + g.k_split) : g.K;
     const uint16_t* __restrict__ A = static_cast<const uint16_t*>(g.a);
@@ -273,7 +276,7 @@ gemm_kernel(const GemmArgs g) {
         if (EPI == kEpiAccum && g.accumulate) {
             // C += acc, one 32-row tile at a time: its 64 reads are issued together.
             if (m0 + wm * kWaveM + kWaveM <= g.M && n0 + wn * kWaveN + kWaveN <= g.N) {
-                // the wavefront's 128 x 128 block lies inside C
+                // the wavefront's kWaveM x kWaveN block lies inside C
 #pragma unroll
                 for (int i = 0; i < kFragM; ++i) {
                     float* base = C + int64_t(m0 + row_of_e(i, 0)) * g.ldc + n0 + col_of_j(0);
@@ -399,66 +402,81 @@ gemm_kernel(const GemmArgs g) {
             }
         }
         if (g.col_part) {
-            // Column sums of dz over the tile's 256 rows (fixed order: the lane's rows,
-            // the two lane halves, the two row wavefronts).
+            // Column sums of dz over the tile's rows (fixed order: the lane's rows,
+            // the two lane halves, the row wavefronts in order).
 #pragma unroll
             for (int j = 0; j < kFragN; ++j) {
                 const float s = csum[j] + __shfl_xor(csum[j], 32, 64);
                 if (lane < 32) red_a[wm][col_of_j(j)] = s;
             }
             __syncthreads();
-            const int col = n0 + threadIdx.x;
-            if (col < g.N) g.col_part[int64_t(tm) * g.N + col] = red_a[0][threadIdx.x] + red_a[1][threadIdx.x];
+            const int col = n0 + int(threadIdx.x);
+            if (threadIdx.x < kGemmBN && col < g.N) {
+                float t = red_a[0][threadIdx.x];
+#pragma unroll
+                for (int w = 1; w < kGemmWavesM; ++w) t += red_a[w][threadIdx.x];
+                g.col_part[int64_t(tm) * g.N + col] = t;
+            }
         }
         return;
     }
 
     // kEpiLse: per row of the tile, (max, sum exp(z - max)) over its 256 columns, and
-    // the target logit.  Each lane reduces its own four columns of a row; the 64
-    // partials of a row (two column wavefronts x 32 lanes) meet in LDS, laid out
-    // [partial p][row ^ (p % 32)] so that both the writes (32 lanes, one row) and
-    // the reads (one row per thread) are free of bank conflicts; one thread per
-    // row then merges them in partial order.
-    float2* parts = reinterpret_cast<float2*>(ring);   // 64 x kGemmBM float2, inside the ring
-    int* tgt_col = reinterpret_cast<int*>(red_b);       // target column within the tile, or -1
-    static_assert(64 * kGemmBM * 8 <= kGemmDynLds && kGemmBM <= 2 * kGemmBN, "partials fit");
+    // the target logit.  Each lane reduces its own kFragN columns of a row; the
+    // kGemmWavesN * 32 partials of a row (column wavefronts x 32 lanes) meet in LDS,
+    // laid out [partial p][row ^ (p % 32)] so that both the writes (32 lanes, one
+    // row) and the reads (one row per thread) are free of bank conflicts; one
+    // thread per row then merges them in partial order.  When the partials of all
+    // rows do not fit in the ring, the row wavefronts take turns.
+    constexpr int kParts = kGemmWavesN * 32;
+    constexpr int kRounds = kParts * kGemmBM * 8 <= kGemmDynLds ? 1 : kGemmWavesM;
+    constexpr int kRoundRows = kGemmBM / kRounds;
+    float2* parts = reinterpret_cast<float2*>(ring);   // kParts x kRoundRows float2, inside the ring
+    static_assert(kParts * kRoundRows * 8 <= kGemmDynLds && kRoundRows % 32 == 0, "partials fit");
     if (threadIdx.x < kGemmBM) {
         const int row = m0 + int(threadIdx.x);
         const int64_t t = row < g.M ? g.targets[row] : -1;
         tgt_col[threadIdx.x] = (t >= n0 && t < n0 + kGemmBN && t < g.N) ? int(t - n0) : -1;
     }
-    __syncthreads();
     const int pidx = wn * 32 + (lane & 31);
+    const int my_round = wm * kRounds / kGemmWavesM;
 #pragma unroll
-    for (int i = 0; i < kFragM; ++i)
+    for (int w = 0; w < kRounds; ++w) {
+        __syncthreads();                                // tgt_col written; parts free
+        if (my_round == w) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int r = row_of_e(i, e);
-            float m = acc[i][0][e];
+            for (int i = 0; i < kFragM; ++i)
 #pragma unroll
-            for (int j = 1; j < kFragN; ++j) m = fmaxf(m, acc[i][j][e]);
-            float sum = 0.0f;
-            if (m != -__builtin_inff()) {
+                for (int e = 0; e < 16; ++e) {
+                    const int r = row_of_e(i, e);
+                    float m = acc[i][0][e];
 #pragma unroll
-                for (int j = 0; j < kFragN; ++j) sum += __builtin_amdgcn_exp2f((acc[i][j][e] - m) * kLog2eG);
+                    for (int j = 1; j < kFragN; ++j) m = fmaxf(m, acc[i][j][e]);
+                    float sum = 0.0f;
+                    if (m != -__builtin_inff()) {
+#pragma unroll
+                        for (int j = 0; j < kFragN; ++j) sum += __builtin_amdgcn_exp2f((acc[i][j][e] - m) * kLog2eG);
+                    }
+                    const int rr = r - w * kRoundRows;
+                    parts[pidx * kRoundRows + (rr ^ (pidx & 31))] = make_float2(m, sum);
+                    const int tc = tgt_col[r];
+#pragma unroll
+                    for (int j = 0; j < kFragN; ++j)
+                        if (col_of_j(j) == tc && m0 + r < g.M) g.target_logit[m0 + r] = acc[i][j][e];
+                }
+        }
+        __syncthreads();
+        if (threadIdx.x < kRoundRows) {
+            const int rr = threadIdx.x, row = m0 + w * kRoundRows + rr;
+            float M = -__builtin_inff();
+            for (int q = 0; q < kParts; ++q) M = fmaxf(M, parts[q * kRoundRows + (rr ^ (q & 31))].x);
+            float S = 0.0f;
+            for (int q = 0; q < kParts; ++q) {
+                const float2 v = parts[q * kRoundRows + (rr ^ (q & 31))];
+                S += v.y * __builtin_amdgcn_exp2f((v.x - M) * kLog2eG);
             }
-            parts[pidx * kGemmBM + (r ^ (pidx & 31))] = make_float2(m, sum);
-            const int tc = tgt_col[r];
-#pragma unroll
-            for (int j = 0; j < kFragN; ++j)
-                if (col_of_j(j) == tc && m0 + r < g.M) g.target_logit[m0 + r] = acc[i][j][e];
+            if (row < g.M) reinterpret_cast<float2*>(g.part)[int64_t(row) * g.tiles_n + tn] = make_float2(M, S);
         }
-    __syncthreads();
-    if (threadIdx.x < kGemmBM) {
-        const int r = threadIdx.x, row = m0 + r;
-        float M = -__builtin_inff();
-        for (int q = 0; q < 64; ++q) M = fmaxf(M, parts[q * kGemmBM + (r ^ (q & 31))].x);
-        float S = 0.0f;
-        for (int q = 0; q < 64; ++q) {
-            const float2 v = parts[q * kGemmBM + (r ^ (q & 31))];
-            S += v.y * __builtin_amdgcn_exp2f((v.x - M) * kLog2eG);
-        }
-        if (row < g.M) reinterpret_cast<float2*>(g.part)[int64_t(row) * g.tiles_n + tn] = make_float2(M, S);
     }
 }
 
