@@ -5,7 +5,7 @@
 // weight-gradient accumulation across chunks).
 //
 // Forward: logits tiles z = hidden . weight^T (+ bias) come out of the MFMA
-// contraction and never leave the chip: each 128 x 256 tile's epilogue
+// contraction and never leave the chip: each 256 x 256 tile's epilogue
 // reduces its rows to (max, sum exp(z - max)) partials and picks out the
 // target's logit; a small kernel combines a row's partials into its
 // log-sum-exp and log-probability.
@@ -16,15 +16,17 @@
 // one owner per element) are two more contractions of the same kernel with
 // transposed operand layouts; d bias is a column sum of dz.
 //
-// The contraction: 256 threads (2 x 2 wavefronts), a 128 x 256 output tile,
-// each wavefront a 64 x 128 block of eight v_mfma_f32_32x32x16 accumulators
-// held in VGPRs; two workgroups share a compute unit.  K advances in steps of
-// 32 through a ring of three LDS stages filled by buffer-to-LDS copies (two
-// stages in flight while the third is consumed; copies past the operand's end
-// read as zeros).  K-contiguous operands are read from LDS as one 16-byte
-// fragment per lane; MN-contiguous ones with transposing 8-byte LDS reads.
-// Blocks are mapped so that each XCD works on a contiguous run of tiles
-// (shared weight panels stay in its L2).
+// The contraction: 512 threads (2 x 4 wavefronts), a 256 x 256 output tile,
+// each wavefront a 128 x 64 block of eight v_mfma_f32_32x32x16 accumulators
+// held in VGPRs; one workgroup per compute unit.  K advances in steps of 32
+// through a ring of four LDS stages (128 KB) filled by buffer-to-LDS copies
+// (three stages in flight while the fourth is consumed; copies past the
+// operand's end read as zeros).  K-contiguous operands are read from LDS as
+// one 16-byte fragment per lane; MN-contiguous ones with transposing 8-byte
+// LDS reads.  Blocks are mapped so that each XCD works on a contiguous run of
+// tiles (shared weight panels stay in its L2).  The tile and wave grid are
+// the constants of logprob_kernels.h; the code holds for other grids whose
+// wavefront blocks are multiples of 32 x 32.
 #include <hip/hip_runtime.h>
 #include <float.h>
 #include <stdint.h>
@@ -174,6 +176,12 @@ __device__ __forceinline__ uint4 fragment(const uint16_t* __restrict__ t, int wb
 // The value of the neighbouring lane (lane ^ 1), by a DPP quad permute [1, 0, 3, 2].
 __device__ __forceinline__ float swap_pair(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+
+// The value of lane ^ X within a quad (X = 1: permute [1, 0, 3, 2]; X = 2: [2, 3, 0, 1]).
+template <int X>
+__device__ __forceinline__ float quad_xor(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), X == 1 ? 0xB1 : 0x4E, 0xF, 0xF, false));
 }
 
 // XCD-aware tile order: consecutive block indices go to different XCDs, so
@@ -431,6 +439,9 @@ gemm_kernel(const GemmArgs g) {
     constexpr int kParts = kGemmWavesN * 32;
     constexpr int kRounds = kParts * kGemmBM * 8 <= kGemmDynLds ? 1 : kGemmWavesM;
     constexpr int kRoundRows = kGemmBM / kRounds;
+    constexpr int kQ = kGemmThreads / kRoundRows;       // threads merging one row's partials
+    constexpr int kShare = kParts / kQ;
+    static_assert((kQ == 2 || kQ == 4) && kShare * kQ == kParts, "row merge split");
     float2* parts = reinterpret_cast<float2*>(ring);   // kParts x kRoundRows float2, inside the ring
     static_assert(kParts * kRoundRows * 8 <= kGemmDynLds && kRoundRows % 32 == 0, "partials fit");
     if (threadIdx.x < kGemmBM) {
@@ -466,16 +477,25 @@ gemm_kernel(const GemmArgs g) {
                 }
         }
         __syncthreads();
-        if (threadIdx.x < kRoundRows) {
-            const int rr = threadIdx.x, row = m0 + w * kRoundRows + rr;
+        {
+            // kQ neighbouring threads per row, each over a 1/kQ share of the partials;
+            // the row maximum is their common maximum, the sum adds the shares in pairs
+            // ((0 + 1) + (2 + 3)), so the order is fixed.
+            const int rr = threadIdx.x / kQ, qq = threadIdx.x % kQ, row = m0 + w * kRoundRows + rr;
             float M = -__builtin_inff();
-            for (int q = 0; q < kParts; ++q) M = fmaxf(M, parts[q * kRoundRows + (rr ^ (q & 31))].x);
+            for (int q = qq * kShare; q < (qq + 1) * kShare; ++q)
+                M = fmaxf(M, parts[q * kRoundRows + (rr ^ (q & 31))].x);
+            M = fmaxf(M, quad_xor<1>(M));
+            if constexpr (kQ == 4) M = fmaxf(M, quad_xor<2>(M));
             float S = 0.0f;
-            for (int q = 0; q < kParts; ++q) {
+            for (int q = qq * kShare; q < (qq + 1) * kShare; ++q) {
                 const float2 v = parts[q * kRoundRows + (rr ^ (q & 31))];
                 S += v.y * __builtin_amdgcn_exp2f((v.x - M) * kLog2eG);
             }
-            if (row < g.M) reinterpret_cast<float2*>(g.part)[int64_t(row) * g.tiles_n + tn] = make_float2(M, S);
+            S += quad_xor<1>(S);
+            if constexpr (kQ == 4) S += quad_xor<2>(S);
+            if (qq == 0 && row < g.M)
+                reinterpret_cast<float2*>(g.part)[int64_t(row) * g.tiles_n + tn] = make_float2(M, S);
         }
     }
 }
