@@ -8,16 +8,15 @@
 namespace rlpl {
 
 // Tiles of the MFMA contraction: 256 x 256 outputs per workgroup (eight
-// wavefronts of 128 x 64), 32-deep K steps in a ring of four stages (128 KB);
-// one workgroup per compute unit.
+// wavefronts of 128 x 64), K in 64-deep stages through a 128 KB LDS ring
+// (two stages); one workgroup per compute unit.
 constexpr int kGemmBM = 256;
 constexpr int kGemmBN = 256;
-constexpr int kGemmBK = 32;
+constexpr int kGemmBK = 64;               // stage depth (also the split-K granule)
 constexpr int kGemmWavesM = 2;            // wavefronts along M
 constexpr int kGemmWavesN = 4;            // and along N
 constexpr int kGemmThreads = 64 * kGemmWavesM * kGemmWavesN;
-constexpr int kGemmStages = 4;            // LDS ring of K stages (three in flight)
-constexpr int kGemmDynLds = kGemmStages * (kGemmBM + kGemmBN) * kGemmBK * 2;   // dynamic LDS bytes per workgroup
+constexpr int kGemmDynLds = 128 * 1024;   // dynamic LDS bytes per workgroup (the ring)
 constexpr int kLogprobChunk = 1024;       // rows of logits gradient formed at a time (backward)
 constexpr int kSplitK = 4;                // K splits of the hidden-gradient contraction
 

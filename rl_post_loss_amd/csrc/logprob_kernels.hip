@@ -18,10 +18,10 @@
 //
 // The contraction: 512 threads (2 x 4 wavefronts), a 256 x 256 output tile,
 // each wavefront a 128 x 64 block of eight v_mfma_f32_32x32x16 accumulators
-// held in VGPRs; one workgroup per compute unit.  K advances in steps of 32
-// through a ring of four LDS stages (128 KB) filled by buffer-to-LDS copies
-// (three stages in flight while the fourth is consumed; copies past the
-// operand's end read as zeros).  K-contiguous operands are read from LDS as
+// held in VGPRs; one workgroup per compute unit.  K advances through a 128 KB
+// ring of two 64-deep LDS stages filled by buffer-to-LDS copies (one in
+// flight while the other is consumed; copies past the operand's end read as
+// zeros).  K-contiguous operands are read from LDS as
 // one 16-byte fragment per lane; MN-contiguous ones with transposing 8-byte
 // LDS reads.  Blocks are mapped so that each XCD works on a contiguous run of
 // tiles (shared weight panels stay in its L2).  The tile and wave grid are
@@ -63,61 +63,77 @@ constexpr int kWaveM = kGemmBM / kGemmWavesM;   // rows of C per wavefront
 constexpr int kWaveN = kGemmBN / kGemmWavesN;   // columns of C per wavefront
 constexpr int kFragM = kWaveM / 32;      // 32 x 32 MFMA tiles per wavefront, rows
 constexpr int kFragN = kWaveN / 32;      // and columns
-constexpr int kBytesA = kGemmBM * kGemmBK * 2;   // A tile of one stage
-constexpr int kBytesB = kGemmBN * kGemmBK * 2;   // B tile of one stage
-constexpr int kStageBytes = kBytesA + kBytesB;
-constexpr int kDmaA = kBytesA / 1024 / kGemmWaves;   // 1 KB copies per wavefront for the A tile
-constexpr int kDmaB = kBytesB / 1024 / kGemmWaves;   // and for the B tile
 constexpr float kLog2eG = 1.4426950408889634f;
 
-static_assert(kGemmBK == 32 && kWaveM % 32 == 0 && kWaveN % 32 == 0, "32 x 32 matrix tiles, 32-deep stages");
-static_assert(kDmaA * kGemmWaves * 1024 == kBytesA && kDmaB * kGemmWaves * 1024 == kBytesB, "whole copies");
-static_assert(kGemmStages * kStageBytes == kGemmDynLds, "LDS ring size");
+static_assert(kWaveM % 32 == 0 && kWaveN % 32 == 0, "32 x 32 matrix tiles");
 static_assert(kGemmBN == 256 && kGemmBM <= kGemmThreads && kGemmBN <= kGemmThreads,
               "the epilogues use one thread per tile column / row");
 static_assert(kWaveM == 64 || kWaveM == 128, "log-sum-exp partial layout");
 
-// LDS layout of one R x 32 operand tile (R = 128 or 256 rows), filled by 16-byte
-// global->LDS copies (each wavefront copy writes 1 KB contiguously: lane l's
-// 16 bytes at +16*l), with an XOR swizzle of 16-byte chunks that keeps the
-// matrix-core fragment reads free of bank conflicts.
+// LDS layout of one R x BK operand tile (R = kGemmBM or kGemmBN rows, BK the stage depth),
+// filled by 16-byte global->LDS copies (each wavefront copy writes 1 KB
+// contiguously: lane l's 16 bytes at +16*l), with an XOR swizzle of 16-byte
+// chunks that keeps the matrix-core fragment reads free of bank conflicts.
+// A 16-byte read serves 16 lanes per pass over all 64 banks (256 bytes), so
+// the 16 rows a pass reads must spread over distinct 16-byte bank groups.
 //
-// K-contiguous operand (element (r, k) at x[r*ld + k]): row r (0..R-1) is 64
-// bytes; its K chunk c (elements 8c..8c+7) sits in slot c ^ ((r >> 2) & 3).
-// Rows four apart fall on the same banks in a 16-byte read, so the swizzle
-// gives rows r, r+4, r+8, r+12 different slots (measured free of bank
-// conflicts on gfx950).  Fragment reads are one 16-byte read per lane.
+// K-contiguous operand (element (r, k) at x[r*ld + k]): row r is 2 BK bytes,
+// kC = BK / 8 chunks; chunk c (elements 8c..8c+7) sits in slot
+// c ^ swizzle(r).  64-byte rows (BK = 32): rows four apart share banks,
+// swizzle (r >> 2) & 3 (measured free of bank conflicts on gfx950; (r >> 1) & 3
+// had 2-way conflicts).  128-byte rows (BK = 64): rows two apart share
+// banks, swizzle (r >> 1) & 7.  Fragment reads are one 16-byte read per lane;
+// a copy covers 1024 / (2 BK) whole rows, so it reads full 64- or 128-byte
+// row segments (the 128-byte ones copy about 1.5x faster from cache,
+// measured).
 //
-// MN-contiguous operand (element (r, k) at x[k*ld + r]): eight 2 KB blocks of
-// 32 r each; in a block, K row k is 64 bytes and its chunk c (r = 8c..8c+7 of
-// the block) sits in slot c ^ (k & 2).  Fragment reads are two transposing
+// MN-contiguous operand (element (r, k) at x[k*ld + r]): blocks of 32 r by
+// BK K rows; in a block, K row k is 64 bytes and its chunk c (r = 8c..8c+7
+// of the block) sits in slot c ^ (k & 2).  Fragment reads are two transposing
 // 8-byte reads per lane (ds_read_b64_tr_b16).
-__device__ __forceinline__ int kc_swizzle(int r) { return (r >> 2) & 3; }
-__device__ __forceinline__ int kc_offset(int r, int c) { return r * 64 + 16 * (c ^ kc_swizzle(r)); }
-__device__ __forceinline__ int mn_offset(int k, int r) {
-    return (r >> 5) * 2048 + k * 64 + 16 * (((r & 31) >> 3) ^ (k & 2)) + 2 * (r & 7);
-}
+// The stages of depth BK: sizes, copy counts and LDS layouts.
+template <int BK>
+struct Stage {
+    static constexpr int kBytesA = kGemmBM * BK * 2;   // A tile of one stage
+    static constexpr int kBytesB = kGemmBN * BK * 2;   // B tile of one stage
+    static constexpr int kBytes = kBytesA + kBytesB;
+    static constexpr int kCount = kGemmDynLds / kBytes;   // ring slots
+    static constexpr int kDmaA = kBytesA / 1024 / kGemmWaves;   // 1 KB copies per wavefront for the A tile
+    static constexpr int kDmaB = kBytesB / 1024 / kGemmWaves;   // and for the B tile
+    static constexpr int kC = BK / 8;                 // 16-byte chunks per K-contiguous row
+    static constexpr int kRowsPerCopy = 1024 / (2 * BK);
+    static_assert(kC == 4 || kC == 8, "32- or 64-deep stages");
+    static_assert(kCount >= 2 && kCount * kBytes == kGemmDynLds, "LDS ring");
+    static_assert(kDmaA * kGemmWaves * 1024 == kBytesA && kDmaB * kGemmWaves * 1024 == kBytesB, "whole copies");
+    static __device__ __forceinline__ int kc_swizzle(int r) { return kC == 4 ? (r >> 2) & 3 : (r >> 1) & 7; }
+    static __device__ __forceinline__ int kc_offset(int r, int c) { return r * (2 * BK) + 16 * (c ^ kc_swizzle(r)); }
+    static __device__ __forceinline__ int mn_offset(int k, int r) {
+        return (r >> 5) * (64 * BK) + k * 64 + 16 * (((r & 31) >> 3) ^ (k & 2)) + 2 * (r & 7);
+    }
+};
 
 // Per-lane source of the wavefront's 1 KB copies of one operand tile: copy q
-// (0 .. R/16-1; each wavefront issues a quarter of them) of the tile whose first element is
-// (r0, k0).  Returns the byte offset of the lane's 16 bytes from that element
-// (the copy goes through a buffer descriptor based there), or kOutOfRange for a
-// chunk of rows past R or of K at or past ke, which the buffer unit reads as
-// zeros.  A chunk that starts before ke is read whole: the caller guarantees
-// that the elements past ke in it are zeros or that ke is a multiple of 8.
-// Offsets stay below 2 * (32 + 256 * ld) bytes.
+// (0 .. R * BK / 512 - 1; each wavefront issues 1/kGemmWaves of them) of
+// the tile whose first element is (r0, k0).  Returns the byte offset of the
+// lane's 16 bytes from that element (the copy goes through a buffer descriptor
+// based there), or kOutOfRange for a chunk of rows past R or of K at or past
+// ke, which the buffer unit reads as zeros.  A chunk that starts before ke is
+// read whole: the caller guarantees that the elements past ke in it are zeros
+// or that ke is a multiple of 8.  Offsets stay below 2 * (BK + 256 * ld)
+// bytes.
 constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;
 constexpr int kBufferRecords = 0x7FFFFFF0;
 
-template <bool KCONTIG>
+template <bool KCONTIG, int BK>
 __device__ __forceinline__ uint32_t dma_source(int q, int lane, uint32_t ld, int R, int ke, int r0, int k0) {
+    using St = Stage<BK>;
     if constexpr (KCONTIG) {
-        const int r = 16 * q + (lane >> 2);
-        const int c = (lane & 3) ^ kc_swizzle(r);
+        const int r = St::kRowsPerCopy * q + lane / St::kC;
+        const int c = (lane % St::kC) ^ St::kc_swizzle(r);
         const bool ok = r0 + r < R && k0 + 8 * c < ke;
         return ok ? 2u * (uint32_t(r) * ld + uint32_t(8 * c)) : kOutOfRange;
     } else {
-        const int cb = q >> 1, k = 16 * (q & 1) + (lane >> 2);
+        const int cb = q / (BK / 16), k = 16 * (q % (BK / 16)) + (lane >> 2);
         const int c = (lane & 3) ^ (k & 2);
         const int rr = 32 * cb + 8 * c;
         const bool ok = r0 + rr < R && k0 + k < ke;
@@ -139,10 +155,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_at(const void* p) {
 constexpr int vmcnt_imm(int v) { return 0x0F70 | (v & 15) | ((v >> 4) << 14); }
 
 // Wait until at most `pending` (compile-time) stages of this wavefront's copies
-// (kDmaA + kDmaB per stage) are in flight, then meet the other wavefronts.
-template <int PENDING>
+// (kDmaA + kDmaB of Stage<BK> per stage) are in flight, then meet the other
+// wavefronts.
+template <int PENDING, int BK>
 __device__ __forceinline__ void wait_stages() {
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(PENDING * (kDmaA + kDmaB)));
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(PENDING * (Stage<BK>::kDmaA + Stage<BK>::kDmaB)));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 }
@@ -150,11 +167,11 @@ __device__ __forceinline__ void wait_stages() {
 // Matrix-core fragments of stage tile t for wavefront row/column block wb (of
 // WT rows), 32-row tile f, K step kk (16 K): the eight K values lane l needs
 // for row/column wb*WT + f*32 + l%32, K 8*(l/32) .. +8.
-template <bool KCONTIG, int WT>
+template <bool KCONTIG, int WT, int BK>
 __device__ __forceinline__ uint4 fragment(const uint16_t* __restrict__ t, int wb, int f, int kk, int lane) {
     if constexpr (KCONTIG) {
         const int r = wb * WT + f * 32 + (lane & 31);
-        return *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(t) + kc_offset(r, kk * 2 + (lane >> 5)));
+        return *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(t) + Stage<BK>::kc_offset(r, kk * 2 + (lane >> 5)));
     } else {
         // 16-lane group G: columns 16*(G%2) .. +16 of the 32-wide tile, K base 8*(G/2).
         // Input lane q = 4j + t of the group points at K row kbase + j, columns 4t .. 4t+3;
@@ -165,13 +182,19 @@ __device__ __forceinline__ uint4 fragment(const uint16_t* __restrict__ t, int wb
         typedef short v4s __attribute__((ext_vector_type(4)));
         const char* base = reinterpret_cast<const char*>(t);
         const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4s*)(base + mn_offset(k, r)));
+            (__attribute__((address_space(3))) v4s*)(base + Stage<BK>::mn_offset(k, r)));
         const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4s*)(base + mn_offset(k + 4, r)));
+            (__attribute__((address_space(3))) v4s*)(base + Stage<BK>::mn_offset(k + 4, r)));
         const uint2 a = __builtin_bit_cast(uint2, lo), b = __builtin_bit_cast(uint2, hi);
         return make_uint4(a.x, a.y, b.x, b.y);
     }
 }
+
+// Column of partial p's row in the log-sum-exp partial layout: rows XOR p % 32
+// (32 writing lanes, one row: distinct banks), and the four 32-partial shares
+// of a row, read at once by the row's four merging threads, moved apart by
+// 4 (p / 32) (16 lanes of four rows: distinct banks).
+__device__ __forceinline__ int part_swizzle(int p) { return (p & 31) ^ ((p >> 5) << 2); }
 
 // The value of the neighbouring lane (lane ^ 1), by a DPP quad permute [1, 0, 3, 2].
 __device__ __forceinline__ float swap_pair(float v) {
@@ -201,7 +224,9 @@ __device__ __forceinline__ void tile_of(uint32_t b, uint32_t tiles_m, uint32_t t
 template <typename T, int EPI, bool A_KCONTIG, bool B_KCONTIG>
 __global__ void __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm_kernel(const GemmArgs g) {
-    extern __shared__ __attribute__((aligned(1024))) uint16_t ring[];   // kGemmStages x (A tile, B tile)
+    extern __shared__ __attribute__((aligned(1024))) uint16_t ring[];   // St::kCount x (A tile, B tile)
+    constexpr int BK = kGemmBK;   // stage depth
+    using St = Stage<BK>;
     __shared__ float red_a[kGemmWavesM][kGemmBN];
     __shared__ int tgt_col[kGemmBM];
 
@@ -228,47 +253,48 @@ gemm_kernel(const GemmArgs g) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    const int nst = kb < ke ? (ke - kb + kGemmBK - 1) / kGemmBK : 0;
-    // This wavefront's copies of stage s (kDmaA of the A tile, kDmaB of the B tile,
+    const int nst = kb < ke ? (ke - kb + BK - 1) / BK : 0;
+    // This wavefront's copies of stage s (St::kDmaA of the A tile, St::kDmaB of the B tile,
     // 1 KB each) into ring slot s % stages.  Copies of a stage past the last are all
     // out of range (zeros).
     auto issue = [&](int s) {
-        const int k0 = kb + s * kGemmBK;
-        char* slot = reinterpret_cast<char*>(ring) + (s % kGemmStages) * kStageBytes;
+        const int k0 = kb + s * BK;
+        char* slot = reinterpret_cast<char*>(ring) + (s % St::kCount) * St::kBytes;
         // first element (tile row 0, K k0) of each operand's tile
         const __amdgpu_buffer_rsrc_t a0 =
             buffer_at(A + (A_KCONTIG ? int64_t(m0) * g.lda + k0 : int64_t(k0) * g.lda + m0));
         const __amdgpu_buffer_rsrc_t b0 =
             buffer_at(B + (B_KCONTIG ? int64_t(n0) * g.ldb + k0 : int64_t(k0) * g.ldb + n0));
 #pragma unroll
-        for (int u = 0; u < kDmaA; ++u) {
-            const int q = wave * kDmaA + u;
-            dma16(a0, dma_source<A_KCONTIG>(q, lane, uint32_t(g.lda), g.M, ke, m0, k0), slot + q * 1024);
+        for (int u = 0; u < St::kDmaA; ++u) {
+            const int q = wave * St::kDmaA + u;
+            dma16(a0, dma_source<A_KCONTIG, BK>(q, lane, uint32_t(g.lda), g.M, ke, m0, k0), slot + q * 1024);
         }
 #pragma unroll
-        for (int u = 0; u < kDmaB; ++u) {
-            const int q = wave * kDmaB + u;
-            dma16(b0, dma_source<B_KCONTIG>(q, lane, uint32_t(g.ldb), g.N, ke, n0, k0), slot + kBytesA + q * 1024);
+        for (int u = 0; u < St::kDmaB; ++u) {
+            const int q = wave * St::kDmaB + u;
+            dma16(b0, dma_source<B_KCONTIG, BK>(q, lane, uint32_t(g.ldb), g.N, ke, n0, k0),
+                  slot + St::kBytesA + q * 1024);
         }
     };
-    // Step s: wait for stage s's copies (stage s+1's may stay in flight), meet the
-    // other wavefronts (so every one is done with stage s-1), refill stage s-1's slot
-    // with stage s+2, then the matrix instructions of stage s, one 16-deep K step at a
-    // time.  The other workgroup on the compute unit covers the waits.
+    // Step s: wait for stage s's copies (later stages may stay in flight), meet the
+    // other wavefronts (so every one is done with stage s-1), refill stage s-1's
+    // slot with stage s + kCount - 1, then the matrix instructions of stage s, one
+    // 16-deep K step at a time.
     if (nst > 0) {
-        for (int s = 0; s < kGemmStages - 1; ++s) issue(s);
+        for (int s = 0; s < St::kCount - 1; ++s) issue(s);
         for (int s = 0; s < nst; ++s) {
-            wait_stages<kGemmStages - 2>();
-            issue(s + kGemmStages - 1);
-            const uint16_t* at = ring + (s % kGemmStages) * (kStageBytes / 2);
-            const uint16_t* bt = at + kBytesA / 2;
+            wait_stages<St::kCount - 2, BK>();
+            issue(s + St::kCount - 1);
+            const uint16_t* at = ring + (s % St::kCount) * (St::kBytes / 2);
+            const uint16_t* bt = at + St::kBytesA / 2;
 #pragma unroll
-            for (int kk = 0; kk < kGemmBK / 16; ++kk) {
+            for (int kk = 0; kk < BK / 16; ++kk) {
                 uint4 af[kFragM], bf[kFragN];
 #pragma unroll
-                for (int i = 0; i < kFragM; ++i) af[i] = fragment<A_KCONTIG, kWaveM>(at, wm, i, kk, lane);
+                for (int i = 0; i < kFragM; ++i) af[i] = fragment<A_KCONTIG, kWaveM, BK>(at, wm, i, kk, lane);
 #pragma unroll
-                for (int j = 0; j < kFragN; ++j) bf[j] = fragment<B_KCONTIG, kWaveN>(bt, wn, j, kk, lane);
+                for (int j = 0; j < kFragN; ++j) bf[j] = fragment<B_KCONTIG, kWaveN, BK>(bt, wn, j, kk, lane);
 #pragma unroll
                 for (int i = 0; i < kFragM; ++i)
 #pragma unroll
@@ -432,10 +458,10 @@ gemm_kernel(const GemmArgs g) {
     // kEpiLse: per row of the tile, (max, sum exp(z - max)) over its 256 columns, and
     // the target logit.  Each lane reduces its own kFragN columns of a row; the
     // kGemmWavesN * 32 partials of a row (column wavefronts x 32 lanes) meet in LDS,
-    // laid out [partial p][row ^ (p % 32)] so that both the writes (32 lanes, one
-    // row) and the reads (one row per thread) are free of bank conflicts; one
-    // thread per row then merges them in partial order.  When the partials of all
-    // rows do not fit in the ring, the row wavefronts take turns.
+    // laid out [partial p][row ^ part_swizzle(p)] so that both the writes (32
+    // lanes, one row) and the reads (four threads per row) are free of bank
+    // conflicts; the row's threads then merge them in a fixed order.  When the
+    // partials of all rows do not fit in the ring, the row wavefronts take turns.
     constexpr int kParts = kGemmWavesN * 32;
     constexpr int kRounds = kParts * kGemmBM * 8 <= kGemmDynLds ? 1 : kGemmWavesM;
     constexpr int kRoundRows = kGemmBM / kRounds;
@@ -443,7 +469,8 @@ gemm_kernel(const GemmArgs g) {
     constexpr int kShare = kParts / kQ;
     static_assert((kQ == 2 || kQ == 4) && kShare * kQ == kParts, "row merge split");
     float2* parts = reinterpret_cast<float2*>(ring);   // kParts x kRoundRows float2, inside the ring
-    static_assert(kParts * kRoundRows * 8 <= kGemmDynLds && kRoundRows % 32 == 0, "partials fit");
+    static_assert(kParts * kRoundRows * 8 <= kGemmDynLds && kRoundRows % 32 == 0 && kParts <= 256,
+                  "partials fit; part_swizzle stays below 32");
     if (threadIdx.x < kGemmBM) {
         const int row = m0 + int(threadIdx.x);
         const int64_t t = row < g.M ? g.targets[row] : -1;
@@ -469,7 +496,7 @@ gemm_kernel(const GemmArgs g) {
                         for (int j = 0; j < kFragN; ++j) sum += __builtin_amdgcn_exp2f((acc[i][j][e] - m) * kLog2eG);
                     }
                     const int rr = r - w * kRoundRows;
-                    parts[pidx * kRoundRows + (rr ^ (pidx & 31))] = make_float2(m, sum);
+                    parts[pidx * kRoundRows + (rr ^ part_swizzle(pidx))] = make_float2(m, sum);
                     const int tc = tgt_col[r];
 #pragma unroll
                     for (int j = 0; j < kFragN; ++j)
@@ -484,12 +511,12 @@ gemm_kernel(const GemmArgs g) {
             const int rr = threadIdx.x / kQ, qq = threadIdx.x % kQ, row = m0 + w * kRoundRows + rr;
             float M = -__builtin_inff();
             for (int q = qq * kShare; q < (qq + 1) * kShare; ++q)
-                M = fmaxf(M, parts[q * kRoundRows + (rr ^ (q & 31))].x);
+                M = fmaxf(M, parts[q * kRoundRows + (rr ^ part_swizzle(q))].x);
             M = fmaxf(M, quad_xor<1>(M));
             if constexpr (kQ == 4) M = fmaxf(M, quad_xor<2>(M));
             float S = 0.0f;
             for (int q = qq * kShare; q < (qq + 1) * kShare; ++q) {
-                const float2 v = parts[q * kRoundRows + (rr ^ (q & 31))];
+                const float2 v = parts[q * kRoundRows + (rr ^ part_swizzle(q))];
                 S += v.y * __builtin_amdgcn_exp2f((v.x - M) * kLog2eG);
             }
             S += quad_xor<1>(S);
