@@ -87,10 +87,12 @@ static_assert(kWaveM == 64 || kWaveM == 128, "log-sum-exp partial layout");
 // row segments (the 128-byte ones copy about 1.5x faster from cache,
 // measured).
 //
-// MN-contiguous operand (element (r, k) at x[k*ld + r]): blocks of 32 r by
-// BK K rows; in a block, K row k is 64 bytes and its chunk c (r = 8c..8c+7
-// of the block) sits in slot c ^ (k & 2).  Fragment reads are two transposing
-// 8-byte reads per lane (ds_read_b64_tr_b16).
+// MN-contiguous operand (element (r, k) at x[k*ld + r]): blocks of 64 r by
+// BK K rows; in a block, K row k is 128 bytes and its chunk c (r = 8c..8c+7 of
+// the block) sits in slot c ^ (4 ((k >> 1) & 1)), so that a copy brings 8 K
+// rows of 128 bytes.  Fragment reads are two transposing 8-byte reads per
+// lane (ds_read_b64_tr_b16); a pass of 32 lanes reads 4 K rows of 32 r, and
+// the swizzle puts K rows two apart on the other half of the banks.
 // The stages of depth BK: sizes, copy counts and LDS layouts.
 template <int BK>
 struct Stage {
@@ -107,8 +109,9 @@ struct Stage {
     static_assert(kDmaA * kGemmWaves * 1024 == kBytesA && kDmaB * kGemmWaves * 1024 == kBytesB, "whole copies");
     static __device__ __forceinline__ int kc_swizzle(int r) { return kC == 4 ? (r >> 2) & 3 : (r >> 1) & 7; }
     static __device__ __forceinline__ int kc_offset(int r, int c) { return r * (2 * BK) + 16 * (c ^ kc_swizzle(r)); }
+    static __device__ __forceinline__ int mn_swizzle(int k) { return ((k >> 1) & 1) << 2; }
     static __device__ __forceinline__ int mn_offset(int k, int r) {
-        return (r >> 5) * (64 * BK) + k * 64 + 16 * (((r & 31) >> 3) ^ (k & 2)) + 2 * (r & 7);
+        return (r >> 6) * (128 * BK) + k * 128 + 16 * (((r & 63) >> 3) ^ mn_swizzle(k)) + 2 * (r & 7);
     }
 };
 
@@ -133,9 +136,9 @@ __device__ __forceinline__ uint32_t dma_source(int q, int lane, uint32_t ld, int
         const bool ok = r0 + r < R && k0 + 8 * c < ke;
         return ok ? 2u * (uint32_t(r) * ld + uint32_t(8 * c)) : kOutOfRange;
     } else {
-        const int cb = q / (BK / 16), k = 16 * (q % (BK / 16)) + (lane >> 2);
-        const int c = (lane & 3) ^ (k & 2);
-        const int rr = 32 * cb + 8 * c;
+        const int cb = q / (BK / 8), k = 8 * (q % (BK / 8)) + (lane >> 3);
+        const int c = (lane & 7) ^ St::mn_swizzle(k);
+        const int rr = 64 * cb + 8 * c;
         const bool ok = r0 + rr < R && k0 + k < ke;
         return ok ? 2u * (uint32_t(k) * ld + uint32_t(rr)) : kOutOfRange;
     }
