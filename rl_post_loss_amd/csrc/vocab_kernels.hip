@@ -24,13 +24,16 @@
 //    sum e^(s-m_s) (s - t), rescaled when a group raises a maximum (the
 //    online normaliser of Milakov and Gimelshein, 2018).  Four interleaved
 //    accumulators per lane (sharing the maxima) keep the dependency chains
-//    short and each float32 sum to a quarter of a lane's terms.  Lanes are
-//    merged with the same rule over the wavefront, then over the four waves
-//    in LDS.
+//    short and each float32 sum to a quarter of a lane's terms.  A wavefront
+//    merges its lanes maxima first (a butterfly), rescales each lane's sums
+//    once and adds them in a butterfly; the four waves are merged alike
+//    through LDS.  The pieces of a split row are merged the same way, one
+//    piece per lane.
 //  * The forward-only kernel stops there.  The fwd+bwd kernel then writes
 //    grad_v = p_v (d_v - E_p[d]) / N: from the registers that still hold its
 //    piece of the row (one group per lane), or, for rows too long for that,
-//    by reading the piece a second time.
+//    by reading the piece a second time.  p_v / N is one exponential of one
+//    fma, 2^(s_v log2 e - (lse_s log2 e + log2 N)).
 //  * N needs no exchange: every workgroup counts the (rows-byte) mask itself.
 //    The loss is the fixed-order sum of per-workgroup partials that
 //    workgroup 0 gathers from the workspace (the protocol of the policy-loss
@@ -65,7 +68,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNone = -FLT_MAX;   // logit of a position outside the row: never the maximum, weight 0
 
-// Online sums of one lane (or, after merging, of a wavefront or a workgroup).
+// Online sums of one lane (or, after merging, of a wavefront, a workgroup or a
+// row).
 struct Stats {
     float ms, mt;       // running maxima of s and t
     float zs, zt;       // sum exp(s - ms), sum exp(t - mt)
@@ -75,6 +79,7 @@ struct Stats {
 // exp(x) for x <= 0 on the hardware base-2 unit; exp(0) is exactly 1.
 __device__ __forceinline__ float exp_le0(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
 
+// Symmetric in a and b (so both lanes of a butterfly get the same bits).
 __device__ __forceinline__ Stats merge(const Stats& a, const Stats& b) {
     Stats r;
     r.ms = fmaxf(a.ms, b.ms);
@@ -87,22 +92,45 @@ __device__ __forceinline__ Stats merge(const Stats& a, const Stats& b) {
     return r;
 }
 
-__device__ __forceinline__ Stats shfl_xor(const Stats& a, int off) {
-    return Stats{__shfl_xor(a.ms, off, 64), __shfl_xor(a.mt, off, 64), __shfl_xor(a.zs, off, 64),
-                 __shfl_xor(a.zt, off, 64), __shfl_xor(a.as, off, 64)};
+// Merge over the 64 lanes of a wavefront: the maxima first, then each lane's
+// sums rescaled once and added in an xor butterfly.  Every lane gets the same
+// bits (each addition has the same two operands in both lanes).
+__device__ __forceinline__ Stats wave_merge(const Stats& v) {
+    float ms = v.ms, mt = v.mt;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        ms = fmaxf(ms, __shfl_xor(ms, off, 64));
+        mt = fmaxf(mt, __shfl_xor(mt, off, 64));
+    }
+    const float f = exp_le0(v.ms - ms), g = exp_le0(v.mt - mt);
+    float zs = v.zs * f, as = v.as * f, zt = v.zt * g;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        zs += __shfl_xor(zs, off, 64);
+        as += __shfl_xor(as, off, 64);
+        zt += __shfl_xor(zt, off, 64);
+    }
+    return Stats{ms, mt, zs, zt, as};
 }
 
 // Merge over the workgroup in a fixed order; the result is valid in every thread.
-__device__ __forceinline__ Stats block_merge(Stats v, Stats* red) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v = merge(v, shfl_xor(v, off));
+__device__ __forceinline__ Stats block_merge(const Stats& v, Stats* red) {
+    const Stats w = wave_merge(v);
     __syncthreads();                        // red[] may still be read by the previous row
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = w;
     __syncthreads();
-    Stats t = red[0];
+    float ms = red[0].ms, mt = red[0].mt;
 #pragma unroll
-    for (int i = 1; i < kWaves; ++i) t = merge(t, red[i]);
-    return t;
+    for (int i = 1; i < kWaves; ++i) { ms = fmaxf(ms, red[i].ms); mt = fmaxf(mt, red[i].mt); }
+    float zs = 0.0f, zt = 0.0f, as = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) {
+        const float f = exp_le0(red[i].ms - ms), g = exp_le0(red[i].mt - mt);
+        zs += red[i].zs * f;
+        as += red[i].as * f;
+        zt += red[i].zt * g;
+    }
+    return Stats{ms, mt, zs, zt, as};
 }
 
 // Valid rows: the number of nonzero bytes of mask[0, rows), summed by the whole workgroup.
@@ -306,29 +334,27 @@ __device__ __forceinline__ Stats lane_total(const LaneSums& L) {
     return st;
 }
 
-// grad_v = p_v (d_v - E_p[d]) / N for the positions of one block (others unused).
+// grad_v = p_v (d_v - E_p[d]) / N for the positions of one block (others unused):
+// p_v / N = 2^(s_v log2 e - c) with c = lse_s log2 e + log2 N, the exponent one fma.
 template <typename T, int VEC>
 __device__ __forceinline__ void grad_block(const Plane<T, VEC>& ps, const Plane<T, VEC>& pt, uint32_t bits,
-                                           float lse_s, float ed, float inv_n, float (&g)[VEC]) {
+                                           float c, float ed, float (&g)[VEC]) {
     float s[VEC], t[VEC];
     block_values<T, VEC>(ps, bits, s);
     block_values<T, VEC>(pt, bits, t);
 #pragma unroll
-    for (int k = 0; k < VEC; ++k) {
-        const float p = exp_le0(s[k] - lse_s);
-        g[k] = p * ((s[k] - t[k]) - ed) * inv_n;
-    }
+    for (int k = 0; k < VEC; ++k) g[k] = __builtin_amdgcn_exp2f(fmaf(s[k], kLog2e, -c)) * ((s[k] - t[k]) - ed);
 }
 
 // The gradient of a group's blocks (g0 as in load_group).
 template <typename T, int VEC>
-__device__ __forceinline__ void grad_group(const Group<T, VEC>& G, T* __restrict__ grad, uint64_t g0, float lse_s,
-                                           float ed, float inv_n) {
+__device__ __forceinline__ void grad_group(const Group<T, VEC>& G, T* __restrict__ grad, uint64_t g0, float c,
+                                           float ed) {
 #pragma unroll
     for (int j = 0; j < kGroup; ++j) {
         if (G.bits[j]) {
             float g[VEC];
-            grad_block<T, VEC>(G.s[j], G.t[j], G.bits[j], lse_s, ed, inv_n, g);
+            grad_block<T, VEC>(G.s[j], G.t[j], G.bits[j], c, ed, g);
             store_bits<T, VEC>(grad, g0 + threadIdx.x + uint64_t(j) * kThreads, G.bits[j], g);
         }
     }
@@ -340,7 +366,7 @@ __device__ __forceinline__ void grad_group(const Group<T, VEC>& G, T* __restrict
 // piece, the whole row, when there are enough rows to fill the device);
 // workgroup w owns piece w % chunks of rows w / chunks, w / chunks + R, ...
 // (R = gridDim.x / chunks), one row per round.  With several pieces, their
-// online sums go to the workspace and are merged in piece order (so every
+// online sums go to the workspace and are merged in one fixed order (so every
 // workgroup of the row, and the forward-only kernel, gets the same bits).  The
 // fwd+bwd kernel then writes the gradient of its piece: from the registers
 // that still hold it (kVocabResident, pieces of at most kVocabResidentBlocks
@@ -374,8 +400,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
     const T* __restrict__ Tt = static_cast<const T*>(a.teacher);
     const uint32_t N = count_rows(a.mask, rows, red_u);
     gen = share_generation(gen, word);
-    const float inv_n = 1.0f / float(N);        // unclamped: inf when N == 0, used by no row then
-    float part = 0.0f;                          // sum of kl_r over the rows whose chunk 0 this is
+    const float log2_n = __builtin_amdgcn_logf(float(N));   // -inf when N == 0, used by no row then
+    float part = 0.0f;                        // sum of kl_r over the rows whose chunk 0 this is
     const uint32_t rounds = (rows + R - 1) / R;
     // Exchanges so far: the stats buffer alternates per exchange (not per round:
     // masked rows exchange nothing), so a workgroup writes a buffer only after
@@ -418,7 +444,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
         Stats st = block_merge(lane_total(acc), red_s);
         Stats row = st;
         if (C > 1) {
-            // Publish the chunk's sums, read every chunk's of this row, merge them in chunk order.
+            // Publish the chunk's sums, read every chunk's of this row, merge them in a
+            // fixed order: lane q of each wavefront takes chunks q, q + 64, ... in turn,
+            // then the wavefront merges its lanes.
             const uint32_t tag = gen + 1u + round;
             const uint32_t buf = exch++ & 1u;
             uint64_t* mine = &ws->slot[blockIdx.x].stats[buf][0];
@@ -433,26 +461,28 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
                 peer[i] = __uint_as_float(uint32_t(x));
             }
             __syncthreads();
-            row = Stats{peer[0], peer[1], peer[2], peer[3], peer[4]};
-            for (uint32_t q = 1; q < C; ++q)
-                row = merge(row, Stats{peer[5 * q], peer[5 * q + 1], peer[5 * q + 2], peer[5 * q + 3],
-                                       peer[5 * q + 4]});
+            Stats mine_q{kNone, kNone, 0.0f, 0.0f, 0.0f};
+            for (uint32_t q = threadIdx.x & 63u; q < C; q += 64u)
+                mine_q = merge(mine_q, Stats{peer[5 * q], peer[5 * q + 1], peer[5 * q + 2], peer[5 * q + 3],
+                                             peer[5 * q + 4]});
+            row = wave_merge(mine_q);
             __syncthreads();                    // peer[] is rewritten next round
         }
-        // ln z = log2(z) * ln 2 (v_log_f32 is base 2); z >= 1.
-        const float ln_zs = __builtin_amdgcn_logf(row.zs) * kLn2;
-        const float ln_zt = __builtin_amdgcn_logf(row.zt) * kLn2;
+        // log2 z (v_log_f32 is base 2); z >= 1.
+        const float l2zs = __builtin_amdgcn_logf(row.zs);
+        const float l2zt = __builtin_amdgcn_logf(row.zt);
         const float ed = row.as / row.zs;                       // E_p[s - t]
-        if (c == 0) part += (ed - (row.ms - row.mt)) - (ln_zs - ln_zt);   // kl_r
+        if (c == 0) part += (ed - (row.ms - row.mt)) - (l2zs * kLn2 - l2zt * kLn2);   // kl_r
         if constexpr (WRITE_GRAD) {
-            // grad_v = p_v (d_v - E_p[d]) / N, p_v = exp(s_v - lse_s).
-            const float lse_s = row.ms + ln_zs;
+            // grad_v = p_v (d_v - E_p[d]) / N = 2^(s_v log2 e - c) (d_v - E_p[d]),
+            // c = lse_s log2 e + log2 N = m_s log2 e + log2 z_s + log2 N.
+            const float cg = fmaf(row.ms, kLog2e, l2zs + log2_n);
             if constexpr (MODE == kVocabResident) {
-                grad_group<T, VEC>(G, static_cast<T*>(a.grad), cb0, lse_s, ed, inv_n);
+                grad_group<T, VEC>(G, static_cast<T*>(a.grad), cb0, cg, ed);
             } else {
                 for (uint64_t g0 = cb0; g0 < cb1; g0 += kGroup * kThreads) {
                     load_group<T, VEC>(G, S, Tt, g0, cb1, lo, hi, end16);
-                    grad_group<T, VEC>(G, static_cast<T*>(a.grad), g0, lse_s, ed, inv_n);
+                    grad_group<T, VEC>(G, static_cast<T*>(a.grad), g0, cg, ed);
                 }
             }
         }
