@@ -211,15 +211,22 @@ __device__ __forceinline__ float quad_xor(float v) {
 }
 
 // XCD-aware tile order: consecutive block indices go to different XCDs, so
-// XCD x (block % 8) takes a contiguous run of tiles; within the run the M
-// tile varies fastest, so that neighbours share the N operand's panel.
+// XCD x (block % 8) takes a contiguous run of tiles.  Within the run, tiles
+// come in groups of kTileGroupM M tiles by all N tiles, M varying fastest
+// inside a group: the 32 tiles an XCD runs at once form a 4 x 8 block that
+// shares 4 A panels and 8 B panels in its L2 (M fastest over the whole
+// range would, for a tall product, put 32 A panels beside one B panel).
+constexpr uint32_t kTileGroupM = 4;
 __device__ __forceinline__ void tile_of(uint32_t b, uint32_t tiles_m, uint32_t tiles_n, uint32_t& tm, uint32_t& tn) {
     const uint32_t T = tiles_m * tiles_n;
     const uint32_t x = b & 7u, idx = b >> 3;
     const uint32_t q = T >> 3, r = T & 7u;
     const uint32_t t = (x < r ? x * (q + 1u) : r * (q + 1u) + (x - r) * q) + idx;
-    tm = t % tiles_m;
-    tn = t / tiles_m;
+    const uint32_t group = t / (kTileGroupM * tiles_n), in = t % (kTileGroupM * tiles_n);
+    const uint32_t m_first = group * kTileGroupM;
+    const uint32_t rows = tiles_m - m_first < kTileGroupM ? tiles_m - m_first : kTileGroupM;
+    tm = m_first + in % rows;
+    tn = in / rows;
 }
 
 }  // namespace
