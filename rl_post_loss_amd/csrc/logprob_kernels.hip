@@ -211,17 +211,23 @@ __device__ __forceinline__ float quad_xor(float v) {
 }
 
 // XCD-aware tile order: consecutive block indices go to different XCDs, so
-// XCD x (block % 8) takes a contiguous run of tiles.  Within the run, tiles
-// come in groups of kTileGroupM M tiles by all N tiles, M varying fastest
-// inside a group: the 32 tiles an XCD runs at once form a 4 x 8 block that
-// shares 4 A panels and 8 B panels in its L2 (M fastest over the whole
-// range would, for a tall product, put 32 A panels beside one B panel).
+// XCD x (block % 8) takes a contiguous run of the (split, tile) pairs, split
+// slowest (a split-K product gives each split's tiles to whole XCDs).
+// Within the run, tiles come in groups of kTileGroupM M tiles by all N
+// tiles, M varying fastest inside a group: the 32 tiles an XCD runs at once
+// form a 4 x 8 block that shares 4 A panels and 8 B panels in its L2 (M
+// fastest over the whole range would, for a tall product, put 32 A panels
+// beside one B panel).  b is the linear block index over splits blocks of
+// tiles_m * tiles_n.
 constexpr uint32_t kTileGroupM = 4;
-__device__ __forceinline__ void tile_of(uint32_t b, uint32_t tiles_m, uint32_t tiles_n, uint32_t& tm, uint32_t& tn) {
-    const uint32_t T = tiles_m * tiles_n;
+__device__ __forceinline__ void tile_of(uint32_t b, uint32_t tiles_m, uint32_t tiles_n, uint32_t splits, uint32_t& tm,
+                                        uint32_t& tn, uint32_t& split) {
+    const uint32_t T = tiles_m * tiles_n, all = T * splits;
     const uint32_t x = b & 7u, idx = b >> 3;
-    const uint32_t q = T >> 3, r = T & 7u;
-    const uint32_t t = (x < r ? x * (q + 1u) : r * (q + 1u) + (x - r) * q) + idx;
+    const uint32_t q = all >> 3, r = all & 7u;
+    const uint32_t v = (x < r ? x * (q + 1u) : r * (q + 1u) + (x - r) * q) + idx;
+    split = v / T;
+    const uint32_t t = v % T;
     const uint32_t group = t / (kTileGroupM * tiles_n), in = t % (kTileGroupM * tiles_n);
     const uint32_t m_first = group * kTileGroupM;
     const uint32_t rows = tiles_m - m_first < kTileGroupM ? tiles_m - m_first : kTileGroupM;
@@ -240,12 +246,12 @@ gemm_kernel(const GemmArgs g) {
     __shared__ float red_a[kGemmWavesM][kGemmBN];
     __shared__ int tgt_col[kGemmBM];
 
-    uint32_t tm, tn;
-    tile_of(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
+    uint32_t tm, tn, split;
+    tile_of(blockIdx.x + gridDim.x * blockIdx.z, g.tiles_m, g.tiles_n, gridDim.z, tm, tn, split);
     const int m0 = int(tm) * kGemmBM, n0 = int(tn) * kGemmBN;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / kGemmWavesN, wn = wave % kGemmWavesN;
-    const int kb = EPI == kEpiSplit ? int(blockIdx.z) * g.k_split : 0;
+    const int kb = EPI == kEpiSplit ? int(split) * g.k_split : 0;
     const int ke = EPI == kEpiSplit ? min(g.K, kb + g.k_split) : g.K;
     const uint16_t* __restrict__ A = static_cast<const uint16_t*>(g.a);
     const uint16_t* __restrict__ B = static_cast<const uint16_t*>(g.b);
@@ -316,7 +322,7 @@ gemm_kernel(const GemmArgs g) {
 
     if constexpr (EPI == kEpiSplit || EPI == kEpiAccum) {
         float* __restrict__ C = static_cast<float*>(g.c);
-        if constexpr (EPI == kEpiSplit) C += int64_t(blockIdx.z) * g.M * g.ldc;
+        if constexpr (EPI == kEpiSplit) C += int64_t(split) * g.M * g.ldc;
         if (EPI == kEpiAccum && g.accumulate) {
             // C += acc, one 32-row tile at a time: its 64 reads are issued together.
             if (m0 + wm * kWaveM + kWaveM <= g.M && n0 + wn * kWaveN + kWaveN <= g.N) {
