@@ -25,8 +25,8 @@
 //    online normaliser of Milakov and Gimelshein, 2018).  Four interleaved
 //    accumulators per lane (sharing the maxima) keep the dependency chains
 //    short and each float32 sum to a quarter of a lane's terms.  A wavefront
-//    merges its lanes maxima first (a butterfly), rescales each lane's sums
-//    once and adds them in a butterfly; the four waves are merged alike
+//    merges its lanes: the maxima first (a butterfly), then each lane's sums
+//    rescaled once and added in a butterfly; the four waves are merged alike
 //    through LDS.  The pieces of a split row are merged the same way, one
 //    piece per lane.
 //  * The forward-only kernel stops there.  The fwd+bwd kernel then writes
