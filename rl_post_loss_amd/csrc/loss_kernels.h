@@ -34,12 +34,6 @@ enum { kShapeSmall = 0, kShapeLarge = 1, kShapeStream = 2, kShapes = 3 };
 #define RLPL_SMALL_TILES_PER_CU 1
 #endif
 constexpr int kSmallTilesPerCu = RLPL_SMALL_TILES_PER_CU;
-// When each workgroup owns a single tile: issue the plane loads together with
-// the mask load (1) or only for lanes whose mask turned out nonzero (0).
-#ifndef RLPL_SPECULATIVE_LOADS
-#define RLPL_SPECULATIVE_LOADS 0
-#endif
-constexpr bool kSpeculativeLoads = RLPL_SPECULATIVE_LOADS != 0;
 constexpr int kMaxGrid = 4096;              // upper bound on the persistent grid (gfx950: <= 256 CUs x 8)
 constexpr uint64_t kWaitLimitTicks = 100000000ull;   // ~1 s of the 100 MHz wall clock
 constexpr uint32_t kWaitLimitPolls = 1u << 24;        // second bound on the same wait

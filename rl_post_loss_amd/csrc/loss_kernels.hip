@@ -183,18 +183,23 @@ struct Lane {
 };
 
 // Issues one lane's mask and plane loads (mask first) and returns its valid
-// count.  By default the plane loads wait for the mask and are skipped when
-// all of its bytes are zero (no plane bytes move for masked lanes; measured
-// faster than issuing them together with the mask, as well as leaner).  A lane
-// entirely in range takes straight-line code; the lane that runs past `slots`
-// (one per launch at most) loads element by element.  No workgroup barrier
-// inside, so the divergent branch is safe.
-template <typename T, int MODE, bool HAS_KL, int VEC>
+// count.  SPEC: the plane loads go out together with the mask (one memory
+// latency instead of two, at the price of plane bytes for masked slots);
+// otherwise they wait for the mask and are skipped when all of its bytes are
+// zero.  Interleaved A/B on one-tile launches: speculative loads are faster
+// for the forward-only kernels and for GRPO (bf16 64x4096 forward-only BNPO
+// -4 to -9 %, GRPO 128x2048 -3 to -5 %), and no faster for BNPO and
+// reverse-KL fwd+bwd, whose count exchange takes longer than the second
+// latency, so there they keep the leaner order.  A lane entirely in range
+// takes straight-line code; the lane that runs past `slots` (one per launch
+// at most) loads element by element.  No workgroup barrier inside, so the
+// divergent branch is safe.
+template <typename T, int MODE, bool HAS_KL, int VEC, bool SPEC>
 __device__ __forceinline__ uint32_t load_lane_count(const Args& a, uint32_t s, Lane<T, VEC>& L) {
     const uint32_t slots = uint32_t(a.slots);
     if (s + VEC <= slots) {
         L.m.d.load(a.mask + s);
-        if constexpr (kSpeculativeLoads) {
+        if constexpr (SPEC) {
             L.lp.d.load(static_cast<const T*>(a.lp) + s);
             if constexpr (MODE != kModeRKL) L.old.d.load(static_cast<const T*>(a.old) + s);
             if constexpr (HAS_KL) L.ref.d.load(static_cast<const T*>(a.ref) + s);
@@ -500,7 +505,7 @@ __global__ void __launch_bounds__(kThreads) loss_kernel(const Args a) {
             // published as soon as the mask (loaded first) has arrived, so the exchange
             // runs while the planes are still arriving and being computed on; the
             // partial loss follows as the slot's second word.
-            const uint32_t n_wg = block_sum(load_lane_count<T, MODE, HAS_KL, VEC>(a, s, L), red_u);
+            const uint32_t n_wg = block_sum(load_lane_count<T, MODE, HAS_KL, VEC, false>(a, s, L), red_u);
             gen = share_generation(gen, word);
             if (threadIdx.x == 0) publish_count(ws, worker, gen, n_wg);
             float g[VEC];
@@ -518,7 +523,7 @@ __global__ void __launch_bounds__(kThreads) loss_kernel(const Args a) {
                 const uint32_t s0 = worker * kTileV;
                 grpo_row_scales(a, s0, s0 + kTileV < slots ? s0 + kTileV : slots, row_lds, row_base);
             }
-            n_lane = load_lane_count<T, MODE, HAS_KL, VEC>(a, s, L);
+            n_lane = load_lane_count<T, MODE, HAS_KL, VEC, true>(a, s, L);
             float g[VEC];
             part = lane_terms<T, MODE, HAS_KL, VEC>(a, s, L, reinterpret_cast<const float*>(row_lds),
                                                     row_base, 1.0f, g);
