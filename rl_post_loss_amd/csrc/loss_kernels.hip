@@ -187,10 +187,12 @@ struct Lane {
 // latency instead of two, at the price of plane bytes for masked slots);
 // otherwise they wait for the mask and are skipped when all of its bytes are
 // zero.  Interleaved A/B on one-tile launches: speculative loads are faster
-// for the forward-only kernels and for GRPO (bf16 64x4096 forward-only BNPO
-// -4 to -9 %, GRPO 128x2048 -3 to -5 %), and no faster for BNPO and
-// reverse-KL fwd+bwd, whose count exchange takes longer than the second
-// latency, so there they keep the leaner order.  A lane entirely in range
+// for the narrow-lane forward-only and GRPO kernels, which serve the
+// smallest, latency-bound problems (bf16 64x4096 forward-only BNPO -3 to
+// -9 %, GRPO 128x2048 -1 to -5 %); slower for the wide-lane ones, where the
+// extra bytes start to count (forward-only BNPO 1024x4096 +13 %, GRPO +9 %);
+// and no faster for BNPO and reverse-KL fwd+bwd, whose count exchange takes
+// longer than the second latency.  A lane entirely in range
 // takes straight-line code; the lane that runs past `slots` (one per launch
 // at most) loads element by element.  No workgroup barrier inside, so the
 // divergent branch is safe.
@@ -523,7 +525,7 @@ __global__ void __launch_bounds__(kThreads) loss_kernel(const Args a) {
                 const uint32_t s0 = worker * kTileV;
                 grpo_row_scales(a, s0, s0 + kTileV < slots ? s0 + kTileV : slots, row_lds, row_base);
             }
-            n_lane = load_lane_count<T, MODE, HAS_KL, VEC, true>(a, s, L);
+            n_lane = load_lane_count<T, MODE, HAS_KL, VEC, VEC == kVecSmall>(a, s, L);
             float g[VEC];
             part = lane_terms<T, MODE, HAS_KL, VEC>(a, s, L, reinterpret_cast<const float*>(row_lds),
                                                     row_base, 1.0f, g);
