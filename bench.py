@@ -432,7 +432,7 @@ def main() -> int:
     ap.add_argument("--floor", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus} is not supported: this build measures one GPU only "
+        print(f"bench.py: --gpus {args.gpus} is not supported: the library is measured on one GPU only "
               f"(the loss shards by rows; see the design notes)", file=sys.stderr)
         return 2
 
