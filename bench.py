@@ -433,7 +433,7 @@ def main() -> int:
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported: the library is measured on one GPU only "
-              f"(the loss shards by rows; see the design notes)", file=sys.stderr)
+              f"(the loss shards by rows across GPUs)", file=sys.stderr)
         return 2
 
     import numpy as np

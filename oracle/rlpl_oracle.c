@@ -23,8 +23,7 @@
  *     gradient p_v (log p_v - log q_v - kl_row) * mask[r] / mask.sum(); the
  *     same normalisation for the per-token estimator below.
  *
- * Readings of points the card leaves open (each is also listed with its
- * reason in the design notes):
+ * Readings of points the card leaves open:
  *   - per_token = -A * min(ratio, clip(ratio, 1-eps, 1+eps_high)) literally;
  *     when ratio equals its clipped value the unclipped branch is taken, so
  *     d per_token / d lp = -A*ratio unless clipping lowered ratio to 1+eps_high.
