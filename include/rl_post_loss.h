@@ -34,6 +34,17 @@
  * once by the caller before its first use.  Every call leaves it in the state
  * the next call needs, so it is re-used as is.  Only one call may be in flight
  * per workspace (calls on one stream are serialised and may share one).
+ * Calls on other streams or workspaces may run concurrently.
+ *
+ * The per-token losses form their global count without host synchronisation:
+ * workgroups publish values in the workspace tagged with their launch's
+ * identity (its dispatch id on its hardware queue), and a coordinating
+ * workgroup combines them.  No workgroup relies on any other being resident:
+ * a value not published within a time limit is computed by the waiting
+ * workgroup itself, with the same arithmetic, so results are bit-identical
+ * however the launch was scheduled (for instance beside other kernels that
+ * hold compute units).  Bytes 256..267 of the workspace hold optional limits
+ * for these waits (rlpl_workspace_set_limits); zero selects the defaults.
  *
  * Errors: arguments are validated on the host before anything is enqueued; a
  * rejected call enqueues nothing and returns a nonzero rlpl_status.  A failed
@@ -313,10 +324,25 @@ int rlpl_launch_shape(int64_t bs, int64_t seq_len, int dtype, int op, int* grid_
                       int* tiles_out);
 
 /* Sticky error bits the kernels left in a workspace (host pointer `flags_out`
- * receives them; synchronises `stream`).  Bit 0: a cross-workgroup wait gave
- * up after its time limit, so that call's results are not valid and the
- * workspace must be zero-filled again before its next use. */
+ * receives them; synchronises `stream`).  Bit 0: a wait of a full-vocab
+ * reverse-KL call for the partial sums of other workgroups gave up after its
+ * time limit (~1 s); that call's loss was written as NaN, its gradient is not
+ * valid, and the workspace must be zero-filled again before its next use.
+ * The per-token losses never give up a wait (see Workspace above). */
 int rlpl_workspace_flags(const void* workspace, uint32_t* flags_out, hipStream_t stream);
+
+/* Limits of the cross-workgroup waits of calls that use `workspace`, in ticks
+ * of the GPU's 100 MHz clock; 0 selects the default.  steal_ticks: how long a
+ * coordinating workgroup waits for a value another workgroup publishes before
+ * computing it itself (default 5,000 = 50 us); release_ticks: how long a
+ * workgroup waits for the global count before forming it itself (default
+ * 20,000); giveup_ticks: how long a full-vocab reverse-KL call waits before it
+ * gives up (default 100,000,000 = 1 s).  Results never depend on these limits
+ * (tests set them small to exercise every path); only timing does.
+ * Enqueued on `stream` (three 4-byte fills, not synchronised); the workspace
+ * must be 256-byte aligned and at least rlpl_workspace_bytes long. */
+int rlpl_workspace_set_limits(void* workspace, uint32_t steal_ticks, uint32_t release_ticks,
+                              uint32_t giveup_ticks, hipStream_t stream);
 
 /* Human-readable name of an rlpl_status value (static string). */
 const char* rlpl_status_string(int status);

@@ -42,6 +42,7 @@ is created on first use and reused.
 """
 from __future__ import annotations
 
+import atexit
 import ctypes
 import os
 import threading
@@ -52,6 +53,7 @@ from . import build as _build
 
 __all__ = ["bnpo_loss", "bnpo_loss_fwd", "grpo_loss", "grpo_loss_fwd", "reverse_kl",
            "reverse_kl_fwd", "library", "library_path", "RlplError", "STATUS", "workspace_for",
+           "set_wait_limits", "workspace_flags", "check_workspace",
            "launch_shape", "reverse_kl_logits", "reverse_kl_logits_fwd", "bnpo_loss_autograd",
            "grpo_loss_autograd", "reverse_kl_autograd", "reverse_kl_logits_autograd",
            "selective_logprob_fwd", "selective_logprob_bwd", "selective_logprob_autograd"]
@@ -75,6 +77,24 @@ class RlplError(RuntimeError):
 _lib = None
 _lock = threading.Lock()
 _workspaces: dict = {}
+
+
+def _release_device_state():
+    """Interpreter exit: wait for the device, drop the cached workspaces and hand torch's
+    cached device memory back to the HIP runtime.  Python's exit handlers run before the
+    C-level ones (the HIP runtime's own teardown, and the finalisation of a profiler tool
+    attached to it), so no device buffer of ours is still to be freed once those start."""
+    if not torch.cuda.is_initialized():
+        return
+    try:
+        torch.cuda.synchronize()
+    except RuntimeError:
+        pass
+    _workspaces.clear()
+    torch.cuda.empty_cache()
+
+
+atexit.register(_release_device_state)
 
 
 def library_path() -> str:
@@ -107,6 +127,9 @@ def _declare(lib):
     lib.rlpl_workspace_bytes.argtypes, lib.rlpl_workspace_bytes.restype = [i64, i64, i32], sz
     lib.rlpl_workspace_flags.argtypes = [vp, ctypes.POINTER(ctypes.c_uint32), vp]
     lib.rlpl_workspace_flags.restype = ctypes.c_int
+    u32 = ctypes.c_uint32
+    lib.rlpl_workspace_set_limits.argtypes = [vp, u32, u32, u32, vp]
+    lib.rlpl_workspace_set_limits.restype = ctypes.c_int
     lib.rlpl_launch_shape.argtypes = [i64, i64, i32, i32] + [ctypes.POINTER(ctypes.c_int)] * 3
     lib.rlpl_launch_shape.restype = ctypes.c_int
     lib.rlpl_status_string.argtypes, lib.rlpl_status_string.restype = [i32], ctypes.c_char_p
@@ -135,6 +158,33 @@ def workspace_for(device: torch.device, stream_ptr: int, op: str = "bnpo") -> to
         ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
+
+
+def set_wait_limits(workspace: torch.Tensor, steal_ticks: int = 0, release_ticks: int = 0,
+                    giveup_ticks: int = 0) -> None:
+    """Limits (100 MHz ticks; 0 = default) of the cross-workgroup waits of calls using
+    `workspace`, enqueued on the current stream (C ABI rlpl_workspace_set_limits)."""
+    stream = torch.cuda.current_stream(workspace.device).cuda_stream
+    _check("rlpl_workspace_set_limits", library().rlpl_workspace_set_limits(
+        workspace.data_ptr(), int(steal_ticks), int(release_ticks), int(giveup_ticks), stream))
+
+
+def workspace_flags(workspace: torch.Tensor) -> int:
+    """Sticky error bits left in `workspace` (synchronises the current stream)."""
+    flags = ctypes.c_uint32(0)
+    stream = torch.cuda.current_stream(workspace.device).cuda_stream
+    _check("rlpl_workspace_flags", library().rlpl_workspace_flags(workspace.data_ptr(), ctypes.byref(flags), stream))
+    return flags.value
+
+
+def check_workspace(workspace: torch.Tensor) -> None:
+    """Raises if a call on `workspace` gave up a wait (its results are then invalid);
+    the workspace is zero-filled again first, so it can be re-used."""
+    flags = workspace_flags(workspace)
+    if flags:
+        workspace.zero_()
+        raise RuntimeError(f"rl_post_loss: a cross-workgroup wait gave up (workspace flags {flags:#x}); "
+                           "the results of the calls since the last check are not valid")
 
 
 def launch_shape(bs: int, seq_len: int, dtype: torch.dtype, op: str = "bnpo"):
@@ -300,7 +350,8 @@ def reverse_kl_fwd(student_logprobs, teacher_logprobs, completions_mask, *, retu
     return _rkl(False, student_logprobs, teacher_logprobs, completions_mask, return_n_valid, workspace)
 
 
-def _rkl_logits(fused: bool, student_logits, teacher_logits, completions_mask, return_n_valid, workspace):
+def _rkl_logits(fused: bool, student_logits, teacher_logits, completions_mask, return_n_valid, workspace,
+                check=False):
     s = student_logits.detach()
     if not isinstance(s, torch.Tensor) or not s.is_cuda or s.dtype not in DTYPE or s.dim() < 1:
         raise TypeError("student_logits must be a float32, float16 or bfloat16 CUDA (HIP) tensor")
@@ -327,6 +378,8 @@ def _rkl_logits(fused: bool, student_logits, teacher_logits, completions_mask, r
     args += [None if n is None else n.data_ptr(), ws.data_ptr(), ws.numel(), stream]
     name = "reverse_kl_logits" if fused else "reverse_kl_logits_fwd"
     _check(name, getattr(library(), name)(*args))
+    if check:
+        check_workspace(ws)
     out = (loss, grad.reshape(s.shape)) if fused else (loss,)
     if return_n_valid:
         out = out + (n,)
@@ -334,16 +387,20 @@ def _rkl_logits(fused: bool, student_logits, teacher_logits, completions_mask, r
 
 
 def reverse_kl_logits(student_logits, teacher_logits, completions_mask, *, return_n_valid=False,
-                      workspace=None):
+                      workspace=None, check=False):
     """Reverse KL(student || teacher) over full (*, V) logit rows, fused forward+backward:
-    (loss, d loss / d student_logits) from one launch."""
-    return _rkl_logits(True, student_logits, teacher_logits, completions_mask, return_n_valid, workspace)
+    (loss, d loss / d student_logits) from one launch.  check=True synchronises and raises
+    if the call gave up a cross-workgroup wait (see check_workspace)."""
+    return _rkl_logits(True, student_logits, teacher_logits, completions_mask, return_n_valid, workspace,
+                       check)
 
 
 def reverse_kl_logits_fwd(student_logits, teacher_logits, completions_mask, *, return_n_valid=False,
-                          workspace=None):
-    """Reverse KL over full logit rows, forward only: the scalar loss (one read of each valid row)."""
-    return _rkl_logits(False, student_logits, teacher_logits, completions_mask, return_n_valid, workspace)
+                          workspace=None, check=False):
+    """Reverse KL over full logit rows, forward only: the scalar loss (one read of each valid row).
+    check=True as for reverse_kl_logits."""
+    return _rkl_logits(False, student_logits, teacher_logits, completions_mask, return_n_valid, workspace,
+                       check)
 
 
 

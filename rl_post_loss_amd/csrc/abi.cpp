@@ -68,9 +68,9 @@ void init_device(int dev, DeviceInfo& info) {
         for (int mode = 0; mode < 3; ++mode)
             for (int shape = 0; shape < rlpl::kShapes; ++shape) {
                 // The whole family shares one grid size so that its forward-only and
-                // fwd+bwd kernels reduce over identical partitions (identical losses),
-                // and that size never exceeds what is co-resident on the device, which
-                // the fwd+bwd count exchange relies on.
+                // fwd+bwd kernels reduce over identical partitions (identical losses);
+                // the size is what the device holds at once, so that on an idle
+                // device no workgroup waits for another to be dispatched.
                 int occ = 1 << 30;
                 for (int kl = 0; kl < 2; ++kl)
                     for (int wg = 0; wg < 2; ++wg) {
@@ -136,11 +136,11 @@ int check_common(const void* mask, int64_t bs, int64_t seq_len, int dtype, int m
     return RLPL_OK;
 }
 
-// A plain launch: the grid is capped at the co-resident capacity, so every
-// workgroup of an exchange kernel is resident together on an otherwise idle
-// device (and, with other work present, becomes resident as that work drains;
-// the exchange wait is also bounded in time).  A cooperative launch would
-// guarantee the same but costs ~16 us of extra dispatch latency per call here.
+// A plain launch.  The grid is capped at what the device holds at once, so on
+// an idle device every workgroup of an exchange kernel is resident together;
+// correctness does not rest on it (a workgroup that waits too long for another
+// computes the awaited value itself).  A cooperative launch would guarantee
+// co-residency but costs ~16 us of extra dispatch latency per call here.
 template <typename A>
 int launch(const void* kernel, const A& a, dim3 grid, hipStream_t stream, int threads = rlpl::kThreads,
            size_t dyn_lds = 0) {
@@ -671,6 +671,20 @@ int rlpl_workspace_flags(const void* workspace, uint32_t* flags_out, hipStream_t
     if (hipMemcpyAsync(flags_out, src, sizeof(uint32_t), hipMemcpyDeviceToHost, stream) != hipSuccess ||
         hipStreamSynchronize(stream) != hipSuccess)
         return RLPL_ERR_LAUNCH;
+    return RLPL_OK;
+}
+
+int rlpl_workspace_set_limits(void* workspace, uint32_t steal_ticks, uint32_t release_ticks,
+                              uint32_t giveup_ticks, hipStream_t stream) {
+    if (!workspace) return RLPL_ERR_NULL;
+    if (!aligned(workspace, 256)) return RLPL_ERR_ALIGN;
+    auto* w = static_cast<unsigned char*>(workspace) + rlpl::kLimitsOffset;
+    const uint32_t v[3] = {steal_ticks, release_ticks, giveup_ticks};
+    for (int i = 0; i < 3; ++i)
+        if (hipMemsetD32Async(reinterpret_cast<hipDeviceptr_t>(w + 4 * i), int(v[i]), 1, stream) != hipSuccess) {
+            (void)hipGetLastError();
+            return RLPL_ERR_LAUNCH;
+        }
     return RLPL_OK;
 }
 

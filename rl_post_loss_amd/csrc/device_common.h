@@ -161,19 +161,212 @@ __device__ __forceinline__ V block_sum(V v, V* red) {
     return t;
 }
 
-// ----------------------------------------------------------------------------- workspace protocol
+// ----------------------------------------------------------------------------- launch identity
+
+// The dispatch id of the running launch: the index of its packet in its
+// hardware queue (the LLVM intrinsic behind the code object's dispatch-id
+// register; it has no clang builtin).
+extern "C" __device__ uint64_t rlpl_dispatch_id(void) __asm("llvm.amdgcn.dispatch.id");
+
+// A launch's pair of 32-bit tags: its dispatch id plus two independent hashes
+// of its queue's address.  Two launches on one queue differ in both tags (for
+// 2^32 launches); two launches on different queues agree in both only where
+// the queues' two hash differences coincide (chance 2^-32 per queue pair) and
+// the dispatch ids differ by exactly that amount.  Never zero, so a
+// zero-filled entry is never taken for a published one.
+struct Tag {
+    uint32_t t0, t1;
+};
+__device__ __forceinline__ uint32_t mix32(uint32_t h) {   // MurmurHash3's finaliser
+    h ^= h >> 16;
+    h *= 0x85ebca6bu;
+    h ^= h >> 13;
+    h *= 0xc2b2ae35u;
+    h ^= h >> 16;
+    return h;
+}
+__device__ __forceinline__ Tag launch_tag() {
+    const uint32_t did = uint32_t(rlpl_dispatch_id());
+    const uint64_t q = uint64_t(reinterpret_cast<uintptr_t>(__builtin_amdgcn_queue_ptr()));
+    const uint32_t lo = uint32_t(q), hi = uint32_t(q >> 32);
+    Tag t{did + mix32(lo ^ mix32(hi)), did + mix32(lo ^ mix32(hi ^ 0x9e3779b9u))};
+    if (t.t0 == 0u) t.t0 = 0x80000000u;
+    if (t.t1 == 0u) t.t1 = 0x80000000u;
+    return t;
+}
+
+// ----------------------------------------------------------------------------- published entries
 //
-// Cross-workgroup traffic uses no read-modify-write atomics at all (on this
-// chip device-scope atomics to one line serialise at several ns each, which a
-// grid of a thousand workgroups turns into microseconds).  Instead every
-// workgroup owns one slot of the workspace and publishes two tagged 64-bit
-// words there: its valid-token count and its partial loss.  A tag is the
-// launch generation + 1, so a reader can tell this launch's words from older
-// ones.  A workgroup that needs the global count reads every slot's count
-// word (all-gather by polling); workgroup 0 reads every partial word in slot
-// order, writes the loss and advances the generation for the next launch.
-// All accesses are agent-scope relaxed atomic loads/stores (device-coherent,
-// never an L2-wide writeback or invalidate).
+// The policy-loss kernels exchange values through Entry records of the
+// workspace (per worker: its valid count and its partial loss; from the
+// coordinator: the global count).  No read-modify-write atomics: on this chip
+// device-scope atomics to one line serialise at several ns each.  Entries are
+// packed 16 bytes apart, because reading lines that other compute units have
+// just written costs per line read; each is written and read with one 16-byte
+// device-coherent access (cache policy sc1, the bits of an agent-scope atomic).
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kCoherent = 16;   // buffer cache policy: sc1
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t entry_view(const Workspace* ws) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<Workspace*>(ws), 0, int(kEntryViewBytes), 0x00020000);
+}
+constexpr uint32_t kReleaseOff = uint32_t(offsetof(Workspace, release));
+__device__ __forceinline__ uint32_t cnt_off(uint32_t w) { return uint32_t(offsetof(Workspace, cnt)) + 16u * w; }
+__device__ __forceinline__ uint32_t par_off(uint32_t w) { return uint32_t(offsetof(Workspace, par)) + 16u * w; }
+
+__device__ __forceinline__ void publish(__amdgpu_buffer_rsrc_t v, uint32_t off, Tag t, uint32_t value) {
+    const u32x4 x = {value, t.t0, value, t.t1};
+    __builtin_amdgcn_raw_buffer_store_b128(x, v, off, 0, kCoherent);
+}
+// One read of an entry: true, with its value, when it holds this launch's value.
+__device__ __forceinline__ bool read_entry(__amdgpu_buffer_rsrc_t v, uint32_t off, Tag t, uint32_t& value) {
+    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(v, off, 0, kCoherent);
+    value = x[0];
+    return x[1] == t.t0 && x[3] == t.t1 && x[0] == x[2];
+}
+// Between two polls: a pause, and a compiler barrier so that the next poll is a new load.
+__device__ __forceinline__ void poll_pause() {
+    __builtin_amdgcn_s_sleep(kPollSleep);
+    __asm__ volatile("" ::: "memory");
+}
+
+// The wait limits of the policy-loss kernels in 100 MHz ticks: the caller's
+// overrides in the workspace header (written by the host only), else the
+// defaults.  Read once at the start of a workgroup, where the read overlaps
+// the first data loads: a read just before a poll would hold the poll up by
+// a memory round trip.
+struct Limits {
+    uint32_t steal, release, giveup;
+};
+__device__ __forceinline__ Limits read_limits(const Workspace* ws) {
+    const uint4 v = *reinterpret_cast<const uint4*>(&ws->steal_ticks);
+    return Limits{v.x != 0u ? v.x : kStealTicks, v.y != 0u ? v.y : kReleaseTicks, v.z != 0u ? v.z : kGiveUpTicks};
+}
+
+// Sum over the W workers' entries at `base` (valid counts, or the float bits
+// of partial losses: V = uint32_t / float), in every thread.  Thread i takes
+// workers i, i + kThreads, ... in turn, B at a time (a chunk).  Entries not yet
+// published are polled until they are, or until `limit` ticks have passed;
+// entries still missing then are computed here, one worker at a time by the
+// whole workgroup (compute(w) is workgroup-uniform and bit-identical to what
+// worker w publishes).  The sum is taken in one fixed order (each thread's
+// workers in turn, then the workgroup tree), so it never depends on which
+// entries were computed here.  `list` is LDS of kThreads + 1 words.
+//
+// between() runs once the first chunk's reads are issued and before they are
+// used: a store made there (the release) does not hold them up.  Loads and
+// stores of a wavefront share one in-order completion counter, so a load
+// issued after a device-coherent store waits for that store's write-through.
+template <typename V, typename F, typename G>
+__device__ inline V gather(__amdgpu_buffer_rsrc_t view, uint32_t base, uint32_t W, Tag tg, uint32_t limit,
+                           uint32_t* list, V* red, F&& compute, G&& between) {
+    constexpr int B = 4;
+    V s = 0;
+    for (uint32_t c0 = 0; c0 < W; c0 += B * kThreads) {
+        u32x4 raw[B];
+#pragma unroll
+        for (int j = 0; j < B; ++j) {
+            const uint32_t i = c0 + threadIdx.x + j * kThreads;
+            raw[j] = i < W ? __builtin_amdgcn_raw_buffer_load_b128(view, base + 16u * i, 0, kCoherent) : u32x4{0, 0, 0, 0};
+        }
+        if (c0 == 0) between();
+        uint32_t val[B];
+        uint32_t miss = 0;                     // bit j: worker c0 + tid + j * kThreads not seen yet
+#pragma unroll
+        for (int j = 0; j < B; ++j) {
+            const uint32_t i = c0 + threadIdx.x + j * kThreads;
+            const u32x4 x = raw[j];
+            val[j] = i < W ? x[0] : 0u;
+            if (i < W && !(x[1] == tg.t0 && x[3] == tg.t1 && x[0] == x[2])) miss |= 1u << j;
+        }
+        if (miss) {
+            const uint64_t t0 = wall_clock64();
+            for (uint32_t n = 1; miss; ++n) {
+                poll_pause();
+#pragma unroll
+                for (int j = 0; j < B; ++j)
+                    if (miss & (1u << j)) {
+                        uint32_t v;
+                        if (read_entry(view, base + 16u * (c0 + threadIdx.x + j * kThreads), tg, v)) {
+                            val[j] = v;
+                            miss &= ~(1u << j);
+                        }
+                    }
+                if ((n & 7u) == 0u && uint64_t(wall_clock64()) - t0 > limit) break;
+            }
+        }
+        // Workers still missing: computed here.  The list holds the threads that
+        // have any (their order does not matter: each value lands in its own place).
+        if (__syncthreads_or(miss != 0u)) {
+            if (threadIdx.x == 0) list[kThreads] = 0;
+            __syncthreads();
+            if (miss) list[atomicAdd(&list[kThreads], 1u)] = threadIdx.x | (miss << 16);
+            __syncthreads();
+            const uint32_t n_list = list[kThreads];
+            for (uint32_t k = 0; k < n_list; ++k) {
+                const uint32_t t = list[k] & 0xFFFFu, bits = list[k] >> 16;
+#pragma unroll
+                for (int j = 0; j < B; ++j)
+                    if (bits & (1u << j)) {
+                        const V v = compute(c0 + t + uint32_t(j) * kThreads);
+                        if (threadIdx.x == t) {
+                            if constexpr (std::is_same<V, float>::value) val[j] = __float_as_uint(v);
+                            else val[j] = v;
+                        }
+                    }
+            }
+            __syncthreads();                   // list[] is reused by the next chunk
+        }
+#pragma unroll
+        for (int j = 0; j < B; ++j) {
+            if constexpr (std::is_same<V, float>::value) s += __uint_as_float(val[j]);
+            else s += val[j];
+        }
+    }
+    return block_sum(s, red);
+}
+
+// The thread of each workgroup that publishes its count, the one that
+// publishes its partial, and the one that polls for the release: each in a
+// wavefront of its own, so that no poll waits for the write-through of a
+// store made before it in the same wavefront.
+constexpr uint32_t kCountThread = 0;
+constexpr uint32_t kPartialThread = 64;
+constexpr uint32_t kReleaseThread = 128;
+
+// The global count, in every thread: the coordinator's release, or, when it
+// has not come within the release limit, this workgroup's own gather of the
+// counts (gather_counts(), workgroup-uniform).  `word` is LDS of two words.
+template <typename F>
+__device__ inline uint32_t await_release(__amdgpu_buffer_rsrc_t view, uint32_t limit, Tag tg, uint32_t* word,
+                                         F&& gather_counts) {
+    __syncthreads();
+    if (threadIdx.x == kReleaseThread) {
+        uint32_t v = 0;
+        bool ok = read_entry(view, kReleaseOff, tg, v);
+        if (!ok) {
+            const uint64_t t0 = wall_clock64();
+            for (uint32_t n = 1; !ok; ++n) {
+                poll_pause();
+                ok = read_entry(view, kReleaseOff, tg, v);
+                if ((n & 7u) == 0u && uint64_t(wall_clock64()) - t0 > limit) break;
+            }
+        }
+        word[0] = v;
+        word[1] = ok ? 1u : 0u;
+    }
+    __syncthreads();
+    if (word[1]) return word[0];
+    return gather_counts();
+}
+
+// ----------------------------------------------------------------------------- full-vocab protocol
+//
+// The full-vocab kernels publish generation-tagged 64-bit words in per-
+// workgroup slots: [63:32 tag | 31:0 value], with tag = generation + 1 (+ the
+// exchange round); workgroup 0 advances the generation once it has read every
+// partial of the launch (after which no workgroup of the launch reads it).
 
 __device__ __forceinline__ uint64_t load_relaxed(const uint64_t* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -186,95 +379,71 @@ __device__ __forceinline__ void store_relaxed(V* p, V v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Tags published by the launch of generation `gen`.  A zero-filled workspace
-// holds tag 0 everywhere, which is the tag of no launch's first use; a slot
-// left from an older launch carries an older tag (32-bit, so a stale tag
-// could only match after 2^32 launches on one workspace).
 __device__ __forceinline__ uint32_t tag_of(uint32_t gen) { return gen + 1u; }
 __device__ __forceinline__ uint64_t tagged(uint32_t tag, uint32_t value) {
     return (uint64_t(tag) << 32) | value;
 }
 
-// Polls a tagged word until it carries `tag`.  Bounded: the grid never exceeds
-// the co-resident capacity, so every workgroup publishes within microseconds;
-// the wait gives up after ~1 s of the 100 MHz clock (or kWaitLimitPolls polls,
-// should that clock not advance) and leaves a sticky flag.
-__device__ inline uint64_t wait_tagged(Workspace* ws, const uint64_t* word, uint32_t tag) {
-    uint64_t v = load_relaxed(word);
-    if (uint32_t(v >> 32) == tag) return v;
-    // The clock is read once per 64 polls: reading it is itself a slow scalar
-    // memory access that would otherwise sit between consecutive polls.
+// Polls a tagged word until it carries `tag`, for at most `limit` ticks of the
+// 100 MHz clock (and kWaitLimitPolls polls, should that clock not advance).
+// Returns whether it did; `v` holds the last word read.
+__device__ inline bool wait_tagged(const uint64_t* word, uint32_t tag, uint64_t limit, uint64_t& v) {
+    v = load_relaxed(word);
+    if (uint32_t(v >> 32) == tag) return true;
+    // The clock is read after the first failed poll and then once per 64 polls:
+    // reading it is itself a slow scalar memory access that would otherwise sit
+    // between consecutive polls.
     const uint64_t t0 = wall_clock64();
     uint32_t polls = 0;
     while (uint32_t((v = load_relaxed(word)) >> 32) != tag) {
         __builtin_amdgcn_s_sleep(kPollSleep);
-        if ((++polls & 63) == 0 && (wall_clock64() - t0 > kWaitLimitTicks || polls > kWaitLimitPolls)) {
-            __hip_atomic_fetch_or(&ws->flags, kFlagWaitTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            break;
-        }
+        ++polls;
+        if ((polls == 1u || (polls & 63u) == 0u) &&
+            (uint64_t(wall_clock64()) - t0 > limit || polls > kWaitLimitPolls))
+            return false;
     }
-    return v;
+    return true;
 }
 
-// Thread 0 of worker `w` publishes its count / partial for the launch of generation `gen`.
-__device__ __forceinline__ void publish_count(Workspace* ws, uint32_t w, uint32_t gen, uint32_t n) {
-    store_relaxed(&ws->slot[w].count, tagged(tag_of(gen), n));
-}
 __device__ __forceinline__ void publish_partial(Workspace* ws, uint32_t w, uint32_t gen, float part) {
     store_relaxed(&ws->slot[w].partial, tagged(tag_of(gen), __float_as_uint(part)));
 }
 
-// Sum over the W workers' slots of this launch's count words (COUNTS) or
-// partial words (otherwise), in every thread.  Each thread owns slots tid, tid+256, ...: eight
-// independent loads in flight, then any word still carrying an older tag is
-// waited for, then the values are added in slot order and reduced with the fixed
-// workgroup tree, so the result is deterministic.
-template <bool COUNTS>
-__device__ inline auto gather_slots(Workspace* ws, uint32_t G, uint32_t gen, float* red_f, uint32_t* red_u) {
-    using V = typename std::conditional<COUNTS, uint32_t, float>::type;
+// Workgroup 0's sum of the G workgroups' partial words of this launch, in
+// every thread, in slot order then the fixed workgroup tree (deterministic).
+// Each thread owns slots tid, tid+256, ...: eight loads in flight, then any
+// word still carrying an older tag is waited for.  A wait that gives up (after
+// `limit` ticks) sets the sticky flag and makes the sum NaN.
+__device__ inline float gather_partials(Workspace* ws, uint32_t G, uint32_t gen, uint32_t limit, float* red_f) {
     constexpr int kBatch = 8;
     const uint32_t tag = tag_of(gen);
-    V s = 0;
+    float s = 0.0f;
+    bool lost = false;
     for (uint32_t base = threadIdx.x; base < G; base += kThreads * kBatch) {
         uint64_t v[kBatch];
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
             const uint32_t i = base + u * kThreads;
-            const uint64_t* w = COUNTS ? &ws->slot[i].count : &ws->slot[i].partial;
-            v[u] = i < G ? load_relaxed(w) : tagged(tag, 0);
+            v[u] = i < G ? load_relaxed(&ws->slot[i].partial) : tagged(tag, 0);
         }
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
             const uint32_t i = base + u * kThreads;
-            const uint64_t* w = COUNTS ? &ws->slot[i].count : &ws->slot[i].partial;
-            if (i < G && uint32_t(v[u] >> 32) != tag) v[u] = wait_tagged(ws, w, tag);
+            if (i < G && uint32_t(v[u] >> 32) != tag && !wait_tagged(&ws->slot[i].partial, tag, limit, v[u]))
+                lost = true;
         }
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            if (base + u * kThreads < G) {
-                if constexpr (COUNTS) s += uint32_t(v[u]);
-                else s += __uint_as_float(uint32_t(v[u]));
-            }
-        }
+        for (int u = 0; u < kBatch; ++u)
+            if (base + u * kThreads < G) s += __uint_as_float(uint32_t(v[u]));
     }
-    if constexpr (COUNTS) return block_sum(s, red_u);
-    else return block_sum(s, red_f);
+    if (lost) {
+        __hip_atomic_fetch_or(&ws->flags, kFlagWaitTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s = __builtin_nanf("");
+    }
+    return block_sum(s, red_f);
 }
 
-// The global count: the coordinator gathers every count word and publishes the
-// total on the release line; every worker reads the release line (one poller
-// per workgroup on one line, one reader per slot line).
-__device__ __forceinline__ void release_count(Workspace* ws, uint32_t gen, uint32_t n) {
-    if (threadIdx.x == 0) store_relaxed(&ws->release, tagged(tag_of(gen), n));
-}
-__device__ inline uint32_t await_count(Workspace* ws, uint32_t gen, uint32_t* word) {
-    __syncthreads();
-    if (threadIdx.x == 0) *word = uint32_t(wait_tagged(ws, &ws->release, tag_of(gen)));
-    __syncthreads();
-    return *word;
-}
-
-// The coordinator, once it has read every partial of the launch: every workgroup
+// Workgroup 0, once it has read every partial of the launch: every workgroup
 // has read the generation by then, so the next launch may use the next one.
 __device__ __forceinline__ void advance_generation(Workspace* ws, uint32_t gen, uint32_t by = 1u) {
     if (threadIdx.x == 0) store_relaxed(&ws->generation, gen + by);

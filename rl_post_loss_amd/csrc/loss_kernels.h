@@ -19,62 +19,81 @@ constexpr int kVecSmall = 4;
 // (512 B per tile): 56 (28 KB) for BNPO and 40 (20 KB) for reverse-KL, which
 // leaves each kernel's register-bound occupancy (4 and 6 workgroups per CU)
 // within the 128 KB of LDS per CU that the host budgets.
-#ifndef RLPL_BIT_TILES_POLICY
-#define RLPL_BIT_TILES_POLICY 56
-#endif
-#ifndef RLPL_BIT_TILES_RKL
-#define RLPL_BIT_TILES_RKL 40
-#endif
-constexpr int kBitTilesPolicy = RLPL_BIT_TILES_POLICY;
-constexpr int kBitTilesRkl = RLPL_BIT_TILES_RKL;
+constexpr int kBitTilesPolicy = 56;
+constexpr int kBitTilesRkl = 40;
 // Kernel shapes: one tile per worker with the narrow or the wide lane, or the
 // wide lane striding over several tiles per worker.
 enum { kShapeSmall = 0, kShapeLarge = 1, kShapeStream = 2, kShapes = 3 };
-#ifndef RLPL_SMALL_TILES_PER_CU
-#define RLPL_SMALL_TILES_PER_CU 1
-#endif
-constexpr int kSmallTilesPerCu = RLPL_SMALL_TILES_PER_CU;
+// The narrow lane is taken when a problem has fewer wide tiles than compute units.
+constexpr int kSmallTilesPerCu = 1;
 constexpr int kMaxGrid = 4096;              // upper bound on the persistent grid (gfx950: <= 256 CUs x 8)
-constexpr uint64_t kWaitLimitTicks = 100000000ull;   // ~1 s of the 100 MHz wall clock
-constexpr uint32_t kWaitLimitPolls = 1u << 24;        // second bound on the same wait
+// Waits of the policy-loss kernels, in ticks of the 100 MHz wall clock.  A
+// coordinator that has waited kStealTicks for a worker's published count or
+// partial computes that value itself from the inputs; a worker that has waited
+// kReleaseTicks for the global count gathers it itself.  Either way the result
+// is bit-identical, so no wait depends on another workgroup being resident.
+constexpr uint32_t kStealTicks = 5000;      // 50 us
+constexpr uint32_t kReleaseTicks = 20000;   // 200 us
+// The full-vocab kernels' waits for the partial sums of their peers give up
+// after ~1 s (kGiveUpTicks, or kWaitLimitPolls polls should the clock not
+// advance): the loss is then NaN and a sticky flag is set.
+constexpr uint32_t kGiveUpTicks = 100000000u;
+constexpr uint32_t kWaitLimitPolls = 1u << 24;
 constexpr uint32_t kFlagWaitTimeout = 1u;
 // Pause between two polls of a word another workgroup will publish, in units
-// of 64 clocks (s_sleep); spaces out the polling of a whole grid.
-#ifndef RLPL_POLL_SLEEP
-#define RLPL_POLL_SLEEP 1
-#endif
-constexpr int kPollSleep = RLPL_POLL_SLEEP;
+// of 64 clocks (s_sleep).
+constexpr int kPollSleep = 1;
 
 enum { kModeBNPO = 0, kModeGRPO = 1, kModeRKL = 2 };
 enum { kF32 = 0, kF16 = 1, kBF16 = 2 };
 
-// One workgroup's published words: [63:32 tag (generation + 1) | 31:0 value].
-// One slot per 256-byte line: stores from many workgroups to a shared line
-// become visible to the other compute units markedly later than stores to
-// lines of their own.
-struct alignas(256) Slot {
-    uint64_t count;            // valid-token count of the workgroup's tiles
-    uint64_t partial;          // float bits of the workgroup's partial loss
-    uint64_t stats[2][5];      // full-vocab reverse KL: a row chunk's online sums,
-                               // double-buffered by round (tag = generation + 1 + round)
+// One value published by one workgroup for the others: two 64-bit words
+// [63:32 tag t0 | 31:0 value] and [63:32 tag t1 | 31:0 value], written and
+// read as one 16-byte access.  A reader takes it only when both tags are its
+// launch's and both values agree, so a torn or stale entry is never taken.
+struct alignas(16) Entry {
+    uint64_t w[2];
 };
 
-// Device workspace.  Zero-filled once by the caller; every launch advances
-// `generation` by one and leaves nothing else that the next launch depends on.
-struct Workspace {
-    uint32_t generation;       // launch counter: read by every workgroup at its start,
-    uint32_t pad0[63];         // advanced by workgroup 0 at the end of the launch
-    uint32_t flags;            // sticky error bits (kFlagWaitTimeout)
-    uint32_t pad1[63];
-    uint64_t release;          // [63:32 tag | 31:0 global count], published by workgroup 0
-    uint64_t pad2[31];
-    Slot slot[kMaxGrid];
+// Per-workgroup words of the full-vocab kernels: [63:32 tag (generation + 1 +
+// round) | 31:0 value].  One slot per 256-byte line: stores from many
+// workgroups to a shared line become visible to the other compute units
+// markedly later than stores to lines of their own.
+struct alignas(256) Slot {
+    uint64_t partial;          // float bits of the workgroup's partial loss
+    uint64_t stats[2][5];      // a row piece's online sums, double-buffered by exchange
 };
-static_assert(offsetof(Workspace, flags) == 256, "header words on separate lines");
-static_assert(offsetof(Workspace, release) == 512, "header words on separate lines");
-static_assert(offsetof(Workspace, slot) == 768, "workspace header");
+
+// Device workspace.  Zero-filled once by the caller.  The policy-loss kernels
+// tag what they publish with their launch's identity (no state carried from
+// one launch to the next); the full-vocab kernels advance `generation` by the
+// number of tags they used.  Header words sit on 128-byte lines of their own.
+struct Workspace {
+    uint32_t generation;       // full-vocab kernels: launch counter
+    uint32_t pad0[31];
+    uint32_t flags;            // sticky error bits (kFlagWaitTimeout)
+    uint32_t pad1[31];
+    uint32_t steal_ticks;      // caller-set wait limits (0 selects kStealTicks,
+    uint32_t release_ticks;    // kReleaseTicks and kGiveUpTicks); written by the
+    uint32_t giveup_ticks;     // host only (rlpl_workspace_set_limits)
+    uint32_t pad2[29];
+    Entry release;             // the global valid count N, published by the coordinator
+    uint64_t pad3[14];
+    Entry cnt[kMaxGrid];       // per worker: its valid-token count
+    Entry par[kMaxGrid];       // per worker: float bits of its partial loss
+    Slot slot[kMaxGrid];       // full-vocab kernels
+};
+static_assert(offsetof(Workspace, flags) == 128, "header words on separate lines");
+static_assert(offsetof(Workspace, steal_ticks) == 256, "header words on separate lines");
+static_assert(offsetof(Workspace, release) == 384, "header words on separate lines");
+static_assert(offsetof(Workspace, cnt) == 512, "workspace header");
+static_assert(sizeof(Slot) == 256, "one slot per line");
 constexpr size_t kWorkspaceBytes = sizeof(Workspace);
 constexpr size_t kFlagsOffset = offsetof(Workspace, flags);
+constexpr size_t kLimitsOffset = offsetof(Workspace, steal_ticks);
+// Bytes from the workspace's start that the policy-loss kernels address with
+// 16-byte buffer accesses (the header and both entry arrays).
+constexpr size_t kEntryViewBytes = offsetof(Workspace, slot);
 
 // Kernel arguments (passed by value).
 struct Args {

@@ -15,23 +15,28 @@
 //    bytes and its VEC log-probs per plane with 32/64/128-bit loads.  VEC is
 //    16 for large problems and 4 for small ones, so that a small problem
 //    still spreads over every compute unit.
-//  * A persistent grid of G <= (co-resident workgroups): workgroup 0
-//    coordinates, workers 1..G-1 take tiles w, w+(G-1), ...  Per-token math
-//    is fp32 in registers and
-//    branch-free: every slot of a lane is computed and masked slots are
-//    selected away (their values never reach a result).
+//  * A grid of G workgroups (at most what the device holds at once):
+//    workgroup 0 coordinates, workers take tiles w, w+(G-1), ...  Per-token
+//    math is fp32 in registers and branch-free: every slot of a lane is
+//    computed and masked slots are selected away (their values never reach
+//    a result).
 //  * Reductions: per-lane sums -> wavefront shuffle tree -> LDS across the
 //    4 waves -> one partial per worker in the workspace.  The coordinator
 //    sums the partials in worker order, so the loss is deterministic and
 //    identical between the fwd+bwd and forward-only kernels.
 //  * BNPO / RKL fwd+bwd need the global valid count N before any gradient is
-//    scaled: each worker publishes its count in a slot of its own; the
-//    coordinator gathers them and publishes N on a release line that the
-//    workers read once their own tile is computed.  All cross-workgroup
-//    traffic is device-coherent loads/stores of generation-tagged words: no
-//    read-modify-write atomics, never an L2-wide writeback or invalidate.
-//    The grid never exceeds the co-resident capacity; every wait is bounded
-//    in time anyway and sets a sticky flag if it ever gives up.
+//    scaled: each worker publishes its count as an entry of the workspace;
+//    the coordinator gathers them and publishes N (the release) that the
+//    workers read once their own tile is computed.  Entries carry the
+//    launch's tags (its dispatch id on its queue), so nothing carries over
+//    from one launch to the next; all cross-workgroup traffic is
+//    device-coherent 16-byte loads and stores: no read-modify-write atomics,
+//    never an L2-wide writeback or invalidate.
+//  * No workgroup depends on another being resident: a value not published
+//    within a time limit is computed by the waiting workgroup itself (the
+//    coordinator a worker's count or partial, a worker the global count),
+//    by the same code, so the results are bit-identical however the launch
+//    is scheduled (beside other kernels, on several streams).
 //    When a workgroup owns a single tile, its count is published as soon as
 //    its mask has arrived (the exchange then overlaps the plane loads and the
 //    per-token math) and the tile never leaves registers; with more tiles it
@@ -49,6 +54,11 @@
 
 #include "device_common.h"
 #include "loss_kernels.h"
+
+// No implicit a*b+c contraction: a value the coordinator computes in place of
+// a worker must round exactly as the worker's own (the fmaf calls below are
+// the intended fused operations).
+#pragma clang fp contract(off)
 
 namespace rlpl {
 
@@ -343,7 +353,7 @@ __device__ __forceinline__ void store_grad(const Args& a, uint32_t s, const Mask
 // cnt[row - r_first] (LDS), then turns each count into the row's gradient
 // scale 1 / (max(n_r, 1) * bs) in place.  Writes n_out for rows that start in
 // the tile (exactly one tile per row does).
-__device__ void grpo_row_scales(const Args& a, uint32_t s0, uint32_t s1, uint32_t* cnt,
+__device__ __forceinline__ void grpo_row_scales(const Args& a, uint32_t s0, uint32_t s1, uint32_t* cnt,
                                 uint32_t& r_first) {
     const uint32_t T = uint32_t(a.seq_len);
     r_first = row_of(a, s0);
@@ -450,18 +460,26 @@ __device__ __forceinline__ void stream_tiles(const Args& a, uint32_t worker, uin
 }
 
 // Workgroup 0 coordinates: it gathers the workers' counts, releases N (fwd+bwd
-// BNPO / reverse-KL), gathers their partials in worker order, writes the loss
-// and advances the generation.  ONE_TILE kernels are launched with exactly one
-// tile per worker and a coordinator that owns no tile (G = tiles + 1), and
-// keep the tile in registers in straight-line code.  The others (G at most the
-// co-resident capacity, G <= tiles) stride over any number of tiles per
-// worker, which costs registers, and workgroup 0 is a worker as well.
+// BNPO / reverse-KL), gathers their partials in worker order and writes the
+// loss.  ONE_TILE kernels are launched with exactly one tile per worker and a
+// coordinator that owns no tile (G = tiles + 1), and keep the tile in registers
+// in straight-line code.  The others (G at most the co-resident capacity,
+// G <= tiles) stride over any number of tiles per worker, which costs
+// registers, and workgroup 0 is a worker as well.
+//
+// No wait depends on another workgroup being resident: a count or partial the
+// coordinator has not seen within the steal limit is computed by the
+// coordinator itself from the inputs (the worker, whenever it runs, computes
+// and stores the same values), and a worker that has not seen N within the
+// release limit gathers it itself.  Every such value is computed by the same
+// code as the worker's own, so the results are bit-identical either way.
 template <typename T, int MODE, bool HAS_KL, bool WRITE_GRAD, int VEC, bool ONE_TILE>
 __global__ void __launch_bounds__(kThreads) loss_kernel(const Args a) {
     constexpr uint32_t kTileV = kThreads * VEC;
     __shared__ float red_f[kWaves];
     __shared__ uint32_t red_u[kWaves];
-    __shared__ uint32_t word[1];
+    __shared__ uint32_t word[2];
+    __shared__ uint32_t list[kThreads + 1];
     // GRPO: per-row counts, then per-row scales, of the rows a tile touches.
     constexpr int kRowLds = (MODE == kModeGRPO) ? int(kTileV) + 2 : 1;
     __shared__ uint32_t row_lds[kRowLds];
@@ -472,49 +490,85 @@ __global__ void __launch_bounds__(kThreads) loss_kernel(const Args a) {
     constexpr int kBitTiles = kKeepBits ? (MODE == kModeRKL ? kBitTilesRkl : kBitTilesPolicy) : 1;
     __shared__ uint16_t mask_bits[kBitTiles * kThreads];
 
-    Workspace* ws = a.ws;
-    // The launch generation tags everything this launch publishes; thread 0 reads it
-    // first so that the read is in flight together with the data loads.  Every word
-    // a workgroup publishes carries a value derived from it, so its stores cannot be
-    // issued before the read has returned.
-    uint32_t gen = 0;
-    if (threadIdx.x == 0) gen = load_relaxed(&ws->generation);
-
     constexpr bool kGlobalN = MODE != kModeGRPO;
     constexpr bool kExchange = kGlobalN && WRITE_GRAD;
+    const Workspace* ws = a.ws;
+    const __amdgpu_buffer_rsrc_t view = entry_view(ws);
+    const Tag tg = launch_tag();
+    const Limits lim = read_limits(ws);
     const uint32_t slots = uint32_t(a.slots);
+    const uint32_t W = ONE_TILE ? gridDim.x - 1 : gridDim.x;   // workers
+    const uint32_t lane_off = threadIdx.x * VEC;
+
+    // Worker w's valid count and partial loss, computed by the calling workgroup
+    // (uniform), exactly as worker w forms its own.
+    auto count_of = [&](uint32_t w) -> uint32_t {
+        uint32_t n = 0;
+        for (uint32_t tile = w; tile < a.tiles; tile += ONE_TILE ? a.tiles : W) {
+            Mask<VEC> m;
+            m.load(a.mask, tile * kTileV + lane_off, slots);
+            n += m.count();
+        }
+        return block_sum(n, red_u);
+    };
+    auto partial_of = [&](uint32_t w) -> float {
+        float part = 0.0f;
+        if constexpr (ONE_TILE) {
+            const uint32_t s = w * kTileV + lane_off;
+            uint32_t row_base = 0;
+            if constexpr (MODE == kModeGRPO) {
+                const uint32_t s0 = w * kTileV;
+                grpo_row_scales(a, s0, s0 + kTileV < slots ? s0 + kTileV : slots, row_lds, row_base);
+            }
+            Lane<T, VEC> L;
+            (void)load_lane_count<T, MODE, HAS_KL, VEC, false>(a, s, L);
+            float g[VEC];
+            part = lane_terms<T, MODE, HAS_KL, VEC>(a, s, L, reinterpret_cast<const float*>(row_lds), row_base,
+                                                    1.0f, g);
+        } else {
+            uint32_t n_unused = 0;
+            stream_tiles<T, MODE, HAS_KL, false, VEC>(a, w, W, row_lds, part, n_unused, 1.0f);
+        }
+        return block_sum(part, red_f);
+    };
+    auto nothing = [] {};
+    auto gather_counts = [&]() -> uint32_t {
+        return gather<uint32_t>(view, cnt_off(0), W, tg, lim.steal, list, red_u, count_of, nothing);
+    };
+    // The partials' first reads go out before the release (when there is one) is stored.
+    auto gather_partials = [&](auto&& between) -> float {
+        return gather<float>(view, par_off(0), W, tg, lim.steal, list, red_f, partial_of, between);
+    };
+
     float part = 0.0f;
     uint32_t n_lane = 0;
 
     if constexpr (ONE_TILE) {
         // Workgroup 0 coordinates only; workgroup w > 0 is worker w - 1 and owns tile w - 1.
-        const uint32_t W = gridDim.x - 1;
         if (blockIdx.x == 0) {
-            gen = share_generation(gen, word);
             uint32_t N = 0;
-            if constexpr (kGlobalN) N = gather_slots<true>(ws, W, gen, red_f, red_u);
-            if constexpr (kExchange) release_count(ws, gen, N);
-            const float total = gather_slots<false>(ws, W, gen, red_f, red_u);
-            advance_generation(ws, gen);
+            if constexpr (kGlobalN) N = gather_counts();
+            const float total = gather_partials([&] {
+                if (kExchange && threadIdx.x == 0) publish(view, kReleaseOff, tg, N);
+            });
             if (threadIdx.x == 0) write_results<MODE>(a, total, N);
             return;
         }
         const uint32_t worker = blockIdx.x - 1;
-        const uint32_t s = worker * kTileV + threadIdx.x * VEC;
+        const uint32_t s = worker * kTileV + lane_off;
         Lane<T, VEC> L;
         if constexpr (kExchange) {
             // The tile stays in registers across the count exchange.  The count is
             // published as soon as the mask (loaded first) has arrived, so the exchange
             // runs while the planes are still arriving and being computed on; the
-            // partial loss follows as the slot's second word.
+            // partial loss follows.
             const uint32_t n_wg = block_sum(load_lane_count<T, MODE, HAS_KL, VEC, false>(a, s, L), red_u);
-            gen = share_generation(gen, word);
-            if (threadIdx.x == 0) publish_count(ws, worker, gen, n_wg);
+            if (threadIdx.x == kCountThread) publish(view, cnt_off(worker), tg, n_wg);
             float g[VEC];
             part = lane_terms<T, MODE, HAS_KL, VEC>(a, s, L, nullptr, 0, 1.0f, g);
             const float part_wg = block_sum(part, red_f);
-            if (threadIdx.x == 0) publish_partial(ws, worker, gen, part_wg);
-            const uint32_t N = await_count(ws, gen, word);
+            if (threadIdx.x == kPartialThread) publish(view, par_off(worker), tg, __float_as_uint(part_wg));
+            const uint32_t N = await_release(view, lim.release, tg, word, gather_counts);
             store_grad<T, VEC, true>(a, s, L.m, g, inv_count<MODE>(N));
         } else {
             // Forward-only (any mode) and GRPO fwd+bwd.  GRPO first scans the masks of
@@ -530,26 +584,23 @@ __global__ void __launch_bounds__(kThreads) loss_kernel(const Args a) {
             part = lane_terms<T, MODE, HAS_KL, VEC>(a, s, L, reinterpret_cast<const float*>(row_lds),
                                                     row_base, 1.0f, g);
             if constexpr (WRITE_GRAD) store_grad<T, VEC, false>(a, s, L.m, g, 1.0f);
-            gen = share_generation(gen, word);
             const float part_wg = block_sum(part, red_f);
             uint32_t n_wg = 0;
             if constexpr (kGlobalN) n_wg = block_sum(n_lane, red_u);
-            if (threadIdx.x == 0) {
-                if constexpr (kGlobalN) publish_count(ws, worker, gen, n_wg);
-                publish_partial(ws, worker, gen, part_wg);
+            if constexpr (kGlobalN) {
+                if (threadIdx.x == kCountThread) publish(view, cnt_off(worker), tg, n_wg);
             }
+            if (threadIdx.x == kPartialThread) publish(view, par_off(worker), tg, __float_as_uint(part_wg));
         }
     } else {
         // Every workgroup is a worker striding over the tiles; workgroup 0 also
         // coordinates (a dedicated coordinator would take one of the co-resident
         // slots, and with it a whole extra tile from some worker's share).
-        const uint32_t W = gridDim.x;
         const uint32_t worker = blockIdx.x;
         uint32_t N = 0;
         if constexpr (kExchange) {
             // Count every owned mask (eight loads in flight per lane) and keep the
             // bits of the first kBitTiles tiles, exchange, then stream.
-            const uint32_t lane_off = threadIdx.x * VEC;
             uint32_t tile = worker, j = 0;
             for (; tile + 7 * W < a.tiles; tile += 8 * W, j += 8) {
                 Mask<VEC> m[8];
@@ -570,36 +621,36 @@ __global__ void __launch_bounds__(kThreads) loss_kernel(const Args a) {
                 if (j < uint32_t(kBitTiles)) mask_bits[j * kThreads + threadIdx.x] = uint16_t(b);
             }
             const uint32_t n_bits = j < uint32_t(kBitTiles) ? j : uint32_t(kBitTiles);
-            gen = share_generation(gen, word);
             const uint32_t n_wg = block_sum(n_lane, red_u);
-            if (threadIdx.x == 0) publish_count(ws, worker, gen, n_wg);
             if (blockIdx.x == 0) {
-                N = gather_slots<true>(ws, W, gen, red_f, red_u);
-                release_count(ws, gen, N);
+                // The coordinator's own count goes out once its reads of the others' are issued.
+                N = gather<uint32_t>(view, cnt_off(0), W, tg, lim.steal, list, red_u, count_of, [&] {
+                    if (threadIdx.x == kCountThread) publish(view, cnt_off(worker), tg, n_wg);
+                });
+                if (threadIdx.x == kCountThread) publish(view, kReleaseOff, tg, N);
             } else {
-                N = await_count(ws, gen, word);
+                if (threadIdx.x == kCountThread) publish(view, cnt_off(worker), tg, n_wg);
+                N = await_release(view, lim.release, tg, word, gather_counts);
             }
             uint32_t unused_n = 0;
             stream_tiles<T, MODE, HAS_KL, true, VEC>(a, worker, W, row_lds, part, unused_n, inv_count<MODE>(N),
                                                      mask_bits, n_bits);
             const float part_wg = block_sum(part, red_f);
-            if (threadIdx.x == 0) publish_partial(ws, worker, gen, part_wg);
+            if (threadIdx.x == kPartialThread) publish(view, par_off(worker), tg, __float_as_uint(part_wg));
         } else {
             // Forward-only (any mode) and GRPO fwd+bwd: one streaming pass, no exchange.
             stream_tiles<T, MODE, HAS_KL, WRITE_GRAD, VEC>(a, worker, W, row_lds, part, n_lane, 1.0f);
-            gen = share_generation(gen, word);
             const float part_wg = block_sum(part, red_f);
             uint32_t n_wg = 0;
             if constexpr (kGlobalN) n_wg = block_sum(n_lane, red_u);
-            if (threadIdx.x == 0) {
-                if constexpr (kGlobalN) publish_count(ws, worker, gen, n_wg);
-                publish_partial(ws, worker, gen, part_wg);
+            if constexpr (kGlobalN) {
+                if (threadIdx.x == kCountThread) publish(view, cnt_off(worker), tg, n_wg);
             }
-            if (kGlobalN && blockIdx.x == 0) N = gather_slots<true>(ws, W, gen, red_f, red_u);
+            if (threadIdx.x == kPartialThread) publish(view, par_off(worker), tg, __float_as_uint(part_wg));
+            if (kGlobalN && blockIdx.x == 0) N = gather_counts();
         }
         if (blockIdx.x == 0) {
-            const float total = gather_slots<false>(ws, W, gen, red_f, red_u);
-            advance_generation(ws, gen);
+            const float total = gather_partials(nothing);
             if (threadIdx.x == 0) write_results<MODE>(a, total, N);
         }
     }

@@ -389,6 +389,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
     Workspace* ws = a.ws;
     uint32_t gen = 0;
     if (threadIdx.x == 0) gen = load_relaxed(&ws->generation);
+    const Limits lim = read_limits(ws);
 
     const uint32_t C = a.chunks;
     const uint32_t R = gridDim.x / C;
@@ -457,7 +458,10 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
             for (uint32_t i = threadIdx.x; i < 5 * C; i += kThreads) {
                 const uint64_t* w = &ws->slot[grp * C + i / 5].stats[buf][i % 5];
                 uint64_t x = load_relaxed(w);
-                if (uint32_t(x >> 32) != tag) x = wait_tagged(ws, w, tag);
+                if (uint32_t(x >> 32) != tag && !wait_tagged(w, tag, lim.giveup, x)) {
+                    __hip_atomic_fetch_or(&ws->flags, kFlagWaitTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    x = __float_as_uint(__builtin_nanf(""));
+                }
                 peer[i] = __uint_as_float(uint32_t(x));
             }
             __syncthreads();
@@ -490,7 +494,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
 
     if (threadIdx.x == 0) publish_partial(ws, blockIdx.x, gen, part);
     if (blockIdx.x == 0) {
-        const float total = gather_slots<false>(ws, gridDim.x, gen, red_f, red_u);
+        const float total = gather_partials(ws, gridDim.x, gen, lim.giveup, red_f);
         // This launch used tags gen + 1 .. gen + rounds; the next starts above them.
         advance_generation(ws, gen, rounds + 1u);
         if (threadIdx.x == 0) {

@@ -174,6 +174,11 @@ def test_workspace_flags_validation(lib):
     assert rl.STATUS[lib.rlpl_workspace_flags(WS + 4, ctypes.byref(flags), None)] == "RLPL_ERR_ALIGN"
 
 
+def test_workspace_set_limits_validation(lib):
+    assert rl.STATUS[lib.rlpl_workspace_set_limits(None, 1, 1, 1, None)] == "RLPL_ERR_NULL"
+    assert rl.STATUS[lib.rlpl_workspace_set_limits(WS + 16, 1, 1, 1, None)] == "RLPL_ERR_ALIGN"
+
+
 def test_beta_zero_allows_missing_ref_without_a_device(lib):
     # Passes validation (beta == 0 compiles the KL term out, ref may be NULL) and then
     # stops at the device check: only meaningful, and only safe, on a host with no GPU.

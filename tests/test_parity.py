@@ -133,7 +133,10 @@ def test_forward_only_loss_equals_fused_loss_bitwise(op):
     assert a.cpu().view(torch.int32).item() == b.cpu().view(torch.int32).item()
 
 
-def test_repeated_calls_are_bitwise_identical_and_rearm_the_workspace():
+def test_repeated_calls_are_bitwise_identical_and_leave_tagged_entries():
+    """Every call publishes its values as entries carrying its launch's two tags (workspace
+    header: flags at byte 128, release entry at 384; per-worker count entries from byte 512,
+    16 bytes each: value, t0, value, t1); the next call carries other tags."""
     w = synthetic.WORKLOADS["bnpo_bf16_64x4096"]
     x = dev(synthetic.inputs(w))
     kw = dict(epsilon=w.epsilon, epsilon_high=w.epsilon_high, beta=w.beta)
@@ -144,21 +147,23 @@ def test_repeated_calls_are_bitwise_identical_and_rearm_the_workspace():
         assert torch.equal(g1.view(torch.int16), g0.view(torch.int16))
     torch.cuda.synchronize()
     ws = rl.workspace_for(DEV, torch.cuda.current_stream(DEV).cuda_stream, "bnpo")
-    head = ws[:768 + 256 * 64].cpu()
-    gen = int(head[0:4].view(torch.int32)[0]) & 0xFFFFFFFF
-    assert int(head[256:260].view(torch.int32)[0]) == 0   # no timeout flag
-    release = int(head[512:520].view(torch.int64)[0]) & (2**64 - 1)
-    assert release >> 32 == gen                           # the last release carries its tag
-    assert release & 0xFFFFFFFF == int(torch.count_nonzero(x["mask"]))
-    w64 = head[768:].view(torch.int64).numpy()
-    # every slot (256 B apart) the last fused call used carries its tag (= gen now)
-    n_used = 0
-    for i in range(64):
-        words = [int(w64[32 * i]) & (2**64 - 1), int(w64[32 * i + 1]) & (2**64 - 1)]
-        if words[0] >> 32 == gen:
-            assert words[1] >> 32 == gen
-            n_used += 1
-    assert n_used >= 16
+    n_valid = int(torch.count_nonzero(x["mask"]))
+    grid, vec, tiles = rl.launch_shape(64, 4096, torch.bfloat16, "bnpo")
+    assert grid == tiles + 1                              # one coordinator plus one worker per tile
+
+    def head():
+        return ws[:512 + 16 * tiles].cpu().view(torch.int32).numpy().view(np.uint32)
+    h = head()
+    assert h[128 // 4] == 0                               # no timeout flag
+    rel = h[384 // 4:384 // 4 + 4]
+    assert rel[0] == rel[2] == n_valid and rel[1] != 0 and rel[3] != 0
+    cnt = h[512 // 4:].reshape(tiles, 4)
+    assert (cnt[:, 1] == rel[1]).all() and (cnt[:, 3] == rel[3]).all()   # the same launch's tags
+    assert (cnt[:, 0] == cnt[:, 2]).all() and int(cnt[:, 0].sum()) == n_valid
+    rl.bnpo_loss(x["policy"], x["old"], x["ref"], x["advantages"], x["mask"], **kw)
+    torch.cuda.synchronize()
+    rel2 = head()[384 // 4:384 // 4 + 4]
+    assert rel2[0] == n_valid and rel2[1] != rel[1] and rel2[3] != rel[3]
     import ctypes
     flags = ctypes.c_uint32(7)
     assert rl.library().rlpl_workspace_flags(ws.data_ptr(), ctypes.byref(flags),
