@@ -309,6 +309,24 @@ int selective_logprob_bwd(const void* hidden, const void* weight, const void* bi
                           void* grad_hidden, float* grad_weight, float* grad_bias, int accumulate,
                           void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* bnpo_loss for callers that cannot allocate (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same kernels,
+ * results bit-identical to bnpo_loss, with no workspace argument.  The
+ * exchange entries live in the library's own scratch, a static device array
+ * of 131,584 bytes per GPU, held until the process ends; this entry point
+ * never calls hipMalloc, hipFree or an allocating routine.  Its first call on
+ * a device finds the scratch's address and enqueues a kernel on `stream` that
+ * zero-fills it.  Every bnpo_loss_noalloc call on a GPU shares that GPU's
+ * scratch: calls that overlap on one GPU (on different streams) race and
+ * must not be made.  Limits: those of bnpo_loss (bs * seq_len < 2^31); the
+ * scratch holds the entries of every grid these kernels launch, so no problem
+ * size that bnpo_loss accepts is refused for lack of space.  Returns
+ * RLPL_ERR_DEVICE when the scratch cannot be set up. */
+int bnpo_loss_noalloc(const void* policy_lp, const void* old_lp, const void* ref_lp, const void* advantages,
+                      const void* mask, int64_t bs, int64_t seq_len, int dtype, int mask_dtype, float beta,
+                      float epsilon, float epsilon_high, float* loss_out, void* grad_out,
+                      uint32_t* n_valid_out, hipStream_t stream);
+
 /* Bytes of workspace an `op` call on a (bs, seq_len) problem needs (0 for a bad op). */
 size_t rlpl_workspace_bytes(int64_t bs, int64_t seq_len, int op);
 

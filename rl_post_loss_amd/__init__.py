@@ -115,6 +115,8 @@ def _declare(lib):
     for name, args in (("reverse_kl_logits", rkl), ("reverse_kl_logits_fwd", rkl_fwd)):
         f = getattr(lib, name)
         f.argtypes, f.restype = args, ctypes.c_int
+    lib.bnpo_loss_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i32, i32, f32, f32, f32, vp, vp, vp, vp]
+    lib.bnpo_loss_noalloc.restype = ctypes.c_int
     lp_common = [vp, vp, vp, vp]
     lib.selective_logprob_workspace_bytes.argtypes = [i64, i64, i64, i32]
     lib.selective_logprob_workspace_bytes.restype = sz

@@ -123,6 +123,7 @@ size_t elem_bytes(int dtype) { return dtype == RLPL_F32 ? 4 : 2; }
 int check_common(const void* mask, int64_t bs, int64_t seq_len, int dtype, int mask_dtype,
                  const float* loss_out, const uint32_t* n_valid_out, const void* workspace,
                  size_t workspace_bytes) {
+    // The per-token kernels address the workspace's header and entry arrays only.
     if (!mask || !loss_out) return RLPL_ERR_NULL;
     if (bs < 1 || seq_len < 1 || bs > (int64_t(1) << 31) / seq_len ||
         bs * seq_len >= (int64_t(1) << 31))
@@ -131,7 +132,7 @@ int check_common(const void* mask, int64_t bs, int64_t seq_len, int dtype, int m
     if (mask_dtype != RLPL_MASK_BOOL && mask_dtype != RLPL_MASK_INT8) return RLPL_ERR_DTYPE;
     if (!aligned(mask, 16) || !aligned(loss_out, 4) || (n_valid_out && !aligned(n_valid_out, 4)))
         return RLPL_ERR_ALIGN;
-    if (!workspace || workspace_bytes < rlpl::kWorkspaceBytes) return RLPL_ERR_WORKSPACE;
+    if (!workspace || workspace_bytes < rlpl::kEntryViewBytes) return RLPL_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return RLPL_ERR_ALIGN;
     return RLPL_OK;
 }
@@ -198,11 +199,11 @@ int run(int mode, bool write_grad, bool has_kl, Args& a, int dtype, hipStream_t 
     return launch(kernel, a, dim3(unsigned(sh.grid)), stream);
 }
 
-int policy_loss(int mode, bool write_grad, bool sign_aware, const void* policy_lp, const void* old_lp,
-                const void* ref_lp, const void* advantages, const void* mask, int64_t bs,
-                int64_t seq_len, int dtype, int mask_dtype, float beta, float epsilon,
-                float epsilon_high, float* loss_out, void* grad_out, uint32_t* n_valid_out,
-                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+// Validates a policy-loss call (host only, nothing enqueued) and fills its kernel arguments.
+int policy_args(bool write_grad, bool sign_aware, const void* policy_lp, const void* old_lp, const void* ref_lp,
+                const void* advantages, const void* mask, int64_t bs, int64_t seq_len, int dtype, int mask_dtype,
+                float beta, float epsilon, float epsilon_high, float* loss_out, void* grad_out,
+                uint32_t* n_valid_out, void* workspace, size_t workspace_bytes, Args* out) {
     int st = check_common(mask, bs, seq_len, dtype, mask_dtype, loss_out, n_valid_out, workspace,
                           workspace_bytes);
     if (st != RLPL_OK) return st;
@@ -234,7 +235,21 @@ int policy_loss(int mode, bool write_grad, bool sign_aware, const void* policy_l
     a.lo = lo;
     a.hi = hi;
     a.sign_aware = sign_aware ? 1u : 0u;
-    return run(mode, write_grad, has_kl, a, dtype, stream);
+    *out = a;
+    return RLPL_OK;
+}
+
+int policy_loss(int mode, bool write_grad, bool sign_aware, const void* policy_lp, const void* old_lp,
+                const void* ref_lp, const void* advantages, const void* mask, int64_t bs,
+                int64_t seq_len, int dtype, int mask_dtype, float beta, float epsilon,
+                float epsilon_high, float* loss_out, void* grad_out, uint32_t* n_valid_out,
+                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    Args a{};
+    const int st = policy_args(write_grad, sign_aware, policy_lp, old_lp, ref_lp, advantages, mask, bs, seq_len,
+                               dtype, mask_dtype, beta, epsilon, epsilon_high, loss_out, grad_out, n_valid_out,
+                               workspace, workspace_bytes, &a);
+    if (st != RLPL_OK) return st;
+    return run(mode, write_grad, beta != 0.0f, a, dtype, stream);
 }
 
 int rkl_loss(bool write_grad, const void* student_lp, const void* teacher_lp, const void* mask,
@@ -390,6 +405,42 @@ int launch_gemm(int dtype, int epi, bool ak, bool bk, const rlpl::GemmArgs& g, u
     const void* k = rlpl::pick_gemm_kernel(dtype, epi, ak, bk);
     if (!k) return RLPL_ERR_DTYPE;
     return launch(k, g, dim3(g.tiles_m * g.tiles_n, 1, splits), stream, rlpl::kGemmThreads, rlpl::kGemmDynLds);
+}
+
+// The library's scratch on the current device: its address is found once per
+// device (hipGetSymbolAddress, in the file that defines it) and the scratch is
+// zero-filled by a kernel enqueued on the first caller's stream, ahead of that
+// caller's launch.  Nothing is allocated.
+struct Scratch {
+    std::once_flag once;
+    void* ptr = nullptr;
+    int status = RLPL_ERR_DEVICE;
+};
+Scratch g_scratch[kMaxDevices];
+
+int scratch_on_current_device(void** out, hipStream_t stream) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return RLPL_ERR_DEVICE;
+    Scratch& s = g_scratch[dev];
+    std::call_once(s.once, [&s, stream] {
+        void* p = nullptr;
+        if (rlpl::scratch_address(&p) != 0 || !p) {
+            (void)hipGetLastError();
+            return;
+        }
+        void* words = p;
+        uint32_t n = uint32_t(rlpl::kScratchBytes / 16);
+        void* params[] = {&words, &n};
+        if (hipLaunchKernel(rlpl::clear_kernel_ptr(), dim3(32), dim3(rlpl::kThreads), params, 0, stream) !=
+            hipSuccess) {
+            (void)hipGetLastError();
+            return;
+        }
+        s.ptr = p;
+        s.status = RLPL_OK;
+    });
+    *out = s.ptr;
+    return s.status;
 }
 
 }  // namespace
@@ -551,6 +602,26 @@ int bnpo_loss(const void* policy_lp, const void* old_lp, const void* ref_lp, con
     return policy_loss(kModeBNPO, true, false, policy_lp, old_lp, ref_lp, advantages, mask, bs, seq_len,
                        dtype, mask_dtype, beta, epsilon, epsilon_high, loss_out, grad_out,
                        n_valid_out, workspace, workspace_bytes, stream);
+}
+
+int bnpo_loss_noalloc(const void* policy_lp, const void* old_lp, const void* ref_lp, const void* advantages,
+                      const void* mask, int64_t bs, int64_t seq_len, int dtype, int mask_dtype, float beta,
+                      float epsilon, float epsilon_high, float* loss_out, void* grad_out,
+                      uint32_t* n_valid_out, hipStream_t stream) {
+    // Validate first (the scratch stands in as an aligned placeholder), so that a
+    // rejected call enqueues nothing; then the scratch of the current device.
+    alignas(256) static const unsigned char placeholder[256] = {};
+    Args a{};
+    int st = policy_args(true, false, policy_lp, old_lp, ref_lp, advantages, mask, bs, seq_len, dtype, mask_dtype,
+                         beta, epsilon, epsilon_high, loss_out, grad_out, n_valid_out,
+                         const_cast<unsigned char*>(placeholder), rlpl::kScratchBytes, &a);
+    if (st != RLPL_OK) return st;
+    const DeviceInfo* info = nullptr;
+    if ((st = current_device(&info)) != RLPL_OK) return st;
+    void* ws = nullptr;
+    if ((st = scratch_on_current_device(&ws, stream)) != RLPL_OK) return st;
+    a.ws = static_cast<rlpl::Workspace*>(ws);
+    return run(kModeBNPO, true, beta != 0.0f, a, dtype, stream);
 }
 
 int bnpo_loss_fwd(const void* policy_lp, const void* old_lp, const void* ref_lp,

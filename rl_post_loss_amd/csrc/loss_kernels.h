@@ -121,4 +121,11 @@ struct Args {
 // The kernel instantiation for (dtype, mode, KL on/off, gradient on/off, VEC), or NULL.
 const void* pick_kernel(int dtype, int mode, bool has_kl, bool write_grad, int shape);
 
+// The library's own scratch (the per-token kernels' part of a workspace), for
+// the entry point that allocates nothing: its device address on the current
+// device (0 on success), and a kernel that zero-fills n 16-byte words.
+constexpr size_t kScratchBytes = kEntryViewBytes;
+int scratch_address(void** out);
+const void* clear_kernel_ptr();
+
 }  // namespace rlpl

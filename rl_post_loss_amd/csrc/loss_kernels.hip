@@ -692,4 +692,24 @@ const void* pick_kernel(int dtype, int mode, bool has_kl, bool write_grad, int s
     return nullptr;
 }
 
+// ----------------------------------------------------------------------------- the library's own scratch
+
+// The workspace of the entry point that allocates nothing: the header and the
+// entry arrays of a Workspace (what the per-token kernels address), one copy
+// per device, held until the process ends.  In host code `scratch` names a
+// host-side stand-in, never the device memory: its device address comes from
+// scratch_address(), per device.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+int scratch_address(void** out) {
+    return hipGetSymbolAddress(out, HIP_SYMBOL(scratch)) == hipSuccess ? 0 : -1;
+}
+
+// Zero-fills n 16-byte words (the scratch's first use on a device).
+__global__ void __launch_bounds__(kThreads) clear_kernel(uint4* p, uint32_t n) {
+    for (uint32_t i = blockIdx.x * kThreads + threadIdx.x; i < n; i += gridDim.x * kThreads)
+        p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+const void* clear_kernel_ptr() { return reinterpret_cast<const void*>(&clear_kernel); }
+
 }  // namespace rlpl
