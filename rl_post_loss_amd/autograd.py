@@ -6,8 +6,9 @@ call traces under ``torch.compile(fullgraph=True)``).
 Each op runs the fused forward+backward launch of the C ABI once, returns the
 loss and keeps the gradient the launch wrote; backward multiplies that
 gradient by the incoming scalar gradient of the loss (the chain rule for a
-scalar loss).  There is no other computation and no fallback: the ops call the
-same HIP kernels as the direct entry points.
+scalar loss), in float32, rounding once to the gradient's dtype.  There is no
+other computation and no fallback: the ops call the same HIP kernels as the
+direct entry points.
 
 The direct entry points stay the lowest-overhead path; these add the custom-op
 dispatch (and, under compile, a graph break-free call).
@@ -24,6 +25,12 @@ __all__ = ["bnpo_loss_autograd", "grpo_loss_autograd", "reverse_kl_autograd",
            "reverse_kl_logits_autograd", "selective_logprob_autograd"]
 
 _LIB = "rlpl"
+
+
+def _scaled(g: torch.Tensor, grad_loss: torch.Tensor) -> torch.Tensor:
+    """g * grad_loss with the product formed in float32 and rounded once to g's dtype
+    (grad_loss itself is never rounded to a half-precision type)."""
+    return (g.float() * grad_loss.float()).to(g.dtype)
 
 
 def _policy_op(op: str):
@@ -47,7 +54,7 @@ def _policy_op(op: str):
 
     def backward(ctx, grad_loss, _grad_of_grad):
         (g,) = ctx.saved_tensors
-        return (g * grad_loss.to(g.dtype), None, None, None, None, None, None, None, None)
+        return (_scaled(g, grad_loss), None, None, None, None, None, None, None, None)
 
     fused.register_autograd(backward, setup_context=setup_context)
     return fused
@@ -69,7 +76,7 @@ def _rkl_op(name: str, direct):
 
     def backward(ctx, grad_loss, _grad_of_grad):
         (g,) = ctx.saved_tensors
-        return g * grad_loss.to(g.dtype), None, None
+        return _scaled(g, grad_loss), None, None
 
     fused.register_autograd(backward, setup_context=setup_context)
     return fused

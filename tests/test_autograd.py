@@ -54,7 +54,34 @@ def test_policy_autograd_matches_direct(op, clip):
     assert torch.equal(lp.grad, grad0)
     lp.grad = None
     (3.0 * auto(lp, x["old"], x["ref"], x["advantages"], x["mask"], **kw)).backward()
-    assert torch.equal(lp.grad, (grad0 * 3.0).to(grad0.dtype))
+    assert torch.equal(lp.grad, (grad0.float() * 3.0).to(grad0.dtype))
+
+
+@pytest.mark.gpu
+def test_autograd_upstream_scale_against_the_oracle():
+    """An upstream gradient that is not a power of two (gradient accumulation over 1/k):
+    the gradient loss.backward() leaves is the oracle gradient times that scale, within
+    2 ulp of the output dtype (the kernel rounds once, the scaling in float32 once)."""
+    import numpy as np
+    import oracle
+    from parity import f32, kink_alternative, kink_tokens, policy_grad_magnitude, check_grad
+    w = synthetic.WORKLOADS["bnpo_bf16_64x4096"]
+    xc = synthetic.inputs(w)
+    x = {k: v.to(DEV) for k, v in xc.items() if k != "lengths"}
+    kw = dict(epsilon=w.epsilon, epsilon_high=w.epsilon_high, beta=w.beta)
+    s = 1.0 / 3.0
+    lp = x["policy"].clone().requires_grad_()
+    (s * rl.bnpo_loss_autograd(lp, x["old"], x["ref"], x["advantages"], x["mask"], **kw)).backward()
+    torch.cuda.synchronize()
+    ref = oracle.bnpo(xc["policy"], xc["old"], xc["ref"], xc["advantages"], xc["mask"], f32(w.beta),
+                      f32(w.epsilon), f32(w.epsilon_high))
+    scale = s / max(ref.n_valid, 1)
+    kinks = kink_tokens(xc["policy"], xc["old"], xc["mask"], w.epsilon_high)
+    alt = kink_alternative(ref.grad * s, xc["policy"], xc["old"], xc["advantages"], xc["mask"], w.epsilon_high,
+                           scale)
+    mag = policy_grad_magnitude(xc["policy"], xc["old"], xc["ref"], xc["advantages"], f32(w.beta), scale)
+    check_grad(lp.grad, ref.grad * s, torch.bfloat16, "autograd x 1/3", alt, kinks, mag)
+    assert np.all(lp.grad.detach().float().cpu().numpy()[xc["mask"].numpy() == 0] == 0)
 
 
 @pytest.mark.gpu
