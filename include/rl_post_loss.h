@@ -342,17 +342,22 @@ int rlpl_launch_shape(int64_t bs, int64_t seq_len, int dtype, int op, int* grid_
                       int* tiles_out);
 
 /* Sticky error bits the kernels left in a workspace (host pointer `flags_out`
- * receives them; synchronises `stream`).  Bit 0: a wait of a full-vocab
- * reverse-KL call for the partial sums of other workgroups gave up after its
- * time limit (~1 s); that call's loss was written as NaN, its gradient is not
- * valid, and the workspace must be zero-filled again before its next use.
- * The per-token losses never give up a wait (see Workspace above). */
+ * receives them; synchronises `stream`).  Bit 0: workgroup 0 of a full-vocab
+ * reverse-KL call gave up its wait for the other workgroups' row partials
+ * after its time limit (~1 s; every other workgroup publishes its partial
+ * without waiting on anything unbounded, so this happens only when no other
+ * workgroup of the launch could run in that time); that call's loss was
+ * written as NaN, and the workspace must be zero-filled again before its next
+ * use.  The other waits never give up: the sums of a split row's pieces and
+ * the per-token losses' values are computed by the waiting workgroup when they
+ * do not come within the steal limit (see Workspace above). */
 int rlpl_workspace_flags(const void* workspace, uint32_t* flags_out, hipStream_t stream);
 
 /* Limits of the cross-workgroup waits of calls that use `workspace`, in ticks
  * of the GPU's 100 MHz clock; 0 selects the default.  steal_ticks: how long a
  * coordinating workgroup waits for a value another workgroup publishes before
- * computing it itself (default 5,000 = 50 us); release_ticks: how long a
+ * computing it itself (default 5,000 = 50 us; the same limit holds for the
+ * piece sums of a full-vocab call's split rows); release_ticks: how long a
  * workgroup waits for the global count before forming it itself (default
  * 20,000); giveup_ticks: how long a full-vocab reverse-KL call waits before it
  * gives up (default 100,000,000 = 1 s).  Results never depend on these limits

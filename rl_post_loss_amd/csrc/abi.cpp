@@ -300,7 +300,7 @@ int vocab_loss(bool write_grad, const void* student, const void* teacher, const 
     if (st != RLPL_OK) return st;
     const int64_t cap = info->vocab_cap[dtype];
     if (cap < 1) return RLPL_ERR_DEVICE;
-    // groups of `chunks` workgroups (one per piece of a row), all co-resident.
+    // groups of `chunks` workgroups (one per piece of a row), sized to be co-resident.
     const rlpl::VocabSplit sp = rlpl::vocab_split(rows, vocab, int(elem_bytes(dtype)), cap, write_grad);
     rlpl::VocabArgs a{};
     a.student = student;

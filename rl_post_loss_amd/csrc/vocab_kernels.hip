@@ -14,7 +14,7 @@
 // of lse, and both are exactly 0 when the rows are equal or vocab is 1.
 //
 // Design (HBM-bound streaming; no contraction, so no MFMA):
-//  * A persistent grid of co-resident workgroups, each taking one piece of a
+//  * A persistent grid sized to be co-resident, each workgroup taking one piece of a
 //    row per round (the whole row when rows are plentiful and the kernel is
 //    forward only).  Rows whose mask byte is zero are never read (the fwd+bwd
 //    kernel writes their gradient as +0).
@@ -370,9 +370,13 @@ __device__ __forceinline__ void grad_group(const Group<T, VEC>& G, T* __restrict
 // workgroup of the row, and the forward-only kernel, gets the same bits).  The
 // fwd+bwd kernel then writes the gradient of its piece: from the registers
 // that still hold it (kVocabResident, pieces of at most kVocabResidentBlocks
-// blocks), or by reading it again (kVocabStream, longer pieces).  All
-// workgroups are co-resident and a round's waits are among workgroups of that
-// round only.
+// blocks), or by reading it again (kVocabStream, longer pieces).  A piece's
+// sums that have not arrived within the steal limit are computed by the waiting
+// workgroup itself, so the only unbounded wait is workgroup 0's for the row
+// partials, which every other workgroup publishes without waiting on anything
+// unbounded: it ends once they have all run, which needs one free workgroup
+// slot on the device besides workgroup 0.  Past the give-up limit that wait
+// stops, writes a NaN loss and sets the workspace's sticky flag.
 template <typename T, int MODE>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) vocab_kernel(const VocabArgs a) {
     constexpr int VEC = 32 / int(sizeof(T));   // elements per 32-byte block
@@ -385,6 +389,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
     __shared__ uint32_t word[1];
     __shared__ Stats red_s[kWaves];
     __shared__ float peer[kVocabMaxChunks * 5];
+    __shared__ uint32_t missing[kVocabMaxChunks / 32];
 
     Workspace* ws = a.ws;
     uint32_t gen = 0;
@@ -447,30 +452,66 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
         if (C > 1) {
             // Publish the chunk's sums, read every chunk's of this row, merge them in a
             // fixed order: lane q of each wavefront takes chunks q, q + 64, ... in turn,
-            // then the wavefront merges its lanes.
+            // then the wavefront merges its lanes.  A chunk whose sums have not come
+            // within the steal limit is summed here from the slabs, by the same code
+            // as its own workgroup's (the same bits), so no workgroup depends on
+            // another being resident.
             const uint32_t tag = gen + 1u + round;
             const uint32_t buf = exch++ & 1u;
             uint64_t* mine = &ws->slot[blockIdx.x].stats[buf][0];
-            if (threadIdx.x < 5) {
-                const float v[5] = {st.ms, st.mt, st.zs, st.zt, st.as};
-                store_relaxed(mine + threadIdx.x, tagged(tag, __float_as_uint(v[threadIdx.x])));
-            }
+            const float own[5] = {st.ms, st.mt, st.zs, st.zt, st.as};
+            if (threadIdx.x < 5) store_relaxed(mine + threadIdx.x, tagged(tag, __float_as_uint(own[threadIdx.x])));
+            if (threadIdx.x < kVocabMaxChunks / 32) missing[threadIdx.x] = 0;
+            __syncthreads();
             for (uint32_t i = threadIdx.x; i < 5 * C; i += kThreads) {
-                const uint64_t* w = &ws->slot[grp * C + i / 5].stats[buf][i % 5];
-                uint64_t x = load_relaxed(w);
-                if (uint32_t(x >> 32) != tag && !wait_tagged(w, tag, lim.giveup, x)) {
-                    __hip_atomic_fetch_or(&ws->flags, kFlagWaitTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    x = __float_as_uint(__builtin_nanf(""));
+                const uint32_t q = i / 5;
+                if (q == c) {
+                    peer[i] = own[i % 5];
+                    continue;
                 }
-                peer[i] = __uint_as_float(uint32_t(x));
+                const uint64_t* w = &ws->slot[grp * C + q].stats[buf][i % 5];
+                uint64_t x = load_relaxed(w);
+                if (uint32_t(x >> 32) != tag && !wait_tagged(w, tag, lim.steal, x))
+                    atomicOr(&missing[q >> 5], 1u << (q & 31u));
+                else
+                    peer[i] = __uint_as_float(uint32_t(x));
             }
             __syncthreads();
+            uint32_t any = 0;
+#pragma unroll
+            for (int k = 0; k < kVocabMaxChunks / 32; ++k) any |= missing[k];
+            if (any) {
+                for (uint32_t q = 0; q < C; ++q) {
+                    if (!((missing[q >> 5] >> (q & 31u)) & 1u)) continue;
+                    const uint64_t qb0 = lo / VEC + q * chunk_blocks;
+                    const uint64_t qb1 = qb0 + chunk_blocks < rb1 ? qb0 + chunk_blocks : rb1;
+                    LaneSums qa;
+                    lane_init(qa);
+                    Group<T, VEC> Q;
+                    for (uint64_t g0 = qb0; g0 < qb1; g0 += kGroup * kThreads) {
+                        load_group<T, VEC>(Q, S, Tt, g0, qb1, lo, hi, end16);
+                        lane_add<T, VEC>(qa, Q);
+                    }
+                    const Stats qs = block_merge(lane_total(qa), red_s);
+                    if (threadIdx.x < 5) {
+                        const float v[5] = {qs.ms, qs.mt, qs.zs, qs.zt, qs.as};
+                        peer[5 * q + threadIdx.x] = v[threadIdx.x];
+                    }
+                }
+                __syncthreads();
+                if constexpr (MODE == kVocabResident) {
+                    // The held piece was given up for the registers of the sums above:
+                    // read it again for the gradient.
+                    load_group<T, VEC>(G, S, Tt, cb0, cb1, lo, hi, end16);
+                    opaque(G);
+                }
+            }
             Stats mine_q{kNone, kNone, 0.0f, 0.0f, 0.0f};
             for (uint32_t q = threadIdx.x & 63u; q < C; q += 64u)
                 mine_q = merge(mine_q, Stats{peer[5 * q], peer[5 * q + 1], peer[5 * q + 2], peer[5 * q + 3],
                                              peer[5 * q + 4]});
             row = wave_merge(mine_q);
-            __syncthreads();                    // peer[] is rewritten next round
+            __syncthreads();                    // peer[] and missing[] are rewritten next round
         }
         // log2 z (v_log_f32 is base 2); z >= 1.
         const float l2zs = __builtin_amdgcn_logf(row.zs);

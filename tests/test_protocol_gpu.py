@@ -9,7 +9,8 @@ that the fallbacks run, and every result must be bit-identical to the
 ordinary path, for every kernel shape and op.  Exchange kernels launched
 together on two streams (whose grids cannot all be resident at once) must
 finish with the same bits.  A full-vocab reverse-KL call whose waits give up
-writes a NaN loss and sets the sticky flag, which check_workspace reports.
+writes a NaN loss and sets the sticky flag, which check_workspace reports;
+the waits for a split row's piece sums fall back like the per-token ones.
 """
 import pytest
 import torch
@@ -114,6 +115,43 @@ def test_exchange_kernels_on_two_streams(op):
         for loss, grad, n in outs[i]:
             same_bits((loss, grad, n), refs[i])
         assert rl.workspace_flags(wss[i]) == 0
+
+
+# Full-vocab shapes whose rows are split into pieces: kept in registers between the
+# two passes (fused; in one round, and in several rounds per workgroup), read a second
+# time (fused, pieces above 1024 blocks), forward only.
+VOCAB_SHAPES = [(8, 248320), (200, 248320), (2, 4_500_000), (5, 33000)]
+
+
+def vocab_call(fused, x, ws):
+    f = rl.reverse_kl_logits if fused else rl.reverse_kl_logits_fwd
+    out = f(x["student"], x["teacher"], x["mask"], return_n_valid=True, workspace=ws)
+    torch.cuda.synchronize()
+    if fused:
+        loss, grad, n = out
+        return loss.clone(), grad.clone(), n.clone()
+    loss, n = out
+    return loss.clone(), None, n.clone()
+
+
+@pytest.mark.parametrize("fused", [True, False])
+@pytest.mark.parametrize("shape", VOCAB_SHAPES)
+def test_vocab_piece_fallback_is_bit_identical(shape, fused):
+    """A split row's workgroups wait for the other pieces' sums; with a steal limit of one
+    tick nearly every wait falls back to summing the piece itself.  Loss, count and
+    gradient are bit-identical to a call with the default limits, and the same workspace
+    then serves a call with other inputs exactly."""
+    rows, V = shape
+    x = synthetic.device_vocab_inputs(rows, V, "bf16", "bool", 0, "cuda:0")
+    ref = vocab_call(fused, x, fresh_workspace())
+    ws = fresh_workspace()
+    rl.set_wait_limits(ws, steal_ticks=1)
+    for _ in range(3):
+        same_bits(vocab_call(fused, x, ws), ref)
+    rl.set_wait_limits(ws)
+    x2 = synthetic.device_vocab_inputs(rows, V, "bf16", "bool", 1, "cuda:0")
+    same_bits(vocab_call(fused, x2, ws), vocab_call(fused, x2, fresh_workspace()))
+    assert rl.workspace_flags(ws) == 0
 
 
 def test_vocab_give_up_is_loud():
