@@ -10,18 +10,28 @@ loss finalise) in one launch through the C ABI.
 Inputs are generated once, copied into rotating sets totalling >= 1 GiB (so
 each step reads from HBM rather than the 256 MB last-level cache) and are
 resident before timing starts.  W warmup steps, then exactly K timed steps
-between two stream synchronisations.  HIP events recorded on the launch
-stream at both ends of the timed region give the per-launch kernel duration
-(span / K) used for the roofline: back-to-back launches keep the GPU busy, so
-this agrees with rocprofv3's kernel durations.
+between two stream synchronisations; the steps are issued by a C loop over
+the public entry point (librlpl_bench.so), one call per step, so that the
+interpreter's per-call cost does not set the pace.  HIP events recorded on
+the launch stream at both ends of the timed region give the per-launch
+kernel duration (span / K) used for the roofline: back-to-back launches keep
+the GPU busy, so this agrees with rocprofv3's kernel durations.  `value`
+counts every (row, position) slot of the batch per step (the mask is read
+and the gradient written for all of them); the valid (completion) tokens per
+second are reported beside it.
 
 Options for context measurements (never the headline line's workload):
   --op bnpo|bnpo_fwd|grpo|grpo_fwd|rkl|rkl_fwd   another entry point
   --bs / --seq-len                               another size (inputs drawn on
                                                  the device above 2^24 slots)
-  --copy-mib M                                   a plain device copy of M MiB
-                                                 (streaming ceiling; also the
-                                                 reference for traffic counters)
+  --copy-mib M                                   a streaming copy of M MiB by our
+                                                 own 128-bit kernel (plain and
+                                                 non-temporal) and by the
+                                                 runtime's copy (the ceiling;
+                                                 also the reference for the
+                                                 traffic counters)
+  --read-mib M                                   a streaming read of M MiB
+                                                 (the forward-only ceiling)
   --op rkl_logits|rkl_logits_fwd [--rows R --vocab V]
                                                  full-vocab reverse KL over
                                                  (R, V) logit slabs (default the
@@ -38,16 +48,20 @@ Options for context measurements (never the headline line's workload):
                                                  into the policy's hidden states,
                                                  projection and bias (B sequences
                                                  of 1024 tokens, default 1)
-  --floor                                        back-to-back launches of a
-                                                 one-element fill kernel (the
-                                                 per-launch floor of the GPU)
+  --floor                                        back-to-back launches of an
+                                                 empty kernel with the launch
+                                                 shape of the workload (the
+                                                 per-launch floor)
   --rotate-gib 0                                 two input sets only, which stay
                                                  in the last-level cache (a
                                                  warm-cache figure)
 
 The CPU baseline is the oracle (double precision C) over the same host-side
-batch: once on one thread, then on every host core at once (one whole batch
-per thread; ctypes releases the GIL), about 10 + 20 s of CPU work.
+batch, the batch's rows split over every host core (one oracle call per row
+range, in parallel threads; ctypes releases the GIL) and the ranges' sums
+combined into the batch's loss and gradient: 3 warmup steps, then the median
+of at least 10 steps.  Beside it: one whole batch on one thread, and whole
+batches on every core at once (throughput of independent batches).
 
 Prints one JSON line.  --gpus above 1 is not supported.
 """
@@ -113,7 +127,8 @@ def recorded_traffic(workload: str):
 
 
 def timed(fn, calls, K, W, stream, torch):
-    """W warmup calls, then K timed back-to-back calls; returns (ms per step wall, ms per launch GPU)."""
+    """W warmup calls, then K timed back-to-back calls from Python (long kernels only);
+    returns (ms per step wall, ms per launch GPU)."""
     n = len(calls)
     for i in range(W):
         rc = fn(*calls[i % n])
@@ -135,37 +150,127 @@ def timed(fn, calls, K, W, stream, torch):
     return (t1 - t0) * 1e3 / K, ev0.elapsed_time(ev1) / K
 
 
+def timed_loop(run, K, W, stream, torch):
+    """run(first, iters) enqueues `iters` steps from rotating index `first` with one C call
+    (returns a status).  W untimed steps, then exactly K timed steps between two
+    synchronisations; returns (ms per step wall, ms per launch GPU from HIP events)."""
+    if W:
+        rc = run(0, W)
+        if rc != 0:
+            raise RuntimeError(f"warmup returned status {rc}")
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    rc = run(W, K)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    if rc != 0:
+        raise RuntimeError(f"a timed step returned status {rc}")
+    return (t1 - t0) * 1e3 / K, ev0.elapsed_time(ev1) / K
+
+
+def bench_lib():
+    """The measurement helpers (librlpl_bench.so, beside the loss library)."""
+    import ctypes
+    import rl_post_loss_amd as rl
+    from rl_post_loss_amd import build as b
+    rl.library()
+    if not os.path.exists(b.BENCH_LIB):
+        b.build()
+    lib = ctypes.CDLL(b.BENCH_LIB)
+    vp, i32, i64, f32, u64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_uint64
+    sz, u32 = ctypes.c_size_t, ctypes.c_uint32
+    lib.rlpl_bench_empty.argtypes = [i32, i32, vp]
+    lib.rlpl_bench_copy.argtypes = [i32, vp, u64, i32, i32, i32, i32, vp]
+    lib.rlpl_bench_read.argtypes = [i32, vp, u64, i32, i32, vp, i32, i32, vp]
+    lib.rlpl_bench_policy.argtypes = [i32, u32, i32, vp, i64, i64, i32, i32, f32, f32, f32, vp, sz, i32, i32, vp]
+    lib.rlpl_bench_rkl.argtypes = [i32, i32, vp, i64, i64, i32, i32, vp, sz, i32, i32, vp]
+    lib.rlpl_bench_noalloc.argtypes = [i32, vp, i64, i64, i32, i32, f32, f32, f32, i32, i32, vp]
+    for f in (lib.rlpl_bench_empty, lib.rlpl_bench_copy, lib.rlpl_bench_read, lib.rlpl_bench_policy,
+              lib.rlpl_bench_rkl, lib.rlpl_bench_noalloc):
+        f.restype = ctypes.c_int
+    return lib
+
+
+def pointer_table(rows):
+    """A contiguous uint64 array of device pointers (rows x columns) for the C loops."""
+    import numpy as np
+    return np.ascontiguousarray(np.array(rows, dtype=np.uint64))
+
+
 def copy_ceiling(args, torch):
+    """Streaming copies of M MiB on rotating buffers (>= 1 GiB in all): our own kernel with
+    plain and with non-temporal 128-bit accesses (grid of 2048 workgroups), and the runtime's
+    copy, for comparison."""
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
+    lib = bench_lib()
     nbytes = int(args.copy_mib * (1 << 20)) // 16 * 16
     nsets = max(2, math.ceil((1 << 30) / (2 * nbytes)))
     pairs = [(torch.empty(nbytes, dtype=torch.uint8, device=dev),
               torch.empty(nbytes, dtype=torch.uint8, device=dev)) for _ in range(nsets)]
-    calls = [(d, s) for s, d in pairs]
+    table = pointer_table([[d.data_ptr(), s.data_ptr()] for s, d in pairs])
+    out = {"metric": "streaming copy (read + write) of the same bytes", "bytes_read": nbytes,
+           "bytes_written": nbytes, "steps": args.steps, "rotating_sets": nsets}
+    for nt in (0, 1):
+        _, ms = timed_loop(lambda first, k: lib.rlpl_bench_copy(nsets, table.ctypes.data, nbytes, 0, nt, k, first,
+                                                                 stream.cuda_stream), args.steps, args.warmup,
+                           stream, torch)
+        gbs = 2 * nbytes / (ms * 1e-3) / 1e9
+        out["own_kernel_nt" if nt else "own_kernel"] = {"us_per_launch": round(ms * 1e3, 3), "GBs": round(gbs, 1),
+                                                        "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4)}
 
     def fn(d, s):
         d.copy_(s)
         return 0
-    ms_wall, ms_gpu = timed(fn, calls, args.steps, args.warmup, stream, torch)
-    gbs = 2 * nbytes / (ms_gpu * 1e-3) / 1e9
-    print(json.dumps({"metric": "plain device copy (read + write)", "bytes_read": nbytes,
-                      "bytes_written": nbytes, "us_per_launch": round(ms_gpu * 1e3, 3),
-                      "GBs": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
-                      "steps": args.steps, "rotating_sets": nsets}), flush=True)
+    _, ms = timed(fn, [(d, s) for s, d in pairs], args.steps, args.warmup, stream, torch)
+    gbs = 2 * nbytes / (ms * 1e-3) / 1e9
+    out["runtime_copy"] = {"us_per_launch": round(ms * 1e3, 3), "GBs": round(gbs, 1),
+                           "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4)}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def read_ceiling(args, torch):
+    """Streaming reads of M MiB (our own 128-bit kernel, plain and non-temporal)."""
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    lib = bench_lib()
+    nbytes = int(args.read_mib * (1 << 20)) // 16 * 16
+    nsets = max(2, math.ceil((1 << 30) / nbytes))
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(nsets)]
+    table = pointer_table([b.data_ptr() for b in bufs])
+    sink = torch.zeros(4096, dtype=torch.int32, device=dev)
+    out = {"metric": "streaming read of the same bytes", "bytes_read": nbytes, "steps": args.steps,
+           "rotating_sets": nsets}
+    for nt in (0, 1):
+        _, ms = timed_loop(lambda first, k: lib.rlpl_bench_read(nsets, table.ctypes.data, nbytes, 0, nt,
+                                                                 sink.data_ptr(), k, first, stream.cuda_stream),
+                           args.steps, args.warmup, stream, torch)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out["own_kernel_nt" if nt else "own_kernel"] = {"us_per_launch": round(ms * 1e3, 3), "GBs": round(gbs, 1),
+                                                        "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4)}
+    print(json.dumps(out), flush=True)
     return 0
 
 
 def launch_floor(args, torch):
+    """Back-to-back launches of an empty kernel with the workload's grid (x 256 threads)."""
+    import rl_post_loss_amd as rl
+    import synthetic
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
-    xs = [torch.empty(1, dtype=torch.float32, device=dev) for _ in range(2)]
-
-    def fn(x):
-        x.fill_(0.0)
-        return 0
-    ms_wall, ms_gpu = timed(fn, [(x,) for x in xs], args.steps, args.warmup, stream, torch)
-    print(json.dumps({"metric": "per-launch floor: one-element fill kernel, back to back",
+    lib = bench_lib()
+    w = synthetic.WORKLOADS[args.workload]
+    grid, vec, tiles = rl.launch_shape(args.bs or w.bs, args.seq_len or w.seq_len, synthetic.DTYPES[w.dtype],
+                                       args.op or w.op)
+    ms_wall, ms_gpu = timed_loop(lambda first, k: lib.rlpl_bench_empty(grid, k, stream.cuda_stream), args.steps,
+                                 args.warmup, stream, torch)
+    print(json.dumps({"metric": "per-launch floor: empty kernel, back to back",
+                      "grid": grid, "threads_per_workgroup": 256,
                       "us_per_launch": round(ms_gpu * 1e3, 3), "us_per_step_wall": round(ms_wall * 1e3, 3),
                       "steps": args.steps}), flush=True)
     return 0
@@ -175,6 +280,17 @@ def cpu_threads() -> int:
     n = os.cpu_count() or 1
     env = os.environ.get("OMP_NUM_THREADS", "")
     return max(1, min(n, int(env))) if env.isdigit() else n
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def oracle_rate(run_once, seconds: float, threads: int):
@@ -196,6 +312,127 @@ def oracle_rate(run_once, seconds: float, threads: int):
     for t in ts:
         t.join()
     return sum(counts) / (time.perf_counter() - t0), sum(counts)
+
+
+def oracle_rows_step(op, x, w, fused, threads):
+    """One batch of the oracle (double precision C), its rows split into `threads`
+    contiguous ranges computed in parallel (one oracle call per range; ctypes releases
+    the GIL), then combined into the batch's loss and gradient: for the global-mean
+    losses each range's sum is loss_c * max(n_c, 1) and its gradient is rescaled by
+    max(n_c, 1) / max(N, 1) (reverse-KL: n_c / N, unclamped); for GRPO, whose rows are
+    independent, by rows_c / bs.  Returns step() -> (loss, grad, N) and the range count."""
+    import ctypes
+    from concurrent.futures import ThreadPoolExecutor
+    import numpy as np
+    import oracle
+    lib = oracle._load()
+    is_rkl = op.startswith("rkl")
+    if is_rkl:
+        lp, rf = oracle.to_f64(x["student"]), oracle.to_f64(x["teacher"])
+        od = adv = None
+    else:
+        lp, od = oracle.to_f64(x["policy"]), oracle.to_f64(x["old"])
+        rf = oracle.to_f64(x["ref"]) if w.beta != 0 else None
+        adv = oracle.to_f64(x["advantages"])
+    m = oracle.to_mask_u8(x["mask"])
+    bs, T = lp.shape
+    bounds = np.linspace(0, bs, threads + 1).astype(int)
+    ranges = [(int(a), int(b)) for a, b in zip(bounds[:-1], bounds[1:]) if b > a]
+    grad = np.empty((bs, T), dtype=np.float64) if fused else None
+    dp = ctypes.POINTER(ctypes.c_double)
+
+    def ptr(a, r0):
+        return None if a is None else ctypes.cast(a.ctypes.data + r0 * a.strides[0], dp)
+
+    def chunk(r):
+        r0, r1 = r
+        loss = ctypes.c_double(0.0)
+        n = np.zeros(r1 - r0 if op.startswith("grpo") else 1, dtype=np.int64)
+        g = ptr(grad, r0) if fused else None
+        mp = ctypes.cast(m.ctypes.data + r0 * m.strides[0], ctypes.POINTER(ctypes.c_uint8))
+        if is_rkl:
+            lib.rlpl_oracle_rkl(r1 - r0, T, ptr(lp, r0), ptr(rf, r0), mp, ctypes.byref(loss), g,
+                                n.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)))
+        else:
+            fn = lib.rlpl_oracle_grpo if op.startswith("grpo") else lib.rlpl_oracle_bnpo
+            fn(r1 - r0, T, ptr(lp, r0), ptr(od, r0), ptr(rf, r0), ctypes.cast(adv.ctypes.data + r0 * 8, dp), mp,
+               float(np.float32(w.beta)), float(np.float32(w.epsilon)), float(np.float32(w.epsilon_high)),
+               ctypes.byref(loss), g, n.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)))
+        return loss.value, int(n.sum())
+
+    pool = ThreadPoolExecutor(max_workers=len(ranges))
+
+    def rescale(args):
+        (r0, r1), f = args
+        if fused:
+            grad[r0:r1] *= f
+
+    def step():
+        res = list(pool.map(chunk, ranges))
+        N = sum(n for _, n in res)
+        if op.startswith("grpo"):
+            loss = sum(l * (r1 - r0) for (l, _), (r0, r1) in zip(res, ranges)) / bs
+            f = [(r1 - r0) / bs for r0, r1 in ranges]
+        elif is_rkl:
+            loss = sum(l * n for l, n in res if n) / N if N else float("nan")
+            f = [n / N if N else 0.0 for _, n in res]
+        else:
+            loss = sum(l * max(n, 1) for l, n in res) / max(N, 1)
+            f = [max(n, 1) / max(N, 1) for _, n in res]
+        list(pool.map(rescale, zip(ranges, f)))
+        return loss, grad, N
+    return step, len(ranges)
+
+
+def cpu_baseline(op, x, w, fused, args):
+    """The oracle timed on the host: one batch with its rows over every core (median of at
+    least 10 steps after 3 warmups, the reported value), one whole batch on one thread, and
+    independent whole batches on every core at once (throughput)."""
+    import numpy as np
+    import oracle
+    threads = cpu_threads()
+    step, n_ranges = oracle_rows_step(op, x, w, fused, threads)
+    for _ in range(3):
+        step()
+    times = []
+    t_end = time.perf_counter() + args.cpu_seconds
+    while len(times) < 10 or (time.perf_counter() < t_end and len(times) < 1000):
+        t0 = time.perf_counter()
+        step()
+        times.append(time.perf_counter() - t0)
+    med = float(np.median(times))
+    # the row-split result is the batch's result (checked once, outside the timed steps)
+    loss_rows, grad_rows, n_rows = step()
+    whole = (oracle.rkl(x["student"], x["teacher"], x["mask"], grad=fused) if op.startswith("rkl") else
+             (oracle.grpo if op.startswith("grpo") else oracle.bnpo)(
+                 x["policy"], x["old"], x.get("ref") if w.beta != 0 else None, x["advantages"], x["mask"],
+                 float(np.float32(w.beta)), float(np.float32(w.epsilon)), float(np.float32(w.epsilon_high)),
+                 grad=fused))
+    if abs(loss_rows - whole.loss) > 1e-9 * max(1.0, abs(whole.loss)) or (
+            fused and float(np.max(np.abs(grad_rows - whole.grad))) > 1e-12):
+        raise RuntimeError("row-split oracle disagrees with the whole-batch oracle")
+    xs = {k: oracle.to_f64(v) for k, v in x.items() if k in ("policy", "old", "ref", "advantages", "student",
+                                                               "teacher")}
+    m8 = oracle.to_mask_u8(x["mask"])
+
+    def run_once():
+        if op.startswith("rkl"):
+            oracle.rkl(xs["student"], xs["teacher"], m8, grad=fused)
+        else:
+            fo = oracle.bnpo if op.startswith("bnpo") else oracle.grpo
+            fo(xs["policy"], xs["old"], xs.get("ref") if w.beta != 0 else None, xs["advantages"], m8,
+               float(np.float32(w.beta)), float(np.float32(w.epsilon)), float(np.float32(w.epsilon_high)),
+               grad=fused)
+    rate1, runs1 = oracle_rate(run_once, 2.0, 1)
+    rate_n, runs_n = oracle_rate(run_once, 3.0, threads) if threads > 1 else (rate1, runs1)
+    return {"value": round(w.slots / med, 1), "unit": "tokens/s", "cores": n_ranges, "kind": "oracle",
+            "sample": f"one full {w.name} batch (loss + gradient, double precision) per step, its rows split "
+                      f"over {n_ranges} threads and combined; median of {len(times)} steps after 3 warmups, "
+                      f"{med * 1e3:.3f} ms per batch",
+            "cpu_model": cpu_model(),
+            "single_thread_value": round(w.slots * rate1, 1),
+            "independent_batches_value": round(w.slots * rate_n, 1),
+            "independent_batches_sample": f"{runs_n} whole batches on {threads} threads at once, one per thread"}
 
 
 def vocab_bench(args, torch):
@@ -429,6 +666,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-mib", type=float, default=None)
+    ap.add_argument("--read-mib", type=float, default=None)
+    ap.add_argument("--noalloc", action="store_true")
     ap.add_argument("--floor", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -441,6 +680,8 @@ def main() -> int:
 
     if args.copy_mib is not None:
         return copy_ceiling(args, torch)
+    if args.read_mib is not None:
+        return read_ceiling(args, torch)
     if args.floor:
         return launch_floor(args, torch)
     if args.op in ("rkl_logits", "rkl_logits_fwd"):
@@ -454,7 +695,7 @@ def main() -> int:
     import synthetic
 
     w = synthetic.WORKLOADS[args.workload]
-    headline = args.op is None and args.bs is None and args.seq_len is None and args.beta is None
+    headline = args.op is None and args.bs is None and args.seq_len is None and args.beta is None and not args.noalloc
     op = args.op or w.op
     if args.bs or args.seq_len:
         w = w.with_(bs=args.bs or w.bs, seq_len=args.seq_len or w.seq_len,
@@ -488,10 +729,8 @@ def main() -> int:
     if nsets == 1 and not on_device:
         nsets = 2
     ws = rl.workspace_for(dev, sptr, w.op)
-    name = {"bnpo": "bnpo_loss", "bnpo_fwd": "bnpo_loss_fwd", "grpo": "grpo_loss",
-            "grpo_fwd": "grpo_loss_fwd", "rkl": "reverse_kl", "rkl_fwd": "reverse_kl_fwd"}[op]
-    fn = getattr(lib, name)
-    sets, calls = [], []
+    blib = bench_lib()
+    sets, rows = [], []
     for i in range(nsets):
         s = base if i == 0 else {k: v.clone() for k, v in base.items()}
         s = dict(s)
@@ -499,19 +738,32 @@ def main() -> int:
         s["loss"] = torch.empty((), dtype=torch.float32, device=dev)
         s["n"] = torch.empty(w.bs, dtype=torch.int32, device=dev)
         sets.append(s)
-        g = [s["grad"].data_ptr()] if fused else []
+        g = s["grad"].data_ptr() if fused else 0
         if is_rkl:
-            a = [s["student"].data_ptr(), s["teacher"].data_ptr(), s["mask"].data_ptr(), w.bs,
-                 w.seq_len, rl.DTYPE[dt], rl.MASK_DTYPE[s["mask"].dtype], s["loss"].data_ptr()]
+            rows.append([s["student"].data_ptr(), s["teacher"].data_ptr(), s["mask"].data_ptr(),
+                         s["loss"].data_ptr(), g, s["n"].data_ptr()])
         else:
-            a = [s["policy"].data_ptr(), s["old"].data_ptr(), s["ref"].data_ptr() if "ref" in s else None,
-                 s["advantages"].data_ptr(), s["mask"].data_ptr(), w.bs, w.seq_len, rl.DTYPE[dt],
-                 rl.MASK_DTYPE[s["mask"].dtype], w.beta, w.epsilon, w.epsilon_high, s["loss"].data_ptr()]
-        calls.append(tuple(a + g + [s["n"].data_ptr(), ws.data_ptr(), ws.numel(), sptr]))
+            rows.append([s["policy"].data_ptr(), s["old"].data_ptr(), s["ref"].data_ptr() if "ref" in s else 0,
+                         s["advantages"].data_ptr(), s["mask"].data_ptr(), s["loss"].data_ptr(), g,
+                         s["n"].data_ptr()])
+    table = pointer_table(rows)
+    dtc, mdc = rl.DTYPE[dt], rl.MASK_DTYPE[base["mask"].dtype]
+    if is_rkl:
+        run = lambda first, k: blib.rlpl_bench_rkl(int(fused), nsets, table.ctypes.data, w.bs, w.seq_len, dtc, mdc,
+                                                   ws.data_ptr(), ws.numel(), k, first, sptr)
+    elif args.noalloc:
+        if op != "bnpo":
+            raise SystemExit("--noalloc measures the fused BNPO loss only")
+        run = lambda first, k: blib.rlpl_bench_noalloc(nsets, table.ctypes.data, w.bs, w.seq_len, dtc, mdc, w.beta,
+                                                       w.epsilon, w.epsilon_high, k, first, sptr)
+    else:
+        run = lambda first, k: blib.rlpl_bench_policy(rl.OP[op], 0, nsets, table.ctypes.data, w.bs, w.seq_len, dtc,
+                                                      mdc, w.beta, w.epsilon, w.epsilon_high, ws.data_ptr(),
+                                                      ws.numel(), k, first, sptr)
     torch.cuda.synchronize()
 
     K, W = args.steps, args.warmup
-    ms_per_step, ms_gpu = timed(fn, calls, K, W, stream, torch)
+    ms_per_step, ms_gpu = timed_loop(run, K, W, stream, torch)
     tokens_per_s = w.slots / (ms_per_step * 1e-3)
 
     if not op.startswith("grpo"):
@@ -528,26 +780,7 @@ def main() -> int:
 
     cpu = None
     if headline and not args.no_cpu_baseline:
-        import oracle
-        xs = {k: oracle.to_f64(v) for k, v in x.items() if k in planes or k == "advantages"}
-        m8 = oracle.to_mask_u8(x["mask"])
-        f32 = lambda v: float(np.float32(v))
-
-        def run_once():
-            if is_rkl:
-                oracle.rkl(xs["student"], xs["teacher"], m8)
-            else:
-                fo = oracle.bnpo if op.startswith("bnpo") else oracle.grpo
-                fo(xs["policy"], xs["old"], xs.get("ref"), xs["advantages"], m8, f32(w.beta),
-                   f32(w.epsilon), f32(w.epsilon_high), grad=fused)
-        rate1, runs1 = oracle_rate(run_once, args.cpu_seconds, 1)
-        nt = cpu_threads()
-        rate_n, runs_n = oracle_rate(run_once, max(1.0, 2.0 * args.cpu_seconds / nt), nt) if nt > 1 else (rate1, runs1)
-        cpu = {"value": round(w.slots * rate_n, 1), "unit": "tokens/s", "cores": nt, "kind": "oracle",
-               "per_core_value": round(w.slots * rate1, 1),
-               "sample": f"full {w.name} batches (loss + grad, double precision): {runs_n} batches on "
-                         f"{nt} threads at once, one batch per thread; {runs1} batches on one thread, "
-                         f"{1e3 / rate1:.1f} ms each"}
+        cpu = cpu_baseline(op, x, w, fused, args)
 
     out = {
         "metric": METRIC,
@@ -566,10 +799,13 @@ def main() -> int:
                    "bs": w.bs, "seq_len": w.seq_len, "beta": 1.0 if is_rkl else w.beta,
                    "epsilon": w.epsilon, "epsilon_high": w.epsilon_high,
                    "mask": f"{w.mask_dtype} prefix U[{w.len_lo},{w.len_hi}]", "valid_tokens": valid,
+                   "tokens_counted": "bs * seq_len (row, position) slots per step",
                    "inputs": "device-generated" if on_device else "host-generated",
-                   "rotating_sets": nsets, "parallelism": "single GPU"},
+                   "rotating_sets": nsets, "entry_point": "bnpo_loss_noalloc" if args.noalloc else "C ABI",
+                   "parallelism": "single GPU"},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "valid_tokens_per_s": round(valid / (ms_per_step * 1e-3), 1),
         "kernel_us_per_launch": round(ms_gpu * 1e3, 3),
         "algorithmic_bytes_per_launch": alg,
     }

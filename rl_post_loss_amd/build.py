@@ -11,6 +11,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "librl_post_loss.so")
 SOURCES = ["loss_kernels.hip", "vocab_kernels.hip", "logprob_kernels.hip", "abi.cpp"]
+# Measurement helpers for bench.py (timing loops over the public entry points,
+# reference kernels); linked against the loss library, found beside it.
+BENCH_LIB = os.path.join(PKG, "librlpl_bench.so")
+BENCH_SOURCES = ["bench_kernels.hip"]
 
 
 def hipcc() -> str:
@@ -20,24 +24,30 @@ def hipcc() -> str:
     return path
 
 
-def command(out: str, extra=()) -> list:
+def command(out: str, extra=(), sources=SOURCES) -> list:
     return [hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
             "-Wall", "-Wno-unused-command-line-argument",
             # no packed-fp32 (v_pk_*_f32) instructions anywhere in the device code
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-I", INCLUDE, "-I", CSRC, *extra,
-            *[os.path.join(CSRC, s) for s in SOURCES], "-o", out]
+            *[os.path.join(CSRC, s) for s in sources], "-o", out]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile the library (always; the result replaces any earlier build atomically)."""
-    tmp = LIB + ".tmp"
-    r = subprocess.run(command(tmp), capture_output=True, text=True)
+def _compile(cmd, target, verbose):
+    r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("HIP build failed:\n" + r.stdout + r.stderr)
     if verbose and (r.stdout or r.stderr):
         print(r.stdout + r.stderr)
-    os.replace(tmp, LIB)
+    os.replace(target + ".tmp", target)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the library and the bench helpers (always; each result replaces any
+    earlier build atomically)."""
+    _compile(command(LIB + ".tmp"), LIB, verbose)
+    _compile(command(BENCH_LIB + ".tmp", extra=("-L", PKG, "-lrl_post_loss", "-Wl,-rpath,$ORIGIN"),
+                     sources=BENCH_SOURCES), BENCH_LIB, verbose)
     return LIB
 
 

@@ -1,0 +1,184 @@
+// Measurement helpers for bench.py (librlpl_bench.so; not part of the loss
+// library's ABI).
+//
+//  * Timing loops that call the library's public entry points back to back
+//    from C, one call per step on rotating input sets, so that the timed
+//    region measures the GPU rather than the interpreter's per-call cost.
+//  * Reference kernels for the roofline: an empty kernel (the launch floor at
+//    a given grid), and streaming copy and read kernels of our own (128-bit
+//    loads and stores, grid-stride, four 16-byte words in flight per lane),
+//    the ceilings the loss kernels are judged against.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "rl_post_loss.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__global__ void __launch_bounds__(kThreads) empty_kernel() {}
+
+template <bool NT>
+__device__ __forceinline__ u32x4 ld(const u32x4* p) {
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+template <bool NT>
+__device__ __forceinline__ void st(u32x4* p, u32x4 v) {
+    if constexpr (NT) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
+
+// dst[i] = src[i] for n 16-byte words; NT: non-temporal loads and stores.
+template <bool NT>
+__global__ void __launch_bounds__(kThreads) copy_kernel(u32x4* __restrict__ dst, const u32x4* __restrict__ src,
+                                                       uint64_t n) {
+    const uint64_t stride = uint64_t(gridDim.x) * kThreads;
+    uint64_t i = uint64_t(blockIdx.x) * kThreads + threadIdx.x;
+    for (; i + 3 * stride < n; i += 4 * stride) {
+        const u32x4 a = ld<NT>(src + i);
+        const u32x4 b = ld<NT>(src + i + stride);
+        const u32x4 c = ld<NT>(src + i + 2 * stride);
+        const u32x4 d = ld<NT>(src + i + 3 * stride);
+        st<NT>(dst + i, a);
+        st<NT>(dst + i + stride, b);
+        st<NT>(dst + i + 2 * stride, c);
+        st<NT>(dst + i + 3 * stride, d);
+    }
+    for (; i < n; i += stride) st<NT>(dst + i, ld<NT>(src + i));
+}
+
+// XOR of n 16-byte words; each workgroup writes one word to sink[blockIdx.x]
+// (so that the loads are not dead).
+template <bool NT>
+__global__ void __launch_bounds__(kThreads) read_kernel(const u32x4* __restrict__ src, uint64_t n,
+                                                       uint32_t* __restrict__ sink) {
+    const uint64_t stride = uint64_t(gridDim.x) * kThreads;
+    uint64_t i = uint64_t(blockIdx.x) * kThreads + threadIdx.x;
+    uint32_t x = 0;
+    for (; i + 3 * stride < n; i += 4 * stride) {
+        const u32x4 a = ld<NT>(src + i);
+        const u32x4 b = ld<NT>(src + i + stride);
+        const u32x4 c = ld<NT>(src + i + 2 * stride);
+        const u32x4 d = ld<NT>(src + i + 3 * stride);
+        x ^= a[0] ^ a[1] ^ a[2] ^ a[3] ^ b[0] ^ b[1] ^ b[2] ^ b[3] ^ c[0] ^ c[1] ^ c[2] ^ c[3] ^ d[0] ^ d[1] ^ d[2] ^ d[3];
+    }
+    for (; i < n; i += stride) {
+        const u32x4 a = ld<NT>(src + i);
+        x ^= a[0] ^ a[1] ^ a[2] ^ a[3];
+    }
+    if (x == 0x9e3779b9u) sink[blockIdx.x] = x;   // practically never: keeps the loads live
+}
+
+int grid_for(int grid) { return grid > 0 ? grid : 2048; }
+
+}  // namespace
+
+extern "C" {
+
+// `iters` back-to-back launches of an empty kernel of `grid` x 256 threads.
+int rlpl_bench_empty(int grid, int iters, hipStream_t stream) {
+    for (int i = 0; i < iters; ++i) {
+        hipLaunchKernelGGL(empty_kernel, dim3(grid), dim3(kThreads), 0, stream);
+        if (hipGetLastError() != hipSuccess) return RLPL_ERR_LAUNCH;
+    }
+    return RLPL_OK;
+}
+
+// `iters` copies of `bytes` (a multiple of 16), call i on pair (first + i) % n_sets of
+// `pairs` (n_sets x {dst, src} device pointers); grid 0 = 2048 workgroups; nt != 0:
+// non-temporal loads and stores.
+int rlpl_bench_copy(int n_sets, const uint64_t* pairs, uint64_t bytes, int grid, int nt, int iters, int first,
+                    hipStream_t stream) {
+    if (!pairs || n_sets < 1 || bytes % 16) return RLPL_ERR_PARAM;
+    for (int i = 0; i < iters; ++i) {
+        const uint64_t* p = pairs + 2 * ((first + i) % n_sets);
+        if (nt)
+            hipLaunchKernelGGL(copy_kernel<true>, dim3(grid_for(grid)), dim3(kThreads), 0, stream,
+                               reinterpret_cast<u32x4*>(p[0]), reinterpret_cast<const u32x4*>(p[1]), bytes / 16);
+        else
+            hipLaunchKernelGGL(copy_kernel<false>, dim3(grid_for(grid)), dim3(kThreads), 0, stream,
+                               reinterpret_cast<u32x4*>(p[0]), reinterpret_cast<const u32x4*>(p[1]), bytes / 16);
+        if (hipGetLastError() != hipSuccess) return RLPL_ERR_LAUNCH;
+    }
+    return RLPL_OK;
+}
+
+// `iters` streaming reads of `bytes` (a multiple of 16) from srcs[(first + i) % n_sets];
+// `sink` holds one word per workgroup.
+int rlpl_bench_read(int n_sets, const uint64_t* srcs, uint64_t bytes, int grid, int nt, uint32_t* sink, int iters,
+                    int first, hipStream_t stream) {
+    if (!srcs || !sink || n_sets < 1 || bytes % 16) return RLPL_ERR_PARAM;
+    for (int i = 0; i < iters; ++i) {
+        const u32x4* src = reinterpret_cast<const u32x4*>(srcs[(first + i) % n_sets]);
+        if (nt)
+            hipLaunchKernelGGL(read_kernel<true>, dim3(grid_for(grid)), dim3(kThreads), 0, stream, src, bytes / 16,
+                               sink);
+        else
+            hipLaunchKernelGGL(read_kernel<false>, dim3(grid_for(grid)), dim3(kThreads), 0, stream, src, bytes / 16,
+                               sink);
+        if (hipGetLastError() != hipSuccess) return RLPL_ERR_LAUNCH;
+    }
+    return RLPL_OK;
+}
+
+// `iters` calls of rlpl_policy_loss(op, flags, ...), call i on set (first + i) % n_sets
+// of `sets` (n_sets x {policy, old, ref, advantages, mask, loss, grad, n_valid}).
+int rlpl_bench_policy(int op, uint32_t flags, int n_sets, const uint64_t* sets, int64_t bs, int64_t seq_len,
+                      int dtype, int mask_dtype, float beta, float epsilon, float epsilon_high, void* workspace,
+                      size_t workspace_bytes, int iters, int first, hipStream_t stream) {
+    if (!sets || n_sets < 1) return RLPL_ERR_PARAM;
+    for (int i = 0; i < iters; ++i) {
+        const uint64_t* s = sets + 8 * ((first + i) % n_sets);
+        const int st = rlpl_policy_loss(op, flags, reinterpret_cast<const void*>(s[0]),
+                                        reinterpret_cast<const void*>(s[1]), reinterpret_cast<const void*>(s[2]),
+                                        reinterpret_cast<const void*>(s[3]), reinterpret_cast<const void*>(s[4]),
+                                        bs, seq_len, dtype, mask_dtype, beta, epsilon, epsilon_high,
+                                        reinterpret_cast<float*>(s[5]), reinterpret_cast<void*>(s[6]),
+                                        reinterpret_cast<uint32_t*>(s[7]), workspace, workspace_bytes, stream);
+        if (st != RLPL_OK) return st;
+    }
+    return RLPL_OK;
+}
+
+// `iters` calls of reverse_kl (fused != 0) or reverse_kl_fwd on rotating sets
+// (n_sets x {student, teacher, mask, loss, grad, n_valid}).
+int rlpl_bench_rkl(int fused, int n_sets, const uint64_t* sets, int64_t bs, int64_t seq_len, int dtype,
+                   int mask_dtype, void* workspace, size_t workspace_bytes, int iters, int first,
+                   hipStream_t stream) {
+    if (!sets || n_sets < 1) return RLPL_ERR_PARAM;
+    for (int i = 0; i < iters; ++i) {
+        const uint64_t* s = sets + 6 * ((first + i) % n_sets);
+        const void* st_lp = reinterpret_cast<const void*>(s[0]);
+        const void* te_lp = reinterpret_cast<const void*>(s[1]);
+        const void* mask = reinterpret_cast<const void*>(s[2]);
+        float* loss = reinterpret_cast<float*>(s[3]);
+        uint32_t* n = reinterpret_cast<uint32_t*>(s[5]);
+        const int st = fused ? reverse_kl(st_lp, te_lp, mask, bs, seq_len, dtype, mask_dtype, loss,
+                                          reinterpret_cast<void*>(s[4]), n, workspace, workspace_bytes, stream)
+                             : reverse_kl_fwd(st_lp, te_lp, mask, bs, seq_len, dtype, mask_dtype, loss, n,
+                                              workspace, workspace_bytes, stream);
+        if (st != RLPL_OK) return st;
+    }
+    return RLPL_OK;
+}
+
+// `iters` calls of bnpo_loss_noalloc on rotating sets (as rlpl_bench_policy).
+int rlpl_bench_noalloc(int n_sets, const uint64_t* sets, int64_t bs, int64_t seq_len, int dtype, int mask_dtype,
+                       float beta, float epsilon, float epsilon_high, int iters, int first, hipStream_t stream) {
+    if (!sets || n_sets < 1) return RLPL_ERR_PARAM;
+    for (int i = 0; i < iters; ++i) {
+        const uint64_t* s = sets + 8 * ((first + i) % n_sets);
+        const int st = bnpo_loss_noalloc(reinterpret_cast<const void*>(s[0]), reinterpret_cast<const void*>(s[1]),
+                                         reinterpret_cast<const void*>(s[2]), reinterpret_cast<const void*>(s[3]),
+                                         reinterpret_cast<const void*>(s[4]), bs, seq_len, dtype, mask_dtype, beta,
+                                         epsilon, epsilon_high, reinterpret_cast<float*>(s[5]),
+                                         reinterpret_cast<void*>(s[6]), reinterpret_cast<uint32_t*>(s[7]), stream);
+        if (st != RLPL_OK) return st;
+    }
+    return RLPL_OK;
+}
+
+}  // extern "C"

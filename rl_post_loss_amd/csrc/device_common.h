@@ -225,9 +225,15 @@ __device__ __forceinline__ bool read_entry(__amdgpu_buffer_rsrc_t v, uint32_t of
     value = x[0];
     return x[1] == t.t0 && x[3] == t.t1 && x[0] == x[2];
 }
-// Between two polls: a pause, and a compiler barrier so that the next poll is a new load.
+// Between two polls: a pause of SLEEP x 64 clocks, and a compiler barrier so
+// that the next poll is a new load.  Each poll is a read that goes to the
+// memory side; the pauses (longer for the release, which up to every worker
+// polls) keep that traffic small without delaying the waits measurably.
+constexpr int kGatherSleep = 4;
+constexpr int kReleaseSleep = 8;
+template <int SLEEP>
 __device__ __forceinline__ void poll_pause() {
-    __builtin_amdgcn_s_sleep(kPollSleep);
+    __builtin_amdgcn_s_sleep(SLEEP);
     __asm__ volatile("" ::: "memory");
 }
 
@@ -283,7 +289,7 @@ __device__ inline V gather(__amdgpu_buffer_rsrc_t view, uint32_t base, uint32_t 
         if (miss) {
             const uint64_t t0 = wall_clock64();
             for (uint32_t n = 1; miss; ++n) {
-                poll_pause();
+                poll_pause<kGatherSleep>();
 #pragma unroll
                 for (int j = 0; j < B; ++j)
                     if (miss & (1u << j)) {
@@ -348,7 +354,7 @@ __device__ inline uint32_t await_release(__amdgpu_buffer_rsrc_t view, uint32_t l
         if (!ok) {
             const uint64_t t0 = wall_clock64();
             for (uint32_t n = 1; !ok; ++n) {
-                poll_pause();
+                poll_pause<kReleaseSleep>();
                 ok = read_entry(view, kReleaseOff, tg, v);
                 if ((n & 7u) == 0u && uint64_t(wall_clock64()) - t0 > limit) break;
             }
