@@ -159,13 +159,17 @@ struct Shape {
     int vec;
     uint32_t tiles;
     int64_t grid;
+    uint32_t per;    // GRPO: tiles per worker (a contiguous run each)
 };
 
 // Kernel shape, tile count and grid of a call on this device: one
 // coordinating workgroup plus one worker per tile whenever that many
 // workgroups of the one-tile kernel are co-resident (small problems take the
 // narrow lane so that every compute unit gets a tile), else the striding
-// kernel on as many workgroups as are co-resident (all of them workers).
+// kernel on as many workgroups as are co-resident (all of them workers).  The
+// striding GRPO kernel gives each worker a contiguous run of `per` tiles: per
+// is the fewest tiles per worker that fit the co-resident workgroups, and the
+// grid the runs it takes (so that every worker has one).
 int launch_shape(const DeviceInfo* info, int dtype, int mode, int64_t slots, Shape* out) {
     const int64_t large_tile = int64_t(rlpl::kThreads) * rlpl::kVecLarge;
     const int64_t small_tile = int64_t(rlpl::kThreads) * rlpl::kVecSmall;
@@ -173,13 +177,20 @@ int launch_shape(const DeviceInfo* info, int dtype, int mode, int64_t slots, Sha
     const int64_t small_tiles = (slots + small_tile - 1) / small_tile;
     const int64_t large_tiles = (slots + large_tile - 1) / large_tile;
     if (slots < int64_t(info->cus) * rlpl::kSmallTilesPerCu * large_tile && small_tiles + 1 <= cap[rlpl::kShapeSmall]) {
-        *out = {rlpl::kShapeSmall, rlpl::kVecSmall, uint32_t(small_tiles), small_tiles + 1};
+        *out = {rlpl::kShapeSmall, rlpl::kVecSmall, uint32_t(small_tiles), small_tiles + 1, 1};
     } else if (large_tiles + 1 <= cap[rlpl::kShapeLarge]) {
-        *out = {rlpl::kShapeLarge, rlpl::kVecLarge, uint32_t(large_tiles), large_tiles + 1};
+        *out = {rlpl::kShapeLarge, rlpl::kVecLarge, uint32_t(large_tiles), large_tiles + 1, 1};
     } else {
         const int64_t c = cap[rlpl::kShapeStream];
         if (c < 1) return RLPL_ERR_DEVICE;
-        *out = {rlpl::kShapeStream, rlpl::kVecLarge, uint32_t(large_tiles), large_tiles < c ? large_tiles : c};
+        if (mode == kModeGRPO) {
+            const int64_t per = (large_tiles + c - 1) / c;
+            if (per > rlpl::kMaxPer) return RLPL_ERR_SHAPE;
+            *out = {rlpl::kShapeStream, rlpl::kVecLarge, uint32_t(large_tiles), (large_tiles + per - 1) / per,
+                    uint32_t(per)};
+        } else {
+            *out = {rlpl::kShapeStream, rlpl::kVecLarge, uint32_t(large_tiles), large_tiles < c ? large_tiles : c, 1};
+        }
     }
     return RLPL_OK;
 }
@@ -195,6 +206,7 @@ int run(int mode, bool write_grad, bool has_kl, Args& a, int dtype, hipStream_t 
     const void* kernel = rlpl::pick_kernel(dtype, mode, has_kl, write_grad, sh.kernel);
     if (!kernel) return RLPL_ERR_DTYPE;
     a.tiles = sh.tiles;
+    a.per = sh.per;
     if (!rlpl::row_divisor(uint32_t(a.seq_len), &a.row_magic, &a.row_shift)) return RLPL_ERR_SHAPE;
     return launch(kernel, a, dim3(unsigned(sh.grid)), stream);
 }

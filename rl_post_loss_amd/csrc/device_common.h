@@ -136,16 +136,32 @@ __device__ __forceinline__ void store_values(T* __restrict__ base, uint32_t s, u
 
 // ----------------------------------------------------------------------------- reductions
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
+// A wavefront's sum, in every lane, from DPP lane moves (each a plain VALU
+// operand modifier; a shuffle would go through the LDS crossbar, about a
+// hundred cycles per step): pairs and quads (quad_perm), half-rows and rows
+// of 16 (row_half_mirror, row_mirror), then rows 1 and 3 take the last lane
+// of rows 0 and 2 (row_bcast:15) and rows 2 and 3 that of row 1
+// (row_bcast:31), which leaves the total in lane 63.  A fixed order, so the
+// float sum is deterministic.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp_move(uint32_t v) {
+    // Rows outside ROW_MASK receive 0 (the identity of the sums below).
+    return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), CTRL, ROW_MASK, 0xF, false));
 }
-__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
+template <typename V>
+__device__ __forceinline__ V wave_sum_dpp(V v) {
+    auto bits = [](V x) { return __builtin_bit_cast(uint32_t, x); };
+    auto from = [](uint32_t x) { return __builtin_bit_cast(V, x); };
+    v = v + from(dpp_move<0xB1>(bits(v)));          // quad_perm [1, 0, 3, 2]
+    v = v + from(dpp_move<0x4E>(bits(v)));          // quad_perm [2, 3, 0, 1]
+    v = v + from(dpp_move<0x141>(bits(v)));         // row_half_mirror
+    v = v + from(dpp_move<0x140>(bits(v)));         // row_mirror
+    v = v + from(dpp_move<0x142, 0xA>(bits(v)));    // row_bcast:15
+    v = v + from(dpp_move<0x143, 0xC>(bits(v)));    // row_bcast:31
+    return from(uint32_t(__builtin_amdgcn_readlane(int(bits(v)), 63)));
 }
+__device__ __forceinline__ float wave_sum(float v) { return wave_sum_dpp(v); }
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) { return wave_sum_dpp(v); }
 
 // Workgroup sum in a fixed order (lane tree, then waves 0..3); result valid in every thread.
 template <typename V>
@@ -159,6 +175,28 @@ __device__ __forceinline__ V block_sum(V v, V* red) {
 #pragma unroll
     for (int i = 1; i < kWaves; ++i) t += red[i];
     return t;
+}
+
+// N workgroup sums at once (one pair of barriers), in every thread, each in
+// the fixed order of block_sum.  `red` is LDS of N * kWaves values.
+template <int N, typename V>
+__device__ __forceinline__ void block_sum_n(V (&v)[N], V* red) {
+#pragma unroll
+    for (int u = 0; u < N; ++u) v[u] = wave_sum(v[u]);
+    const int wave = threadIdx.x >> 6;
+    __syncthreads();                       // red[] may still be read by a previous reduction
+    if ((threadIdx.x & 63) == 0) {
+#pragma unroll
+        for (int u = 0; u < N; ++u) red[u * kWaves + wave] = v[u];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < N; ++u) {
+        V t = red[u * kWaves];
+#pragma unroll
+        for (int i = 1; i < kWaves; ++i) t += red[u * kWaves + i];
+        v[u] = t;
+    }
 }
 
 // ----------------------------------------------------------------------------- launch identity
@@ -214,9 +252,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t entry_view(const Workspace* ws
 constexpr uint32_t kReleaseOff = uint32_t(offsetof(Workspace, release));
 __device__ __forceinline__ uint32_t cnt_off(uint32_t w) { return uint32_t(offsetof(Workspace, cnt)) + 16u * w; }
 __device__ __forceinline__ uint32_t par_off(uint32_t w) { return uint32_t(offsetof(Workspace, par)) + 16u * w; }
+__device__ __forceinline__ uint32_t tail_off(uint32_t w) { return uint32_t(offsetof(Workspace, tail)) + 16u * w; }
+__device__ __forceinline__ uint32_t hpair_off(uint32_t w) { return uint32_t(offsetof(Workspace, hpair)) + 16u * w; }
+__device__ __forceinline__ uint32_t tpair_off(uint32_t w) { return uint32_t(offsetof(Workspace, tpair)) + 16u * w; }
+// An item of a gather that has no entry: it adds nothing and is never awaited.
+constexpr uint32_t kNoEntry = 0xFFFFFFFFu;
 
 __device__ __forceinline__ void publish(__amdgpu_buffer_rsrc_t v, uint32_t off, Tag t, uint32_t value) {
     const u32x4 x = {value, t.t0, value, t.t1};
+    __builtin_amdgcn_raw_buffer_store_b128(x, v, off, 0, kCoherent);
+}
+// A pair entry: values a and b, each beside one of the launch's tags.
+__device__ __forceinline__ void publish_pair(__amdgpu_buffer_rsrc_t v, uint32_t off, Tag t, uint32_t a, uint32_t b) {
+    const u32x4 x = {a, t.t0, b, t.t1};
     __builtin_amdgcn_raw_buffer_store_b128(x, v, off, 0, kCoherent);
 }
 // One read of an entry: true, with its value, when it holds this launch's value.
@@ -237,6 +285,25 @@ __device__ __forceinline__ void poll_pause() {
     __asm__ volatile("" ::: "memory");
 }
 
+// One poll of up to N entries: the reads of those still awaited (bit j of
+// `miss`) go out together, and are checked once all have returned; an entry
+// not awaited reads the workspace's first 16 bytes instead (in bounds, not
+// used), so that no read waits behind the check of another.
+template <int N>
+__device__ __forceinline__ void poll_entries(__amdgpu_buffer_rsrc_t view, const uint32_t (&at)[N], Tag tg,
+                                             uint32_t& miss, uint32_t (&val)[N]) {
+    u32x4 x[N];
+#pragma unroll
+    for (int j = 0; j < N; ++j)
+        x[j] = __builtin_amdgcn_raw_buffer_load_b128(view, (miss >> j) & 1u ? at[j] : 0u, 0, kCoherent);
+#pragma unroll
+    for (int j = 0; j < N; ++j)
+        if (((miss >> j) & 1u) && x[j][1] == tg.t0 && x[j][3] == tg.t1 && x[j][0] == x[j][2]) {
+            val[j] = x[j][0];
+            miss &= ~(1u << j);
+        }
+}
+
 // The wait limits of the policy-loss kernels in 100 MHz ticks: the caller's
 // overrides in the workspace header (written by the host only), else the
 // defaults.  Read once at the start of a workgroup, where the read overlaps
@@ -250,55 +317,51 @@ __device__ __forceinline__ Limits read_limits(const Workspace* ws) {
     return Limits{v.x != 0u ? v.x : kStealTicks, v.y != 0u ? v.y : kReleaseTicks, v.z != 0u ? v.z : kGiveUpTicks};
 }
 
-// Sum over the W workers' entries at `base` (valid counts, or the float bits
-// of partial losses: V = uint32_t / float), in every thread.  Thread i takes
-// workers i, i + kThreads, ... in turn, B at a time (a chunk).  Entries not yet
-// published are polled until they are, or until `limit` ticks have passed;
-// entries still missing then are computed here, one worker at a time by the
-// whole workgroup (compute(w) is workgroup-uniform and bit-identical to what
-// worker w publishes).  The sum is taken in one fixed order (each thread's
-// workers in turn, then the workgroup tree), so it never depends on which
-// entries were computed here.  `list` is LDS of kThreads + 1 words.
+// Sum over W items' entries (valid counts, or the float bits of partial
+// losses: V = uint32_t / float), in every thread; item i's entry is at byte
+// off(i) of the view, or off(i) == kNoEntry for an item that adds nothing.
+// Thread i takes items i, i + kThreads, ... in turn, B at a time (a chunk).
+// Entries not yet published are polled until they are, or until `limit`
+// ticks have passed; entries still missing then are computed here, one item
+// at a time by the whole workgroup (compute(i) is workgroup-uniform and
+// bit-identical to what the item's owner publishes).  The sum is taken in one
+// fixed order (each thread's items in turn, then the workgroup tree), so it
+// never depends on which entries were computed here.  `list` is LDS of
+// kThreads + 1 words, not used by compute().
 //
 // between() runs once the first chunk's reads are issued and before they are
 // used: a store made there (the release) does not hold them up.  Loads and
 // stores of a wavefront share one in-order completion counter, so a load
 // issued after a device-coherent store waits for that store's write-through.
-template <typename V, typename F, typename G>
-__device__ inline V gather(__amdgpu_buffer_rsrc_t view, uint32_t base, uint32_t W, Tag tg, uint32_t limit,
+template <typename V, typename O, typename F, typename G>
+__device__ inline V gather(__amdgpu_buffer_rsrc_t view, O&& off, uint32_t W, Tag tg, uint32_t limit,
                            uint32_t* list, V* red, F&& compute, G&& between) {
     constexpr int B = 4;
     V s = 0;
     for (uint32_t c0 = 0; c0 < W; c0 += B * kThreads) {
         u32x4 raw[B];
+        uint32_t at[B];
 #pragma unroll
         for (int j = 0; j < B; ++j) {
             const uint32_t i = c0 + threadIdx.x + j * kThreads;
-            raw[j] = i < W ? __builtin_amdgcn_raw_buffer_load_b128(view, base + 16u * i, 0, kCoherent) : u32x4{0, 0, 0, 0};
+            at[j] = i < W ? off(i) : kNoEntry;
+            // (an item with no entry reads the workspace's first 16 bytes, unused)
+            raw[j] = __builtin_amdgcn_raw_buffer_load_b128(view, at[j] != kNoEntry ? at[j] : 0u, 0, kCoherent);
         }
         if (c0 == 0) between();
         uint32_t val[B];
-        uint32_t miss = 0;                     // bit j: worker c0 + tid + j * kThreads not seen yet
+        uint32_t miss = 0;                     // bit j: item c0 + tid + j * kThreads not seen yet
 #pragma unroll
         for (int j = 0; j < B; ++j) {
-            const uint32_t i = c0 + threadIdx.x + j * kThreads;
             const u32x4 x = raw[j];
-            val[j] = i < W ? x[0] : 0u;
-            if (i < W && !(x[1] == tg.t0 && x[3] == tg.t1 && x[0] == x[2])) miss |= 1u << j;
+            val[j] = at[j] != kNoEntry ? x[0] : 0u;
+            if (at[j] != kNoEntry && !(x[1] == tg.t0 && x[3] == tg.t1 && x[0] == x[2])) miss |= 1u << j;
         }
         if (miss) {
             const uint64_t t0 = wall_clock64();
             for (uint32_t n = 1; miss; ++n) {
                 poll_pause<kGatherSleep>();
-#pragma unroll
-                for (int j = 0; j < B; ++j)
-                    if (miss & (1u << j)) {
-                        uint32_t v;
-                        if (read_entry(view, base + 16u * (c0 + threadIdx.x + j * kThreads), tg, v)) {
-                            val[j] = v;
-                            miss &= ~(1u << j);
-                        }
-                    }
+                poll_entries<B>(view, at, tg, miss, val);
                 if ((n & 7u) == 0u && uint64_t(wall_clock64()) - t0 > limit) break;
             }
         }
@@ -312,15 +375,21 @@ __device__ inline V gather(__amdgpu_buffer_rsrc_t view, uint32_t base, uint32_t 
             const uint32_t n_list = list[kThreads];
             for (uint32_t k = 0; k < n_list; ++k) {
                 const uint32_t t = list[k] & 0xFFFFu, bits = list[k] >> 16;
+                // One copy of compute() (a rolled loop); the value lands in val[] by
+                // static indices.
+#pragma unroll 1
+                for (uint32_t j = 0; j < uint32_t(B); ++j) {
+                    if (!(bits & (1u << j))) continue;
+                    const V v = compute(c0 + t + j * kThreads);
+                    uint32_t u;
+                    if constexpr (std::is_same<V, float>::value) u = __float_as_uint(v);
+                    else u = v;
+                    if (threadIdx.x == t) {
 #pragma unroll
-                for (int j = 0; j < B; ++j)
-                    if (bits & (1u << j)) {
-                        const V v = compute(c0 + t + uint32_t(j) * kThreads);
-                        if (threadIdx.x == t) {
-                            if constexpr (std::is_same<V, float>::value) val[j] = __float_as_uint(v);
-                            else val[j] = v;
-                        }
+                        for (int q = 0; q < B; ++q)
+                            if (uint32_t(q) == j) val[q] = u;
                     }
+                }
             }
             __syncthreads();                   // list[] is reused by the next chunk
         }

@@ -21,6 +21,13 @@ constexpr int kVecSmall = 4;
 // within the 128 KB of LDS per CU that the host budgets.
 constexpr int kBitTilesPolicy = 56;
 constexpr int kBitTilesRkl = 40;
+// GRPO's striding kernels own contiguous runs of at most kMaxPer tiles per
+// worker (the host sizes the grid so), keep one word per owned tile in LDS
+// (the counts of the tile's first and last row) and the mask bits of the
+// first kBitTilesGrpo tiles: with the per-row counts of a tile (16 KB) that
+// is 28 KB, four workgroups per compute unit.
+constexpr int kMaxPer = 1024;
+constexpr int kBitTilesGrpo = 12;
 // Kernel shapes: one tile per worker with the narrow or the wide lane, or the
 // wide lane striding over several tiles per worker.
 enum { kShapeSmall = 0, kShapeLarge = 1, kShapeStream = 2, kShapes = 3 };
@@ -51,6 +58,9 @@ enum { kF32 = 0, kF16 = 1, kBF16 = 2 };
 // [63:32 tag t0 | 31:0 value] and [63:32 tag t1 | 31:0 value], written and
 // read as one 16-byte access.  A reader takes it only when both tags are its
 // launch's and both values agree, so a torn or stale entry is never taken.
+// A pair entry holds two values instead, [t0 | a] and [t1 | b]: each 8-byte
+// half carries its own tag, so a read that mixes the halves of two stores
+// fails a tag check.
 struct alignas(16) Entry {
     uint64_t w[2];
 };
@@ -79,8 +89,11 @@ struct Workspace {
     uint32_t pad2[29];
     Entry release;             // the global valid count N, published by the coordinator
     uint64_t pad3[14];
-    Entry cnt[kMaxGrid];       // per worker: its valid-token count
-    Entry par[kMaxGrid];       // per worker: float bits of its partial loss
+    Entry cnt[kMaxGrid];       // per worker: its valid-token count (GRPO: that of its run's first row)
+    Entry par[kMaxGrid];       // per worker: float bits of its partial loss (GRPO: of the rows inside its run)
+    Entry tail[kMaxGrid];      // GRPO, per worker: the valid count of its run's last row
+    Entry hpair[kMaxGrid];     // GRPO, per worker: its run's first row's count and unscaled sum of terms
+    Entry tpair[kMaxGrid];     // GRPO, per worker: the same for its run's last row
     Slot slot[kMaxGrid];       // full-vocab kernels
 };
 static_assert(offsetof(Workspace, flags) == 128, "header words on separate lines");
@@ -108,6 +121,7 @@ struct Args {
     Workspace* ws;
     int64_t slots;         // bs * seq_len  (< 2^31)
     uint32_t tiles;        // ceil(slots / (kThreads * VEC))
+    uint32_t per;          // GRPO: tiles per worker (each worker owns a contiguous run)
     int32_t seq_len;
     int32_t bs;
     uint32_t row_magic;    // s / seq_len == (s * row_magic) >> row_shift for every s < 2^31

@@ -283,7 +283,9 @@ def test_every_kernel_shape(op):
     # lane, and the wide lane striding over several tiles per worker), each in
     # its fused and forward-only form, reached through problem size alone.
     kinds = set()
-    for bs, T in [(64, 4096), (1024, 4096), (1024, 8192)]:
+    # (GRPO's one-tile kernels hold fewer workgroups per compute unit, so its
+    # wide one-tile case is a smaller problem.)
+    for bs, T in [(64, 4096), (512 if op == "grpo" else 1024, 4096), (1024, 8192)]:
         grid, vec, tiles = rl.launch_shape(bs, T, torch.bfloat16, op)
         kind = _shape_kind(grid, vec, tiles)
         kinds.add(kind)
@@ -356,6 +358,27 @@ def test_sign_aware_clip_row_crossing_lanes(bs, T):
 def test_grpo_rows_longer_than_a_tile():
     x = _custom("grpo", "fp16", 6, 50000, "prefix", lo=0)
     assert_policy_parity("grpo", x, 0.04, 0.2, 0.2, "grpo long rows")
+
+
+# GRPO row counts across tile and worker-run boundaries: rows spanning many
+# tiles, rows that do not divide a tile, a single row over the whole launch,
+# in the one-tile and the striding kernels (each worker owning a run of tiles).
+GRPO_ROWS = [(16, 131072, "prefix"), (64, 32768, "random"), (1, 1 << 21, "random"), (5, 4099, "random"),
+             (64, 100000, "prefix"), (2000, 3000, "random"), (1, 6_000_000, "prefix"), (700, 8192, "random")]
+
+
+@pytest.mark.parametrize("bs,T,mask", GRPO_ROWS)
+def test_grpo_rows_across_tiles_and_runs(bs, T, mask):
+    grid, vec, tiles = rl.launch_shape(bs, T, torch.float16, "grpo")
+    x = _custom("grpo", "fp16", bs, T, mask, seed=bs + T, lo=0)
+    what = f"grpo rows {bs}x{T} grid={grid} tiles={tiles}"
+    print("[parity]", what, flush=True)
+    first = assert_policy_parity("grpo", x, 0.04, 0.2, 0.28, what)
+    fwd = assert_policy_parity("grpo", x, 0.04, 0.2, 0.28, what + " fwd", fused=False)
+    assert torch.equal(fwd[0], first[0]), what
+    g = dev(x)
+    again = gpu_policy("grpo", True, g, 0.04, 0.2, 0.28)
+    assert all(torch.equal(a, b) for a, b in zip(again, first)), what
 
 
 def test_grpo_one_slot_rows():

@@ -88,6 +88,27 @@ def test_fallbacks_are_bit_identical(op, shape):
         assert rl.workspace_flags(ws) == 0
 
 
+# GRPO rows that cross worker boundaries gather the other workers' pieces of the
+# row: one-tile (long rows; rows not dividing a tile) and striding kernels.
+GRPO_ROW_SHAPES = [(16, 131072), (64, 3000), (64, 100000), (2000, 3000)]
+
+
+@pytest.mark.parametrize("shape", GRPO_ROW_SHAPES)
+@pytest.mark.parametrize("op", ["grpo", "grpo_fwd"])
+def test_grpo_row_piece_fallback_is_bit_identical(op, shape):
+    bs, T = shape
+    x, w = inputs(op, bs, T)
+    ref = call(op, x, w, fresh_workspace())
+    ws = fresh_workspace()
+    rl.set_wait_limits(ws, steal_ticks=1)
+    for _ in range(2):
+        same_bits(call(op, x, w, ws), ref)
+    rl.set_wait_limits(ws)
+    x2, _ = inputs(op, bs, T, seed=1)
+    same_bits(call(op, x2, w, ws), call(op, x2, w, fresh_workspace()))
+    assert rl.workspace_flags(ws) == 0
+
+
 @pytest.mark.parametrize("op", ["bnpo", "rkl"])
 def test_exchange_kernels_on_two_streams(op):
     """Two capacity-sized exchange grids in flight together cannot all be resident; each
