@@ -1078,7 +1078,7 @@ __global__ void __launch_bounds__(kThreads) grpo_kernel(const Args a) {
             if (miss) {
                 const uint64_t t0 = wall_clock64();
                 for (uint32_t n = 1; miss; ++n) {
-                    poll_pause<kGatherSleep>();
+                    poll_pause<1>();           // (one workgroup polls: a short pause)
                     poll();
                     if ((n & 7u) == 0u && uint64_t(wall_clock64()) - t0 > lim.steal) break;
                 }
@@ -1160,34 +1160,46 @@ __global__ void __launch_bounds__(kThreads) grpo_kernel(const Args a) {
         // Each thread's state to LDS (row_lds is free here): the row it passes on
         // (its pieces; reset unless its workers all lie in a row begun before
         // them), the row begun before and ended in its workers, its sum.
+        // Thread t's words sit at (t % 4) * 64 + t / 4 of each array, so that
+        // wavefront 0's lane l reads threads 4l .. 4l + 3 without bank conflicts.
         uint32_t* st = row_lds;
         float* stf = reinterpret_cast<float*>(row_lds);
+        const uint32_t me = (threadIdx.x & 3u) * 64u + (threadIdx.x >> 2);
         __syncthreads();
-        st[threadIdx.x] = (have && from_left ? 0u : 1u) | (left ? 2u : 0u);
-        st[kThreads + threadIdx.x] = have ? cur_n : 0u;
-        stf[2 * kThreads + threadIdx.x] = have ? cur_s : 0.0f;
-        st[3 * kThreads + threadIdx.x] = left_row;
-        st[4 * kThreads + threadIdx.x] = left_n;
-        stf[5 * kThreads + threadIdx.x] = left_s;
-        stf[6 * kThreads + threadIdx.x] = acc;
+        st[me] = (have && from_left ? 0u : 1u) | (left ? 2u : 0u);
+        st[kThreads + me] = have ? cur_n : 0u;
+        stf[2 * kThreads + me] = have ? cur_s : 0.0f;
+        st[3 * kThreads + me] = left_row;
+        st[4 * kThreads + me] = left_n;
+        stf[5 * kThreads + me] = left_s;
+        stf[6 * kThreads + me] = acc;
         __syncthreads();
         float loss = 0.0f;
         if (threadIdx.x < 64u) {
             // Lane l takes threads 4l .. 4l + 3 in order.
             const uint32_t l = threadIdx.x;
+            // Every word first (the reads go out together), then branch-free folds.
+            uint32_t fw[4], xn4[4], lr4[4], ln4[4];
+            float xs4[4], ls4[4], ac4[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t t = 64u * e + l;
+                fw[e] = st[t];
+                xn4[e] = st[kThreads + t];
+                xs4[e] = stf[2 * kThreads + t];
+                lr4[e] = st[3 * kThreads + t];
+                ln4[e] = st[4 * kThreads + t];
+                ls4[e] = stf[5 * kThreads + t];
+                ac4[e] = stf[6 * kThreads + t];
+            }
             uint32_t f = 0, n = 0;             // the lane's fold: whether it restarts, and its run
             float sm = 0.0f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const uint32_t t = 4u * l + e;
-                if (st[t] & 1u) {
-                    f = 1u;
-                    n = st[kThreads + t];
-                    sm = stf[2 * kThreads + t];
-                } else {
-                    n = n + st[kThreads + t];
-                    sm = sm + stf[2 * kThreads + t];
-                }
+                const bool r = (fw[e] & 1u) != 0u;
+                f |= r ? 1u : 0u;
+                n = r ? xn4[e] : n + xn4[e];
+                sm = r ? xs4[e] : sm + xs4[e];
             }
             // Inclusive segmented scan of the lanes' folds (DPP lane moves: within
             // rows of 16 by 1, 2, 4, 8 lanes, then across rows), then each lane's
@@ -1213,23 +1225,17 @@ __global__ void __launch_bounds__(kThreads) grpo_kernel(const Args a) {
             float run_s = __uint_as_float(dpp_move<0x138>(__float_as_uint(sm)));
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const uint32_t t = 4u * l + e;
-                const uint32_t w = st[t];
-                if (w & 2u) {
-                    // The row ended in thread t's workers: the pieces of the threads
-                    // before it, then its own.
-                    const uint32_t n_row = run_n + st[4 * kThreads + t];
-                    loss += (run_s + stf[5 * kThreads + t]) * row_scale(a, n_row);
-                    if (a.n_out) a.n_out[st[3 * kThreads + t]] = n_row;
-                }
-                loss += stf[6 * kThreads + t];
-                if (w & 1u) {
-                    run_n = st[kThreads + t];
-                    run_s = stf[2 * kThreads + t];
-                } else {
-                    run_n = run_n + st[kThreads + t];
-                    run_s = run_s + stf[2 * kThreads + t];
-                }
+                // A row that ended in this thread's workers: the pieces of the
+                // threads before it, then its own.
+                const bool closes = (fw[e] & 2u) != 0u;
+                const uint32_t n_row = run_n + ln4[e];
+                const float term = (run_s + ls4[e]) * row_scale(a, n_row);
+                loss += closes ? term : 0.0f;
+                if (closes && a.n_out) a.n_out[lr4[e]] = n_row;
+                loss += ac4[e];
+                const bool r = (fw[e] & 1u) != 0u;
+                run_n = r ? xn4[e] : run_n + xn4[e];
+                run_s = r ? xs4[e] : run_s + xs4[e];
             }
             loss = wave_sum(loss);
         }
