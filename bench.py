@@ -24,12 +24,15 @@ Options for context measurements (never the headline line's workload):
   --op bnpo|bnpo_fwd|grpo|grpo_fwd|rkl|rkl_fwd   another entry point
   --bs / --seq-len                               another size (inputs drawn on
                                                  the device above 2^24 slots)
-  --copy-mib M                                   a streaming copy of M MiB by our
-                                                 own 128-bit kernel (plain and
-                                                 non-temporal) and by the
-                                                 runtime's copy (the ceiling;
-                                                 also the reference for the
-                                                 traffic counters)
+  --copy-mib M [--copy-variant V] [--copy-grid G]
+                                                 a streaming copy of M MiB by
+                                                 every variant (or variant V,
+                                                 grid G) of our own 128-bit
+                                                 copy kernel, the best of them
+                                                 the ceiling, and by the
+                                                 runtime's copy (also the
+                                                 reference for the traffic
+                                                 counters)
   --read-mib M                                   a streaming read of M MiB
                                                  (the forward-only ceiling)
   --op rkl_logits|rkl_logits_fwd [--rows R --vocab V]
@@ -201,10 +204,14 @@ def pointer_table(rows):
     return np.ascontiguousarray(np.array(rows, dtype=np.uint64))
 
 
+COPY_VARIANTS = {0: "grid-stride x4", 1: "grid-stride x4 nt", 2: "grid-stride x8", 3: "grid-stride x8 nt",
+                 4: "chunked x4", 5: "chunked x4 nt", 6: "chunked x8", 7: "chunked x8 nt"}
+
+
 def copy_ceiling(args, torch):
-    """Streaming copies of M MiB on rotating buffers (>= 1 GiB in all): our own kernel with
-    plain and with non-temporal 128-bit accesses (grid of 2048 workgroups), and the runtime's
-    copy, for comparison."""
+    """Streaming copies of M MiB on rotating buffers (>= 1 GiB in all): every variant of our
+    own 128-bit copy kernel at several grids (the best is the ceiling), and the runtime's copy
+    for comparison."""
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
     lib = bench_lib()
@@ -214,14 +221,21 @@ def copy_ceiling(args, torch):
               torch.empty(nbytes, dtype=torch.uint8, device=dev)) for _ in range(nsets)]
     table = pointer_table([[d.data_ptr(), s.data_ptr()] for s, d in pairs])
     out = {"metric": "streaming copy (read + write) of the same bytes", "bytes_read": nbytes,
-           "bytes_written": nbytes, "steps": args.steps, "rotating_sets": nsets}
-    for nt in (0, 1):
-        _, ms = timed_loop(lambda first, k: lib.rlpl_bench_copy(nsets, table.ctypes.data, nbytes, 0, nt, k, first,
-                                                                 stream.cuda_stream), args.steps, args.warmup,
-                           stream, torch)
-        gbs = 2 * nbytes / (ms * 1e-3) / 1e9
-        out["own_kernel_nt" if nt else "own_kernel"] = {"us_per_launch": round(ms * 1e3, 3), "GBs": round(gbs, 1),
-                                                        "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4)}
+           "bytes_written": nbytes, "steps": args.steps, "rotating_sets": nsets, "own_kernel": {}}
+    best = None
+    variants = COPY_VARIANTS if args.copy_variant is None else {args.copy_variant: COPY_VARIANTS[args.copy_variant]}
+    grids = (1024, 2048, 4096, 8192) if args.copy_grid is None else (args.copy_grid,)
+    for variant, name in variants.items():
+        for grid in grids:
+            _, ms = timed_loop(lambda first, k: lib.rlpl_bench_copy(nsets, table.ctypes.data, nbytes, grid, variant,
+                                                                     k, first, stream.cuda_stream),
+                               args.steps, args.warmup, stream, torch)
+            gbs = 2 * nbytes / (ms * 1e-3) / 1e9
+            out["own_kernel"][f"{name} grid {grid}"] = round(gbs, 1)
+            if best is None or gbs > best[0]:
+                best = (gbs, ms, f"{name} grid {grid}")
+    out["own_kernel_best"] = {"variant": best[2], "us_per_launch": round(best[1] * 1e3, 3), "GBs": round(best[0], 1),
+                              "frac_of_peak": round(best[0] / PEAK_HBM_GBS, 4)}
 
     def fn(d, s):
         d.copy_(s)
@@ -666,6 +680,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-mib", type=float, default=None)
+    ap.add_argument("--copy-variant", type=int, default=None, choices=sorted(COPY_VARIANTS))
+    ap.add_argument("--copy-grid", type=int, default=None)
     ap.add_argument("--read-mib", type=float, default=None)
     ap.add_argument("--noalloc", action="store_true")
     ap.add_argument("--floor", action="store_true")

@@ -166,10 +166,9 @@ struct Shape {
 // coordinating workgroup plus one worker per tile whenever that many
 // workgroups of the one-tile kernel are co-resident (small problems take the
 // narrow lane so that every compute unit gets a tile), else the striding
-// kernel on as many workgroups as are co-resident (all of them workers).  The
-// striding GRPO kernel gives each worker a contiguous run of `per` tiles: per
-// is the fewest tiles per worker that fit the co-resident workgroups, and the
-// grid the runs it takes (so that every worker has one).
+// kernel, each workgroup a worker over a contiguous run of `per` tiles: per is
+// the fewest tiles per worker that fit the co-resident workgroups, and the grid
+// the runs it takes (so that every worker has one).
 int launch_shape(const DeviceInfo* info, int dtype, int mode, int64_t slots, Shape* out) {
     const int64_t large_tile = int64_t(rlpl::kThreads) * rlpl::kVecLarge;
     const int64_t small_tile = int64_t(rlpl::kThreads) * rlpl::kVecSmall;
@@ -183,14 +182,10 @@ int launch_shape(const DeviceInfo* info, int dtype, int mode, int64_t slots, Sha
     } else {
         const int64_t c = cap[rlpl::kShapeStream];
         if (c < 1) return RLPL_ERR_DEVICE;
-        if (mode == kModeGRPO) {
-            const int64_t per = (large_tiles + c - 1) / c;
-            if (per > rlpl::kMaxPer) return RLPL_ERR_SHAPE;
-            *out = {rlpl::kShapeStream, rlpl::kVecLarge, uint32_t(large_tiles), (large_tiles + per - 1) / per,
-                    uint32_t(per)};
-        } else {
-            *out = {rlpl::kShapeStream, rlpl::kVecLarge, uint32_t(large_tiles), large_tiles < c ? large_tiles : c, 1};
-        }
+        const int64_t per = (large_tiles + c - 1) / c;
+        if (mode == kModeGRPO && per > rlpl::kMaxPer) return RLPL_ERR_SHAPE;
+        *out = {rlpl::kShapeStream, rlpl::kVecLarge, uint32_t(large_tiles), (large_tiles + per - 1) / per,
+                uint32_t(per)};
     }
     return RLPL_OK;
 }

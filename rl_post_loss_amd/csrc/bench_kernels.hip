@@ -6,8 +6,9 @@
 //    region measures the GPU rather than the interpreter's per-call cost.
 //  * Reference kernels for the roofline: an empty kernel (the launch floor at
 //    a given grid), and streaming copy and read kernels of our own (128-bit
-//    loads and stores, grid-stride, four 16-byte words in flight per lane),
-//    the ceilings the loss kernels are judged against.
+//    loads and stores; the copy in several variants: four or eight 16-byte
+//    words in flight per lane, grid-stride or one chunk per workgroup, plain
+//    or non-temporal), the ceilings the loss kernels are judged against.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -31,23 +32,53 @@ __device__ __forceinline__ void st(u32x4* p, u32x4 v) {
     else *p = v;
 }
 
-// dst[i] = src[i] for n 16-byte words; NT: non-temporal loads and stores.
-template <bool NT>
+// dst[i] = src[i] for n 16-byte words.  NT: non-temporal loads and stores; U:
+// 16-byte words in flight per lane; CHUNK: each workgroup copies one
+// contiguous chunk (U x 4 KB per step), else the grid strides over the whole
+// range (each lane U words a grid-stride apart).
+template <bool NT, int U, bool CHUNK>
 __global__ void __launch_bounds__(kThreads) copy_kernel(u32x4* __restrict__ dst, const u32x4* __restrict__ src,
                                                        uint64_t n) {
-    const uint64_t stride = uint64_t(gridDim.x) * kThreads;
-    uint64_t i = uint64_t(blockIdx.x) * kThreads + threadIdx.x;
-    for (; i + 3 * stride < n; i += 4 * stride) {
-        const u32x4 a = ld<NT>(src + i);
-        const u32x4 b = ld<NT>(src + i + stride);
-        const u32x4 c = ld<NT>(src + i + 2 * stride);
-        const u32x4 d = ld<NT>(src + i + 3 * stride);
-        st<NT>(dst + i, a);
-        st<NT>(dst + i + stride, b);
-        st<NT>(dst + i + 2 * stride, c);
-        st<NT>(dst + i + 3 * stride, d);
+    if constexpr (CHUNK) {
+        const uint64_t per = (n + gridDim.x - 1) / gridDim.x;
+        const uint64_t b = uint64_t(blockIdx.x) * per;
+        const uint64_t end = b + per < n ? b + per : n;
+        uint64_t i = b + threadIdx.x;
+        for (; i + (U - 1) * kThreads < end; i += U * kThreads) {
+            u32x4 v[U];
+#pragma unroll
+            for (int j = 0; j < U; ++j) v[j] = ld<NT>(src + i + j * kThreads);
+#pragma unroll
+            for (int j = 0; j < U; ++j) st<NT>(dst + i + j * kThreads, v[j]);
+        }
+        for (; i < end; i += kThreads) st<NT>(dst + i, ld<NT>(src + i));
+    } else {
+        const uint64_t stride = uint64_t(gridDim.x) * kThreads;
+        uint64_t i = uint64_t(blockIdx.x) * kThreads + threadIdx.x;
+        for (; i + (U - 1) * stride < n; i += U * stride) {
+            u32x4 v[U];
+#pragma unroll
+            for (int j = 0; j < U; ++j) v[j] = ld<NT>(src + i + j * stride);
+#pragma unroll
+            for (int j = 0; j < U; ++j) st<NT>(dst + i + j * stride, v[j]);
+        }
+        for (; i < n; i += stride) st<NT>(dst + i, ld<NT>(src + i));
     }
-    for (; i < n; i += stride) st<NT>(dst + i, ld<NT>(src + i));
+}
+
+// Copy kernel of a variant: bit 0 non-temporal, bit 1 eight words in flight
+// per lane (else four), bit 2 one contiguous chunk per workgroup.
+const void* copy_variant(int v) {
+    switch (v & 7) {
+    case 0: return reinterpret_cast<const void*>(&copy_kernel<false, 4, false>);
+    case 1: return reinterpret_cast<const void*>(&copy_kernel<true, 4, false>);
+    case 2: return reinterpret_cast<const void*>(&copy_kernel<false, 8, false>);
+    case 3: return reinterpret_cast<const void*>(&copy_kernel<true, 8, false>);
+    case 4: return reinterpret_cast<const void*>(&copy_kernel<false, 4, true>);
+    case 5: return reinterpret_cast<const void*>(&copy_kernel<true, 4, true>);
+    case 6: return reinterpret_cast<const void*>(&copy_kernel<false, 8, true>);
+    default: return reinterpret_cast<const void*>(&copy_kernel<true, 8, true>);
+    }
 }
 
 // XOR of n 16-byte words; each workgroup writes one word to sink[blockIdx.x]
@@ -88,20 +119,22 @@ int rlpl_bench_empty(int grid, int iters, hipStream_t stream) {
 }
 
 // `iters` copies of `bytes` (a multiple of 16), call i on pair (first + i) % n_sets of
-// `pairs` (n_sets x {dst, src} device pointers); grid 0 = 2048 workgroups; nt != 0:
-// non-temporal loads and stores.
-int rlpl_bench_copy(int n_sets, const uint64_t* pairs, uint64_t bytes, int grid, int nt, int iters, int first,
+// `pairs` (n_sets x {dst, src} device pointers); grid 0 = 2048 workgroups; variant:
+// see copy_variant (0..7).
+int rlpl_bench_copy(int n_sets, const uint64_t* pairs, uint64_t bytes, int grid, int variant, int iters, int first,
                     hipStream_t stream) {
-    if (!pairs || n_sets < 1 || bytes % 16) return RLPL_ERR_PARAM;
+    if (!pairs || n_sets < 1 || bytes % 16 || variant < 0 || variant > 7) return RLPL_ERR_PARAM;
+    const void* k = copy_variant(variant);
     for (int i = 0; i < iters; ++i) {
         const uint64_t* p = pairs + 2 * ((first + i) % n_sets);
-        if (nt)
-            hipLaunchKernelGGL(copy_kernel<true>, dim3(grid_for(grid)), dim3(kThreads), 0, stream,
-                               reinterpret_cast<u32x4*>(p[0]), reinterpret_cast<const u32x4*>(p[1]), bytes / 16);
-        else
-            hipLaunchKernelGGL(copy_kernel<false>, dim3(grid_for(grid)), dim3(kThreads), 0, stream,
-                               reinterpret_cast<u32x4*>(p[0]), reinterpret_cast<const u32x4*>(p[1]), bytes / 16);
-        if (hipGetLastError() != hipSuccess) return RLPL_ERR_LAUNCH;
+        u32x4* d = reinterpret_cast<u32x4*>(p[0]);
+        const u32x4* s = reinterpret_cast<const u32x4*>(p[1]);
+        uint64_t n = bytes / 16;
+        void* args[] = {&d, &s, &n};
+        if (hipLaunchKernel(k, dim3(grid_for(grid)), dim3(kThreads), args, 0, stream) != hipSuccess) {
+            (void)hipGetLastError();
+            return RLPL_ERR_LAUNCH;
+        }
     }
     return RLPL_OK;
 }

@@ -15,6 +15,7 @@ namespace rlpl {
 // ----------------------------------------------------------------------------- element types
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
@@ -44,11 +45,21 @@ template <> struct Elem<__bf16> {
 // ----------------------------------------------------------------------------- lane registers
 
 // N dwords moved with the widest aligned accesses (N * 4 bytes aligned to min(N * 4, 16)).
+// NT (N a multiple of 4): non-temporal 16-byte accesses, for data that streams
+// through once (they do not displace what the caches hold).
 template <int N>
 struct Dwords {
     uint32_t w[N];
+    template <bool NT = false>
     __device__ __forceinline__ void load(const void* p) {
-        if constexpr (N == 1) {
+        static_assert(!NT || N % 4 == 0, "non-temporal accesses move 16 bytes");
+        if constexpr (NT) {
+#pragma unroll
+            for (int q = 0; q < N / 4; ++q) {
+                const u32x4 v = __builtin_nontemporal_load(static_cast<const u32x4*>(p) + q);
+                w[4 * q] = v[0]; w[4 * q + 1] = v[1]; w[4 * q + 2] = v[2]; w[4 * q + 3] = v[3];
+            }
+        } else if constexpr (N == 1) {
             w[0] = *static_cast<const uint32_t*>(p);
         } else if constexpr (N == 2) {
             const uint2 v = *static_cast<const uint2*>(p);
@@ -61,8 +72,15 @@ struct Dwords {
             }
         }
     }
+    template <bool NT = false>
     __device__ __forceinline__ void store(void* p) const {
-        if constexpr (N == 1) {
+        static_assert(!NT || N % 4 == 0, "non-temporal accesses move 16 bytes");
+        if constexpr (NT) {
+#pragma unroll
+            for (int q = 0; q < N / 4; ++q)
+                __builtin_nontemporal_store(u32x4{w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]},
+                                            static_cast<u32x4*>(p) + q);
+        } else if constexpr (N == 1) {
             *static_cast<uint32_t*>(p) = w[0];
         } else if constexpr (N == 2) {
             *static_cast<uint2*>(p) = make_uint2(w[0], w[1]);
@@ -81,9 +99,12 @@ struct Plane {
     static constexpr int kWords = VEC * int(sizeof(T)) / 4;
     Dwords<kWords> d;
 
+    // CHECK: the lane may run past `slots` (else the caller knows that its whole
+    // tile is in range, and the test, a branch per lane, is left out).
+    template <bool NT = false, bool CHECK = true>
     __device__ __forceinline__ void load(const T* __restrict__ base, uint32_t s, uint32_t slots) {
-        if (s + VEC <= slots) {
-            d.load(base + s);
+        if (!CHECK || s + VEC <= slots) {
+            d.template load<NT>(base + s);
         } else {
 #pragma unroll
             for (int i = 0; i < kWords; ++i) d.w[i] = 0;
@@ -110,7 +131,7 @@ struct Plane {
 };
 
 // A lane's gradient values, converted to T and stored.
-template <typename T, int VEC>
+template <typename T, int VEC, bool NT = false, bool CHECK = true>
 __device__ __forceinline__ void store_values(T* __restrict__ base, uint32_t s, uint32_t slots,
                                              const float (&v)[VEC]) {
     Dwords<VEC * int(sizeof(T)) / 4> out;
@@ -121,8 +142,8 @@ __device__ __forceinline__ void store_values(T* __restrict__ base, uint32_t s, u
 #pragma unroll
         for (int k = 0; k < VEC; k += 2) out.w[k >> 1] = Elem<T>::pack(v[k], v[k + 1]);
     }
-    if (s + VEC <= slots) {
-        out.store(base + s);
+    if (!CHECK || s + VEC <= slots) {
+        out.template store<NT>(base + s);
     } else {
 #pragma unroll
         for (int k = 0; k < VEC; ++k) {
@@ -243,7 +264,6 @@ __device__ __forceinline__ Tag launch_tag() {
 // just written costs per line read; each is written and read with one 16-byte
 // device-coherent access (cache policy sc1, the bits of an agent-scope atomic).
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kCoherent = 16;   // buffer cache policy: sc1
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t entry_view(const Workspace* ws) {
@@ -311,10 +331,23 @@ __device__ __forceinline__ void poll_entries(__amdgpu_buffer_rsrc_t view, const 
 // a memory round trip.
 struct Limits {
     uint32_t steal, release, giveup;
+    bool steal_set, release_set;   // set by the caller (else the defaults)
+    uint64_t begin;                // the workgroup's start, on the same clock
+    // The limit of a wait that follows this workgroup's own share of the work:
+    // the other workers, doing shares like it, may finish as much later as it
+    // took, so a default limit grows by the time since the start; a limit the
+    // caller set is kept as it is.
+    __device__ __forceinline__ uint32_t steal_now() const {
+        return steal_set ? steal : steal + uint32_t(uint64_t(wall_clock64()) - begin);
+    }
+    __device__ __forceinline__ uint32_t release_now() const {
+        return release_set ? release : release + uint32_t(uint64_t(wall_clock64()) - begin);
+    }
 };
 __device__ __forceinline__ Limits read_limits(const Workspace* ws) {
     const uint4 v = *reinterpret_cast<const uint4*>(&ws->steal_ticks);
-    return Limits{v.x != 0u ? v.x : kStealTicks, v.y != 0u ? v.y : kReleaseTicks, v.z != 0u ? v.z : kGiveUpTicks};
+    return Limits{v.x != 0u ? v.x : kStealTicks, v.y != 0u ? v.y : kReleaseTicks, v.z != 0u ? v.z : kGiveUpTicks,
+                  v.x != 0u, v.y != 0u, uint64_t(wall_clock64())};
 }
 
 // Sum over W items' entries (valid counts, or the float bits of partial

@@ -15,8 +15,10 @@
 //    bytes and its VEC log-probs per plane with 32/64/128-bit loads.  VEC is
 //    16 for large problems and 4 for small ones, so that a small problem
 //    still spreads over every compute unit.
-//  * A grid of G workgroups (at most what the device holds at once):
-//    workgroup 0 coordinates, workers take tiles w, w+(G-1), ...  Per-token
+//  * A grid of G workgroups (at most what the device holds at once): with
+//    one tile per worker, workgroup 0 coordinates and worker w takes tile w;
+//    with more, each workgroup is a worker over a contiguous run of tiles
+//    (non-temporal accesses) and workgroup 0 also coordinates.  Per-token
 //    math is fp32 in registers and branch-free: every slot of a lane is
 //    computed and masked slots are selected away (their values never reach
 //    a result).
@@ -66,9 +68,10 @@ namespace rlpl {
 template <int VEC>
 struct Mask {
     Dwords<VEC / 4> d;
+    template <bool NT = false, bool CHECK = true>
     __device__ __forceinline__ void load(const uint8_t* __restrict__ mask, uint32_t s, uint32_t slots) {
-        if (s + VEC <= slots) {
-            d.load(mask + s);
+        if (!CHECK || s + VEC <= slots) {
+            d.template load<NT>(mask + s);
         } else {
 #pragma unroll
             for (int i = 0; i < VEC / 4; ++i) d.w[i] = 0;
@@ -206,10 +209,10 @@ struct Lane {
 // takes straight-line code; the lane that runs past `slots` (one per launch
 // at most) loads element by element.  No workgroup barrier inside, so the
 // divergent branch is safe.
-template <typename T, int MODE, bool HAS_KL, int VEC, bool SPEC>
+template <typename T, int MODE, bool HAS_KL, int VEC, bool SPEC, bool CHECK = true>
 __device__ __forceinline__ uint32_t load_lane_count(const Args& a, uint32_t s, Lane<T, VEC>& L) {
     const uint32_t slots = uint32_t(a.slots);
-    if (s + VEC <= slots) {
+    if (!CHECK || s + VEC <= slots) {
         L.m.d.load(a.mask + s);
         if constexpr (SPEC) {
             L.lp.d.load(static_cast<const T*>(a.lp) + s);
@@ -235,12 +238,12 @@ __device__ __forceinline__ uint32_t load_lane_count(const Args& a, uint32_t s, L
 
 // Loads one lane's planes once its mask has arrived; skipped when all of the
 // mask's bytes are zero.
-template <typename T, int MODE, bool HAS_KL, int VEC>
+template <typename T, int MODE, bool HAS_KL, int VEC, bool NT = false, bool CHECK = true>
 __device__ __forceinline__ void load_planes(const Args& a, uint32_t s, Lane<T, VEC>& L) {
     if (L.m.any()) {
-        L.lp.load(static_cast<const T*>(a.lp), s, a.slots);
-        if constexpr (MODE != kModeRKL) L.old.load(static_cast<const T*>(a.old), s, a.slots);
-        if constexpr (HAS_KL) L.ref.load(static_cast<const T*>(a.ref), s, a.slots);
+        L.lp.template load<NT, CHECK>(static_cast<const T*>(a.lp), s, a.slots);
+        if constexpr (MODE != kModeRKL) L.old.template load<NT, CHECK>(static_cast<const T*>(a.old), s, a.slots);
+        if constexpr (HAS_KL) L.ref.template load<NT, CHECK>(static_cast<const T*>(a.ref), s, a.slots);
     }
 }
 
@@ -337,13 +340,13 @@ __device__ __forceinline__ float lane_terms(const Args& a, uint32_t s, const Lan
 
 // Stores one lane's gradient, masked slots as +0; SCALE multiplies by `scale`
 // first (the one-tile fwd+bwd path, whose N arrives after the terms are formed).
-template <typename T, int VEC, bool SCALE>
+template <typename T, int VEC, bool SCALE, bool NT = false, bool CHECK = true>
 __device__ __forceinline__ void store_grad(const Args& a, uint32_t s, const Mask<VEC>& m,
                                            const float (&g)[VEC], float scale) {
     float v[VEC];
 #pragma unroll
     for (int k = 0; k < VEC; ++k) v[k] = m.valid(k) ? (SCALE ? g[k] * scale : g[k]) : 0.0f;
-    store_values<T, VEC>(static_cast<T*>(a.grad), s, a.slots, v);
+    store_values<T, VEC, NT, CHECK>(static_cast<T*>(a.grad), s, a.slots, v);
 }
 
 
@@ -374,33 +377,36 @@ __device__ __forceinline__ void write_results(const Args& a, float total, uint32
     }
 }
 
-// Streams worker `worker`'s tiles (worker, worker+G, ... for G workers): per
-// tile, the lane's terms, its count and (WRITE_GRAD) the scaled gradient.  The
-// plane loads wait for the mask, and the next tile's mask is fetched during
-// the current tile.
+// Streams the tiles [t_lo, t_hi) (a worker's run): per tile, the lane's terms,
+// its count and (WRITE_GRAD) the scaled gradient, with non-temporal accesses
+// (the planes and gradient stream through once).  The plane loads wait for the
+// mask, and the next tile's mask is fetched during the current tile.  (Measured
+// A/B: leaving out the per-lane range test on tiles known to be in range, or
+// keeping a second tile's planes in flight, made this loop 4-18 % slower at
+// 2^26 and 2^28 slots.)
 template <typename T, int MODE, bool HAS_KL, bool WRITE_GRAD, int VEC>
-__device__ __forceinline__ void stream_tiles(const Args& a, uint32_t worker, uint32_t G, float& part,
+__device__ __forceinline__ void stream_tiles(const Args& a, uint32_t t_lo, uint32_t t_hi, float& part,
                                              uint32_t& n_lane, float scale, const uint16_t* bits = nullptr,
                                              uint32_t n_bits = 0) {
     constexpr uint32_t kTileV = kThreads * VEC;
     const uint32_t lane_off = threadIdx.x * VEC;
     const uint32_t slots = uint32_t(a.slots);
-    uint32_t tile = worker;
-    // The worker's first n_bits tiles take their masks from `bits` (this lane's
+    // The run's first n_bits tiles take their masks from `bits` (this lane's
     // entry of each, in LDS); later ones read the mask bytes again.
     Mask<VEC> next;
-    if (tile < a.tiles && n_bits == 0) next.load(a.mask, tile * kTileV + lane_off, slots);
-    for (uint32_t j = 0; tile < a.tiles; tile += G, ++j) {
+    if (t_lo < t_hi && n_bits == 0) next.template load<true>(a.mask, t_lo * kTileV + lane_off, slots);
+    uint32_t j = 0;
+    for (uint32_t tile = t_lo; tile < t_hi; ++tile, ++j) {
         const uint32_t s = tile * kTileV + lane_off;
         Lane<T, VEC> L;
         if (j < n_bits) L.m.from_bits(bits[j * kThreads + threadIdx.x]);
         else L.m = next;
-        if (tile + G < a.tiles && j + 1 >= n_bits) next.load(a.mask, (tile + G) * kTileV + lane_off, slots);
-        load_planes<T, MODE, HAS_KL, VEC>(a, s, L);
+        if (tile + 1 < t_hi && j + 1 >= n_bits) next.template load<true>(a.mask, s + kTileV, slots);
+        load_planes<T, MODE, HAS_KL, VEC, true>(a, s, L);
         n_lane += L.m.count();
         float g[VEC];
         part += lane_terms<T, MODE, HAS_KL, VEC>(a, s, L, nullptr, 0, scale, g);
-        if constexpr (WRITE_GRAD) store_grad<T, VEC, false>(a, s, L.m, g, 1.0f);
+        if constexpr (WRITE_GRAD) store_grad<T, VEC, false, true>(a, s, L.m, g, 1.0f);
     }
 }
 
@@ -442,11 +448,18 @@ __global__ void __launch_bounds__(kThreads) loss_kernel(const Args a) {
     const uint32_t W = ONE_TILE ? gridDim.x - 1 : gridDim.x;   // workers
     const uint32_t lane_off = threadIdx.x * VEC;
 
+    // Worker w's run of tiles [w * per, ...) (per = 1 in the one-tile kernels).
+    auto run_lo = [&](uint32_t w) { return ONE_TILE ? w : w * a.per; };
+    auto run_hi = [&](uint32_t w) {
+        if constexpr (ONE_TILE) return w + 1u;
+        const uint32_t hi = w * a.per + a.per;
+        return hi < a.tiles ? hi : a.tiles;
+    };
     // Worker w's valid count and partial loss, computed by the calling workgroup
     // (uniform), exactly as worker w forms its own.
     auto count_of = [&](uint32_t w) -> uint32_t {
         uint32_t n = 0;
-        for (uint32_t tile = w; tile < a.tiles; tile += ONE_TILE ? a.tiles : W) {
+        for (uint32_t tile = run_lo(w); tile < run_hi(w); ++tile) {
             Mask<VEC> m;
             m.load(a.mask, tile * kTileV + lane_off, slots);
             n += m.count();
@@ -463,17 +476,17 @@ __global__ void __launch_bounds__(kThreads) loss_kernel(const Args a) {
             part = lane_terms<T, MODE, HAS_KL, VEC>(a, s, L, nullptr, 0, 1.0f, g);
         } else {
             uint32_t n_unused = 0;
-            stream_tiles<T, MODE, HAS_KL, false, VEC>(a, w, W, part, n_unused, 1.0f);
+            stream_tiles<T, MODE, HAS_KL, false, VEC>(a, run_lo(w), run_hi(w), part, n_unused, 1.0f);
         }
         return block_sum(part, red_f);
     };
     auto nothing = [] {};
     auto gather_counts = [&]() -> uint32_t {
-        return gather<uint32_t>(view, cnt_off, W, tg, lim.steal, list, red_u, count_of, nothing);
+        return gather<uint32_t>(view, cnt_off, W, tg, lim.steal_now(), list, red_u, count_of, nothing);
     };
     // The partials' first reads go out before the release (when there is one) is stored.
     auto gather_partials = [&](auto&& between) -> float {
-        return gather<float>(view, par_off, W, tg, lim.steal, list, red_f, partial_of, between);
+        return gather<float>(view, par_off, W, tg, lim.steal_now(), list, red_f, partial_of, between);
     };
 
     float part = 0.0f;
@@ -503,7 +516,7 @@ __global__ void __launch_bounds__(kThreads) loss_kernel(const Args a) {
             part = lane_terms<T, MODE, HAS_KL, VEC>(a, s, L, nullptr, 0, 1.0f, g);
             const float part_wg = block_sum(part, red_f);
             if (threadIdx.x == kPartialThread) publish(view, par_off(worker), tg, __float_as_uint(part_wg));
-            const uint32_t N = await_release(view, lim.release, tg, word, gather_counts);
+            const uint32_t N = await_release(view, lim.release_now(), tg, word, gather_counts);
             store_grad<T, VEC, true>(a, s, L.m, g, inv_count<MODE>(N));
         } else {
             // Forward only.
@@ -516,19 +529,27 @@ __global__ void __launch_bounds__(kThreads) loss_kernel(const Args a) {
             if (threadIdx.x == kPartialThread) publish(view, par_off(worker), tg, __float_as_uint(part_wg));
         }
     } else {
-        // Every workgroup is a worker striding over the tiles; workgroup 0 also
+        // Every workgroup is a worker over its run of tiles (contiguous runs stream
+        // markedly faster than tiles strided across the grid); workgroup 0 also
         // coordinates (a dedicated coordinator would take one of the co-resident
         // slots, and with it a whole extra tile from some worker's share).
         const uint32_t worker = blockIdx.x;
+        const uint32_t t_lo = run_lo(worker), t_hi = run_hi(worker);
         uint32_t N = 0;
         if constexpr (kExchange) {
             // Count every owned mask (eight loads in flight per lane) and keep the
             // bits of the first kBitTiles tiles, exchange, then stream.
-            uint32_t tile = worker, j = 0;
-            for (; tile + 7 * W < a.tiles; tile += 8 * W, j += 8) {
+            uint32_t tile = t_lo, j = 0;
+            for (; tile + 7 < t_hi; tile += 8, j += 8) {
                 Mask<VEC> m[8];
+                if ((tile + 8) * kTileV <= slots) {
 #pragma unroll
-                for (int u = 0; u < 8; ++u) m[u].load(a.mask, (tile + u * W) * kTileV + lane_off, slots);
+                    for (int u = 0; u < 8; ++u)
+                        m[u].template load<true, false>(a.mask, (tile + u) * kTileV + lane_off, slots);
+                } else {
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) m[u].template load<true>(a.mask, (tile + u) * kTileV + lane_off, slots);
+                }
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
                     const uint32_t b = m[u].bits();
@@ -536,9 +557,9 @@ __global__ void __launch_bounds__(kThreads) loss_kernel(const Args a) {
                     if (j + u < uint32_t(kBitTiles)) mask_bits[(j + u) * kThreads + threadIdx.x] = uint16_t(b);
                 }
             }
-            for (; tile < a.tiles; tile += W, ++j) {
+            for (; tile < t_hi; ++tile, ++j) {
                 Mask<VEC> m;
-                m.load(a.mask, tile * kTileV + lane_off, slots);
+                m.template load<true>(a.mask, tile * kTileV + lane_off, slots);
                 const uint32_t b = m.bits();
                 n_lane += __builtin_popcount(b);
                 if (j < uint32_t(kBitTiles)) mask_bits[j * kThreads + threadIdx.x] = uint16_t(b);
@@ -547,22 +568,22 @@ __global__ void __launch_bounds__(kThreads) loss_kernel(const Args a) {
             const uint32_t n_wg = block_sum(n_lane, red_u);
             if (blockIdx.x == 0) {
                 // The coordinator's own count goes out once its reads of the others' are issued.
-                N = gather<uint32_t>(view, cnt_off, W, tg, lim.steal, list, red_u, count_of, [&] {
+                N = gather<uint32_t>(view, cnt_off, W, tg, lim.steal_now(), list, red_u, count_of, [&] {
                     if (threadIdx.x == kCountThread) publish(view, cnt_off(worker), tg, n_wg);
                 });
                 if (threadIdx.x == kCountThread) publish(view, kReleaseOff, tg, N);
             } else {
                 if (threadIdx.x == kCountThread) publish(view, cnt_off(worker), tg, n_wg);
-                N = await_release(view, lim.release, tg, word, gather_counts);
+                N = await_release(view, lim.release_now(), tg, word, gather_counts);
             }
             uint32_t unused_n = 0;
-            stream_tiles<T, MODE, HAS_KL, true, VEC>(a, worker, W, part, unused_n, inv_count<MODE>(N), mask_bits,
+            stream_tiles<T, MODE, HAS_KL, true, VEC>(a, t_lo, t_hi, part, unused_n, inv_count<MODE>(N), mask_bits,
                                                      n_bits);
             const float part_wg = block_sum(part, red_f);
             if (threadIdx.x == kPartialThread) publish(view, par_off(worker), tg, __float_as_uint(part_wg));
         } else {
             // Forward only: one streaming pass, no exchange.
-            stream_tiles<T, MODE, HAS_KL, false, VEC>(a, worker, W, part, n_lane, 1.0f);
+            stream_tiles<T, MODE, HAS_KL, false, VEC>(a, t_lo, t_hi, part, n_lane, 1.0f);
             const float part_wg = block_sum(part, red_f);
             const uint32_t n_wg = block_sum(n_lane, red_u);
             if (threadIdx.x == kCountThread) publish(view, cnt_off(worker), tg, n_wg);
@@ -848,7 +869,7 @@ __global__ void __launch_bounds__(kThreads) grpo_kernel(const Args a) {
             const Run rv = run_of(a, va + i, kTileV);
             return count_mask(a, b0 > rv.lo ? b0 : rv.lo, b1 < rv.hi ? b1 : rv.hi, red_u);
         };
-        return own + gather<uint32_t>(view, off, vb - va + 1u, tg, lim.steal, list_r, red_u, piece, [] {});
+        return own + gather<uint32_t>(view, off, vb - va + 1u, tg, lim.steal_now(), list_r, red_u, piece, [] {});
     };
     // Publishes a worker's pairs and inner sum (OWN workers, wavefront 1; the
     // last row's pair and the inner sum only when the run ends in another row).
@@ -921,9 +942,15 @@ __global__ void __launch_bounds__(kThreads) grpo_kernel(const Args a) {
         if (!local_rows) {
             for (uint32_t j0 = 0; j0 < nt; j0 += 8u) {
                 Mask<VEC> m[8];
+                if (j0 + 8u <= nt && (t_lo + j0 + 8u) * kTileV <= slots) {
 #pragma unroll
-                for (int u = 0; u < 8; ++u)
-                    if (j0 + u < nt) m[u].load(a.mask, (t_lo + j0 + u) * kTileV + lane_off, slots);
+                    for (int u = 0; u < 8; ++u)
+                        m[u].template load<true, false>(a.mask, (t_lo + j0 + u) * kTileV + lane_off, slots);
+                } else {
+#pragma unroll
+                    for (int u = 0; u < 8; ++u)
+                        if (j0 + u < nt) m[u].template load<true>(a.mask, (t_lo + j0 + u) * kTileV + lane_off, slots);
+                }
                 uint32_t e[8];
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
@@ -957,15 +984,15 @@ __global__ void __launch_bounds__(kThreads) grpo_kernel(const Args a) {
         float v[3] = {0.0f, 0.0f, 0.0f};
         uint32_t cached_r = 0xFFFFFFFFu, cached_n = 0;
         Mask<VEC> next;
-        if (n_bits == 0) next.load(a.mask, t_lo * kTileV + lane_off, slots);
+        if (n_bits == 0) next.template load<true>(a.mask, t_lo * kTileV + lane_off, slots);
         for (uint32_t j = 0; j < nt; ++j) {
             const uint32_t s0 = (t_lo + j) * kTileV, s1 = s0 + kTileV < slots ? s0 + kTileV : slots;
             const uint32_t s = s0 + lane_off;
             Lane<T, VEC> L;
             if (j < n_bits) L.m.from_bits(mask_bits[j * kThreads + threadIdx.x]);
             else L.m = next;
-            if (j + 1u < nt && j + 1u >= n_bits) next.load(a.mask, s0 + kTileV + lane_off, slots);
-            load_planes<T, MODE, HAS_KL, VEC>(a, s, L);
+            if (j + 1u < nt && j + 1u >= n_bits) next.template load<true>(a.mask, s0 + kTileV + lane_off, slots);
+            load_planes<T, MODE, HAS_KL, VEC, true>(a, s, L);
             const uint32_t rf = row_of(a, s0), rl = row_of(a, s1 - 1u), nrows = rl - rf + 1u;
             uint32_t first = 0, last = 0;      // the tile's counts of its first and last row
             if (nrows > 2u) {
@@ -1008,7 +1035,7 @@ __global__ void __launch_bounds__(kThreads) grpo_kernel(const Args a) {
             v[0] += h;
             v[1] += t;
             v[2] += in;
-            if constexpr (OWN && WRITE_GRAD) store_grad<T, VEC, false>(a, s, L.m, g, 1.0f);
+            if constexpr (OWN && WRITE_GRAD) store_grad<T, VEC, false, true>(a, s, L.m, g, 1.0f);
         }
         block_sum_n<3>(v, red_f);
         if (OWN) {
@@ -1077,10 +1104,11 @@ __global__ void __launch_bounds__(kThreads) grpo_kernel(const Args a) {
             poll();
             if (miss) {
                 const uint64_t t0 = wall_clock64();
+                const uint32_t limit = lim.steal_now();
                 for (uint32_t n = 1; miss; ++n) {
                     poll_pause<1>();           // (one workgroup polls: a short pause)
                     poll();
-                    if ((n & 7u) == 0u && uint64_t(wall_clock64()) - t0 > lim.steal) break;
+                    if ((n & 7u) == 0u && uint64_t(wall_clock64()) - t0 > limit) break;
                 }
             }
             // Workers still missing: their values computed here, one at a time.

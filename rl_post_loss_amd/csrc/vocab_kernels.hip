@@ -471,7 +471,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
                 }
                 const uint64_t* w = &ws->slot[grp * C + q].stats[buf][i % 5];
                 uint64_t x = load_relaxed(w);
-                if (uint32_t(x >> 32) != tag && !wait_tagged(w, tag, lim.steal, x))
+                if (uint32_t(x >> 32) != tag && !wait_tagged(w, tag, lim.steal_now(), x))
                     atomicOr(&missing[q >> 5], 1u << (q & 31u));
                 else
                     peer[i] = __uint_as_float(uint32_t(x));
