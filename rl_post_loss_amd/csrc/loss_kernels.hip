@@ -378,12 +378,14 @@ __device__ __forceinline__ void write_results(const Args& a, float total, uint32
 }
 
 // Streams the tiles [t_lo, t_hi) (a worker's run): per tile, the lane's terms,
-// its count and (WRITE_GRAD) the scaled gradient, with non-temporal accesses
-// (the planes and gradient stream through once).  The plane loads wait for the
-// mask, and the next tile's mask is fetched during the current tile.  (Measured
-// A/B: leaving out the per-lane range test on tiles known to be in range, or
-// keeping a second tile's planes in flight, made this loop 4-18 % slower at
-// 2^26 and 2^28 slots.)
+// its count and (WRITE_GRAD) the scaled gradient.  Masks and planes are read
+// with non-temporal loads (they stream through once); the gradient is stored
+// plainly (measured: non-temporal 16-byte stores, each covering every other
+// 16 bytes of a line, wrote 13 % more bytes to HBM and ran 2 % slower).  The
+// plane loads wait for the mask, and the next tile's mask is fetched during
+// the current tile.  (Measured A/B: leaving out the per-lane range test on
+// tiles known to be in range, or keeping a second tile's planes in flight,
+// made this loop 4-18 % slower at 2^26 and 2^28 slots.)
 template <typename T, int MODE, bool HAS_KL, bool WRITE_GRAD, int VEC>
 __device__ __forceinline__ void stream_tiles(const Args& a, uint32_t t_lo, uint32_t t_hi, float& part,
                                              uint32_t& n_lane, float scale, const uint16_t* bits = nullptr,
@@ -406,7 +408,7 @@ __device__ __forceinline__ void stream_tiles(const Args& a, uint32_t t_lo, uint3
         n_lane += L.m.count();
         float g[VEC];
         part += lane_terms<T, MODE, HAS_KL, VEC>(a, s, L, nullptr, 0, scale, g);
-        if constexpr (WRITE_GRAD) store_grad<T, VEC, false, true>(a, s, L.m, g, 1.0f);
+        if constexpr (WRITE_GRAD) store_grad<T, VEC, false>(a, s, L.m, g, 1.0f);
     }
 }
 
@@ -1035,7 +1037,7 @@ __global__ void __launch_bounds__(kThreads) grpo_kernel(const Args a) {
             v[0] += h;
             v[1] += t;
             v[2] += in;
-            if constexpr (OWN && WRITE_GRAD) store_grad<T, VEC, false, true>(a, s, L.m, g, 1.0f);
+            if constexpr (OWN && WRITE_GRAD) store_grad<T, VEC, false>(a, s, L.m, g, 1.0f);
         }
         block_sum_n<3>(v, red_f);
         if (OWN) {
