@@ -313,7 +313,7 @@ int selective_logprob_bwd(const void* hidden, const void* weight, const void* bi
  * tight serving loops, harnesses that forbid hipMalloc): the same kernels,
  * results bit-identical to bnpo_loss, with no workspace argument.  The
  * exchange entries live in the library's own scratch, a static device array
- * of 197,120 bytes per GPU, held until the process ends; this entry point
+ * of 328,192 bytes per GPU, held until the process ends; this entry point
  * never calls hipMalloc, hipFree or an allocating routine.  Its first call on
  * a device finds the scratch's address and enqueues a kernel on `stream` that
  * zero-fills it.  Every bnpo_loss_noalloc call on a GPU shares that GPU's
