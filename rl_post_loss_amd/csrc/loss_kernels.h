@@ -39,6 +39,8 @@ constexpr int kMaxGrid = 4096;              // upper bound on the persistent gri
 // partial computes that value itself from the inputs; a worker that has waited
 // kReleaseTicks for the global count gathers it itself.  Either way the result
 // is bit-identical, so no wait depends on another workgroup being resident.
+// Unless the caller sets them, both limits grow by the time the waiting
+// workgroup has run, since the peers it waits for do shares of work like its own.
 constexpr uint32_t kStealTicks = 5000;      // 50 us
 constexpr uint32_t kReleaseTicks = 20000;   // 200 us
 // The full-vocab kernels' waits for the partial sums of their peers give up
@@ -105,7 +107,7 @@ constexpr size_t kWorkspaceBytes = sizeof(Workspace);
 constexpr size_t kFlagsOffset = offsetof(Workspace, flags);
 constexpr size_t kLimitsOffset = offsetof(Workspace, steal_ticks);
 // Bytes from the workspace's start that the policy-loss kernels address with
-// 16-byte buffer accesses (the header and both entry arrays).
+// 16-byte buffer accesses (the header and the five entry arrays).
 constexpr size_t kEntryViewBytes = offsetof(Workspace, slot);
 
 // Kernel arguments (passed by value).
@@ -121,7 +123,7 @@ struct Args {
     Workspace* ws;
     int64_t slots;         // bs * seq_len  (< 2^31)
     uint32_t tiles;        // ceil(slots / (kThreads * VEC))
-    uint32_t per;          // GRPO: tiles per worker (each worker owns a contiguous run)
+    uint32_t per;          // striding kernels: tiles per worker (each worker owns a contiguous run)
     int32_t seq_len;
     int32_t bs;
     uint32_t row_magic;    // s / seq_len == (s * row_magic) >> row_shift for every s < 2^31

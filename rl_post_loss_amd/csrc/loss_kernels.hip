@@ -22,10 +22,11 @@
 //    math is fp32 in registers and branch-free: every slot of a lane is
 //    computed and masked slots are selected away (their values never reach
 //    a result).
-//  * Reductions: per-lane sums -> wavefront shuffle tree -> LDS across the
-//    4 waves -> one partial per worker in the workspace.  The coordinator
-//    sums the partials in worker order, so the loss is deterministic and
-//    identical between the fwd+bwd and forward-only kernels.
+//  * Reductions: per-lane sums -> wavefront tree on DPP lane moves -> LDS
+//    across the 4 waves -> one partial per worker in the workspace.  The
+//    coordinator sums the partials in worker order, so the loss is
+//    deterministic and identical between the fwd+bwd and forward-only
+//    kernels.
 //  * BNPO / RKL fwd+bwd need the global valid count N before any gradient is
 //    scaled: each worker publishes its count as an entry of the workspace;
 //    the coordinator gathers them and publishes N (the release) that the
@@ -43,9 +44,9 @@
 //    its mask has arrived (the exchange then overlaps the plane loads and the
 //    per-token math) and the tile never leaves registers; with more tiles it
 //    counts its masks first (eight loads in flight) and streams after.
-//  * GRPO needs only each row's own count: a workgroup counts the mask of
-//    every row its tile touches into LDS (no cross-workgroup exchange before
-//    the gradient is scaled), as the card's one-block-per-row design does.
+//  * GRPO needs each row's own count; a row may span several workers' runs.
+//    Its kernel (grpo_kernel below) exchanges only the counts and sums of the
+//    rows that cross a run's ends, and reads each mask byte once.
 //  * Plane loads wait for the mask and are skipped for lanes whose mask
 //    bytes are all zero; when streaming several tiles per workgroup, the next
 //    tile's mask is fetched while the current tile is computed.
