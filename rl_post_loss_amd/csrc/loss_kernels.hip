@@ -831,7 +831,9 @@ __device__ __forceinline__ void grpo_lane(const Args& a, uint32_t s, const Lane<
 // each tile's first and last row, and the mask bits of its first
 // kBitTilesGrpo tiles), then the planes; workgroup 0 then also closes the rows.
 template <typename T, bool HAS_KL, bool WRITE_GRAD, int VEC, bool ONE_TILE>
-__global__ void __launch_bounds__(kThreads) grpo_kernel(const Args a) {
+// (16-bit planes: at most 128 VGPRs, four workgroups per compute unit, which
+// the striding kernel's LDS allows; fp32 planes need more registers.)
+__global__ void __launch_bounds__(kThreads, sizeof(T) == 2 ? 4 : 1) grpo_kernel(const Args a) {
     constexpr int MODE = kModeGRPO;
     constexpr uint32_t kTileV = kThreads * VEC;
     constexpr uint32_t kBits = ONE_TILE ? 1u : uint32_t(kBitTilesGrpo);
@@ -1188,89 +1190,69 @@ __global__ void __launch_bounds__(kThreads) grpo_kernel(const Args a) {
                 }
             }
         }
-        // Each thread's state to LDS (row_lds is free here): the row it passes on
-        // (its pieces; reset unless its workers all lie in a row begun before
-        // them), the row begun before and ended in its workers, its sum.
-        // Thread t's words sit at (t % 4) * 64 + t / 4 of each array, so that
-        // wavefront 0's lane l reads threads 4l .. 4l + 3 without bank conflicts.
-        uint32_t* st = row_lds;
-        float* stf = reinterpret_cast<float*>(row_lds);
-        const uint32_t me = (threadIdx.x & 3u) * 64u + (threadIdx.x >> 2);
-        __syncthreads();
-        st[me] = (have && from_left ? 0u : 1u) | (left ? 2u : 0u);
-        st[kThreads + me] = have ? cur_n : 0u;
-        stf[2 * kThreads + me] = have ? cur_s : 0.0f;
-        st[3 * kThreads + me] = left_row;
-        st[4 * kThreads + me] = left_n;
-        stf[5 * kThreads + me] = left_s;
-        stf[6 * kThreads + me] = acc;
-        __syncthreads();
-        float loss = 0.0f;
-        if (threadIdx.x < 64u) {
-            // Lane l takes threads 4l .. 4l + 3 in order.
-            const uint32_t l = threadIdx.x;
-            // Every word first (the reads go out together), then branch-free folds.
-            uint32_t fw[4], xn4[4], lr4[4], ln4[4];
-            float xs4[4], ls4[4], ac4[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint32_t t = 64u * e + l;
-                fw[e] = st[t];
-                xn4[e] = st[kThreads + t];
-                xs4[e] = stf[2 * kThreads + t];
-                lr4[e] = st[3 * kThreads + t];
-                ln4[e] = st[4 * kThreads + t];
-                ls4[e] = stf[5 * kThreads + t];
-                ac4[e] = stf[6 * kThreads + t];
+        // Carry the rows that run on across threads: a segmented scan over the
+        // threads in worker order.  Thread t's element is the row it passes on
+        // (its pieces; it restarts the carry unless its workers all lie in a row
+        // begun before them); the carry into thread t then completes the row
+        // begun before its workers and ended in them.  Each wavefront scans its
+        // 64 lanes with DPP lane moves (within rows of 16 by 1, 2, 4, 8 lanes,
+        // then across rows), the wavefronts' totals meet in LDS, and each
+        // wavefront folds those of the wavefronts before it into its lanes'
+        // carries: a fixed order, so the loss is deterministic.
+        const uint32_t l = threadIdx.x & 63u, wv = threadIdx.x >> 6;
+        uint32_t f = have && from_left ? 0u : 1u;
+        uint32_t n = have ? cur_n : 0u;
+        float sm = have ? cur_s : 0.0f;
+        auto step = [&](auto ctl, bool take) __attribute__((always_inline)) {
+            constexpr int kCtl = decltype(ctl)::value & 0xFFF, kRows = decltype(ctl)::value >> 12;
+            const uint32_t pf = dpp_move<kCtl, kRows>(f);
+            const uint32_t pn = dpp_move<kCtl, kRows>(n);
+            const float ps = __uint_as_float(dpp_move<kCtl, kRows>(__float_as_uint(sm)));
+            if (take && !f) {
+                n = pn + n;
+                sm = ps + sm;
+                f = pf;
             }
-            uint32_t f = 0, n = 0;             // the lane's fold: whether it restarts, and its run
-            float sm = 0.0f;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const bool r = (fw[e] & 1u) != 0u;
-                f |= r ? 1u : 0u;
-                n = r ? xn4[e] : n + xn4[e];
-                sm = r ? xs4[e] : sm + xs4[e];
-            }
-            // Inclusive segmented scan of the lanes' folds (DPP lane moves: within
-            // rows of 16 by 1, 2, 4, 8 lanes, then across rows), then each lane's
-            // prefix: the scan one lane down.
-            auto step = [&](auto ctl, bool take) __attribute__((always_inline)) {
-                constexpr int kCtl = decltype(ctl)::value & 0xFFF, kRows = decltype(ctl)::value >> 12;
-                const uint32_t pf = dpp_move<kCtl, kRows>(f);
-                const uint32_t pn = dpp_move<kCtl, kRows>(n);
-                const float ps = __uint_as_float(dpp_move<kCtl, kRows>(__float_as_uint(sm)));
-                if (take && !f) {
-                    n = pn + n;
-                    sm = ps + sm;
-                    f = pf;
-                }
-            };
-            step(std::integral_constant<int, 0xF111>{}, (l & 15u) >= 1u);    // row_shr:1
-            step(std::integral_constant<int, 0xF112>{}, (l & 15u) >= 2u);    // row_shr:2
-            step(std::integral_constant<int, 0xF114>{}, (l & 15u) >= 4u);    // row_shr:4
-            step(std::integral_constant<int, 0xF118>{}, (l & 15u) >= 8u);    // row_shr:8
-            step(std::integral_constant<int, 0xA142>{}, (l & 16u) != 0u);    // row_bcast:15
-            step(std::integral_constant<int, 0xC143>{}, (l & 32u) != 0u);    // row_bcast:31
-            uint32_t run_n = dpp_move<0x138>(n);                             // wave_shr:1 (lane 0: 0)
-            float run_s = __uint_as_float(dpp_move<0x138>(__float_as_uint(sm)));
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                // A row that ended in this thread's workers: the pieces of the
-                // threads before it, then its own.
-                const bool closes = (fw[e] & 2u) != 0u;
-                const uint32_t n_row = run_n + ln4[e];
-                const float term = (run_s + ls4[e]) * row_scale(a, n_row);
-                loss += closes ? term : 0.0f;
-                if (closes && a.n_out) a.n_out[lr4[e]] = n_row;
-                loss += ac4[e];
-                const bool r = (fw[e] & 1u) != 0u;
-                run_n = r ? xn4[e] : run_n + xn4[e];
-                run_s = r ? xs4[e] : run_s + xs4[e];
-            }
-            loss = wave_sum(loss);
+        };
+        step(std::integral_constant<int, 0xF111>{}, (l & 15u) >= 1u);    // row_shr:1
+        step(std::integral_constant<int, 0xF112>{}, (l & 15u) >= 2u);    // row_shr:2
+        step(std::integral_constant<int, 0xF114>{}, (l & 15u) >= 4u);    // row_shr:4
+        step(std::integral_constant<int, 0xF118>{}, (l & 15u) >= 8u);    // row_shr:8
+        step(std::integral_constant<int, 0xA142>{}, (l & 16u) != 0u);    // row_bcast:15
+        step(std::integral_constant<int, 0xC143>{}, (l & 32u) != 0u);    // row_bcast:31
+        // the lane's exclusive prefix within its wavefront (lane 0: nothing)
+        uint32_t ef = dpp_move<0x138>(f), en = dpp_move<0x138>(n);       // wave_shr:1
+        float es = __uint_as_float(dpp_move<0x138>(__float_as_uint(sm)));
+        __syncthreads();                       // red_u / red_f are free
+        if (l == 63u) {
+            red_u[2u * wv] = f;
+            red_u[2u * wv + 1u] = n;
+            red_f[wv] = sm;
         }
-        return loss;
+        __syncthreads();
+        uint32_t cf = 0, cn = 0;               // the carry into this wavefront
+        float cs = 0.0f;
+        for (uint32_t v = 0; v < wv; ++v) {
+            const uint32_t vf = red_u[2u * v], vn = red_u[2u * v + 1u];
+            const float vs = red_f[v];
+            cn = vf ? vn : cn + vn;
+            cs = vf ? vs : cs + vs;
+            cf |= vf;
+        }
+        if (!ef) {
+            en = cn + en;
+            es = cs + es;
+        }
+        // A row begun before this thread's workers and ended in them: the carry,
+        // then its own pieces.
+        float loss = acc;
+        if (left) {
+            const uint32_t n_row = en + left_n;
+            loss += (es + left_s) * row_scale(a, n_row);
+            if (a.n_out) a.n_out[left_row] = n_row;
+        }
+        (void)cf;
+        return block_sum(loss, red_f);
     };
 
     if constexpr (ONE_TILE) {
