@@ -362,9 +362,12 @@ def test_grpo_rows_longer_than_a_tile():
 
 # GRPO row counts across tile and worker-run boundaries: rows spanning many
 # tiles, rows that do not divide a tile, a single row over the whole launch,
-# in the one-tile and the striding kernels (each worker owning a run of tiles).
+# in the one-tile and the striding kernels (each worker owning a run of tiles),
+# with 2 to 5 workers per thread of the workgroup that closes the rows (3 x
+# 1,500,000: 1,099 one-tile workers).
 GRPO_ROWS = [(16, 131072, "prefix"), (64, 32768, "random"), (1, 1 << 21, "random"), (5, 4099, "random"),
-             (64, 100000, "prefix"), (2000, 3000, "random"), (1, 6_000_000, "prefix"), (700, 8192, "random")]
+             (64, 100000, "prefix"), (2000, 3000, "random"), (1, 6_000_000, "prefix"), (700, 8192, "random"),
+             (3, 1_500_000, "random")]
 
 
 @pytest.mark.parametrize("bs,T,mask", GRPO_ROWS)

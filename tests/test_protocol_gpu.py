@@ -90,7 +90,7 @@ def test_fallbacks_are_bit_identical(op, shape):
 
 # GRPO rows that cross worker boundaries gather the other workers' pieces of the
 # row: one-tile (long rows; rows not dividing a tile) and striding kernels.
-GRPO_ROW_SHAPES = [(16, 131072), (64, 3000), (64, 100000), (2000, 3000)]
+GRPO_ROW_SHAPES = [(16, 131072), (64, 3000), (64, 100000), (2000, 3000), (3, 1_500_000)]
 
 
 @pytest.mark.parametrize("shape", GRPO_ROW_SHAPES)
