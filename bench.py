@@ -100,7 +100,8 @@ def algorithmic_bytes(op: str, slots: int, valid: int, bs: int, elem: int, has_k
 
 # The sources the per-token loss kernels and their launch are built from (the
 # full-vocab and log-prob kernels live in files of their own).
-LOSS_KERNEL_SOURCES = ("abi.cpp", "device_common.h", "loss_kernels.h", "loss_kernels.hip", "row_divisor.h")
+LOSS_KERNEL_SOURCES = ("abi.cpp", "device_common.h", "loss_kernels.h", "loss_kernels.hip", "loss_kernels_impl.h",
+                       "loss_kernels_bf16.hip", "loss_kernels_f16.hip", "loss_kernels_f32.hip", "row_divisor.h")
 
 
 def kernel_source_hash() -> str:

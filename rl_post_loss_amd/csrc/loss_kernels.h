@@ -136,6 +136,10 @@ struct Args {
 
 // The kernel instantiation for (dtype, mode, KL on/off, gradient on/off, VEC), or NULL.
 const void* pick_kernel(int dtype, int mode, bool has_kl, bool write_grad, int shape);
+// The same for one element type T of the log-probs (float, _Float16, __bf16);
+// instantiated by that dtype's source file.
+template <typename T>
+const void* pick_typed(int mode, bool has_kl, bool write_grad, int shape);
 
 // The library's own scratch (the per-token kernels' part of a workspace), for
 // the entry point that allocates nothing: its device address on the current
