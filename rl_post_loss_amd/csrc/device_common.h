@@ -16,6 +16,7 @@ namespace rlpl {
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
@@ -45,15 +46,20 @@ template <> struct Elem<__bf16> {
 // ----------------------------------------------------------------------------- lane registers
 
 // N dwords moved with the widest aligned accesses (N * 4 bytes aligned to min(N * 4, 16)).
-// NT (N a multiple of 4): non-temporal 16-byte accesses, for data that streams
-// through once (they do not displace what the caches hold).
+// NT: non-temporal accesses (loads of 4, 8 or 16 bytes, stores of 16), for data
+// that streams through once (they do not displace what the caches hold).
 template <int N>
 struct Dwords {
     uint32_t w[N];
     template <bool NT = false>
     __device__ __forceinline__ void load(const void* p) {
-        static_assert(!NT || N % 4 == 0, "non-temporal accesses move 16 bytes");
-        if constexpr (NT) {
+        if constexpr (NT && N == 1) {
+            w[0] = __builtin_nontemporal_load(static_cast<const uint32_t*>(p));
+        } else if constexpr (NT && N == 2) {
+            const u32x2 v = __builtin_nontemporal_load(static_cast<const u32x2*>(p));
+            w[0] = v[0]; w[1] = v[1];
+        } else if constexpr (NT) {
+            static_assert(N % 4 == 0, "non-temporal accesses move 4, 8 or a multiple of 16 bytes");
 #pragma unroll
             for (int q = 0; q < N / 4; ++q) {
                 const u32x4 v = __builtin_nontemporal_load(static_cast<const u32x4*>(p) + q);
@@ -92,8 +98,31 @@ struct Dwords {
     }
 };
 
-// VEC consecutive elements of one plane.  A lane that runs past `slots` (only
-// in the last tile) moves its in-range elements one by one and zero-fills.
+// Where a lane's VEC slots lie.  A lane whose slots would take more than 16
+// bytes of a plane takes them as C = VEC / E chunks of E slots (E = 16 bytes
+// of the plane's elements), chunk c of lane l of a wavefront at
+// wave_start + (c * 64 + l) * E, so that each 16-byte access of a wavefront
+// covers 1 KB of the plane without a gap; with one chunk per lane (E == VEC)
+// the slots are s .. s+VEC-1.  `s` is always the lane's slot in the one-chunk
+// layout (tile * lanes * VEC + lane * VEC): the wavefront covers the same
+// slots either way.  Measured on streaming fwd+bwd BNPO, bf16: a lane of 16
+// consecutive slots (two 16-byte accesses per plane, each wavefront access
+// covering every other 16 bytes of 2 KB) ran 13 % slower at 2^26 slots than
+// two chunks of 8.
+template <typename T, int VEC>
+constexpr int chunk_slots() {
+    return VEC * int(sizeof(T)) > 16 ? 16 / int(sizeof(T)) : VEC;
+}
+template <int VEC, int E>
+__device__ __forceinline__ uint32_t chunk_slot(uint32_t s, int c) {
+    if constexpr (E == VEC) return s;
+    const uint32_t lane = threadIdx.x & 63u;
+    return s - lane * uint32_t(VEC) + (uint32_t(c) * 64u + lane) * uint32_t(E);
+}
+
+// VEC elements of one plane (in E-slot chunks, as above).  A chunk that runs
+// past `slots` (only in the last tile) moves its in-range elements one by one
+// and zero-fills.
 template <typename T, int VEC>
 struct Plane {
     static constexpr int kWords = VEC * int(sizeof(T)) / 4;
@@ -101,18 +130,39 @@ struct Plane {
 
     // CHECK: the lane may run past `slots` (else the caller knows that its whole
     // tile is in range, and the test, a branch per lane, is left out).
-    template <bool NT = false, bool CHECK = true>
+    template <bool NT = false, bool CHECK = true, int E = VEC>
     __device__ __forceinline__ void load(const T* __restrict__ base, uint32_t s, uint32_t slots) {
-        if (!CHECK || s + VEC <= slots) {
-            d.template load<NT>(base + s);
+        if constexpr (E == VEC) {
+            load_run<NT, CHECK, VEC>(base, s, slots, d.w);
+        } else {
+            constexpr int kW = E * int(sizeof(T)) / 4;   // words per chunk (4: 16 bytes)
+#pragma unroll
+            for (int c = 0; c < VEC / E; ++c) {
+                uint32_t w[kW];
+                load_run<NT, CHECK, E>(base, chunk_slot<VEC, E>(s, c), slots, w);
+#pragma unroll
+                for (int i = 0; i < kW; ++i) d.w[c * kW + i] = w[i];
+            }
+        }
+    }
+    // N consecutive elements from slot s into N * sizeof(T) / 4 words.
+    template <bool NT, bool CHECK, int N>
+    static __device__ __forceinline__ void load_run(const T* __restrict__ base, uint32_t s, uint32_t slots,
+                                                    uint32_t (&w)[N * int(sizeof(T)) / 4]) {
+        constexpr int kW = N * int(sizeof(T)) / 4;
+        if (!CHECK || s + N <= slots) {
+            Dwords<kW> v;
+            v.template load<NT>(base + s);
+#pragma unroll
+            for (int i = 0; i < kW; ++i) w[i] = v.w[i];
         } else {
 #pragma unroll
-            for (int i = 0; i < kWords; ++i) d.w[i] = 0;
+            for (int i = 0; i < kW; ++i) w[i] = 0;
 #pragma unroll
-            for (int k = 0; k < VEC; ++k) {
+            for (int k = 0; k < N; ++k) {
                 if (s + k < slots) {
-                    if constexpr (sizeof(T) == 4) d.w[k] = reinterpret_cast<const uint32_t*>(base)[s + k];
-                    else d.w[k >> 1] |= uint32_t(reinterpret_cast<const uint16_t*>(base)[s + k]) << (16 * (k & 1));
+                    if constexpr (sizeof(T) == 4) w[k] = reinterpret_cast<const uint32_t*>(base)[s + k];
+                    else w[k >> 1] |= uint32_t(reinterpret_cast<const uint16_t*>(base)[s + k]) << (16 * (k & 1));
                 }
             }
         }
@@ -130,29 +180,36 @@ struct Plane {
     }
 };
 
-// A lane's gradient values, converted to T and stored.
-template <typename T, int VEC, bool NT = false, bool CHECK = true>
-__device__ __forceinline__ void store_values(T* __restrict__ base, uint32_t s, uint32_t slots,
-                                             const float (&v)[VEC]) {
-    Dwords<VEC * int(sizeof(T)) / 4> out;
+// N consecutive values converted to T and stored from slot s.
+template <typename T, int N, bool NT, bool CHECK>
+__device__ __forceinline__ void store_run(T* __restrict__ base, uint32_t s, uint32_t slots, const float* v) {
+    Dwords<N * int(sizeof(T)) / 4> out;
     if constexpr (sizeof(T) == 4) {
 #pragma unroll
-        for (int k = 0; k < VEC; ++k) out.w[k] = __float_as_uint(v[k]);
+        for (int k = 0; k < N; ++k) out.w[k] = __float_as_uint(v[k]);
     } else {
 #pragma unroll
-        for (int k = 0; k < VEC; k += 2) out.w[k >> 1] = Elem<T>::pack(v[k], v[k + 1]);
+        for (int k = 0; k < N; k += 2) out.w[k >> 1] = Elem<T>::pack(v[k], v[k + 1]);
     }
-    if (!CHECK || s + VEC <= slots) {
+    if (!CHECK || s + N <= slots) {
         out.template store<NT>(base + s);
     } else {
 #pragma unroll
-        for (int k = 0; k < VEC; ++k) {
+        for (int k = 0; k < N; ++k) {
             if (s + k < slots) {
                 if constexpr (sizeof(T) == 4) reinterpret_cast<uint32_t*>(base)[s + k] = out.w[k];
                 else reinterpret_cast<uint16_t*>(base)[s + k] = uint16_t(out.w[k >> 1] >> (16 * (k & 1)));
             }
         }
     }
+}
+
+// A lane's gradient values (in E-slot chunks, as the planes), converted to T and stored.
+template <typename T, int VEC, bool NT = false, bool CHECK = true, int E = VEC>
+__device__ __forceinline__ void store_values(T* __restrict__ base, uint32_t s, uint32_t slots,
+                                             const float (&v)[VEC]) {
+#pragma unroll
+    for (int c = 0; c < VEC / E; ++c) store_run<T, E, NT, CHECK>(base, chunk_slot<VEC, E>(s, c), slots, v + c * E);
 }
 
 // ----------------------------------------------------------------------------- reductions

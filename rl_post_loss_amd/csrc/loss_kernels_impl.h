@@ -70,20 +70,28 @@
 
 namespace rlpl {
 
-// VEC mask bytes of one lane.
+// VEC mask bytes of one lane (in E-slot chunks, as the planes: byte k is the
+// lane's element k).
 template <int VEC>
 struct Mask {
     Dwords<VEC / 4> d;
-    template <bool NT = false, bool CHECK = true>
+    template <bool NT = false, bool CHECK = true, int E = VEC>
     __device__ __forceinline__ void load(const uint8_t* __restrict__ mask, uint32_t s, uint32_t slots) {
-        if (!CHECK || s + VEC <= slots) {
-            d.template load<NT>(mask + s);
-        } else {
 #pragma unroll
-            for (int i = 0; i < VEC / 4; ++i) d.w[i] = 0;
+        for (int c = 0; c < VEC / E; ++c) {
+            const uint32_t sc = chunk_slot<VEC, E>(s, c);
+            if (!CHECK || sc + E <= slots) {
+                Dwords<E / 4> v;
+                v.template load<NT>(mask + sc);
 #pragma unroll
-            for (int k = 0; k < VEC; ++k)
-                if (s + k < slots) d.w[k >> 2] |= uint32_t(mask[s + k]) << (8 * (k & 3));
+                for (int i = 0; i < E / 4; ++i) d.w[c * (E / 4) + i] = v.w[i];
+            } else {
+#pragma unroll
+                for (int i = 0; i < E / 4; ++i) d.w[c * (E / 4) + i] = 0;
+#pragma unroll
+                for (int k = 0; k < E; ++k)
+                    if (sc + k < slots) d.w[c * (E / 4) + (k >> 2)] |= uint32_t(mask[sc + k]) << (8 * (k & 3));
+            }
         }
     }
     __device__ __forceinline__ bool any() const {
@@ -215,9 +223,20 @@ struct Lane {
 // takes straight-line code; the lane that runs past `slots` (one per launch
 // at most) loads element by element.  No workgroup barrier inside, so the
 // divergent branch is safe.
-template <typename T, int MODE, bool HAS_KL, int VEC, bool SPEC, bool CHECK = true>
+template <typename T, int MODE, bool HAS_KL, int VEC, bool SPEC, bool CHECK = true, int E = VEC>
 __device__ __forceinline__ uint32_t load_lane_count(const Args& a, uint32_t s, Lane<T, VEC>& L) {
     const uint32_t slots = uint32_t(a.slots);
+    if constexpr (E != VEC) {
+        // Chunked lanes: each chunk checks its own range.
+        L.m.template load<false, CHECK, E>(a.mask, s, slots);
+        const uint32_t n = L.m.count();
+        if (SPEC || n) {
+            L.lp.template load<false, CHECK, E>(static_cast<const T*>(a.lp), s, slots);
+            if constexpr (MODE != kModeRKL) L.old.template load<false, CHECK, E>(static_cast<const T*>(a.old), s, slots);
+            if constexpr (HAS_KL) L.ref.template load<false, CHECK, E>(static_cast<const T*>(a.ref), s, slots);
+        }
+        return n;
+    }
     if (!CHECK || s + VEC <= slots) {
         L.m.d.load(a.mask + s);
         if constexpr (SPEC) {
@@ -244,12 +263,12 @@ __device__ __forceinline__ uint32_t load_lane_count(const Args& a, uint32_t s, L
 
 // Loads one lane's planes once its mask has arrived; skipped when all of the
 // mask's bytes are zero.
-template <typename T, int MODE, bool HAS_KL, int VEC, bool NT = false, bool CHECK = true>
+template <typename T, int MODE, bool HAS_KL, int VEC, bool NT = false, bool CHECK = true, int E = VEC>
 __device__ __forceinline__ void load_planes(const Args& a, uint32_t s, Lane<T, VEC>& L) {
     if (L.m.any()) {
-        L.lp.template load<NT, CHECK>(static_cast<const T*>(a.lp), s, a.slots);
-        if constexpr (MODE != kModeRKL) L.old.template load<NT, CHECK>(static_cast<const T*>(a.old), s, a.slots);
-        if constexpr (HAS_KL) L.ref.template load<NT, CHECK>(static_cast<const T*>(a.ref), s, a.slots);
+        L.lp.template load<NT, CHECK, E>(static_cast<const T*>(a.lp), s, a.slots);
+        if constexpr (MODE != kModeRKL) L.old.template load<NT, CHECK, E>(static_cast<const T*>(a.old), s, a.slots);
+        if constexpr (HAS_KL) L.ref.template load<NT, CHECK, E>(static_cast<const T*>(a.ref), s, a.slots);
     }
 }
 
@@ -279,48 +298,71 @@ __device__ __forceinline__ Coef row_coef(const Args& a, float A, float row_scale
     return k;
 }
 
-template <typename T, int MODE, bool HAS_KL, int VEC>
+template <typename T, int MODE, bool HAS_KL, int VEC, int E = VEC>
 __device__ __forceinline__ float lane_terms(const Args& a, uint32_t s, const Lane<T, VEC>& L,
                                             const float* row_scale, uint32_t row_base, float gscale,
                                             float (&g)[VEC]) {
+    constexpr int C = VEC / E;   // chunks of E consecutive slots
     float part = 0.0f;
     if (!L.m.any()) return part;
     const uint32_t T_len = uint32_t(a.seq_len);
-    uint32_t r = row_of(a, s);
-    uint32_t t = s - r * T_len;
-    float A = 0.0f, rs = 1.0f;
-    if constexpr (MODE != kModeRKL) A = load_adv<T>(a.adv, r);
-    if constexpr (MODE == kModeGRPO) rs = row_scale[r - row_base];
-    Coef k = row_coef<MODE>(a, A, rs, gscale);
-    if (MODE == kModeRKL || t + VEC <= T_len) {
-        // All VEC slots in one row (always, when seq_len is a multiple of VEC; the
+    uint32_t r[C], t[C];
+    bool one_row = true;         // every chunk within one row
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const uint32_t sc = chunk_slot<VEC, E>(s, c);
+        r[c] = row_of(a, sc);
+        t[c] = sc - r[c] * T_len;
+        one_row = one_row && t[c] + E <= T_len;
+    }
+    if (MODE == kModeRKL || one_row) {
+        // Each chunk in one row (always, when seq_len is a multiple of E; the
         // reverse-KL terms do not depend on the row at all): branch-free.
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) {
-            float c, gi;
-            token_terms<MODE, HAS_KL>(L.lp.get(i), MODE == kModeRKL ? 0.0f : L.old.get(i),
-                                      HAS_KL ? L.ref.get(i) : 0.0f, k, c, gi);
-            if constexpr (MODE == kModeGRPO) { c *= rs; gi *= rs; }
-            part += L.m.valid(i) ? c : 0.0f;
-            g[i] = gi;
+        for (int c = 0; c < C; ++c) {
+            float A = 0.0f, rs = 1.0f;
+            if constexpr (MODE != kModeRKL) A = load_adv<T>(a.adv, r[c]);
+            if constexpr (MODE == kModeGRPO) rs = row_scale[r[c] - row_base];
+            const Coef k = row_coef<MODE>(a, A, rs, gscale);
+#pragma unroll
+            for (int i = c * E; i < c * E + E; ++i) {
+                float cv, gi;
+                token_terms<MODE, HAS_KL>(L.lp.get(i), MODE == kModeRKL ? 0.0f : L.old.get(i),
+                                          HAS_KL ? L.ref.get(i) : 0.0f, k, cv, gi);
+                if constexpr (MODE == kModeGRPO) { cv *= rs; gi *= rs; }
+                part += L.m.valid(i) ? cv : 0.0f;
+                g[i] = gi;
+            }
         }
     } else {
-        // The lane crosses a row boundary: slot by slot, tracking the row.  A rolled
+        // A chunk crosses a row boundary: slot by slot, tracking the row.  A rolled
         // loop keeps one slot's terms live (this path is rare: only lanes that
         // straddle a row end); it always works on slot 0 of a copy of the lane
         // that rotates down one slot per step, and the derivatives rotate in at
-        // the top, so that every register index stays static.
+        // the top, so that every register index stays static.  The row is found
+        // afresh at each chunk's first slot.
         Lane<T, VEC> R = L;
         float out[VEC];
 #pragma unroll
         for (int i = 0; i < VEC; ++i) out[i] = 0.0f;
+        uint32_t rr = 0, tt = 0;
+        float A = 0.0f, rs = 1.0f;
+        Coef k{};
 #pragma unroll 1
         for (int i = 0; i < VEC; ++i) {
-            float c, gi;
+            if ((i & (E - 1)) == 0) {
+                const uint32_t sc = chunk_slot<VEC, E>(s, i / E);
+                rr = row_of(a, sc);
+                tt = sc - rr * T_len;
+                if constexpr (MODE != kModeRKL) A = load_adv<T>(a.adv, rr);
+                if constexpr (MODE == kModeGRPO) rs = row_scale[rr - row_base];
+                k = row_coef<MODE>(a, A, rs, gscale);
+            }
+            float cv, gi;
             token_terms<MODE, HAS_KL>(R.lp.get(0), MODE == kModeRKL ? 0.0f : R.old.get(0),
-                                      HAS_KL ? R.ref.get(0) : 0.0f, k, c, gi);
-            if constexpr (MODE == kModeGRPO) { c *= rs; gi *= rs; }
-            part += R.m.valid(0) ? c : 0.0f;
+                                      HAS_KL ? R.ref.get(0) : 0.0f, k, cv, gi);
+            if constexpr (MODE == kModeGRPO) { cv *= rs; gi *= rs; }
+            part += R.m.valid(0) ? cv : 0.0f;
 #pragma unroll
             for (int j = 0; j + 1 < VEC; ++j) out[j] = out[j + 1];
             out[VEC - 1] = gi;
@@ -328,12 +370,12 @@ __device__ __forceinline__ float lane_terms(const Args& a, uint32_t s, const Lan
             R.lp.rotate();
             if constexpr (MODE != kModeRKL) R.old.rotate();
             if constexpr (HAS_KL) R.ref.rotate();
-            if (++t == T_len) {
-                t = 0;
-                ++r;
-                if (r < uint32_t(a.bs)) {
-                    if constexpr (MODE != kModeRKL) A = load_adv<T>(a.adv, r);
-                    if constexpr (MODE == kModeGRPO) rs = row_scale[r - row_base];
+            if (++tt == T_len) {
+                tt = 0;
+                ++rr;
+                if (rr < uint32_t(a.bs)) {
+                    if constexpr (MODE != kModeRKL) A = load_adv<T>(a.adv, rr);
+                    if constexpr (MODE == kModeGRPO) rs = row_scale[rr - row_base];
                     k = row_coef<MODE>(a, A, rs, gscale);
                 }
             }
@@ -346,13 +388,13 @@ __device__ __forceinline__ float lane_terms(const Args& a, uint32_t s, const Lan
 
 // Stores one lane's gradient, masked slots as +0; SCALE multiplies by `scale`
 // first (the one-tile fwd+bwd path, whose N arrives after the terms are formed).
-template <typename T, int VEC, bool SCALE, bool NT = false, bool CHECK = true>
+template <typename T, int VEC, bool SCALE, bool NT = false, bool CHECK = true, int E = VEC>
 __device__ __forceinline__ void store_grad(const Args& a, uint32_t s, const Mask<VEC>& m,
                                            const float (&g)[VEC], float scale) {
     float v[VEC];
 #pragma unroll
     for (int k = 0; k < VEC; ++k) v[k] = m.valid(k) ? (SCALE ? g[k] * scale : g[k]) : 0.0f;
-    store_values<T, VEC, NT, CHECK>(static_cast<T*>(a.grad), s, a.slots, v);
+    store_values<T, VEC, NT, CHECK, E>(static_cast<T*>(a.grad), s, a.slots, v);
 }
 
 
@@ -383,6 +425,24 @@ __device__ __forceinline__ void write_results(const Args& a, float total, uint32
     }
 }
 
+// The mask bits of this lane's chunks (bit k = the lane's element k), from
+// per-thread mask bits in the one-chunk layout (grp[t] = bits of slots
+// t*VEC .. t*VEC+VEC-1 of the tile, in LDS): each chunk lies inside one
+// thread's VEC slots, of a thread of the same wavefront.
+template <int VEC, int E>
+__device__ __forceinline__ uint32_t chunk_bits(const uint16_t* grp) {
+    if constexpr (E == VEC) return grp[threadIdx.x];
+    const uint32_t w = threadIdx.x >> 6, l = threadIdx.x & 63u;
+    uint32_t b = 0;
+#pragma unroll
+    for (int c = 0; c < VEC / E; ++c) {
+        const uint32_t rel = (uint32_t(c) * 64u + l) * uint32_t(E);   // the chunk's slot in the wavefront's span
+        const uint32_t g = 64u * w + rel / uint32_t(VEC), off = rel % uint32_t(VEC);
+        b |= ((uint32_t(grp[g]) >> off) & ((1u << E) - 1u)) << (c * E);
+    }
+    return b;
+}
+
 // Streams the tiles [t_lo, t_hi) (a worker's run): per tile, the lane's terms,
 // its count and (WRITE_GRAD) the scaled gradient.  Masks and planes are read
 // with non-temporal loads (they stream through once); the gradient is stored
@@ -392,29 +452,34 @@ __device__ __forceinline__ void write_results(const Args& a, float total, uint32
 // the current tile.  (Measured A/B: leaving out the per-lane range test on
 // tiles known to be in range, or keeping a second tile's planes in flight,
 // made this loop 4-18 % slower at 2^26 and 2^28 slots.)
+// The counting pass reads the mask in the one-chunk layout (16 bytes per lane;
+// 8-byte accesses per chunk made that pass slower) and keeps per-thread bits,
+// which reach the lanes' chunks through chunk_bits(); tiles past the kept
+// bits read their mask bytes again, per chunk.
 template <typename T, int MODE, bool HAS_KL, bool WRITE_GRAD, int VEC>
 __device__ __forceinline__ void stream_tiles(const Args& a, uint32_t t_lo, uint32_t t_hi, float& part,
                                              uint32_t& n_lane, float scale, const uint16_t* bits = nullptr,
                                              uint32_t n_bits = 0) {
     constexpr uint32_t kTileV = kThreads * VEC;
+    constexpr int E = chunk_slots<T, VEC>();
     const uint32_t lane_off = threadIdx.x * VEC;
     const uint32_t slots = uint32_t(a.slots);
-    // The run's first n_bits tiles take their masks from `bits` (this lane's
+    // The run's first n_bits tiles take their masks from `bits` (each thread's
     // entry of each, in LDS); later ones read the mask bytes again.
     Mask<VEC> next;
-    if (t_lo < t_hi && n_bits == 0) next.template load<true>(a.mask, t_lo * kTileV + lane_off, slots);
+    if (t_lo < t_hi && n_bits == 0) next.template load<true, true, E>(a.mask, t_lo * kTileV + lane_off, slots);
     uint32_t j = 0;
     for (uint32_t tile = t_lo; tile < t_hi; ++tile, ++j) {
         const uint32_t s = tile * kTileV + lane_off;
         Lane<T, VEC> L;
-        if (j < n_bits) L.m.from_bits(bits[j * kThreads + threadIdx.x]);
+        if (j < n_bits) L.m.from_bits(chunk_bits<VEC, E>(bits + j * kThreads));
         else L.m = next;
-        if (tile + 1 < t_hi && j + 1 >= n_bits) next.template load<true>(a.mask, s + kTileV, slots);
-        load_planes<T, MODE, HAS_KL, VEC, true>(a, s, L);
+        if (tile + 1 < t_hi && j + 1 >= n_bits) next.template load<true, true, E>(a.mask, s + kTileV, slots);
+        load_planes<T, MODE, HAS_KL, VEC, true, true, E>(a, s, L);
         n_lane += L.m.count();
         float g[VEC];
-        part += lane_terms<T, MODE, HAS_KL, VEC>(a, s, L, nullptr, 0, scale, g);
-        if constexpr (WRITE_GRAD) store_grad<T, VEC, false>(a, s, L.m, g, 1.0f);
+        part += lane_terms<T, MODE, HAS_KL, VEC, E>(a, s, L, nullptr, 0, scale, g);
+        if constexpr (WRITE_GRAD) store_grad<T, VEC, false, false, true, E>(a, s, L.m, g, 1.0f);
     }
 }
 
@@ -435,6 +500,7 @@ __device__ __forceinline__ void stream_tiles(const Args& a, uint32_t t_lo, uint3
 template <typename T, int MODE, bool HAS_KL, bool WRITE_GRAD, int VEC, bool ONE_TILE>
 __global__ void __launch_bounds__(kThreads) loss_kernel(const Args a) {
     constexpr uint32_t kTileV = kThreads * VEC;
+    constexpr int E = chunk_slots<T, VEC>();   // slots per chunk of a lane
     __shared__ float red_f[kWaves];
     __shared__ uint32_t red_u[kWaves];
     __shared__ uint32_t word[2];
@@ -479,9 +545,9 @@ __global__ void __launch_bounds__(kThreads) loss_kernel(const Args a) {
         if constexpr (ONE_TILE) {
             const uint32_t s = w * kTileV + lane_off;
             Lane<T, VEC> L;
-            (void)load_lane_count<T, MODE, HAS_KL, VEC, false>(a, s, L);
+            (void)load_lane_count<T, MODE, HAS_KL, VEC, false, true, E>(a, s, L);
             float g[VEC];
-            part = lane_terms<T, MODE, HAS_KL, VEC>(a, s, L, nullptr, 0, 1.0f, g);
+            part = lane_terms<T, MODE, HAS_KL, VEC, E>(a, s, L, nullptr, 0, 1.0f, g);
         } else {
             uint32_t n_unused = 0;
             stream_tiles<T, MODE, HAS_KL, false, VEC>(a, run_lo(w), run_hi(w), part, n_unused, 1.0f);
@@ -518,19 +584,19 @@ __global__ void __launch_bounds__(kThreads) loss_kernel(const Args a) {
             // published as soon as the mask (loaded first) has arrived, so the exchange
             // runs while the planes are still arriving and being computed on; the
             // partial loss follows.
-            const uint32_t n_wg = block_sum(load_lane_count<T, MODE, HAS_KL, VEC, false>(a, s, L), red_u);
+            const uint32_t n_wg = block_sum(load_lane_count<T, MODE, HAS_KL, VEC, false, true, E>(a, s, L), red_u);
             if (threadIdx.x == kCountThread) publish(view, cnt_off(worker), tg, n_wg);
             float g[VEC];
-            part = lane_terms<T, MODE, HAS_KL, VEC>(a, s, L, nullptr, 0, 1.0f, g);
+            part = lane_terms<T, MODE, HAS_KL, VEC, E>(a, s, L, nullptr, 0, 1.0f, g);
             const float part_wg = block_sum(part, red_f);
             if (threadIdx.x == kPartialThread) publish(view, par_off(worker), tg, __float_as_uint(part_wg));
             const uint32_t N = await_release(view, lim.release_now(), tg, word, gather_counts);
-            store_grad<T, VEC, true>(a, s, L.m, g, inv_count<MODE>(N));
+            store_grad<T, VEC, true, false, true, E>(a, s, L.m, g, inv_count<MODE>(N));
         } else {
             // Forward only.
-            n_lane = load_lane_count<T, MODE, HAS_KL, VEC, VEC == kVecSmall>(a, s, L);
+            n_lane = load_lane_count<T, MODE, HAS_KL, VEC, VEC == kVecSmall, true, E>(a, s, L);
             float g[VEC];
-            part = lane_terms<T, MODE, HAS_KL, VEC>(a, s, L, nullptr, 0, 1.0f, g);
+            part = lane_terms<T, MODE, HAS_KL, VEC, E>(a, s, L, nullptr, 0, 1.0f, g);
             const float part_wg = block_sum(part, red_f);
             const uint32_t n_wg = block_sum(n_lane, red_u);
             if (threadIdx.x == kCountThread) publish(view, cnt_off(worker), tg, n_wg);
