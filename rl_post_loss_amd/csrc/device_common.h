@@ -105,10 +105,10 @@ struct Dwords {
 // covers 1 KB of the plane without a gap; with one chunk per lane (E == VEC)
 // the slots are s .. s+VEC-1.  `s` is always the lane's slot in the one-chunk
 // layout (tile * lanes * VEC + lane * VEC): the wavefront covers the same
-// slots either way.  Measured on streaming fwd+bwd BNPO, bf16: a lane of 16
-// consecutive slots (two 16-byte accesses per plane, each wavefront access
-// covering every other 16 bytes of 2 KB) ran 13 % slower at 2^26 slots than
-// two chunks of 8.
+// slots either way.  Measured on fwd+bwd BNPO, bf16: a lane of 16 consecutive
+// slots (two 16-byte accesses per plane, each wavefront access covering every
+// other 16 bytes of 2 KB) ran 8 % slower at 2^22, 2^26 and 2^27 slots than two
+// chunks of 8.
 template <typename T, int VEC>
 constexpr int chunk_slots() {
     return VEC * int(sizeof(T)) > 16 ? 16 / int(sizeof(T)) : VEC;

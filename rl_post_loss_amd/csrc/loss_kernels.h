@@ -16,10 +16,11 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kVecLarge = 16;
 constexpr int kVecSmall = 4;
 // Tiles per worker whose mask bits the striding fwd+bwd kernels keep in LDS
-// (512 B per tile): 56 (28 KB) for BNPO and 40 (20 KB) for reverse-KL, which
+// (512 B per tile): 60 (30 KB) for BNPO and 40 (20 KB) for reverse-KL, which
 // leaves each kernel's register-bound occupancy (4 and 6 workgroups per CU)
-// within the 128 KB of LDS per CU that the host budgets.
-constexpr int kBitTilesPolicy = 56;
+// within the 128 KB of LDS per CU that the host budgets.  Tiles past them
+// read their mask bytes a second time (slower per tile than kept bits).
+constexpr int kBitTilesPolicy = 60;
 constexpr int kBitTilesRkl = 40;
 // GRPO's striding kernels own contiguous runs of at most kMaxPer tiles per
 // worker (the host sizes the grid so), keep one word per owned tile in LDS
