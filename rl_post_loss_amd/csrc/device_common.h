@@ -135,15 +135,18 @@ struct Plane {
         if constexpr (E == VEC) {
             load_run<NT, CHECK, VEC>(base, s, slots, d.w);
         } else {
-            constexpr int kW = E * int(sizeof(T)) / 4;   // words per chunk (4: 16 bytes)
 #pragma unroll
-            for (int c = 0; c < VEC / E; ++c) {
-                uint32_t w[kW];
-                load_run<NT, CHECK, E>(base, chunk_slot<VEC, E>(s, c), slots, w);
-#pragma unroll
-                for (int i = 0; i < kW; ++i) d.w[c * kW + i] = w[i];
-            }
+            for (int c = 0; c < VEC / E; ++c) load_chunk<NT, CHECK, E>(base, s, slots, c);
         }
+    }
+    // Chunk c of the lane (E slots) only.
+    template <bool NT, bool CHECK, int E>
+    __device__ __forceinline__ void load_chunk(const T* __restrict__ base, uint32_t s, uint32_t slots, int c) {
+        constexpr int kW = E * int(sizeof(T)) / 4;   // words per chunk (4: 16 bytes)
+        uint32_t w[kW];
+        load_run<NT, CHECK, E>(base, chunk_slot<VEC, E>(s, c), slots, w);
+#pragma unroll
+        for (int i = 0; i < kW; ++i) d.w[c * kW + i] = w[i];
     }
     // N consecutive elements from slot s into N * sizeof(T) / 4 words.
     template <bool NT, bool CHECK, int N>

@@ -100,6 +100,14 @@ struct Mask {
         for (int i = 0; i < VEC / 4; ++i) o |= d.w[i];
         return o != 0;
     }
+    // Whether chunk c (E slots) has a valid slot.
+    template <int E>
+    __device__ __forceinline__ bool any_in(int c) const {
+        uint32_t o = 0;
+#pragma unroll
+        for (int i = 0; i < E / 4; ++i) o |= d.w[c * (E / 4) + i];
+        return o != 0;
+    }
     __device__ __forceinline__ bool valid(int k) const { return ((d.w[k >> 2] >> (8 * (k & 3))) & 0xFFu) != 0; }
     // Moves every byte down one position (byte k+1 becomes k; the last becomes 0).
     __device__ __forceinline__ void rotate() {
@@ -227,15 +235,19 @@ template <typename T, int MODE, bool HAS_KL, int VEC, bool SPEC, bool CHECK = tr
 __device__ __forceinline__ uint32_t load_lane_count(const Args& a, uint32_t s, Lane<T, VEC>& L) {
     const uint32_t slots = uint32_t(a.slots);
     if constexpr (E != VEC) {
-        // Chunked lanes: each chunk checks its own range.
+        // Chunked lanes: each chunk checks its own range, and loads its planes
+        // only where it has a valid slot.
         L.m.template load<false, CHECK, E>(a.mask, s, slots);
-        const uint32_t n = L.m.count();
-        if (SPEC || n) {
-            L.lp.template load<false, CHECK, E>(static_cast<const T*>(a.lp), s, slots);
-            if constexpr (MODE != kModeRKL) L.old.template load<false, CHECK, E>(static_cast<const T*>(a.old), s, slots);
-            if constexpr (HAS_KL) L.ref.template load<false, CHECK, E>(static_cast<const T*>(a.ref), s, slots);
+#pragma unroll
+        for (int c = 0; c < VEC / E; ++c) {
+            if (SPEC || L.m.template any_in<E>(c)) {
+                L.lp.template load_chunk<false, CHECK, E>(static_cast<const T*>(a.lp), s, slots, c);
+                if constexpr (MODE != kModeRKL)
+                    L.old.template load_chunk<false, CHECK, E>(static_cast<const T*>(a.old), s, slots, c);
+                if constexpr (HAS_KL) L.ref.template load_chunk<false, CHECK, E>(static_cast<const T*>(a.ref), s, slots, c);
+            }
         }
-        return n;
+        return L.m.count();
     }
     if (!CHECK || s + VEC <= slots) {
         L.m.d.load(a.mask + s);
@@ -261,14 +273,21 @@ __device__ __forceinline__ uint32_t load_lane_count(const Args& a, uint32_t s, L
     return L.m.count();
 }
 
-// Loads one lane's planes once its mask has arrived; skipped when all of the
-// mask's bytes are zero.
+// Loads one lane's planes once its mask has arrived, chunk by chunk; a chunk
+// whose mask bytes are all zero loads nothing (its registers are never used
+// for a valid slot).
 template <typename T, int MODE, bool HAS_KL, int VEC, bool NT = false, bool CHECK = true, int E = VEC>
 __device__ __forceinline__ void load_planes(const Args& a, uint32_t s, Lane<T, VEC>& L) {
-    if (L.m.any()) {
-        L.lp.template load<NT, CHECK, E>(static_cast<const T*>(a.lp), s, a.slots);
-        if constexpr (MODE != kModeRKL) L.old.template load<NT, CHECK, E>(static_cast<const T*>(a.old), s, a.slots);
-        if constexpr (HAS_KL) L.ref.template load<NT, CHECK, E>(static_cast<const T*>(a.ref), s, a.slots);
+#pragma unroll
+    for (int c = 0; c < VEC / E; ++c) {
+        // Per chunk (a lane's chunks are a wavefront access apart): the row end
+        // of a prefix mask leaves one chunk of a lane valid and the other not.
+        if (L.m.template any_in<E>(c)) {
+            L.lp.template load_chunk<NT, CHECK, E>(static_cast<const T*>(a.lp), s, a.slots, c);
+            if constexpr (MODE != kModeRKL)
+                L.old.template load_chunk<NT, CHECK, E>(static_cast<const T*>(a.old), s, a.slots, c);
+            if constexpr (HAS_KL) L.ref.template load_chunk<NT, CHECK, E>(static_cast<const T*>(a.ref), s, a.slots, c);
+        }
     }
 }
 
