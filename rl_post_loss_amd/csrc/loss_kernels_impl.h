@@ -777,24 +777,45 @@ __device__ __forceinline__ uint32_t lane_ends(const Args& a, uint32_t s, uint32_
     return v;
 }
 
+// The same for a lane of E-slot chunks (`bits` in the lane's element order):
+// the sum of each chunk's counts.
+template <int VEC, int E>
+__device__ __forceinline__ uint32_t lane_ends_chunked(const Args& a, uint32_t s, uint32_t bits, uint32_t rf,
+                                                      uint32_t rl) {
+    if constexpr (E == VEC) {
+        return lane_ends<VEC>(a, s, bits, rf, rl);
+    } else {
+        uint32_t v = 0;
+#pragma unroll
+        for (int c = 0; c < VEC / E; ++c)
+            v += lane_ends<E>(a, chunk_slot<VEC, E>(s, c), (bits >> (c * E)) & ((1u << E) - 1u), rf, rl);
+        return v;
+    }
+}
+
 // The tile's valid count of each row it touches (rows rf .. rf + nrows - 1)
-// into cnt[row - rf] (LDS), from every lane's mask bits.
-template <int VEC>
+// into cnt[row - rf] (LDS), from every lane's mask bits (E-slot chunks).
+template <int VEC, int E = VEC>
 __device__ __forceinline__ void tile_rows(const Args& a, uint32_t s, uint32_t bits, uint32_t rf, uint32_t nrows,
                                           uint32_t* cnt) {
     __syncthreads();                           // cnt[] may still hold scales being read
     for (uint32_t i = threadIdx.x; i < nrows; i += kThreads) cnt[i] = 0;
     __syncthreads();
     const uint32_t T = uint32_t(a.seq_len);
-    uint32_t r = row_of(a, s), e = (r + 1u) * T, pos = s;
-    while (bits) {
-        const uint32_t k = e - pos < uint32_t(VEC) ? e - pos : uint32_t(VEC);   // slots of row r from pos
-        const uint32_t c = __builtin_popcount(bits & ((1u << k) - 1u));
-        if (c) atomicAdd(&cnt[r - rf], c);
-        bits = k < uint32_t(VEC) ? bits >> k : 0u;
-        pos += k;
-        ++r;
-        e += T;
+#pragma unroll
+    for (int ch = 0; ch < VEC / E; ++ch) {
+        uint32_t b = E == VEC ? bits : (bits >> (ch * E)) & ((1u << E) - 1u);
+        uint32_t pos = chunk_slot<VEC, E>(s, ch);
+        uint32_t r = row_of(a, pos), e = (r + 1u) * T;
+        while (b) {
+            const uint32_t k = e - pos < uint32_t(E) ? e - pos : uint32_t(E);   // slots of row r from pos
+            const uint32_t c = __builtin_popcount(b & ((1u << k) - 1u));
+            if (c) atomicAdd(&cnt[r - rf], c);
+            b = k < uint32_t(E) ? b >> k : 0u;
+            pos += k;
+            ++r;
+            e += T;
+        }
     }
     __syncthreads();
 }
@@ -818,14 +839,16 @@ __device__ __forceinline__ void row_scales(const Args& a, uint32_t s0, uint32_t 
     __syncthreads();
 }
 
-// GRPO terms of one lane (slots s .. s+VEC-1): slots of the run's first row r0
-// add c to h and of its last row r1 (!= r0) to t, unscaled; those of any other
-// row add c * scale[row - rf] to `in`.  g: each slot's derivative times its
-// row's scale, with g0 and g1 standing for those of r0 and r1.
-template <typename T, bool HAS_KL, int VEC>
+// GRPO terms of one lane (slots s .. s+VEC-1, or its E-slot chunks): slots of
+// the run's first row r0 add c to h and of its last row r1 (!= r0) to t,
+// unscaled; those of any other row add c * scale[row - rf] to `in`.  g: each
+// slot's derivative times its row's scale, with g0 and g1 standing for those
+// of r0 and r1.
+template <typename T, bool HAS_KL, int VEC, int E = VEC>
 __device__ __forceinline__ void grpo_lane(const Args& a, uint32_t s, const Lane<T, VEC>& L, uint32_t r0, uint32_t r1,
                                           float g0, float g1, const float* scale, uint32_t rf, float& h, float& t,
                                           float& in, float (&g)[VEC]) {
+    constexpr int C = VEC / E;   // chunks of E consecutive slots
     // Sums in locals, each class added branch-free (an if-chain over the three
     // outputs becomes an indexed array in private memory).
     float sh = 0.0f, st = 0.0f, si = 0.0f;
@@ -835,8 +858,6 @@ __device__ __forceinline__ void grpo_lane(const Args& a, uint32_t s, const Lane<
     if (!L.m.any()) return;                   // every slot masked: g is never stored
     const uint32_t TL = uint32_t(a.seq_len);
     const uint32_t bs = uint32_t(a.bs);
-    uint32_t r = row_of(a, s);
-    uint32_t pos = s - r * TL;
     // Row r's class (0: r0, 1: r1, 2: other), gradient scale and term scale.
     auto info = [&](uint32_t row, int& cls, float& gs, float& cs) __attribute__((always_inline)) {
         if (row == r0) {
@@ -858,37 +879,60 @@ __device__ __forceinline__ void grpo_lane(const Args& a, uint32_t s, const Lane<
         st += cls == 1 ? sum : 0.0f;
         si += cls == 2 ? sum * cs : 0.0f;
     };
-    int cls_a;
-    float gs_a, cs_a;
-    info(r, cls_a, gs_a, cs_a);
-    const Coef ka = row_coef<kModeGRPO>(a, load_adv<T>(a.adv, r), 1.0f, 1.0f);
-    if (pos + VEC <= TL) {
-        // All the lane's slots in one row (always, when seq_len is a multiple of
-        // VEC): straight-line code, the row's sum scaled once.
-        float sum = 0.0f;
+    uint32_t rc[C], pc[C];
+    bool one_row = true;                      // every chunk within one row
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) {
-            float c, gi;
-            token_terms<kModeGRPO, HAS_KL>(L.lp.get(i), L.old.get(i), HAS_KL ? L.ref.get(i) : 0.0f, ka, c, gi);
-            sum += L.m.valid(i) ? c : 0.0f;
-            g[i] = gi * gs_a;
+    for (int c = 0; c < C; ++c) {
+        const uint32_t sc = chunk_slot<VEC, E>(s, c);
+        rc[c] = row_of(a, sc);
+        pc[c] = sc - rc[c] * TL;
+        one_row = one_row && pc[c] + E <= TL;
+    }
+    if (one_row) {
+        // Each chunk's slots in one row (always, when seq_len is a multiple of
+        // E): straight-line code, each chunk's sum scaled once.
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            int cls;
+            float gs, cs;
+            info(rc[c], cls, gs, cs);
+            const Coef k = row_coef<kModeGRPO>(a, load_adv<T>(a.adv, rc[c]), 1.0f, 1.0f);
+            float sum = 0.0f;
+#pragma unroll
+            for (int i = c * E; i < c * E + E; ++i) {
+                float cv, gi;
+                token_terms<kModeGRPO, HAS_KL>(L.lp.get(i), L.old.get(i), HAS_KL ? L.ref.get(i) : 0.0f, k, cv, gi);
+                sum += L.m.valid(i) ? cv : 0.0f;
+                g[i] = gi * gs;
+            }
+            add(cls, sum, cs);
         }
-        add(cls_a, sum, cs_a);
         h = sh;
         t = st;
         in = si;
         return;
     }
-    // The lane crosses a row boundary (rare: one lane per row end): slot by slot
+    // A chunk crosses a row boundary (rare: one lane per row end): slot by slot
     // on a copy of the lane that rotates down one slot per step (static register
-    // indices, one slot's terms live), tracking the row.
+    // indices, one slot's terms live), tracking the row, found afresh at each
+    // chunk's first slot.
     Lane<T, VEC> R = L;
-    Coef k = ka;
+    Coef k{};
+    int cls_a = 0;
+    float gs_a = 0.0f, cs_a = 0.0f;
+    uint32_t r = 0, pos = 0;
     float out[VEC];
 #pragma unroll
     for (int i = 0; i < VEC; ++i) out[i] = 0.0f;
 #pragma unroll 1
     for (int i = 0; i < VEC; ++i) {
+        if ((i & (E - 1)) == 0) {
+            const uint32_t sc = chunk_slot<VEC, E>(s, i / E);
+            r = row_of(a, sc);
+            pos = sc - r * TL;
+            k = row_coef<kModeGRPO>(a, load_adv<T>(a.adv, r), 1.0f, 1.0f);
+            info(r, cls_a, gs_a, cs_a);
+        }
         float c, gi;
         token_terms<kModeGRPO, HAS_KL>(R.lp.get(0), R.old.get(0), HAS_KL ? R.ref.get(0) : 0.0f, k, c, gi);
         add(cls_a, R.m.valid(0) ? c : 0.0f, cs_a);
@@ -927,6 +971,7 @@ __global__ void __launch_bounds__(kThreads, sizeof(T) == 2 ? 4 : 1) grpo_kernel(
     constexpr int MODE = kModeGRPO;
     constexpr uint32_t kTileV = kThreads * VEC;
     constexpr uint32_t kBits = ONE_TILE ? 1u : uint32_t(kBitTilesGrpo);
+    constexpr int E = chunk_slots<T, VEC>();   // slots per chunk of a lane
     __shared__ float red_f[3 * kWaves];
     __shared__ uint32_t red_u[8 * kWaves];
     __shared__ uint32_t list[kThreads + 1];      // workers whose entries workgroup 0 computes itself
@@ -984,19 +1029,19 @@ __global__ void __launch_bounds__(kThreads, sizeof(T) == 2 ? 4 : 1) grpo_kernel(
         const uint32_t s0 = w * kTileV, s1 = s0 + kTileV < slots ? s0 + kTileV : slots;
         const uint32_t s = s0 + lane_off;
         Lane<T, VEC> L;
-        (void)load_lane_count<T, MODE, HAS_KL, VEC, VEC == kVecSmall>(a, s, L);
+        (void)load_lane_count<T, MODE, HAS_KL, VEC, VEC == kVecSmall, true, E>(a, s, L);
         const uint32_t bits = L.m.bits();
         const uint32_t rf = row_of(a, s0), rl = row_of(a, s1 - 1u), nrows = rl - rf + 1u;
-        const uint32_t ends = block_sum(lane_ends<VEC>(a, s, bits, rf, rl), red_u);
+        const uint32_t ends = block_sum(lane_ends_chunked<VEC, E>(a, s, bits, rf, rl), red_u);
         const uint32_t n_first = ends & 0xFFFFu, n_last = rl != rf ? ends >> 16 : n_first;
         if (OWN && threadIdx.x == kHeadThread) publish(view, cnt_off(w), tg, n_first);
         if (OWN && rl != rf && threadIdx.x == kTailThread) publish(view, tail_off(w), tg, n_last);
-        if (nrows > 2u) tile_rows<VEC>(a, s, bits, rf, nrows, row_lds);
+        if (nrows > 2u) tile_rows<VEC, E>(a, s, bits, rf, nrows, row_lds);
         else __syncthreads();                  // row_lds may still hold scales being read
         row_scales<OWN>(a, s0, rf, nrows, 0u, 0u, rf, rl, row_lds);
         float h, t, in;
         float g[VEC];
-        grpo_lane<T, HAS_KL, VEC>(a, s, L, rf, rl, 1.0f, 1.0f, scale, rf, h, t, in, g);
+        grpo_lane<T, HAS_KL, VEC, E>(a, s, L, rf, rl, 1.0f, 1.0f, scale, rf, h, t, in, g);
         float v[3] = {h, t, in};
         block_sum_n<3>(v, red_f);
         if (OWN) publish_sums(w, n_first, n_last, v, rl != rf);
@@ -1006,8 +1051,11 @@ __global__ void __launch_bounds__(kThreads, sizeof(T) == 2 ? 4 : 1) grpo_kernel(
             const float f1 = rl != rf ? row_scale(a, row_count(w, rl, n_last)) : f0;
             const uint32_t e0 = (rf + 1u) * TL, b1 = rl * TL;
 #pragma unroll
-            for (int i = 0; i < VEC; ++i) g[i] *= s + i < e0 ? f0 : (rl != rf && s + i >= b1 ? f1 : 1.0f);
-            store_grad<T, VEC, false>(a, s, L.m, g, 1.0f);
+            for (int i = 0; i < VEC; ++i) {
+                const uint32_t p = chunk_slot<VEC, E>(s, i / E) + uint32_t(i % E);   // slot of element i
+                g[i] *= p < e0 ? f0 : (rl != rf && p >= b1 ? f1 : 1.0f);
+            }
+            store_grad<T, VEC, false, false, true, E>(a, s, L.m, g, 1.0f);
         }
         return GrpoPart{n_first, n_last, v[0], v[1], v[2]};
     };
@@ -1079,24 +1127,25 @@ __global__ void __launch_bounds__(kThreads, sizeof(T) == 2 ? 4 : 1) grpo_kernel(
         float v[3] = {0.0f, 0.0f, 0.0f};
         uint32_t cached_r = 0xFFFFFFFFu, cached_n = 0;
         Mask<VEC> next;
-        if (n_bits == 0) next.template load<true>(a.mask, t_lo * kTileV + lane_off, slots);
+        if (n_bits == 0) next.template load<true, true, E>(a.mask, t_lo * kTileV + lane_off, slots);
         for (uint32_t j = 0; j < nt; ++j) {
             const uint32_t s0 = (t_lo + j) * kTileV, s1 = s0 + kTileV < slots ? s0 + kTileV : slots;
             const uint32_t s = s0 + lane_off;
             Lane<T, VEC> L;
-            if (j < n_bits) L.m.from_bits(mask_bits[j * kThreads + threadIdx.x]);
+            if (j < n_bits) L.m.from_bits(chunk_bits<VEC, E>(mask_bits + j * kThreads));
             else L.m = next;
-            if (j + 1u < nt && j + 1u >= n_bits) next.template load<true>(a.mask, s0 + kTileV + lane_off, slots);
-            load_planes<T, MODE, HAS_KL, VEC, true>(a, s, L);
+            if (j + 1u < nt && j + 1u >= n_bits)
+                next.template load<true, true, E>(a.mask, s0 + kTileV + lane_off, slots);
+            load_planes<T, MODE, HAS_KL, VEC, true, true, E>(a, s, L);
             const uint32_t rf = row_of(a, s0), rl = row_of(a, s1 - 1u), nrows = rl - rf + 1u;
             uint32_t first = 0, last = 0;      // the tile's counts of its first and last row
             if (nrows > 2u) {
-                tile_rows<VEC>(a, s, L.m.bits(), rf, nrows, row_lds);
+                tile_rows<VEC, E>(a, s, L.m.bits(), rf, nrows, row_lds);
                 first = row_lds[0];
                 last = row_lds[nrows - 1u];
             } else {
                 const uint32_t ends =
-                    local_rows ? block_sum(lane_ends<VEC>(a, s, L.m.bits(), rf, rl), red_u) : pieces[j];
+                    local_rows ? block_sum(lane_ends_chunked<VEC, E>(a, s, L.m.bits(), rf, rl), red_u) : pieces[j];
                 first = ends & 0xFFFFu;
                 last = rl != rf ? ends >> 16 : first;
             }
@@ -1126,11 +1175,11 @@ __global__ void __launch_bounds__(kThreads, sizeof(T) == 2 ? 4 : 1) grpo_kernel(
             row_scales<OWN>(a, s0, rf, nrows, first, last, r0, r1, row_lds);
             float h, t, in;
             float g[VEC];
-            grpo_lane<T, HAS_KL, VEC>(a, s, L, r0, r1, f0, f1, scale, rf, h, t, in, g);
+            grpo_lane<T, HAS_KL, VEC, E>(a, s, L, r0, r1, f0, f1, scale, rf, h, t, in, g);
             v[0] += h;
             v[1] += t;
             v[2] += in;
-            if constexpr (OWN && WRITE_GRAD) store_grad<T, VEC, false>(a, s, L.m, g, 1.0f);
+            if constexpr (OWN && WRITE_GRAD) store_grad<T, VEC, false, false, true, E>(a, s, L.m, g, 1.0f);
         }
         block_sum_n<3>(v, red_f);
         if (OWN) {
