@@ -303,6 +303,37 @@ def test_every_kernel_shape(op):
     assert kinds == {"one-tile vec4", "one-tile vec16", "stream"}, kinds
 
 
+# 16-slot lanes take their slots as chunks of 16 bytes of a plane (two of 8
+# slots for fp16/bf16, four of 4 for fp32), a wavefront access apart.  Odd
+# seq_len puts row ends inside chunks (the per-slot path), random masks leave
+# some chunks of a lane valid and others not (planes loaded per chunk), in
+# the wide one-tile kernel (257 x 4093) and the striding one (1000 x 8191).
+@pytest.mark.parametrize("dtype", ["fp32", "bf16", "fp16"])
+@pytest.mark.parametrize("bs,T", [(257, 4093), (1000, 8191)])
+def test_chunked_lanes_rows_ending_inside_chunks(dtype, bs, T):
+    kinds = set()
+    for op in ("bnpo", "grpo"):
+        grid, vec, tiles = rl.launch_shape(bs, T, TORCH_DT[dtype], op)
+        assert vec == 16, (op, grid, vec, tiles)
+        kinds.add(_shape_kind(grid, vec, tiles))
+        for mask in ("random", "prefix"):
+            x = _custom(op, dtype, bs, T, mask, seed=bs + T, lo=0)
+            what = f"chunked {op} {dtype} {bs}x{T} {mask} grid={grid} tiles={tiles}"
+            print("[parity]", what, flush=True)
+            first = assert_policy_parity(op, x, 0.04, 0.2, 0.28, what)
+            fwd = assert_policy_parity(op, x, 0.04, 0.2, 0.28, what + " fwd", fused=False)
+            assert torch.equal(fwd[0], first[0]), what
+    w = synthetic.Workload("edge", "rkl", dtype, "bool", bs, T, 1, T, seed=bs + T)
+    x = synthetic.inputs(w)
+    x["mask"] = torch.from_numpy(np.random.default_rng(bs + T).random((bs, T)) < 0.6)
+    what = f"chunked rkl {dtype} {bs}x{T} random"
+    print("[parity]", what, flush=True)
+    first = assert_rkl_parity(x, what)
+    fwd = assert_rkl_parity(x, what + " fwd", fused=False)
+    assert torch.equal(fwd[0], first[0]), what
+    assert kinds <= {"one-tile vec16", "stream"}, kinds
+
+
 @pytest.mark.parametrize("bs,T", [(2048, 4096), (8192, 1024)])
 def test_grpo_striding_kernel_repeats_bitwise(bs, T):
     # Each worker streams several tiles and rebuilds the per-row scales in LDS
