@@ -166,9 +166,10 @@ struct Shape {
 // coordinating workgroup plus one worker per tile whenever that many
 // workgroups of the one-tile kernel are co-resident (small problems take the
 // narrow lane so that every compute unit gets a tile), else the striding
-// kernel, each workgroup a worker over a contiguous run of `per` tiles: per is
-// the fewest tiles per worker that fit the co-resident workgroups, and the grid
-// the runs it takes (so that every worker has one).
+// kernel: per is the fewest tiles per worker that fit the co-resident
+// workgroups, and the grid the runs of `per` tiles it takes (so that every
+// worker has one).  GRPO's workers own those contiguous runs; BNPO's and
+// reverse-KL's share the tiles out in groups (Sweep in loss_kernels_impl.h).
 int launch_shape(const DeviceInfo* info, int dtype, int mode, int64_t slots, Shape* out) {
     const int64_t large_tile = int64_t(rlpl::kThreads) * rlpl::kVecLarge;
     const int64_t small_tile = int64_t(rlpl::kThreads) * rlpl::kVecSmall;

@@ -124,7 +124,7 @@ struct Args {
     Workspace* ws;
     int64_t slots;         // bs * seq_len  (< 2^31)
     uint32_t tiles;        // ceil(slots / (kThreads * VEC))
-    uint32_t per;          // striding kernels: tiles per worker (each worker owns a contiguous run)
+    uint32_t per;          // striding GRPO kernels: tiles per worker (each worker owns a contiguous run)
     int32_t seq_len;
     int32_t bs;
     uint32_t row_magic;    // s / seq_len == (s * row_magic) >> row_shift for every s < 2^31

@@ -334,6 +334,25 @@ def test_chunked_lanes_rows_ending_inside_chunks(dtype, bs, T):
     assert kinds <= {"one-tile vec16", "stream"}, kinds
 
 
+def test_striding_sweep_full_rounds_and_remainder():
+    # The striding BNPO and reverse-KL workers take groups of eight tiles side
+    # by side, then split what is left into one contiguous piece each: 8300 x
+    # 4099 has more tiles than eight per worker and a remainder, and rows that
+    # cross tiles.
+    bs, T = 8300, 4099
+    grid, vec, tiles = rl.launch_shape(bs, T, torch.bfloat16, "bnpo")
+    assert vec == 16 and tiles >= 8 * grid and tiles % (8 * grid) != 0, (grid, tiles)
+    x = _custom("bnpo", "bf16", bs, T, "prefix", seed=7, lo=0)
+    what = f"sweep bnpo {bs}x{T} grid={grid} tiles={tiles}"
+    print("[parity]", what, flush=True)
+    first = assert_policy_parity("bnpo", x, 0.04, 0.2, 0.28, what)
+    fwd = assert_policy_parity("bnpo", x, 0.04, 0.2, 0.28, what + " fwd", fused=False)
+    assert torch.equal(fwd[0], first[0]), what
+    r = {"student": x["policy"], "teacher": x["ref"], "mask": x["mask"] != 0}
+    print("[parity] sweep rkl", flush=True)
+    assert_rkl_parity(r, "sweep rkl")
+
+
 @pytest.mark.parametrize("bs,T", [(2048, 4096), (8192, 1024)])
 def test_grpo_striding_kernel_repeats_bitwise(bs, T):
     # Each worker streams several tiles and rebuilds the per-row scales in LDS
