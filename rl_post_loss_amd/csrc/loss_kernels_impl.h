@@ -202,6 +202,15 @@ __device__ __forceinline__ uint32_t row_of(const Args& a, uint32_t s) {
     return uint32_t((uint64_t(s) * a.row_magic) >> a.row_shift);
 }
 
+// The row and position that a lane chunk starting at slot sc takes its row's
+// coefficients from: a chunk that starts past the last slot (the last tile's
+// tail, all of it masked) takes those of the last slot, so that no row index
+// reaches bs (no read past the advantages, no scale of a row outside the tile).
+__device__ __forceinline__ uint32_t chunk_row_slot(const Args& a, uint32_t sc) {
+    const uint32_t last = uint32_t(a.slots) - 1u;
+    return sc < last ? sc : last;
+}
+
 template <typename T>
 __device__ __forceinline__ float load_adv(const void* adv, uint32_t r) {
     if constexpr (sizeof(T) == 4) return static_cast<const float*>(adv)[r];
@@ -331,7 +340,7 @@ __device__ __forceinline__ float lane_terms(const Args& a, uint32_t s, const Lan
     bool one_row = true;         // every chunk within one row
 #pragma unroll
     for (int c = 0; c < C; ++c) {
-        const uint32_t sc = chunk_slot<VEC, E>(s, c);
+        const uint32_t sc = chunk_row_slot(a, chunk_slot<VEC, E>(s, c));
         r[c] = row_of(a, sc);
         t[c] = sc - r[c] * T_len;
         one_row = one_row && t[c] + E <= T_len;
@@ -372,7 +381,7 @@ __device__ __forceinline__ float lane_terms(const Args& a, uint32_t s, const Lan
 #pragma unroll 1
         for (int i = 0; i < VEC; ++i) {
             if ((i & (E - 1)) == 0) {
-                const uint32_t sc = chunk_slot<VEC, E>(s, i / E);
+                const uint32_t sc = chunk_row_slot(a, chunk_slot<VEC, E>(s, i / E));
                 rr = row_of(a, sc);
                 tt = sc - rr * T_len;
                 if constexpr (MODE != kModeRKL) A = load_adv<T>(a.adv, rr);
@@ -920,7 +929,7 @@ __device__ __forceinline__ void grpo_lane(const Args& a, uint32_t s, const Lane<
     bool one_row = true;                      // every chunk within one row
 #pragma unroll
     for (int c = 0; c < C; ++c) {
-        const uint32_t sc = chunk_slot<VEC, E>(s, c);
+        const uint32_t sc = chunk_row_slot(a, chunk_slot<VEC, E>(s, c));
         rc[c] = row_of(a, sc);
         pc[c] = sc - rc[c] * TL;
         one_row = one_row && pc[c] + E <= TL;
@@ -964,7 +973,7 @@ __device__ __forceinline__ void grpo_lane(const Args& a, uint32_t s, const Lane<
 #pragma unroll 1
     for (int i = 0; i < VEC; ++i) {
         if ((i & (E - 1)) == 0) {
-            const uint32_t sc = chunk_slot<VEC, E>(s, i / E);
+            const uint32_t sc = chunk_row_slot(a, chunk_slot<VEC, E>(s, i / E));
             r = row_of(a, sc);
             pos = sc - r * TL;
             k = row_coef<kModeGRPO>(a, load_adv<T>(a.adv, r), 1.0f, 1.0f);
