@@ -334,6 +334,23 @@ def test_chunked_lanes_rows_ending_inside_chunks(dtype, bs, T):
     assert kinds <= {"one-tile vec16", "stream"}, kinds
 
 
+# Rows of a few slots in 16-slot lanes: nearly every chunk holds a row end
+# (the per-slot path of every lane), in the wide one-tile kernel and the
+# striding one; GRPO's tiles then touch hundreds of rows each.
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("bs,T", [(300_000, 7), (2_100_000, 3)])
+def test_chunked_lanes_tiny_rows(dtype, bs, T):
+    for op in ("bnpo", "grpo"):
+        grid, vec, tiles = rl.launch_shape(bs, T, TORCH_DT[dtype], op)
+        assert vec == 16, (op, grid, vec, tiles)
+        x = _custom(op, dtype, bs, T, "random", seed=bs + T, lo=0)
+        what = f"tiny rows {op} {dtype} {bs}x{T} grid={grid} tiles={tiles}"
+        print("[parity]", what, flush=True)
+        first = assert_policy_parity(op, x, 0.04, 0.2, 0.28, what)
+        fwd = assert_policy_parity(op, x, 0.04, 0.2, 0.28, what + " fwd", fused=False)
+        assert torch.equal(fwd[0], first[0]), what
+
+
 def test_striding_sweep_full_rounds_and_remainder():
     # The striding BNPO and reverse-KL workers take groups of eight tiles side
     # by side, then split what is left into one contiguous piece each: 8300 x
