@@ -155,7 +155,7 @@ int launch(const void* kernel, const A& a, dim3 grid, hipStream_t stream, int th
 }
 
 struct Shape {
-    int kernel;      // rlpl::kShapeSmall / kShapeLarge / kShapeStream
+    int kernel;      // rlpl::kShapeSmall / kShapeLarge / kShapeStream / kShapeStreamNt
     int vec;
     uint32_t tiles;
     int64_t grid;
@@ -170,7 +170,8 @@ struct Shape {
 // workgroups, and the grid the runs of `per` tiles it takes (so that every
 // worker has one).  GRPO's workers own those contiguous runs; BNPO's and
 // reverse-KL's share the tiles out in groups (Sweep in loss_kernels_impl.h).
-int launch_shape(const DeviceInfo* info, int dtype, int mode, int64_t slots, Shape* out) {
+// nt_grad: a striding launch stores its gradient non-temporally.
+int launch_shape(const DeviceInfo* info, int dtype, int mode, int64_t slots, bool nt_grad, Shape* out) {
     const int64_t large_tile = int64_t(rlpl::kThreads) * rlpl::kVecLarge;
     const int64_t small_tile = int64_t(rlpl::kThreads) * rlpl::kVecSmall;
     const int* cap = info->grid_cap[dtype][mode];
@@ -181,14 +182,23 @@ int launch_shape(const DeviceInfo* info, int dtype, int mode, int64_t slots, Sha
     } else if (large_tiles + 1 <= cap[rlpl::kShapeLarge]) {
         *out = {rlpl::kShapeLarge, rlpl::kVecLarge, uint32_t(large_tiles), large_tiles + 1, 1};
     } else {
-        const int64_t c = cap[rlpl::kShapeStream];
+        const int shape = nt_grad ? rlpl::kShapeStreamNt : rlpl::kShapeStream;
+        const int64_t c = cap[shape];
         if (c < 1) return RLPL_ERR_DEVICE;
         const int64_t per = (large_tiles + c - 1) / c;
         if (mode == kModeGRPO && per > rlpl::kMaxPer) return RLPL_ERR_SHAPE;
-        *out = {rlpl::kShapeStream, rlpl::kVecLarge, uint32_t(large_tiles), (large_tiles + per - 1) / per,
-                uint32_t(per)};
+        *out = {shape, rlpl::kVecLarge, uint32_t(large_tiles), (large_tiles + per - 1) / per, uint32_t(per)};
     }
     return RLPL_OK;
+}
+
+// Whether a fwd+bwd launch stores its gradient non-temporally: from
+// kNtGradBytes of mask, planes and gradient on (whole arrays).
+bool nt_grad(int mode, bool write_grad, bool has_kl, int64_t slots, int dtype) {
+    if (!write_grad) return false;
+    const int64_t planes = mode == kModeRKL ? 2 : (has_kl ? 3 : 2);
+    const int64_t e = int64_t(elem_bytes(dtype));
+    return slots * (1 + planes * e + e) >= rlpl::kNtGradBytes;
 }
 
 // Shared tail of every entry point: launch shape, row divisor and the launch.
@@ -197,7 +207,7 @@ int run(int mode, bool write_grad, bool has_kl, Args& a, int dtype, hipStream_t 
     int st = current_device(&info);
     if (st != RLPL_OK) return st;
     Shape sh;
-    st = launch_shape(info, dtype, mode, a.slots, &sh);
+    st = launch_shape(info, dtype, mode, a.slots, nt_grad(mode, write_grad, has_kl, a.slots, dtype), &sh);
     if (st != RLPL_OK) return st;
     const void* kernel = rlpl::pick_kernel(dtype, mode, has_kl, write_grad, sh.kernel);
     if (!kernel) return RLPL_ERR_DTYPE;
@@ -735,7 +745,8 @@ int rlpl_launch_shape(int64_t bs, int64_t seq_len, int dtype, int op, int* grid_
     int st = current_device(&info);
     if (st != RLPL_OK) return st;
     Shape sh;
-    st = launch_shape(info, dtype, mode, bs * seq_len, &sh);
+    const bool fused = op == RLPL_OP_BNPO || op == RLPL_OP_GRPO || op == RLPL_OP_RKL;
+    st = launch_shape(info, dtype, mode, bs * seq_len, nt_grad(mode, fused, true, bs * seq_len, dtype), &sh);
     if (st != RLPL_OK) return st;
     *grid_out = int(sh.grid);
     *vec_out = sh.vec;

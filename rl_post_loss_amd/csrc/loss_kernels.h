@@ -30,8 +30,16 @@ constexpr int kBitTilesRkl = 40;
 constexpr int kMaxPer = 1024;
 constexpr int kBitTilesGrpo = 12;
 // Kernel shapes: one tile per worker with the narrow or the wide lane, or the
-// wide lane striding over several tiles per worker.
-enum { kShapeSmall = 0, kShapeLarge = 1, kShapeStream = 2, kShapes = 3 };
+// wide lane striding over several tiles per worker, its gradient stored
+// through the caches or, from kNtGradBytes of inputs and gradient on,
+// non-temporally.
+enum { kShapeSmall = 0, kShapeLarge = 1, kShapeStream = 2, kShapeStreamNt = 3, kShapes = 4 };
+// Bytes of mask, planes and gradient (whole arrays) from which a striding
+// fwd+bwd launch stores its gradient non-temporally.  Measured crossover on
+// gfx950 (interleaved A/B, fused BNPO bf16 at seq_len 4096): cached stores
+// 6 % faster at 1.28 GB, non-temporal ones 1 % faster at 1.36 GB and 6-8 %
+// from 1.5 GB on; fp32 BNPO, reverse KL and GRPO cross in the same range.
+constexpr int64_t kNtGradBytes = int64_t(5) << 28;   // 1.25 GiB
 // The narrow lane is taken when a problem has fewer wide tiles than compute units.
 constexpr int kSmallTilesPerCu = 1;
 constexpr int kMaxGrid = 4096;              // upper bound on the persistent grid (gfx950: <= 256 CUs x 8)

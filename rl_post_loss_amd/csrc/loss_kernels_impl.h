@@ -476,8 +476,10 @@ __device__ __forceinline__ uint32_t chunk_bits(const uint16_t* grp) {
 // Streams a worker's tiles (`sw`): per tile, the lane's terms,
 // its count and (WRITE_GRAD) the scaled gradient.  Masks and planes are read
 // with non-temporal loads (they stream through once); the gradient is stored
-// plainly (measured: non-temporal 16-byte stores, each covering every other
-// 16 bytes of a line, wrote 13 % more bytes to HBM and ran 2 % slower).  The
+// through the caches, or non-temporally with NT_GRAD (the host's choice from
+// kNtGradBytes of inputs and gradient on: below, cached stores measured 6-20 %
+// faster, above, non-temporal ones 1-8 %; a wavefront's store covers 1 KB
+// without a gap, so either way whole lines are written).  The
 // plane loads wait for the mask, and the next tile's mask is fetched during
 // the current tile.  (Measured A/B: leaving out the per-lane range test on
 // tiles known to be in range, or keeping a second tile's planes in flight,
@@ -516,7 +518,7 @@ struct Sweep {
     }
 };
 
-template <typename T, int MODE, bool HAS_KL, bool WRITE_GRAD, int VEC>
+template <typename T, int MODE, bool HAS_KL, bool WRITE_GRAD, int VEC, bool NT_GRAD = false>
 __device__ __forceinline__ void stream_tiles(const Args& a, const Sweep& sw, float& part, uint32_t& n_lane,
                                              float scale, const uint16_t* bits = nullptr, uint32_t n_bits = 0) {
     constexpr uint32_t kTileV = kThreads * VEC;
@@ -539,7 +541,7 @@ __device__ __forceinline__ void stream_tiles(const Args& a, const Sweep& sw, flo
         n_lane += L.m.count();
         float g[VEC];
         part += lane_terms<T, MODE, HAS_KL, VEC, E>(a, s, L, nullptr, 0, scale, g);
-        if constexpr (WRITE_GRAD) store_grad<T, VEC, false, false, true, E>(a, s, L.m, g, 1.0f);
+        if constexpr (WRITE_GRAD) store_grad<T, VEC, false, NT_GRAD, true, E>(a, s, L.m, g, 1.0f);
     }
 }
 
@@ -557,7 +559,7 @@ __device__ __forceinline__ void stream_tiles(const Args& a, const Sweep& sw, flo
 // and stores the same values), and a worker that has not seen N within the
 // release limit gathers it itself.  Every such value is computed by the same
 // code as the worker's own, so the results are bit-identical either way.
-template <typename T, int MODE, bool HAS_KL, bool WRITE_GRAD, int VEC, bool ONE_TILE>
+template <typename T, int MODE, bool HAS_KL, bool WRITE_GRAD, int VEC, bool ONE_TILE, bool NT_GRAD = false>
 __global__ void __launch_bounds__(kThreads) loss_kernel(const Args a) {
     constexpr uint32_t kTileV = kThreads * VEC;
     constexpr int E = chunk_slots<T, VEC>();   // slots per chunk of a lane
@@ -717,7 +719,8 @@ __global__ void __launch_bounds__(kThreads) loss_kernel(const Args a) {
                 N = await_release(view, lim.release_now(), tg, word, gather_counts);
             }
             uint32_t unused_n = 0;
-            stream_tiles<T, MODE, HAS_KL, true, VEC>(a, sw, part, unused_n, inv_count<MODE>(N), mask_bits, n_bits);
+            stream_tiles<T, MODE, HAS_KL, true, VEC, NT_GRAD>(a, sw, part, unused_n, inv_count<MODE>(N), mask_bits,
+                                                          n_bits);
             const float part_wg = block_sum(part, red_f);
             if (threadIdx.x == kPartialThread) publish(view, par_off(worker), tg, __float_as_uint(part_wg));
         } else {
@@ -1010,7 +1013,7 @@ __device__ __forceinline__ void grpo_lane(const Args& a, uint32_t s, const Lane<
 // which it walks twice: the masks first (eight loads in flight; the counts of
 // each tile's first and last row, and the mask bits of its first
 // kBitTilesGrpo tiles), then the planes; workgroup 0 then also closes the rows.
-template <typename T, bool HAS_KL, bool WRITE_GRAD, int VEC, bool ONE_TILE>
+template <typename T, bool HAS_KL, bool WRITE_GRAD, int VEC, bool ONE_TILE, bool NT_GRAD = false>
 // (16-bit planes: at most 128 VGPRs, four workgroups per compute unit, which
 // the striding kernel's LDS allows; fp32 planes need more registers.)
 __global__ void __launch_bounds__(kThreads, sizeof(T) == 2 ? 4 : 1) grpo_kernel(const Args a) {
@@ -1225,7 +1228,7 @@ __global__ void __launch_bounds__(kThreads, sizeof(T) == 2 ? 4 : 1) grpo_kernel(
             v[0] += h;
             v[1] += t;
             v[2] += in;
-            if constexpr (OWN && WRITE_GRAD) store_grad<T, VEC, false, false, true, E>(a, s, L.m, g, 1.0f);
+            if constexpr (OWN && WRITE_GRAD) store_grad<T, VEC, false, NT_GRAD, true, E>(a, s, L.m, g, 1.0f);
         }
         block_sum_n<3>(v, red_f);
         if (OWN) {
@@ -1464,6 +1467,11 @@ static const void* kernel_ptr(int shape) {
     case kShapeSmall: return reinterpret_cast<const void*>(&loss_kernel<T, MODE, HAS_KL, WRITE_GRAD, kVecSmall, true>);
     case kShapeLarge: return reinterpret_cast<const void*>(&loss_kernel<T, MODE, HAS_KL, WRITE_GRAD, kVecLarge, true>);
     case kShapeStream: return reinterpret_cast<const void*>(&loss_kernel<T, MODE, HAS_KL, WRITE_GRAD, kVecLarge, false>);
+    case kShapeStreamNt:   // (no gradient: the same kernel as kShapeStream)
+        if constexpr (WRITE_GRAD)
+            return reinterpret_cast<const void*>(&loss_kernel<T, MODE, HAS_KL, true, kVecLarge, false, true>);
+        else
+            return reinterpret_cast<const void*>(&loss_kernel<T, MODE, HAS_KL, false, kVecLarge, false>);
     }
     return nullptr;
 }
@@ -1474,6 +1482,11 @@ static const void* grpo_ptr(int shape) {
     case kShapeSmall: return reinterpret_cast<const void*>(&grpo_kernel<T, HAS_KL, WRITE_GRAD, kVecSmall, true>);
     case kShapeLarge: return reinterpret_cast<const void*>(&grpo_kernel<T, HAS_KL, WRITE_GRAD, kVecLarge, true>);
     case kShapeStream: return reinterpret_cast<const void*>(&grpo_kernel<T, HAS_KL, WRITE_GRAD, kVecLarge, false>);
+    case kShapeStreamNt:
+        if constexpr (WRITE_GRAD)
+            return reinterpret_cast<const void*>(&grpo_kernel<T, HAS_KL, true, kVecLarge, false, true>);
+        else
+            return reinterpret_cast<const void*>(&grpo_kernel<T, HAS_KL, false, kVecLarge, false>);
     }
     return nullptr;
 }

@@ -370,6 +370,78 @@ def test_striding_sweep_full_rounds_and_remainder():
     assert_rkl_parity(r, "sweep rkl")
 
 
+# From this many bytes of mask, planes and gradient (whole arrays) on, a
+# striding fwd+bwd launch stores its gradient non-temporally (the library's
+# kNtGradBytes, 1.25 GiB): these launches take that kernel.
+NT_GRAD_BYTES = 5 << 28
+
+
+def _sample_rows(bs, seed):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, bs - 1], rng.integers(0, bs, 10)]))
+
+
+@pytest.mark.parametrize("op,name,bs,T", [("bnpo", "bnpo_bf16_64x4096", 40960, 4096),
+                                          ("grpo", "grpo_fp16_128x2048", 40960, 4096),
+                                          ("rkl", "rkl_bf16_256x8192", 24576, 8192)])
+def test_streaming_sizes_non_temporal_gradient(op, name, bs, T):
+    # At these sizes the oracle runs on sampled rows alone: each row's gradient
+    # depends on the other rows only through the normaliser (the global count
+    # for BNPO and reverse KL, the row count for GRPO), so the oracle's rows are
+    # rescaled from their own to the launch's.  The loss is checked against the
+    # forward-only kernel (the same partition, so bit-equal), the count exactly,
+    # and every masked slot's gradient is +0.
+    w = synthetic.WORKLOADS[name]
+    w = w.with_(bs=bs, seq_len=T, len_lo=min(w.len_lo, T), len_hi=T, name=f"{name}@{bs}x{T}")
+    g = synthetic.device_policy_inputs(w, "cuda:0")
+    e = g["policy"].element_size()
+    planes = 2 if op == "rkl" else 3
+    assert bs * T * (1 + planes * e + e) >= NT_GRAD_BYTES
+    what = f"non-temporal gradient {op} {bs}x{T}"
+    print("[parity]", what, flush=True)
+    rows = _sample_rows(bs, bs + T)
+    dt = g["policy"].dtype
+    if op == "rkl":
+        mask = g["mask"] != 0
+        loss, grad, n = rl.reverse_kl(g["policy"], g["ref"], mask, return_n_valid=True)
+        loss_f, n_f = rl.reverse_kl_fwd(g["policy"], g["ref"], mask, return_n_valid=True)
+        torch.cuda.synchronize()
+        N = int(torch.count_nonzero(mask))
+        assert int(n.cpu()[0]) == N and int(n_f.cpu()[0]) == N, what
+        assert torch.equal(loss, loss_f), what
+        sub = {"student": g["policy"][rows].cpu(), "teacher": g["ref"][rows].cpu(), "mask": mask[rows].cpu()}
+        ref = oracle.rkl(sub["student"], sub["teacher"], sub["mask"])
+        want = ref.grad * (max(ref.n_valid, 1) / max(N, 1))
+        mag = rkl_grad_magnitude(sub["student"], sub["teacher"], 1.0 / max(N, 1))
+        check_grad(grad[rows].cpu(), want, dt, what, mag=mag)
+    else:
+        out = gpu_policy(op, True, g, w.beta, w.epsilon, w.epsilon_high)
+        out_f = gpu_policy(op, False, g, w.beta, w.epsilon, w.epsilon_high)
+        loss, grad, n = out
+        assert torch.equal(loss, out_f[0]), what
+        sub = {k: g[k][rows].cpu() for k in ("policy", "old", "ref", "advantages", "mask")}
+        ref = oracle_policy(op, sub, w.beta, w.epsilon, w.epsilon_high)
+        if op == "bnpo":
+            N = int(torch.count_nonzero(g["mask"]))
+            assert int(n.cpu()[0]) == N and int(out_f[-1].cpu()[0]) == N, what
+            want = ref.grad * (max(ref.n_valid, 1) / max(N, 1))
+            scale = 1.0 / max(N, 1)
+        else:
+            counts = torch.count_nonzero(g["mask"], dim=1).cpu().numpy().astype(np.int64)
+            np.testing.assert_array_equal(n.cpu().numpy().astype(np.int64), counts, err_msg=what)
+            np.testing.assert_array_equal(counts[rows], ref.n_valid, err_msg=what)
+            want = ref.grad * (len(rows) / bs)
+            scale = (1.0 / (np.maximum(ref.n_valid, 1) * bs))[:, None]
+        kinks = kink_tokens(sub["policy"], sub["old"], sub["mask"], w.epsilon_high)
+        alt = kink_alternative(want, sub["policy"], sub["old"], sub["advantages"], sub["mask"], w.epsilon_high,
+                               scale)
+        mag = policy_grad_magnitude(sub["policy"], sub["old"], sub["ref"], sub["advantages"], f32(w.beta), scale)
+        check_grad(grad[rows].cpu(), want, dt, what, alt, kinks, mag)
+        mask = g["mask"] != 0
+    bits = grad.view(torch.int16 if e == 2 else torch.int32)
+    assert not bool(torch.any(bits[~mask] != 0)), what + ": a masked slot is not +0"
+
+
 @pytest.mark.parametrize("bs,T", [(2048, 4096), (8192, 1024)])
 def test_grpo_striding_kernel_repeats_bitwise(bs, T):
     # Each worker streams several tiles and rebuilds the per-row scales in LDS
